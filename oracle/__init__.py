@@ -1,0 +1,129 @@
+"""CPU oracle for the selective state-space scan -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, the smoke check in ``__graft_entry__`` and the ``cpu_baseline``
+leg of ``bench.py`` may import this package.  The GPU library never imports,
+links or calls it, and the two share no code.
+
+* ``ssd_scan``, ``ssd_decode``, ``selective_scan``: the sequential float64
+  recurrences in ``ssd_oracle.c`` (the definition of what the scan computes).
+* ``forms``: independent numpy float64 formulations used to pin the sequential
+  oracle -- the quadratic "dual" form and the chunked block decomposition.
+
+Parity status: every function is pinned by the CPU tests in
+``tests/test_oracle_pins.py`` (closed forms, the dual form, the block
+decomposition, state hand-off, linearity, reductions between the scan
+variants); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import time
+
+import numpy as np
+
+from . import forms  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssd_oracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+
+
+def build(verbose=False):
+    """Compile ssd_oracle.c with gcc (-O2, no fast-math, OpenMP)."""
+    from .build import build_oracle
+    build_oracle(verbose=verbose)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        build()
+    lib = ctypes.CDLL(LIB_PATH)
+    i = ctypes.c_int
+    lib.oracle_ssd_scan.argtypes = [i] * 7 + [_dp] * 9
+    lib.oracle_ssd_scan.restype = None
+    lib.oracle_ssd_decode.argtypes = [i] * 6 + [_dp] * 8
+    lib.oracle_ssd_decode.restype = None
+    lib.oracle_selective_scan.argtypes = [i] * 5 + [_dp] * 9
+    lib.oracle_selective_scan.restype = None
+    lib.oracle_threads.restype = ctypes.c_int
+    lib.oracle_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return _load().oracle_threads()
+
+
+def _f64(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(_dp)
+
+
+last_seconds = 0.0  # wall time of the last oracle call's compute
+
+
+def ssd_scan(x, dt, A, B, C, D=None, h0=None, dt_softplus=True, return_final_state=False):
+    """Sequential fp64 SSD scan.  Shapes: x [b,L,H,P], dt [b,L,H], A [H],
+    B, C [b,L,G,N], D [H] or None, h0 [b,H,N,P] or None."""
+    global last_seconds
+    lib = _load()
+    x, dt, A, B, C, D, h0 = map(_f64, (x, dt, A, B, C, D, h0))
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert dt.shape == (b, L, H) and A.shape == (H,)
+    assert B.shape == (b, L, G, N) and C.shape == B.shape and H % G == 0
+    y = np.empty_like(x)
+    hf = np.empty((b, H, N, P)) if return_final_state else None
+    t0 = time.perf_counter()
+    lib.oracle_ssd_scan(b, L, H, P, N, G, int(bool(dt_softplus)), _ptr(x), _ptr(dt), _ptr(A),
+                        _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y), _ptr(hf))
+    last_seconds = time.perf_counter() - t0
+    return (y, hf) if return_final_state else y
+
+
+def ssd_decode(x, dt, A, B, C, D, state, dt_softplus=True):
+    """One fp64 decode step.  x [b,H,P], dt [b,H], B, C [b,G,N], state [b,H,N,P].
+    Returns (y, new_state); the input state array is not modified."""
+    global last_seconds
+    lib = _load()
+    x, dt, A, B, C, D = map(_f64, (x, dt, A, B, C, D))
+    st = np.array(state, dtype=np.float64, order="C", copy=True)
+    b, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    assert st.shape == (b, H, N, P) and dt.shape == (b, H) and H % G == 0
+    y = np.empty_like(x)
+    t0 = time.perf_counter()
+    lib.oracle_ssd_decode(b, H, P, N, G, int(bool(dt_softplus)), _ptr(x), _ptr(dt), _ptr(A),
+                          _ptr(B), _ptr(C), _ptr(D), _ptr(st), _ptr(y))
+    last_seconds = time.perf_counter() - t0
+    return y, st
+
+
+def selective_scan(u, delta, A, B, C, D=None, z=None, delta_softplus=True,
+                   return_final_state=False):
+    """Sequential fp64 Mamba-1 scan.  u, delta, z [b,L,dim]; A [dim,N];
+    B, C [b,L,N]; D [dim] or None."""
+    global last_seconds
+    lib = _load()
+    u, delta, A, B, C, D, z = map(_f64, (u, delta, A, B, C, D, z))
+    b, L, dim = u.shape
+    N = A.shape[1]
+    assert A.shape == (dim, N) and B.shape == (b, L, N) and C.shape == B.shape
+    out = np.empty_like(u)
+    hf = np.empty((b, dim, N)) if return_final_state else None
+    t0 = time.perf_counter()
+    lib.oracle_selective_scan(b, L, dim, N, int(bool(delta_softplus)), _ptr(u), _ptr(delta),
+                              _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(out), _ptr(hf))
+    last_seconds = time.perf_counter() - t0
+    return (out, hf) if return_final_state else out

@@ -1,0 +1,147 @@
+"""Independent float64 numpy formulations of the SSD scan -- TEST INFRASTRUCTURE.
+
+These do not call the sequential oracle; they are other ways of writing the
+same result, used to pin it.
+
+* ``ssd_dual``: the quadratic ("dual", attention-like) form Y = M X with a
+  causal semiseparable M, page "5.3 텐서 병렬화(Tensor Parallelism) 지원과 대규모
+  클러스터 학습", §3 and §3.1:
+      M[t, s] = (C_t · B_s) · exp(Σ_{k=s+1..t} Δ_k A) · Δ_s     for s <= t, 0 otherwise
+      y_t     = Σ_s M[t, s] x_s + exp(Σ_{k=0..t} Δ_k A) · C_tᵀ h0 + D x_t
+* ``ssd_chunked``: the block decomposition of §3.2 with chunks of length Q:
+  diagonal blocks as masked quadratic products inside each chunk, off-diagonal
+  blocks through an N x P state handed from chunk to chunk.  Stage by stage:
+      cs_i    = Σ_{k<=i} Δ_k A                 (within-chunk inclusive cumsum)
+      S_c     = Σ_i B_i exp(cs_end - cs_i) Δ_i x_iᵀ          (chunk state)
+      H_c     = exp(cs_end) H_{c-1} + S_c,  H_{-1} = h0      (state passing)
+      Y_diag  = (C Bᵀ ∘ exp(cs_i - cs_j) ∘ Δ_j, j <= i) X_c  (intra-chunk)
+      Y_off_i = exp(cs_i) C_iᵀ H_{c-1}                       (state -> output)
+      y       = Y_diag + Y_off + D x
+  The last chunk may be shorter than Q.
+* ``selective_scan_dual``: the Mamba-1 diagonal-A scan of §2.1 written as a
+  sum over source tokens, y_t = Σ_{s<=t} Σ_n C_t[n] B_s[n] exp(A[n] Σ_{k=s+1..t} Δ_k) Δ_s u_s.
+
+Only for small inputs (the dual forms build L x L matrices).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def softplus(r):
+    r = np.asarray(r, dtype=np.float64)
+    return np.where(r > 0, r + np.log1p(np.exp(-np.abs(r))), np.log1p(np.exp(np.minimum(r, 0))))
+
+
+def _causal_decay(cum):
+    """exp(cum[t] - cum[s]) for s <= t, else 0 (exponent masked before exp)."""
+    diff = cum[:, None] - cum[None, :]
+    mask = np.tril(np.ones_like(diff, dtype=bool))
+    return np.exp(np.where(mask, diff, -np.inf))
+
+
+def ssd_dual(x, dt, A, B, C, D=None, h0=None, dt_softplus=True):
+    """Returns (y, final_state) of the quadratic form."""
+    x = np.asarray(x, np.float64)
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    R = H // G
+    delta = softplus(dt) if dt_softplus else np.asarray(dt, np.float64)
+    y = np.zeros_like(x)
+    hf = np.zeros((b, H, N, P))
+    for bb in range(b):
+        for h in range(H):
+            g = h // R
+            d = delta[bb, :, h]
+            cum = np.cumsum(d * A[h])
+            Bm = np.asarray(B[bb, :, g], np.float64)
+            Cm = np.asarray(C[bb, :, g], np.float64)
+            X = x[bb, :, h]
+            M = (Cm @ Bm.T) * _causal_decay(cum) * d[None, :]
+            yy = M @ X
+            fin = (Bm * (np.exp(cum[-1] - cum) * d)[:, None]).T @ X
+            if h0 is not None:
+                s0 = np.asarray(h0[bb, h], np.float64)
+                yy += np.exp(cum)[:, None] * (Cm @ s0)
+                fin += np.exp(cum[-1]) * s0
+            if D is not None:
+                yy += D[h] * X
+            y[bb, :, h] = yy
+            hf[bb, h] = fin
+    return y, hf
+
+
+def ssd_chunked(x, dt, A, B, C, D=None, h0=None, chunk=64, dt_softplus=True,
+                return_stages=False):
+    """Block decomposition.  Returns (y, final_state) and, on request, a dict of
+    the per-chunk stages: delta, cs [b,H,K,Q] (padded with nan past the end),
+    S (chunk states) and Hprev (state entering each chunk), [b,K,H,N,P]."""
+    x = np.asarray(x, np.float64)
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    R = H // G
+    Q = chunk
+    K = (L + Q - 1) // Q
+    delta = softplus(dt) if dt_softplus else np.asarray(dt, np.float64)
+    y = np.zeros_like(x)
+    hf = np.zeros((b, H, N, P))
+    st = None
+    if return_stages:
+        st = dict(delta=np.full((b, H, K, Q), np.nan), cs=np.full((b, H, K, Q), np.nan),
+                  S=np.zeros((b, K, H, N, P)), Hprev=np.zeros((b, K, H, N, P)))
+    for bb in range(b):
+        for h in range(H):
+            g = h // R
+            state = np.zeros((N, P)) if h0 is None else np.array(h0[bb, h], np.float64)
+            for c in range(K):
+                s0, s1 = c * Q, min(L, c * Q + Q)
+                d = delta[bb, s0:s1, h]
+                cs = np.cumsum(d * A[h])
+                X = x[bb, s0:s1, h]
+                Bc = np.asarray(B[bb, s0:s1, g], np.float64)
+                Cc = np.asarray(C[bb, s0:s1, g], np.float64)
+                # diagonal block: masked quadratic form inside the chunk
+                y_diag = ((Cc @ Bc.T) * _causal_decay(cs) * d[None, :]) @ X
+                # off-diagonal blocks: state entering the chunk, read out by C
+                y_off = np.exp(cs)[:, None] * (Cc @ state)
+                y[bb, s0:s1, h] = y_diag + y_off + (D[h] * X if D is not None else 0.0)
+                # chunk state and hand-off to the next chunk
+                S_c = Bc.T @ ((np.exp(cs[-1] - cs) * d)[:, None] * X)
+                if st is not None:
+                    st["delta"][bb, h, c, :s1 - s0] = d
+                    st["cs"][bb, h, c, :s1 - s0] = cs
+                    st["S"][bb, c, h] = S_c
+                    st["Hprev"][bb, c, h] = state
+                state = np.exp(cs[-1]) * state + S_c
+            hf[bb, h] = state
+    if return_stages:
+        return y, hf, st
+    return y, hf
+
+
+def selective_scan_dual(u, delta, A, B, C, D=None, z=None, delta_softplus=True):
+    """Mamba-1 output as a causal sum over source tokens; returns (out, final_state)."""
+    u = np.asarray(u, np.float64)
+    b, L, dim = u.shape
+    N = A.shape[1]
+    dl = softplus(delta) if delta_softplus else np.asarray(delta, np.float64)
+    out = np.zeros_like(u)
+    hf = np.zeros((b, dim, N))
+    for bb in range(b):
+        Bm = np.asarray(B[bb], np.float64)
+        Cm = np.asarray(C[bb], np.float64)
+        for d in range(dim):
+            w = dl[bb, :, d] * u[bb, :, d]
+            yy = np.zeros(L)
+            for n in range(N):
+                cum = np.cumsum(dl[bb, :, d] * A[d, n])
+                Kn = Cm[:, n][:, None] * Bm[:, n][None, :] * _causal_decay(cum)
+                yy += Kn @ w
+                hf[bb, d, n] = np.sum(np.exp(cum[-1] - cum) * Bm[:, n] * w)
+            if D is not None:
+                yy += D[d] * u[bb, :, d]
+            if z is not None:
+                zz = np.asarray(z[bb, :, d], np.float64)
+                yy *= zz / (1.0 + np.exp(-zz))
+            out[bb, :, d] = yy
+    return out, hf

@@ -1,0 +1,208 @@
+/*
+ * CPU oracle for the selective state-space scan -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, sequential, float64.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this; the GPU library neither links
+ * nor calls it and shares no code, header or table with it.
+ *
+ * Sources (pages, by title and section):
+ *  [TP]  "5.3 텐서 병렬화(Tensor Parallelism) 지원과 대규모 클러스터 학습"
+ *        §2.1  selective-scan recurrence h_t = Ā_t h_{t-1} + B̄_t x_t, with
+ *              input-dependent B, C and Δ, strictly sequential in t;
+ *        §3.1  Mamba-2 restricts the state matrix to a scalar times identity,
+ *              A_t = a_t I, so all N state rows of a head share one decay;
+ *        §4.3  a zero transition (A_t = 0) forgets the previous state.
+ *  [INF] "Scaling State-Space Models on Multiple GPUs with Tensor Parallelism",
+ *        Abstract: an SSM state cache carried from prefill into decode.
+ *
+ * The pages leave Ā and B̄ undefined.  Reading used here: Ā = exp(Δ·A),
+ * B̄ = Δ·B, the output y_t = C_tᵀ h_t + D·x_t reads the state after token t's
+ * own update, and Δ = softplus(raw) when the caller asks for it.
+ *
+ * Every function here is the definition written out: one time step after
+ * another, no chunking, no reordering.  OpenMP only splits independent
+ * sequences (batch row x head, or batch row x channel block).
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#include <stddef.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* softplus(r) = log(1 + e^r), written so that neither branch overflows. */
+static double softplus(double r)
+{
+    return r > 0.0 ? r + log1p(exp(-r)) : log1p(exp(r));
+}
+
+int oracle_version(void) { return 1; }
+
+/* Number of threads a parallel region here uses (1 without OpenMP). */
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Mamba-2 SSD scan over a whole sequence ([TP] §2.1 with the scalar-identity
+ * state matrix of §3.1).  For every batch row b and head h, with group
+ * g = h / (nheads/ngroups) and the N x P state S (S = h0 or 0 before t = 0):
+ *     Δ_t      = softplus(dt[b,t,h])  (or dt itself)
+ *     S       <- exp(Δ_t·A[h]) · S + Δ_t · B[b,t,g,:] x[b,t,h,:]ᵀ
+ *     y[b,t,h] = Sᵀ C[b,t,g,:] + D[h] · x[b,t,h,:]
+ * Layouts (row-major): x, y [b][L][H][P]; dt [b][L][H]; B, C [b][L][G][N];
+ * A, D [H]; h0, hfinal [b][H][N][P].  D, h0 and hfinal may be NULL.
+ */
+void oracle_ssd_scan(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
+                     int dt_softplus, const double *x, const double *dt, const double *A,
+                     const double *B, const double *C, const double *D, const double *h0,
+                     double *y, double *hfinal)
+{
+    const int P = headdim, N = dstate, H = nheads, G = ngroups, L = seqlen;
+    const int R = H / G;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int b = 0; b < batch; ++b) {
+        for (int h = 0; h < H; ++h) {
+            const int g = h / R;
+            double *S = (double *)malloc(sizeof(double) * (size_t)N * P);
+            double *acc = (double *)malloc(sizeof(double) * (size_t)P);
+            const size_t soff = ((size_t)b * H + h) * (size_t)N * P;
+            if (h0)
+                memcpy(S, h0 + soff, sizeof(double) * (size_t)N * P);
+            else
+                memset(S, 0, sizeof(double) * (size_t)N * P);
+            for (int t = 0; t < L; ++t) {
+                const size_t row = (size_t)b * L + t;
+                const double *xt = x + (row * H + h) * P;
+                const double *Bt = B + (row * G + g) * N;
+                const double *Ct = C + (row * G + g) * N;
+                const double raw = dt[row * H + h];
+                const double delta = dt_softplus ? softplus(raw) : raw;
+                const double a = exp(delta * A[h]);
+                for (int n = 0; n < N; ++n) {
+                    const double coef = delta * Bt[n];
+                    double *Sn = S + (size_t)n * P;
+                    for (int p = 0; p < P; ++p)
+                        Sn[p] = a * Sn[p] + coef * xt[p];
+                }
+                const double d = D ? D[h] : 0.0;
+                for (int p = 0; p < P; ++p)
+                    acc[p] = d * xt[p];
+                for (int n = 0; n < N; ++n) {
+                    const double cn = Ct[n];
+                    const double *Sn = S + (size_t)n * P;
+                    for (int p = 0; p < P; ++p)
+                        acc[p] += cn * Sn[p];
+                }
+                memcpy(y + (row * H + h) * P, acc, sizeof(double) * P);
+            }
+            if (hfinal)
+                memcpy(hfinal + soff, S, sizeof(double) * (size_t)N * P);
+            free(acc);
+            free(S);
+        }
+    }
+}
+
+/*
+ * One decode step against a cached state ([INF] Abstract: the state cache
+ * carried from prefill into decode; the update is the same single step of
+ * [TP] §2.1 as above).  state [b][H][N][P] is read and overwritten;
+ * x, y [b][H][P]; dt [b][H]; B, C [b][G][N].
+ */
+void oracle_ssd_decode(int batch, int nheads, int headdim, int dstate, int ngroups,
+                       int dt_softplus, const double *x, const double *dt, const double *A,
+                       const double *B, const double *C, const double *D, double *state,
+                       double *y)
+{
+    const int P = headdim, N = dstate, H = nheads, G = ngroups;
+    const int R = H / G;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < batch; ++b) {
+        for (int h = 0; h < H; ++h) {
+            const int g = h / R;
+            const double *xt = x + ((size_t)b * H + h) * P;
+            const double *Bt = B + ((size_t)b * G + g) * N;
+            const double *Ct = C + ((size_t)b * G + g) * N;
+            double *S = state + ((size_t)b * H + h) * (size_t)N * P;
+            double *yt = y + ((size_t)b * H + h) * P;
+            const double raw = dt[(size_t)b * H + h];
+            const double delta = dt_softplus ? softplus(raw) : raw;
+            const double a = exp(delta * A[h]);
+            for (int n = 0; n < N; ++n) {
+                const double coef = delta * Bt[n];
+                for (int p = 0; p < P; ++p)
+                    S[(size_t)n * P + p] = a * S[(size_t)n * P + p] + coef * xt[p];
+            }
+            const double d = D ? D[h] : 0.0;
+            for (int p = 0; p < P; ++p)
+                yt[p] = d * xt[p];
+            for (int n = 0; n < N; ++n)
+                for (int p = 0; p < P; ++p)
+                    yt[p] += Ct[n] * S[(size_t)n * P + p];
+        }
+    }
+}
+
+/*
+ * Mamba-1 selective scan with a diagonal state matrix per channel ([TP] §2.1:
+ * input-dependent B, C, Δ; one recurrence per channel).  For batch row b and
+ * channel d, with an N-vector state s (zero before t = 0):
+ *     Δ      = softplus(delta[b,t,d])  (or delta itself)
+ *     s[n]  <- exp(Δ·A[d,n]) · s[n] + Δ · B[b,t,n] · u[b,t,d]
+ *     y      = Σ_n C[b,t,n] s[n] + Dk[d] · u[b,t,d]
+ *     out    = y · z · sigmoid(z)     with z = z[b,t,d]   (no gate if z == NULL)
+ * Layouts: u, delta, z, out [b][L][dim]; A [dim][N]; B, C [b][L][N]; Dk [dim];
+ * hfinal [b][dim][N].  Dk, z and hfinal may be NULL.
+ * Channels are processed in blocks of 64 with t as the outer loop, which is
+ * the same arithmetic per channel in a cache-friendly order.
+ */
+void oracle_selective_scan(int batch, int seqlen, int dim, int dstate, int delta_softplus,
+                           const double *u, const double *delta, const double *A,
+                           const double *B, const double *C, const double *Dk, const double *z,
+                           double *out, double *hfinal)
+{
+    const int L = seqlen, N = dstate;
+    const int DB = 64;
+    const int nblk = (dim + DB - 1) / DB;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int b = 0; b < batch; ++b) {
+        for (int blk = 0; blk < nblk; ++blk) {
+            const int d0 = blk * DB;
+            const int d1 = d0 + DB < dim ? d0 + DB : dim;
+            double *s = (double *)calloc((size_t)DB * N, sizeof(double));
+            for (int t = 0; t < L; ++t) {
+                const size_t row = (size_t)b * L + t;
+                const double *Bt = B + row * N;
+                const double *Ct = C + row * N;
+                for (int d = d0; d < d1; ++d) {
+                    double *sd = s + (size_t)(d - d0) * N;
+                    const double ut = u[row * dim + d];
+                    const double raw = delta[row * dim + d];
+                    const double dl = delta_softplus ? softplus(raw) : raw;
+                    double yv = Dk ? Dk[d] * ut : 0.0;
+                    for (int n = 0; n < N; ++n) {
+                        sd[n] = exp(dl * A[(size_t)d * N + n]) * sd[n] + dl * Bt[n] * ut;
+                        yv += Ct[n] * sd[n];
+                    }
+                    if (z) {
+                        const double zt = z[row * dim + d];
+                        yv *= zt / (1.0 + exp(-zt));
+                    }
+                    out[row * dim + d] = yv;
+                }
+            }
+            if (hfinal)
+                for (int d = d0; d < d1; ++d)
+                    memcpy(hfinal + ((size_t)b * dim + d) * N, s + (size_t)(d - d0) * N,
+                           sizeof(double) * N);
+            free(s);
+        }
+    }
+}

@@ -1,0 +1,321 @@
+"""Pins for the CPU oracle (no GPU).
+
+The sequential oracle is the definition of the scan; these tests tie it to
+things other than itself: closed forms, the independent dual (quadratic) and
+chunked (block decomposition) formulations, state hand-off, linearity and the
+reductions between the scan variants.  Each one is chosen so that a plausible
+slip in the oracle -- a dropped term, a wrong sign in the decay, an off-by-one
+in the decay product, a wrong head-to-group map, a transposed operand -- fails.
+
+Page cited: "5.3 텐서 병렬화(Tensor Parallelism) 지원과 대규모 클러스터 학습"
+(§2.1 recurrence, §3/§3.1 duality and scalar-identity A, §3.2 block
+decomposition, §4.2 state hand-off, §4.3 reset by a zero transition) and
+"Scaling State-Space Models on Multiple GPUs with Tensor Parallelism"
+(Abstract: prefill-to-decode state cache).
+"""
+import math
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle
+from oracle import forms
+
+
+def rel_err(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    rms = np.sqrt(np.mean(b * b))
+    return np.max(np.abs(a - b)) / max(rms, 1e-300)
+
+
+def rand_ssd(rng, b, L, H, P, N, G, with_D=True, with_h0=True, dt_scale=1.0):
+    x = rng.standard_normal((b, L, H, P))
+    dt = rng.uniform(-4.0, 1.0, (b, L, H)) * dt_scale
+    A = -np.exp(rng.uniform(0.0, math.log(16.0), H))
+    B = rng.standard_normal((b, L, G, N)) / math.sqrt(N)
+    C = rng.standard_normal((b, L, G, N)) / math.sqrt(N)
+    D = rng.standard_normal(H) if with_D else None
+    h0 = rng.standard_normal((b, H, N, P)) * 0.3 if with_h0 else None
+    return x, dt, A, B, C, D, h0
+
+
+# ----------------------------------------------------------------- closed forms
+
+def test_pin1_zero_decay_is_masked_matmul():
+    """A = 0: no decay, so y = tril(C Bᵀ) (Δ x) + D x, a plain causal matmul."""
+    rng = np.random.default_rng(1)
+    b, L, H, P, N, G = 2, 37, 4, 5, 8, 2
+    x, dt, A, B, C, D, _ = rand_ssd(rng, b, L, H, P, N, G)
+    A = np.zeros(H)
+    y = oracle.ssd_scan(x, dt, A, B, C, D)
+    delta = np.log1p(np.exp(dt))
+    for bb in range(b):
+        for h in range(H):
+            g = h // (H // G)
+            CB = np.tril(C[bb, :, g] @ B[bb, :, g].T)
+            ref = CB @ (delta[bb, :, h][:, None] * x[bb, :, h]) + D[h] * x[bb, :, h]
+            assert rel_err(y[bb, :, h], ref) < 1e-12
+
+
+def test_pin2_constant_input_geometric_series():
+    """N = P = 1, constant inputs: h_t = Δ B x (1 - a^{t+1}) / (1 - a), y_t = C h_t."""
+    L = 300
+    raw, A_h, Bv, Cv, xv = -1.3, -2.5, 0.7, -1.1, 0.9
+    delta = math.log1p(math.exp(raw))
+    a = math.exp(delta * A_h)
+    x = np.full((1, L, 1, 1), xv)
+    dt = np.full((1, L, 1), raw)
+    B = np.full((1, L, 1, 1), Bv)
+    C = np.full((1, L, 1, 1), Cv)
+    y, hf = oracle.ssd_scan(x, dt, np.array([A_h]), B, C, return_final_state=True)
+    t = np.arange(L)
+    h = delta * Bv * xv * (1.0 - a ** (t + 1)) / (1.0 - a)
+    np.testing.assert_allclose(y[0, :, 0, 0], Cv * h, rtol=1e-13, atol=0)
+    np.testing.assert_allclose(hf[0, 0, 0, 0], h[-1], rtol=1e-13)
+    # steady state
+    assert abs(hf[0, 0, 0, 0] - delta * Bv * xv / (1.0 - a)) < 1e-12
+
+
+def test_pin3_single_step():
+    """L = 1: y = Δ (C·B) x + a Cᵀ h0 + D x; state = a h0 + Δ B xᵀ."""
+    rng = np.random.default_rng(3)
+    b, H, P, N, G = 3, 4, 6, 5, 1
+    x, dt, A, B, C, D, h0 = rand_ssd(rng, b, 1, H, P, N, G)
+    y, hf = oracle.ssd_scan(x, dt, A, B, C, D, h0, return_final_state=True)
+    for bb in range(b):
+        for h in range(H):
+            d = math.log1p(math.exp(dt[bb, 0, h]))
+            a = math.exp(d * A[h])
+            Bv, Cv, xv = B[bb, 0, 0], C[bb, 0, 0], x[bb, 0, h]
+            st = a * h0[bb, h] + d * np.outer(Bv, xv)
+            np.testing.assert_allclose(hf[bb, h], st, rtol=1e-13, atol=1e-15)
+            ref = d * (Cv @ Bv) * xv + a * (Cv @ h0[bb, h]) + D[h] * xv
+            np.testing.assert_allclose(y[bb, 0, h], ref, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("raw", [-30.0, -7.0, -2.25, 0.0, 0.5, 3.0, 25.0])
+def test_softplus_values(raw):
+    """With N = P = 1, B = C = x = 1, h0 = 0, L = 1, the output is softplus(raw)."""
+    one = np.ones((1, 1, 1, 1))
+    y = oracle.ssd_scan(one[:, :, :, :], np.full((1, 1, 1), raw), np.array([-1.0]),
+                        one, one)
+    expect = math.log(2.0) if raw == 0.0 else math.log1p(math.exp(raw))
+    assert abs(y[0, 0, 0, 0] - expect) <= 1e-15 * max(1.0, expect)
+    # and without softplus the raw value is the step itself
+    y2 = oracle.ssd_scan(one, np.full((1, 1, 1), abs(raw) + 0.1), np.array([-1.0]), one, one,
+                         dt_softplus=False)
+    assert abs(y2[0, 0, 0, 0] - (abs(raw) + 0.1)) < 1e-15 * (abs(raw) + 1)
+
+
+def test_reset_by_full_decay_forgets_history():
+    """A step whose decay exp(Δ·A) underflows to 0 erases the state (§4.3 reset
+    by a zero transition): the output after it does not depend on earlier tokens."""
+    rng = np.random.default_rng(7)
+    b, L, H, P, N, G = 1, 40, 2, 4, 6, 1
+    x, dt, A, B, C, D, h0 = rand_ssd(rng, b, L, H, P, N, G)
+    k = 17
+    dt[:, k, :] = 5e3  # Δ·A <= -5e3: the decay is exactly 0 in float64
+    y1 = oracle.ssd_scan(x, dt, A, B, C, D, h0)
+    x2 = x.copy()
+    x2[:, :k] = rng.standard_normal(x2[:, :k].shape)
+    y2 = oracle.ssd_scan(x2, dt, A, B, C, D, None)
+    np.testing.assert_array_equal(y1[:, k + 1:], y2[:, k + 1:])
+    assert np.max(np.abs(y1[:, :k] - y2[:, :k])) > 1e-3
+
+
+# ------------------------------------------------------------- formulations
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 1, 1, 1), (2, 23, 4, 3, 5, 2), (1, 64, 3, 8, 16, 1),
+                                   (2, 50, 6, 4, 7, 3)])
+@pytest.mark.parametrize("softplus_on", [True, False])
+def test_pin4_sequential_equals_dual(shape, softplus_on):
+    b, L, H, P, N, G = shape
+    rng = np.random.default_rng(sum(shape) + softplus_on)
+    x, dt, A, B, C, D, h0 = rand_ssd(rng, b, L, H, P, N, G)
+    if not softplus_on:
+        dt = np.log1p(np.exp(dt))  # a positive step, passed through as-is
+    y, hf = oracle.ssd_scan(x, dt, A, B, C, D, h0, dt_softplus=softplus_on,
+                            return_final_state=True)
+    yd, hfd = forms.ssd_dual(x, dt, A, B, C, D, h0, dt_softplus=softplus_on)
+    assert rel_err(y, yd) < 1e-12
+    assert rel_err(hf, hfd) < 1e-12
+
+
+@pytest.mark.parametrize("Q", [1, 3, 16, 64, 97, 200])
+def test_pin5_block_decomposition_equals_sequential(Q):
+    rng = np.random.default_rng(Q)
+    b, L, H, P, N, G = 2, 97, 4, 3, 6, 2
+    x, dt, A, B, C, D, h0 = rand_ssd(rng, b, L, H, P, N, G)
+    y, hf = oracle.ssd_scan(x, dt, A, B, C, D, h0, return_final_state=True)
+    yc, hfc = forms.ssd_chunked(x, dt, A, B, C, D, h0, chunk=Q)
+    assert rel_err(y, yc) < 1e-12
+    assert rel_err(hf, hfc) < 1e-12
+
+
+def test_pin5_no_h0_final_state():
+    rng = np.random.default_rng(55)
+    x, dt, A, B, C, D, _ = rand_ssd(rng, 1, 130, 2, 4, 8, 1)
+    y, hf = oracle.ssd_scan(x, dt, A, B, C, D, None, return_final_state=True)
+    yc, hfc = forms.ssd_chunked(x, dt, A, B, C, D, None, chunk=32)
+    assert rel_err(y, yc) < 1e-12 and rel_err(hf, hfc) < 1e-12
+
+
+def test_pin6_state_handoff_split_sequence():
+    """prefill(0..L1) -> H; prefill(L1..L, h0 = H) == prefill(0..L) (§4.2 hand-off)."""
+    rng = np.random.default_rng(6)
+    b, L, H, P, N, G = 2, 80, 4, 5, 6, 2
+    x, dt, A, B, C, D, h0 = rand_ssd(rng, b, L, H, P, N, G)
+    y, hf = oracle.ssd_scan(x, dt, A, B, C, D, h0, return_final_state=True)
+    L1 = 29
+    y1, h1 = oracle.ssd_scan(x[:, :L1], dt[:, :L1], A, B[:, :L1], C[:, :L1], D, h0,
+                             return_final_state=True)
+    y2, h2 = oracle.ssd_scan(x[:, L1:], dt[:, L1:], A, B[:, L1:], C[:, L1:], D, h1,
+                             return_final_state=True)
+    assert rel_err(np.concatenate([y1, y2], axis=1), y) < 1e-13
+    assert rel_err(h2, hf) < 1e-13
+
+
+def test_pin6_prefill_then_decode_equals_longer_prefill():
+    """Prefill(L) then one decode step on token L == prefill(L+1) (state cache)."""
+    rng = np.random.default_rng(66)
+    b, L, H, P, N, G = 3, 41, 4, 5, 6, 2
+    x, dt, A, B, C, D, h0 = rand_ssd(rng, b, L + 1, H, P, N, G)
+    y, hf = oracle.ssd_scan(x, dt, A, B, C, D, h0, return_final_state=True)
+    _, hL = oracle.ssd_scan(x[:, :L], dt[:, :L], A, B[:, :L], C[:, :L], D, h0,
+                            return_final_state=True)
+    yd, st = oracle.ssd_decode(x[:, L], dt[:, L], A, B[:, L], C[:, L], D, hL)
+    assert rel_err(yd, y[:, L]) < 1e-13
+    assert rel_err(st, hf) < 1e-13
+    # the caller's state array is left untouched
+    _, hL2 = oracle.ssd_scan(x[:, :L], dt[:, :L], A, B[:, :L], C[:, :L], D, h0,
+                             return_final_state=True)
+    np.testing.assert_array_equal(hL, hL2)
+
+
+def test_pin7_linearity_in_x_and_h0():
+    rng = np.random.default_rng(77)
+    b, L, H, P, N, G = 1, 33, 3, 4, 5, 1
+    x1, dt, A, B, C, D, h01 = rand_ssd(rng, b, L, H, P, N, G)
+    x2 = rng.standard_normal(x1.shape)
+    h02 = rng.standard_normal(h01.shape)
+    al, be = 0.7, -1.9
+    ya = oracle.ssd_scan(al * x1 + be * x2, dt, A, B, C, D, al * h01 + be * h02)
+    y1 = oracle.ssd_scan(x1, dt, A, B, C, D, h01)
+    y2 = oracle.ssd_scan(x2, dt, A, B, C, D, h02)
+    assert rel_err(ya, al * y1 + be * y2) < 1e-12
+
+
+def test_pin9_groups_replicated_equals_single_group():
+    rng = np.random.default_rng(9)
+    b, L, H, P, N = 2, 30, 4, 3, 5
+    x, dt, A, B1, C1, D, h0 = rand_ssd(rng, b, L, H, P, N, 1)
+    y1 = oracle.ssd_scan(x, dt, A, B1, C1, D, h0)
+    BH = np.repeat(B1, H, axis=2)
+    CH = np.repeat(C1, H, axis=2)
+    yH = oracle.ssd_scan(x, dt, A, BH, CH, D, h0)
+    assert rel_err(yH, y1) < 1e-14
+
+
+def test_group_map_contiguous_blocks():
+    """Head h reads group h // (H/G): each block of H/G heads equals a one-group
+    scan over that group's B and C alone."""
+    rng = np.random.default_rng(10)
+    b, L, H, P, N, G = 1, 25, 6, 3, 4, 3
+    x, dt, A, B, C, D, h0 = rand_ssd(rng, b, L, H, P, N, G)
+    y = oracle.ssd_scan(x, dt, A, B, C, D, h0)
+    R = H // G
+    for g in range(G):
+        hs = slice(g * R, (g + 1) * R)
+        yg = oracle.ssd_scan(x[:, :, hs], dt[:, :, hs], A[hs], B[:, :, g:g + 1],
+                             C[:, :, g:g + 1], D[hs], h0[:, hs])
+        assert rel_err(y[:, :, hs], yg) < 1e-14
+
+
+@settings(max_examples=25, deadline=None)
+@given(b=st.integers(1, 2), L=st.integers(1, 70), R=st.integers(1, 3), G=st.integers(1, 2),
+       P=st.integers(1, 6), N=st.integers(1, 6), Q=st.integers(1, 80), seed=st.integers(0, 10**6))
+def test_random_shapes_three_forms_agree(b, L, R, G, P, N, Q, seed):
+    rng = np.random.default_rng(seed)
+    H = R * G
+    x, dt, A, B, C, D, h0 = rand_ssd(rng, b, L, H, P, N, G, with_h0=bool(seed % 2))
+    y, hf = oracle.ssd_scan(x, dt, A, B, C, D, h0, return_final_state=True)
+    yd, hfd = forms.ssd_dual(x, dt, A, B, C, D, h0)
+    yc, hfc = forms.ssd_chunked(x, dt, A, B, C, D, h0, chunk=Q)
+    assert rel_err(y, yd) < 1e-11 and rel_err(y, yc) < 1e-11
+    if np.any(hfd != 0):
+        assert rel_err(hf, hfd) < 1e-11 and rel_err(hf, hfc) < 1e-11
+
+
+# ------------------------------------------------------------------- Mamba-1
+
+def rand_m1(rng, b, L, dim, N, gate=True, dskip=True):
+    u = rng.standard_normal((b, L, dim))
+    delta = rng.uniform(-4.0, 1.0, (b, L, dim))
+    A = -np.exp(rng.uniform(0.0, 2.5, (dim, N)))
+    B = rng.standard_normal((b, L, N)) / math.sqrt(N)
+    C = rng.standard_normal((b, L, N)) / math.sqrt(N)
+    D = rng.standard_normal(dim) if dskip else None
+    z = rng.standard_normal((b, L, dim)) if gate else None
+    return u, delta, A, B, C, D, z
+
+
+@pytest.mark.parametrize("gate", [True, False])
+@pytest.mark.parametrize("shape", [(1, 1, 1, 1), (2, 31, 5, 4), (1, 60, 3, 16)])
+def test_mamba1_sequential_equals_dual(shape, gate):
+    b, L, dim, N = shape
+    rng = np.random.default_rng(sum(shape) + gate)
+    u, delta, A, B, C, D, z = rand_m1(rng, b, L, dim, N, gate)
+    out, hf = oracle.selective_scan(u, delta, A, B, C, D, z, return_final_state=True)
+    od, hfd = forms.selective_scan_dual(u, delta, A, B, C, D, z)
+    assert rel_err(out, od) < 1e-12
+    assert rel_err(hf, hfd) < 1e-12
+
+
+def test_pin8_mamba1_shared_decay_equals_ssd_p1():
+    """Selective scan with A[d, n] = A_d for all n and no gate equals the SSD scan
+    with H = dim heads, P = 1, one group and A_h = A_d."""
+    rng = np.random.default_rng(8)
+    b, L, dim, N = 2, 45, 6, 5
+    u, delta, _, B, C, D, _ = rand_m1(rng, b, L, dim, N, gate=False)
+    Ad = -np.exp(rng.uniform(0.0, 2.0, dim))
+    A = np.repeat(Ad[:, None], N, axis=1)
+    out, hf = oracle.selective_scan(u, delta, A, B, C, D, None, return_final_state=True)
+    y, hs = oracle.ssd_scan(u[..., None], delta, Ad, B[:, :, None, :], C[:, :, None, :], D,
+                            None, return_final_state=True)
+    assert rel_err(out, y[..., 0]) < 1e-13
+    assert rel_err(hf, hs[..., 0]) < 1e-13
+
+
+def test_mamba1_gate_closed_forms():
+    """z = 0 gives 0; z = ln 3 gives (3/4)·ln 3 times the ungated output."""
+    rng = np.random.default_rng(11)
+    b, L, dim, N = 1, 20, 3, 4
+    u, delta, A, B, C, D, _ = rand_m1(rng, b, L, dim, N, gate=False)
+    base = oracle.selective_scan(u, delta, A, B, C, D, None)
+    zero = oracle.selective_scan(u, delta, A, B, C, D, np.zeros_like(u))
+    assert np.all(zero == 0.0)
+    z = np.full_like(u, math.log(3.0))
+    g = oracle.selective_scan(u, delta, A, B, C, D, z)
+    np.testing.assert_allclose(g, base * 0.75 * math.log(3.0), rtol=1e-14, atol=1e-300)
+
+
+def test_mamba1_constant_input_closed_form():
+    """N = 1, constant inputs: s_t = Δ B u (1 - a^{t+1})/(1 - a), out = C s_t + D u."""
+    L = 200
+    raw, An, Bv, Cv, uv, Dv = -0.4, -3.0, 0.8, 1.3, -0.6, 0.25
+    d = math.log1p(math.exp(raw))
+    a = math.exp(d * An)
+    out, hf = oracle.selective_scan(np.full((1, L, 1), uv), np.full((1, L, 1), raw),
+                                    np.array([[An]]), np.full((1, L, 1), Bv),
+                                    np.full((1, L, 1), Cv), np.array([Dv]), None,
+                                    return_final_state=True)
+    t = np.arange(L)
+    s = d * Bv * uv * (1 - a ** (t + 1)) / (1 - a)
+    np.testing.assert_allclose(out[0, :, 0], Cv * s + Dv * uv, rtol=1e-13)
+    np.testing.assert_allclose(hf[0, 0, 0], s[-1], rtol=1e-13)
+
+
+def test_oracle_uses_threads():
+    assert oracle.threads() >= 1

@@ -1,0 +1,148 @@
+"""Seeded synthetic inputs.
+
+Every tensor gets its own PCG64 stream, ``default_rng([seed, config_id,
+tensor_id(, step)])``, so a tensor does not change when another one is added
+or resized.  Low-precision inputs are rounded to bf16 once (round to nearest
+even) and the stored bits are the ground truth: the oracle widens exactly those
+values to float64 and the GPU reads exactly those bits.
+
+A generated tensor is a ``Tensor``: ``data`` holds float32 values for "f32" and
+uint16 bf16 bit patterns for "bf16".
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+# tensor ids of the per-tensor streams
+_X, _DT, _A, _B, _C, _D, _H0, _Z = range(8)
+
+
+@dataclass
+class Tensor:
+    data: np.ndarray
+    dtype: str  # "f32" or "bf16"
+
+    @property
+    def shape(self):
+        return self.data.shape
+
+    def f32(self) -> np.ndarray:
+        if self.dtype == "f32":
+            return self.data
+        return bf16_bits_to_f32(self.data)
+
+    def f64(self) -> np.ndarray:
+        return self.f32().astype(np.float64)
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (nearest, ties to even); returns uint16 bits."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _store(values_f32: np.ndarray, dtype: str) -> Tensor:
+    if dtype == "f32":
+        return Tensor(np.ascontiguousarray(values_f32, dtype=np.float32), "f32")
+    if dtype == "bf16":
+        return Tensor(f32_to_bf16_bits(values_f32), "bf16")
+    raise ValueError(dtype)
+
+
+def _rng(seed, config_id, tensor_id, step=None):
+    key = [seed, config_id, tensor_id] + ([] if step is None else [step])
+    return np.random.default_rng(key)
+
+
+def _normal(rng, shape, scale=1.0):
+    v = rng.standard_normal(size=shape, dtype=np.float32)
+    if scale != 1.0:
+        v *= np.float32(scale)
+    return v
+
+
+def _dt_raw(rng, shape, lo=1e-3, hi=1e-1):
+    """Raw step sizes whose softplus is log-uniform in [lo, hi].
+
+    The target step dt is drawn log-uniformly and stored as its softplus
+    preimage log(expm1(dt)) = dt + log(-expm1(-dt)).
+    """
+    u = rng.random(size=shape)
+    dt = np.exp(math.log(lo) + u * (math.log(hi) - math.log(lo)))
+    return (dt + np.log(-np.expm1(-dt))).astype(np.float32)
+
+
+def ssd_params(nheads, seed=0, config_id=0):
+    """Per-head decay rates A_h = -exp(U[log 1, log 16]) and skip weights D_h (fp32)."""
+    a = -np.exp(_rng(seed, config_id, _A).uniform(0.0, math.log(16.0), size=nheads))
+    d = _rng(seed, config_id, _D).standard_normal(size=nheads)
+    return Tensor(a.astype(np.float32), "f32"), Tensor(d.astype(np.float32), "f32")
+
+
+def ssd_inputs(batch, seqlen, nheads, headdim, dstate, ngroups, dtype,
+               seed=0, config_id=0, with_D=True, with_h0=False):
+    """Inputs of one chunked-scan call, in the library's layouts.
+
+    x [batch, seqlen, nheads, headdim], dt [batch, seqlen, nheads] (raw),
+    B and C [batch, seqlen, ngroups, dstate], A and D [nheads] fp32,
+    h0 [batch, nheads, dstate, headdim] fp32 (state scale of a long prefill).
+    """
+    A, D = ssd_params(nheads, seed, config_id)
+    out = dict(
+        x=_store(_normal(_rng(seed, config_id, _X), (batch, seqlen, nheads, headdim)), dtype),
+        dt=_store(_dt_raw(_rng(seed, config_id, _DT), (batch, seqlen, nheads)), dtype),
+        A=A,
+        B=_store(_normal(_rng(seed, config_id, _B), (batch, seqlen, ngroups, dstate),
+                         1.0 / math.sqrt(dstate)), dtype),
+        C=_store(_normal(_rng(seed, config_id, _C), (batch, seqlen, ngroups, dstate),
+                         1.0 / math.sqrt(dstate)), dtype),
+        D=D if with_D else None,
+        h0=None,
+    )
+    if with_h0:
+        out["h0"] = _store(_normal(_rng(seed, config_id, _H0), (batch, nheads, dstate, headdim),
+                                   0.05), "f32")
+    return out
+
+
+def decode_inputs(batch, nheads, headdim, dstate, ngroups, dtype, step, seed=0, config_id=0):
+    """Per-token inputs of one decode step: x [b, H, P], dt [b, H] (raw), B, C [b, G, N]."""
+    return dict(
+        x=_store(_normal(_rng(seed, config_id, _X, step), (batch, nheads, headdim)), dtype),
+        dt=_store(_dt_raw(_rng(seed, config_id, _DT, step), (batch, nheads)), dtype),
+        B=_store(_normal(_rng(seed, config_id, _B, step), (batch, ngroups, dstate),
+                         1.0 / math.sqrt(dstate)), dtype),
+        C=_store(_normal(_rng(seed, config_id, _C, step), (batch, ngroups, dstate),
+                         1.0 / math.sqrt(dstate)), dtype),
+    )
+
+
+def mamba1_inputs(batch, seqlen, dim, dstate, dtype, seed=0, config_id=0,
+                  gate=True, dskip=True):
+    """Inputs of one Mamba-1 selective scan.
+
+    u, delta (raw), z [batch, seqlen, dim]; B, C [batch, seqlen, dstate];
+    A [dim, dstate] = -(n+1) fp32; D [dim] fp32.
+    """
+    A = -np.tile(np.arange(1, dstate + 1, dtype=np.float32), (dim, 1))
+    return dict(
+        u=_store(_normal(_rng(seed, config_id, _X), (batch, seqlen, dim)), dtype),
+        delta=_store(_dt_raw(_rng(seed, config_id, _DT), (batch, seqlen, dim)), dtype),
+        A=Tensor(np.ascontiguousarray(A), "f32"),
+        B=_store(_normal(_rng(seed, config_id, _B), (batch, seqlen, dstate),
+                         1.0 / math.sqrt(dstate)), dtype),
+        C=_store(_normal(_rng(seed, config_id, _C), (batch, seqlen, dstate),
+                         1.0 / math.sqrt(dstate)), dtype),
+        D=Tensor(_rng(seed, config_id, _D).standard_normal(size=dim).astype(np.float32), "f32")
+        if dskip else None,
+        z=_store(_normal(_rng(seed, config_id, _Z), (batch, seqlen, dim)), dtype) if gate else None,
+    )
+
