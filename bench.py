@@ -1,0 +1,373 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective state-space scan on one MI355X.
+
+One step = one chunked SSD prefill call (dt cumsum -> state pass -> chunk output)
+over the Mamba-2-2.7B-like layer shape: batch 8, seqlen 2048, 80 heads of
+headdim 64, dstate 128, one B/C group, chunk 256, bf16 inputs with float32
+accumulation and state.  Inputs are seeded synthetic tensors resident in HBM
+before the timed region.  W untimed warm-up steps, then K steps timed back to
+back between two device synchronisations; per-kernel durations come from HIP
+events recorded around each kernel launch on the call's stream.
+
+The same run also times, as separate legs of the JSON line: the single-token
+decode step at batch 256 (state cache of a 2.7B-layer prefill), the 64K-token
+long-context prefill with eight groups, and the Mamba-1 selective scan
+(batch 8, seqlen 4096, 5120 channels, dstate 16); and the CPU float64 oracle on
+the prefill workload (the `cpu_baseline`, timed on this host's cores).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs ...]
+       [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15    # dense bf16 flop/s
+VALU_F32_PEAK = 78.6e12    # non-packed fp32 FMA flop/s (256 CU x 64 lanes x 2 x 2.4 GHz)
+METRIC = "SSD prefill tokens/s and decode tokens/s at 2.7B-layer shape; % MFMA/HBM roofline"
+
+PREFILL_KERNELS = ["dt_cumsum", "state_pass", "chunk_output"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(t):
+    import numpy as np
+    import torch
+    if t is None:
+        return None
+    if t.dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(t.data)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(t.data).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+class LaunchTimer:
+    """HIP events around every kernel launch of the library calls in a region."""
+
+    def __init__(self, nkernels, ncalls):
+        import torch
+        self.nk, self.nc = nkernels, ncalls
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nkernels * ncalls)]
+        s = torch.cuda.current_stream()
+        for e in self.ev:  # materialise the underlying hipEvent_t handles
+            e.record(s)
+        torch.cuda.synchronize()
+        self.handles = [(ctypes.c_void_p * (2 * nkernels))(
+            *[self.ev[2 * nkernels * c + j].cuda_event for j in range(2 * nkernels)])
+            for c in range(ncalls)]
+
+    def arm(self, lib, call):
+        lib.ssd_set_launch_events(self.handles[call], 2 * self.nk)
+
+    @staticmethod
+    def disarm(lib):
+        lib.ssd_set_launch_events(None, 0)
+
+    def per_kernel_ms(self):
+        out = []
+        for k in range(self.nk):
+            ts = [self.ev[2 * self.nk * c + 2 * k].elapsed_time(self.ev[2 * self.nk * c + 2 * k + 1])
+                  for c in range(self.nc)]
+            out.append(sum(ts) / len(ts))
+        return out
+
+
+def time_calls(fn, nkernels, steps, warmup):
+    """Warm-up, then `steps` back-to-back calls; returns (wall ms per call, per-kernel ms)."""
+    import torch
+    import selective_state_space_13_amd as ssd
+    lib = ssd.lib()
+    for _ in range(warmup):
+        fn()
+    timer = LaunchTimer(nkernels, steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        timer.arm(lib, i)
+        fn()
+    LaunchTimer.disarm(lib)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / steps, timer.per_kernel_ms()
+
+
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload, digest):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = rec.get(f"{kernel}@{workload}")
+    if not e or e.get("source_digest") != digest:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def prefill_work(c):
+    """Algorithmic bytes and flops of each prefill kernel (inputs read once,
+    outputs written once; causal flops of the block decomposition)."""
+    b, L, H, P, N, G, Q = (c[k] for k in ("batch", "seqlen", "nheads", "headdim", "dstate",
+                                          "ngroups", "chunk"))
+    K = (L + Q - 1) // Q
+    x_bytes = b * L * H * P * 2
+    bc_bytes = b * L * G * N * 2
+    dt_bytes = b * L * H * 2
+    final = b * H * N * P * 4 if c.get("final_state") else 0
+    units_h = b * K * H
+    units_g = b * K * G
+    return {
+        "dt_cumsum": dict(bytes=dt_bytes, flops=0),
+        # chunk state B^T(w x) and its hand-off: x and B read once (+ final state)
+        "state_pass": dict(bytes=x_bytes + bc_bytes / 2 + final, flops=units_h * 2 * Q * N * P),
+        # intra-chunk C B^T ⊙ mask · X and state -> output: x, B, C read, y written
+        "chunk_output": dict(bytes=2 * x_bytes + bc_bytes,
+                             flops=units_h * (Q * (Q + 1) * P + 2 * Q * N * P) + units_g * Q * (Q + 1) * N),
+        "total": dict(bytes=2 * x_bytes + bc_bytes + dt_bytes + final,
+                      flops=units_h * (4 * Q * N * P + Q * (Q + 1) * P) + units_g * Q * (Q + 1) * N),
+    }
+
+
+def bench_prefill(cfg, steps, warmup, seed=0):
+    import torch
+    import selective_state_space_13_amd as ssd
+    from workloads import gen
+    log(f"[bench] prefill {cfg['name']}: generating inputs")
+    d = gen.ssd_inputs(cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["headdim"], cfg["dstate"],
+                       cfg["ngroups"], cfg["dtype"], seed=seed, config_id=cfg["id"])
+    x, dt, B, C, A, D = (to_dev(d[k]) for k in ("x", "dt", "B", "C", "A", "D"))
+    del d
+    code = ssd.SSD_BF16 if cfg["dtype"] == "bf16" else ssd.SSD_F32
+    ws = torch.empty(ssd.chunk_scan_workspace_size(cfg["batch"], cfg["seqlen"], cfg["nheads"],
+                                                   cfg["headdim"], cfg["dstate"], cfg["ngroups"],
+                                                   cfg["chunk"], code), dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    fs = torch.empty(cfg["batch"], cfg["nheads"], cfg["dstate"], cfg["headdim"], device="cuda") \
+        if cfg.get("final_state") else None
+
+    def step():
+        ssd.ssd_chunk_scan(x, dt, A, B, C, D, chunk=cfg["chunk"], workspace=ws, out=y,
+                           return_final_state=fs is not None, final_state=fs)
+
+    log(f"[bench] prefill {cfg['name']}: timing {steps} steps after {warmup} warm-up")
+    ms, per = time_calls(step, 3, steps, warmup)
+    tokens = cfg["batch"] * cfg["seqlen"]
+    return dict(ms=ms, per_kernel_ms=dict(zip(PREFILL_KERNELS, per)), tokens=tokens,
+                work=prefill_work(cfg), final_state=fs, y=y)
+
+
+def roofline_entry(kernel, ms, work, workload, digest):
+    t = ms * 1e-3
+    byte_frac = work["bytes"] / t / HBM_PEAK
+    flop_frac = work["flops"] / t / MFMA_BF16_PEAK
+    if byte_frac >= flop_frac:
+        bound, achieved, peak, unit = "hbm", work["bytes"] / t / 1e9, HBM_PEAK / 1e9, "GB/s"
+    else:
+        bound, achieved, peak, unit = "mfma", work["flops"] / t / 1e12, MFMA_BF16_PEAK / 1e12, "TFLOP/s"
+    traffic = measured_traffic(kernel, workload, digest)
+    return {"kernel": kernel, "bound": bound, "achieved": round(achieved, 3), "peak": peak,
+            "unit": unit, "frac": round(achieved / peak, 4),
+            "traffic": traffic, "hbm_frac": round(byte_frac, 4), "mfma_frac": round(flop_frac, 4),
+            "avg_launch_ms": round(ms, 5)}
+
+
+def bench_decode(steps, warmup, prefill_state):
+    import torch
+    import selective_state_space_13_amd as ssd
+    from workloads import configs, gen
+    c = configs.DECODE_STATE_CACHE
+    c2 = configs.MAMBA2_LAYER_PREFILL
+    reps = c["batch"] // c2["batch"]
+    state = prefill_state.repeat(reps, 1, 1, 1).contiguous()  # state cache of the 2.7B-layer prefill
+    A, D = (to_dev(t) for t in gen.ssd_params(c["nheads"], config_id=c2["id"]))
+    log("[bench] decode: generating per-step inputs")
+    steps_in = []
+    for k in range(c["steps"]):
+        s = gen.decode_inputs(c["batch"], c["nheads"], c["headdim"], c["dstate"], c["ngroups"],
+                              c["dtype"], step=k, config_id=c["id"])
+        steps_in.append(tuple(to_dev(s[n]) for n in ("x", "dt", "B", "C")))
+    y = torch.empty_like(steps_in[0][0])
+    it = [0]
+
+    def one():
+        x, dt, B, C = steps_in[it[0] % len(steps_in)]
+        it[0] += 1
+        ssd.ssd_decode_step(x, dt, A, B, C, D, state, out=y)
+
+    ms, per = time_calls(one, 1, c["steps"], warmup)
+    state_bytes = c["batch"] * c["nheads"] * c["dstate"] * c["headdim"] * 4
+    io = c["batch"] * (c["nheads"] * c["headdim"] * 2 * 2 + c["nheads"] * 2 + 2 * c["ngroups"] * c["dstate"] * 2)
+    return dict(ms=ms, kernel_ms=per[0], tokens=c["batch"], bytes=2 * state_bytes + io,
+                flops=c["batch"] * c["nheads"] * c["dstate"] * c["headdim"] * 5)
+
+
+def bench_mamba1(steps, warmup):
+    import torch
+    import selective_state_space_13_amd as ssd
+    from workloads import configs, gen
+    c = configs.MAMBA1_SELECTIVE_SCAN
+    log("[bench] mamba1: generating inputs")
+    d = gen.mamba1_inputs(c["batch"], c["seqlen"], c["dim"], c["dstate"], c["dtype"], config_id=c["id"])
+    u, dl, A, B, C, D, z = (to_dev(d[k]) for k in ("u", "delta", "A", "B", "C", "D", "z"))
+    del d
+    out = torch.empty_like(u)
+
+    def one():
+        ssd.selective_scan(u, dl, A, B, C, D, z, out=out)
+
+    ms, per = time_calls(one, 1, steps, warmup)
+    n_el = c["batch"] * c["seqlen"] * c["dim"]
+    return dict(ms=ms, kernel_ms=per[0], tokens=c["batch"] * c["seqlen"],
+                bytes=4 * n_el * 2 + 2 * c["batch"] * c["seqlen"] * c["dstate"] * 2,
+                exps=n_el * c["dstate"])
+
+
+def cpu_baseline(cfg, seed=0, min_seconds=10.0):
+    """The float64 oracle on the prefill workload, on this host's cores."""
+    import oracle
+    from workloads import gen
+    d = gen.ssd_inputs(cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["headdim"], cfg["dstate"],
+                       cfg["ngroups"], cfg["dtype"], seed=seed, config_id=cfg["id"])
+    args = [d[k].f64() for k in ("x", "dt", "A", "B", "C")]
+    D = d["D"].f64()
+    del d
+    total, calls = 0.0, 0
+    while total < min_seconds and calls < 64:
+        oracle.ssd_scan(*args, D=D)
+        total += oracle.last_seconds
+        calls += 1
+        log(f"[bench] cpu oracle call {calls}: {oracle.last_seconds:.2f} s")
+    tokens = cfg["batch"] * cfg["seqlen"] * calls
+    return {"value": round(tokens / total, 1), "unit": "tokens/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{calls} x the full prefill workload (b{cfg['batch']} L{cfg['seqlen']} "
+                      f"H{cfg['nheads']} P{cfg['headdim']} N{cfg['dstate']}), float64 sequential "
+                      f"recurrence, {total:.1f} s of compute"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--legs", default="decode,long,mamba1",
+                    help="extra legs to time besides the prefill step (comma list or 'none')")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU "
+                                   "sharding is not part of this build", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import selective_state_space_13_amd as ssd
+    from workloads import configs
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible: this benchmark needs an MI355X")
+    ssd.lib()
+
+    legs = [] if args.legs == "none" else [s for s in args.legs.split(",") if s]
+    cfg = configs.MAMBA2_LAYER_PREFILL
+    workload = f"{cfg['name']}:b{cfg['batch']}L{cfg['seqlen']}H{cfg['nheads']}P{cfg['headdim']}" \
+               f"N{cfg['dstate']}G{cfg['ngroups']}Q{cfg['chunk']}"
+    digest = source_digest(["selective_state_space_13_amd/csrc/ssd_mfma.hip",
+                            "selective_state_space_13_amd/csrc/ssd_kernels.h"])
+    pf = bench_prefill(cfg, args.steps, args.warmup)
+    per = pf["per_kernel_ms"]
+    dom = max(("state_pass", "chunk_output"), key=lambda k: per[k])
+    roof = roofline_entry(dom, per[dom], pf["work"][dom], workload, digest)
+    total_work = pf["work"]["total"]
+    t_step = pf["ms"] * 1e-3
+    result = {
+        "metric": METRIC,
+        "value": round(pf["tokens"] / t_step, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pf["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workload, "batch": cfg["batch"], "seqlen": cfg["seqlen"],
+                   "nheads": cfg["nheads"], "headdim": cfg["headdim"], "dstate": cfg["dstate"],
+                   "ngroups": cfg["ngroups"], "chunk": cfg["chunk"], "parallelism": "single-gpu"},
+        "roofline": roof,
+        "step_roofline": {"hbm_frac": round(total_work["bytes"] / t_step / HBM_PEAK, 4),
+                          "mfma_frac": round(total_work["flops"] / t_step / MFMA_BF16_PEAK, 4),
+                          "alg_bytes": total_work["bytes"], "alg_flops": total_work["flops"]},
+        "per_kernel_ms": {k: round(v, 5) for k, v in per.items()},
+    }
+    del pf
+    extra = {}
+    if "decode" in legs:
+        # state cache left by the 2.7B-layer prefill (its 8 final states, tiled over the batch)
+        from workloads import gen
+        d = gen.ssd_inputs(cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["headdim"], cfg["dstate"],
+                           cfg["ngroups"], cfg["dtype"], config_id=cfg["id"])
+        x, dt, B, C, A, D = (to_dev(d[k]) for k in ("x", "dt", "B", "C", "A", "D"))
+        del d
+        _, fs8 = ssd.ssd_chunk_scan(x, dt, A, B, C, D, chunk=cfg["chunk"], return_final_state=True)
+        del x, dt, B, C
+        dec = bench_decode(args.steps, args.warmup, fs8)
+        t = dec["kernel_ms"] * 1e-3
+        extra["decode"] = {"workload": "decode_state_cache:b256H80P64N128G1, 64 single-token steps",
+                           "tokens_per_s": round(dec["tokens"] / (dec["ms"] * 1e-3), 1),
+                           "ms_per_step": round(dec["ms"], 5), "kernel_ms": round(dec["kernel_ms"], 5),
+                           "roofline": {"bound": "hbm", "achieved": round(dec["bytes"] / t / 1e9, 2),
+                                        "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                                        "frac": round(dec["bytes"] / t / HBM_PEAK, 4)}}
+    if "long" in legs:
+        c3 = configs.LONG_CONTEXT_PREFILL
+        lp = bench_prefill(c3, max(3, args.steps // 4), 2)
+        t = lp["ms"] * 1e-3
+        w = lp["work"]["total"]
+        extra["long_prefill"] = {"workload": "long_context_prefill:b1L65536H80P64N128G8Q256",
+                                 "tokens_per_s": round(lp["tokens"] / t, 1), "ms": round(lp["ms"], 5),
+                                 "per_kernel_ms": {k: round(v, 5) for k, v in lp["per_kernel_ms"].items()},
+                                 "hbm_frac": round(w["bytes"] / t / HBM_PEAK, 4),
+                                 "mfma_frac": round(w["flops"] / t / MFMA_BF16_PEAK, 4)}
+        del lp
+    if "mamba1" in legs:
+        m1 = bench_mamba1(max(3, args.steps // 4), 1)
+        t = m1["kernel_ms"] * 1e-3
+        extra["mamba1"] = {"workload": "mamba1_selective_scan:b8L4096D5120N16",
+                           "tokens_per_s": round(m1["tokens"] / (m1["ms"] * 1e-3), 1),
+                           "ms": round(m1["ms"], 5),
+                           "hbm_frac": round(m1["bytes"] / t / HBM_PEAK, 4),
+                           "exp_per_s": round(m1["exps"] / t, 1)}
+    if extra:
+        result["legs"] = extra
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline: oracle on the prefill workload")
+        result["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,175 @@
+/*
+ * libssd -- selective state-space scans on AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels.  Plain pointers and sizes only.
+ *
+ * Pages the operations come from (cited by title and section):
+ *  [TP]  "5.3 텐서 병렬화(Tensor Parallelism) 지원과 대규모 클러스터 학습"
+ *        §2.1 the selective-scan recurrence h_t = Ā_t h_{t-1} + B̄_t x_t with
+ *             input-dependent B, C and Δ (Mamba-1), strictly sequential in t;
+ *        §3.1 Mamba-2's state matrix restricted to a scalar times identity,
+ *             A_t = a_t I, and the scan as Y = M X with a causal semiseparable M;
+ *        §3.2 block decomposition into chunks of length Q: intra-chunk
+ *             quadratic products on matrix cores, inter-chunk hand-off of an
+ *             N x P state;
+ *        §4.2 the final state of one part of a sequence starts the next.
+ *  [INF] "Scaling State-Space Models on Multiple GPUs with Tensor Parallelism",
+ *        Abstract: an SSM state cache carried from prefill into decode.
+ *
+ * Discretisation (the pages leave Ā and B̄ open; this is the reading used):
+ *     Δ_t = softplus(dt_t) if requested, else dt_t
+ *     h_t = exp(Δ_t · A) · h_{t-1} + Δ_t · B_t x_tᵀ          (N x P per head)
+ *     y_t = h_tᵀ C_t + D · x_t                                 (reads h after token t)
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are device pointers on the current HIP device,
+ *    contiguous row-major in the layout given, 16-byte aligned.
+ *  - "dtype" tensors hold float (SSD_F32) or bfloat16 (SSD_BF16) elements;
+ *    A, D and every state are always float32.  Arithmetic is float32
+ *    (bf16 inputs feed bf16 matrix-core products with float32 accumulation);
+ *    outputs are rounded to the input dtype, states stay float32.
+ *  - The caller owns every buffer, including the workspace.  The library never
+ *    allocates device memory, never synchronises, and keeps no pointer after
+ *    return.  Work is enqueued on `stream` (a hipStream_t; NULL = null stream).
+ *  - Outputs must not overlap inputs or each other (SSD_ERR_ALIAS).
+ *  - All validation happens on the host before anything is enqueued: on a
+ *    non-zero return nothing ran.  SSD_ERR_HIP means a launch failed part-way
+ *    (outputs undefined).  Device faults surface at the caller's next sync.
+ *  - Return value: 0 (SSD_OK) or a negative ssd_status; ssd_last_error()
+ *    gives a thread-local detail string for the last non-OK return.
+ *  - Reentrant and thread-safe; the only mutable global is that string.
+ */
+#ifndef LIBSSD_SSD_H
+#define LIBSSD_SSD_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL = -1,        /* a required pointer is NULL                      */
+    SSD_ERR_SHAPE = -2,       /* negative size, G does not divide H, ...         */
+    SSD_ERR_UNSUPPORTED = -3, /* valid but not implemented (see "supported")     */
+    SSD_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than the query says   */
+    SSD_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned                */
+    SSD_ERR_ALIAS = -6,       /* an output overlaps an input or another output   */
+    SSD_ERR_HIP = -7          /* a HIP launch or runtime call failed             */
+} ssd_status;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int ssd_version(void);
+
+/* Static name of a status code ("SSD_OK", "SSD_ERR_SHAPE", ...). */
+const char *ssd_status_string(int status);
+
+/* Detail of the calling thread's last non-OK return ("" if none). */
+const char *ssd_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Chunked SSD prefill ([TP] §3.1, §3.2; hand-off of §4.2; cache of [INF]).
+ *
+ * Computes, for every batch row b and head h (group g = h / (nheads/ngroups)),
+ * the scan above over t = 0..seqlen-1 starting from initial_state (or 0), by
+ * the block decomposition with chunks of `chunk` tokens (the last chunk may be
+ * shorter).  The chunk length changes rounding only, not the result.
+ *
+ *   x      [batch][seqlen][nheads][headdim]      dtype
+ *   dt     [batch][seqlen][nheads]               dtype  (raw if dt_softplus)
+ *   A      [nheads]                              float  (A_h, normally < 0)
+ *   B, C   [batch][seqlen][ngroups][dstate]      dtype
+ *   D      [nheads]                              float  or NULL (= 0)
+ *   initial_state [batch][nheads][dstate][headdim] float or NULL (= 0)
+ *   y      [batch][seqlen][nheads][headdim]      dtype, written
+ *   final_state   [batch][nheads][dstate][headdim] float or NULL, written
+ *   workspace     >= ssd_chunk_scan_workspace_size(...) bytes, 256-byte aligned
+ *
+ * Supported: headdim == 64; dstate in {64, 128}; chunk in {64, 128, 256};
+ * ngroups >= 1 dividing nheads; batch, seqlen >= 0 (an empty call writes
+ * final_state = initial_state or 0).  Element counts must stay below 2^62.
+ * ------------------------------------------------------------------------ */
+size_t ssd_chunk_scan_workspace_size(int batch, int seqlen, int nheads, int headdim, int dstate,
+                                     int ngroups, int chunk, int dtype);
+
+int ssd_chunk_scan_fwd(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
+                       int chunk, int dtype, int dt_softplus,
+                       const void *x, const void *dt, const float *A, const void *B,
+                       const void *C, const float *D, const float *initial_state,
+                       void *y, float *final_state,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Byte offsets of the intermediate stages inside the workspace, for
+ * inspection by tests (contents valid after the call has completed):
+ *   delta  [batch][nheads][nchunks][chunk] float   Δ per token (0 past the end)
+ *   cs     [batch][nheads][nchunks][chunk] double  within-chunk inclusive cumsum of Δ·A
+ *   hprev  [batch][nchunks][nheads][dstate][headdim]  the state entering each
+ *          chunk: float for SSD_F32; for SSD_BF16 two bf16 planes of that shape,
+ *          head then tail, whose sum is the state.
+ * Returns SSD_OK, or the status ssd_chunk_scan_fwd would return for the sizes. */
+int ssd_chunk_scan_workspace_layout(int batch, int seqlen, int nheads, int headdim, int dstate,
+                                    int ngroups, int chunk, int dtype, size_t *off_delta,
+                                    size_t *off_cs, size_t *off_hprev);
+
+/* ------------------------------------------------------------------------
+ * One decode step against a cached state ([INF] Abstract; the single step of
+ * [TP] §2.1 with the scalar decay of §3.1).  For each (b, h):
+ *     a = exp(Δ·A_h);  state <- a·state + Δ·B xᵀ;  y = stateᵀ C + D_h·x
+ *
+ *   x      [batch][nheads][headdim]   dtype
+ *   dt     [batch][nheads]            dtype  (raw if dt_softplus)
+ *   A, D   [nheads] float (D may be NULL)
+ *   B, C   [batch][ngroups][dstate]   dtype
+ *   state  [batch][nheads][dstate][headdim] float, read and overwritten in place
+ *   y      [batch][nheads][headdim]   dtype, written
+ *
+ * Supported: headdim == 64; dstate a multiple of 16 in [16, 256].
+ * ------------------------------------------------------------------------ */
+int ssd_decode_step(int batch, int nheads, int headdim, int dstate, int ngroups, int dtype,
+                    int dt_softplus, const void *x, const void *dt, const float *A,
+                    const void *B, const void *C, const float *D, float *state, void *y,
+                    void *stream);
+
+/* ------------------------------------------------------------------------
+ * Mamba-1 selective scan with a diagonal state matrix per channel ([TP] §2.1).
+ * For batch row b and channel d, state s[n] (zero at t = 0):
+ *     Δ = softplus(delta) if delta_softplus, else delta
+ *     s[n] <- exp(Δ·A[d][n])·s[n] + Δ·B[b][t][n]·u;   y = Σ_n C[b][t][n]·s[n] + D[d]·u
+ *     out  = y · z·sigmoid(z)   (gate omitted when z == NULL)
+ *
+ *   u, delta, z, out [batch][seqlen][dim]  dtype  (z may be NULL)
+ *   A      [dim][dstate] float
+ *   B, C   [batch][seqlen][dstate]         dtype
+ *   D      [dim] float or NULL
+ *   final_state [batch][dim][dstate] float or NULL, written
+ *   workspace   >= selective_scan_workspace_size(...) bytes (may be 0 -> NULL ok)
+ *
+ * Supported: dstate in {4, 8, 16}; dim a multiple of 64.
+ * ------------------------------------------------------------------------ */
+size_t selective_scan_workspace_size(int batch, int seqlen, int dim, int dstate, int dtype);
+
+int selective_scan_fwd(int batch, int seqlen, int dim, int dstate, int dtype, int delta_softplus,
+                       const void *u, const void *delta, const float *A, const void *B,
+                       const void *C, const float *D, const void *z, void *out,
+                       float *final_state, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/* ------------------------------------------------------------------------
+ * Timing hook for benchmarks and profilers.  While set, every libssd call made
+ * by the calling thread records events[2k] on its stream just before its k-th
+ * kernel launch and events[2k+1] just after it, for k < count/2 (launches past
+ * that are not bracketed).  `events` are hipEvent_t handles created and owned
+ * by the caller; the library keeps the pointer until cleared with NULL.  The
+ * hook changes no work; it only adds event records between launches.
+ * Returns SSD_OK, or SSD_ERR_SHAPE for a negative count.
+ * ------------------------------------------------------------------------ */
+int ssd_set_launch_events(void *const *events, int count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBSSD_SSD_H */

@@ -1,0 +1,239 @@
+"""libssd: selective state-space scans on AMD Instinct MI355X (gfx950).
+
+A thin Python layer over the C ABI of ``libssd.so`` (declared in
+``include/ssd.h``).  Every function here only marshals arguments: it checks
+devices, dtypes and contiguity, allocates outputs and the workspace with torch
+(torch provides device memory and the current stream, nothing else) and calls
+the library.  All arithmetic runs in the library's HIP kernels; there is no
+CPU or torch fallback, and a missing library is an error.
+
+Functions (names as in the C ABI):
+    ssd_chunk_scan(x, dt, A, B, C, D=None, *, chunk, initial_state=None,
+                   return_final_state=False, dt_softplus=True)  -> y | (y, final_state)
+    ssd_decode_step(x, dt, A, B, C, D, state, *, dt_softplus=True) -> y  (state updated)
+    selective_scan(u, delta, A, B, C, D=None, z=None, *, delta_softplus=True,
+                   return_final_state=False) -> out | (out, final_state)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libssd.so")
+
+SSD_F32, SSD_BF16 = 0, 1
+STATUS = {0: "SSD_OK", -1: "SSD_ERR_NULL", -2: "SSD_ERR_SHAPE", -3: "SSD_ERR_UNSUPPORTED",
+          -4: "SSD_ERR_WORKSPACE", -5: "SSD_ERR_ALIGN", -6: "SSD_ERR_ALIAS", -7: "SSD_ERR_HIP"}
+
+
+class SSDError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+        self.msg = msg
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library with argument types declared (raises if not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    # torch first: its HIP runtime (SONAME libamdhip64.so.7) then also serves
+    # libssd.so, so torch's streams and device pointers are valid in both.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(or python selective_state_space_13_amd/build.py)")
+    L = ctypes.CDLL(LIB_PATH)
+    i, sz, vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+    L.ssd_version.restype = i
+    L.ssd_status_string.argtypes = [i]
+    L.ssd_status_string.restype = ctypes.c_char_p
+    L.ssd_last_error.restype = ctypes.c_char_p
+    L.ssd_chunk_scan_workspace_size.argtypes = [i] * 8
+    L.ssd_chunk_scan_workspace_size.restype = sz
+    L.ssd_chunk_scan_workspace_layout.argtypes = [i] * 8 + [ctypes.POINTER(sz)] * 3
+    L.ssd_chunk_scan_workspace_layout.restype = i
+    L.ssd_chunk_scan_fwd.argtypes = [i] * 9 + [vp] * 10 + [sz, vp]
+    L.ssd_chunk_scan_fwd.restype = i
+    L.ssd_decode_step.argtypes = [i] * 7 + [vp] * 9
+    L.ssd_decode_step.restype = i
+    L.selective_scan_workspace_size.argtypes = [i] * 5
+    L.selective_scan_workspace_size.restype = sz
+    L.selective_scan_fwd.argtypes = [i] * 6 + [vp] * 10 + [sz, vp]
+    L.selective_scan_fwd.restype = i
+    L.ssd_set_launch_events.argtypes = [ctypes.c_void_p, i]
+    L.ssd_set_launch_events.restype = i
+    _lib = L
+    return L
+
+
+def check(status: int):
+    if status != 0:
+        raise SSDError(status, lib().ssd_last_error().decode())
+
+
+def last_error() -> str:
+    return lib().ssd_last_error().decode()
+
+
+# ------------------------------------------------------------------ helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return SSD_F32
+    if t.dtype == torch.bfloat16:
+        return SSD_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _req(t, name, dtype=None, device=None):
+    torch = _torch()
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def chunk_scan_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype):
+    return lib().ssd_chunk_scan_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups,
+                                               chunk, dtype)
+
+
+def chunk_scan_workspace_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype):
+    """(off_delta, off_cs, off_hprev) byte offsets of the stages in the workspace."""
+    offs = [ctypes.c_size_t() for _ in range(3)]
+    check(lib().ssd_chunk_scan_workspace_layout(batch, seqlen, nheads, headdim, dstate, ngroups,
+                                                chunk, dtype, *[ctypes.byref(o) for o in offs]))
+    return tuple(o.value for o in offs)
+
+
+# ---------------------------------------------------------------- functions
+
+def ssd_chunk_scan(x, dt, A, B, C, D=None, *, chunk, initial_state=None,
+                   return_final_state=False, dt_softplus=True, workspace=None,
+                   out=None, final_state=None):
+    """Chunked SSD prefill.  x [b,L,H,P], dt [b,L,H], A [H] fp32, B, C [b,L,G,N],
+    D [H] fp32 or None, initial_state [b,H,N,P] fp32 or None.
+    Returns y (same dtype as x) or (y, final_state fp32 [b,H,N,P]).
+    `workspace` (uint8 tensor), `out` and `final_state` may be passed to reuse
+    buffers."""
+    torch = _torch()
+    x = _req(x, "x")
+    dev = x.device
+    code = _dtype_code(x)
+    b, L, H, P = x.shape
+    _req(dt, "dt", x.dtype, dev)
+    _req(B, "B", x.dtype, dev)
+    _req(C, "C", x.dtype, dev)
+    _req(A, "A", torch.float32, dev)
+    _req(D, "D", torch.float32, dev)
+    _req(initial_state, "initial_state", torch.float32, dev)
+    G, N = B.shape[2], B.shape[3]
+    if tuple(dt.shape) != (b, L, H) or tuple(B.shape) != (b, L, G, N) or C.shape != B.shape:
+        raise ValueError("shape mismatch among x, dt, B, C")
+    if tuple(A.shape) != (H,) or (D is not None and tuple(D.shape) != (H,)):
+        raise ValueError("A and D must have shape [nheads]")
+    if initial_state is not None and tuple(initial_state.shape) != (b, H, N, P):
+        raise ValueError("initial_state must be [batch, nheads, dstate, headdim]")
+    y = out if out is not None else torch.empty_like(x)
+    _req(y, "out", x.dtype, dev)
+    fs = None
+    if return_final_state:
+        fs = final_state if final_state is not None else torch.empty(
+            (b, H, N, P), dtype=torch.float32, device=dev)
+        _req(fs, "final_state", torch.float32, dev)
+    need = chunk_scan_workspace_size(b, L, H, P, N, G, chunk, code)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    check(lib().ssd_chunk_scan_fwd(
+        b, L, H, P, N, G, chunk, code, int(bool(dt_softplus)),
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(initial_state),
+        _ptr(y), _ptr(fs), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return (y, fs) if return_final_state else y
+
+
+def ssd_decode_step(x, dt, A, B, C, D, state, *, dt_softplus=True, out=None):
+    """One decode step.  x [b,H,P], dt [b,H], A [H], B, C [b,G,N], D [H] or None,
+    state [b,H,N,P] fp32 (updated in place).  Returns y [b,H,P]."""
+    torch = _torch()
+    x = _req(x, "x")
+    dev = x.device
+    code = _dtype_code(x)
+    b, H, P = x.shape
+    _req(dt, "dt", x.dtype, dev)
+    _req(B, "B", x.dtype, dev)
+    _req(C, "C", x.dtype, dev)
+    _req(A, "A", torch.float32, dev)
+    _req(D, "D", torch.float32, dev)
+    _req(state, "state", torch.float32, dev)
+    G, N = B.shape[1], B.shape[2]
+    if tuple(dt.shape) != (b, H) or tuple(B.shape) != (b, G, N) or C.shape != B.shape:
+        raise ValueError("shape mismatch among x, dt, B, C")
+    if tuple(state.shape) != (b, H, N, P):
+        raise ValueError("state must be [batch, nheads, dstate, headdim]")
+    y = out if out is not None else torch.empty_like(x)
+    _req(y, "out", x.dtype, dev)
+    check(lib().ssd_decode_step(b, H, P, N, G, code, int(bool(dt_softplus)), _ptr(x), _ptr(dt),
+                                _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(state), _ptr(y),
+                                _stream(dev)))
+    return y
+
+
+def selective_scan(u, delta, A, B, C, D=None, z=None, *, delta_softplus=True,
+                   return_final_state=False, out=None):
+    """Mamba-1 selective scan.  u, delta, z [b,L,dim]; A [dim,N] fp32;
+    B, C [b,L,N]; D [dim] fp32 or None.  Returns out or (out, final_state [b,dim,N])."""
+    torch = _torch()
+    u = _req(u, "u")
+    dev = u.device
+    code = _dtype_code(u)
+    b, L, dim = u.shape
+    _req(delta, "delta", u.dtype, dev)
+    _req(B, "B", u.dtype, dev)
+    _req(C, "C", u.dtype, dev)
+    _req(z, "z", u.dtype, dev)
+    _req(A, "A", torch.float32, dev)
+    _req(D, "D", torch.float32, dev)
+    N = A.shape[1]
+    if delta.shape != u.shape or (z is not None and z.shape != u.shape):
+        raise ValueError("u, delta and z must have the same shape")
+    if tuple(A.shape) != (dim, N) or tuple(B.shape) != (b, L, N) or C.shape != B.shape:
+        raise ValueError("A must be [dim, N] and B, C [batch, seqlen, N]")
+    o = out if out is not None else torch.empty_like(u)
+    _req(o, "out", u.dtype, dev)
+    fs = torch.empty((b, dim, N), dtype=torch.float32, device=dev) if return_final_state else None
+    need = lib().selective_scan_workspace_size(b, L, dim, N, code)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+    check(lib().selective_scan_fwd(b, L, dim, N, code, int(bool(delta_softplus)), _ptr(u),
+                                   _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                   _ptr(o), _ptr(fs), _ptr(ws), need, _stream(dev)))
+    return (o, fs) if return_final_state else o

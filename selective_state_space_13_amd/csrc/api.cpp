@@ -1,0 +1,379 @@
+// libssd C ABI: argument validation, workspace carving and kernel dispatch.
+//
+// Everything that can be checked on the host is checked before the first
+// enqueue, so a non-OK return means nothing ran.  No call allocates device
+// memory or synchronises.
+#include "ssd.h"
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "ssd_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(SSD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr uint64_t kMaxElems = 1ull << 62;
+
+// a*b*... with overflow detection against kMaxElems
+bool mul_ok(uint64_t &acc, uint64_t v) {
+    if (v == 0) {
+        acc = 0;
+        return true;
+    }
+    if (acc > kMaxElems / v) return false;
+    acc *= v;
+    return true;
+}
+
+bool prod(uint64_t &out, std::initializer_list<long long> dims) {
+    uint64_t acc = 1;
+    for (long long d : dims) {
+        if (d < 0) return false;
+        if (!mul_ok(acc, (uint64_t)d)) return false;
+    }
+    out = acc;
+    return true;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+struct Span {
+    const char *name;
+    uintptr_t lo, hi;  // [lo, hi)
+    bool present() const { return hi > lo; }
+};
+Span span(const char *name, const void *p, uint64_t bytes) {
+    return Span{name, (uintptr_t)p, p ? (uintptr_t)p + (uintptr_t)bytes : (uintptr_t)p};
+}
+bool overlaps(const Span &a, const Span &b) {
+    return a.present() && b.present() && a.lo < b.hi && b.lo < a.hi;
+}
+
+// Every output against every input and every other output.
+int check_alias(std::initializer_list<Span> outs, std::initializer_list<Span> ins) {
+    for (auto o = outs.begin(); o != outs.end(); ++o) {
+        for (const Span &i : ins)
+            if (overlaps(*o, i)) return fail(SSD_ERR_ALIAS, "%s overlaps %s", o->name, i.name);
+        for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+            if (overlaps(*o, *o2)) return fail(SSD_ERR_ALIAS, "%s overlaps %s", o->name, o2->name);
+    }
+    return SSD_OK;
+}
+
+// launch-event timing hook (ssd_set_launch_events)
+thread_local void *const *g_events = nullptr;
+thread_local int g_nevents = 0;
+
+// Brackets successive kernel launches of one call with the caller's events.
+struct LaunchMarks {
+    hipStream_t stream;
+    int k = 0;
+    explicit LaunchMarks(hipStream_t s) : stream(s) {}
+    void before() {
+        if (g_events && 2 * k + 1 < g_nevents)
+            (void)hipEventRecord(static_cast<hipEvent_t>(g_events[2 * k]), stream);
+    }
+    void after() {
+        if (g_events && 2 * k + 1 < g_nevents)
+            (void)hipEventRecord(static_cast<hipEvent_t>(g_events[2 * k + 1]), stream);
+        ++k;
+    }
+};
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int elem_size(int dtype) { return dtype == SSD_BF16 ? 2 : 4; }
+
+// bf16 prefill runs on the matrix cores; its hand-off states are bf16.
+bool prefill_uses_mfma(int dtype) { return dtype == SSD_BF16 && ssd::mfma_prefill_enabled; }
+
+struct ScanLayout {
+    int nchunks = 0;
+    size_t off_delta = 0, off_cs = 0, off_hprev = 0, total = 0;
+};
+
+int check_scan_sizes(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
+                     int chunk, int dtype) {
+    if (dtype != SSD_F32 && dtype != SSD_BF16)
+        return fail(SSD_ERR_UNSUPPORTED, "dtype %d is not SSD_F32 or SSD_BF16", dtype);
+    if (batch < 0 || seqlen < 0)
+        return fail(SSD_ERR_SHAPE, "batch (%d) and seqlen (%d) must be >= 0", batch, seqlen);
+    if (nheads < 1 || headdim < 1 || dstate < 1 || ngroups < 1 || chunk < 1)
+        return fail(SSD_ERR_SHAPE, "nheads, headdim, dstate, ngroups and chunk must be >= 1");
+    if (nheads % ngroups)
+        return fail(SSD_ERR_SHAPE, "ngroups (%d) must divide nheads (%d)", ngroups, nheads);
+    if (headdim != 64) return fail(SSD_ERR_UNSUPPORTED, "headdim %d: only 64 is supported", headdim);
+    if (dstate != 64 && dstate != 128)
+        return fail(SSD_ERR_UNSUPPORTED, "dstate %d: only 64 and 128 are supported", dstate);
+    if (chunk != 64 && chunk != 128 && chunk != 256)
+        return fail(SSD_ERR_UNSUPPORTED, "chunk %d: only 64, 128 and 256 are supported", chunk);
+    uint64_t n;
+    if (!prod(n, {batch, seqlen, nheads, headdim}) || !prod(n, {batch, seqlen, ngroups, dstate}))
+        return fail(SSD_ERR_SHAPE, "tensor sizes overflow");
+    return SSD_OK;
+}
+
+int scan_layout(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
+                int chunk, int dtype, ScanLayout &lay) {
+    int st = check_scan_sizes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype);
+    if (st) return st;
+    lay.nchunks = (seqlen + chunk - 1) / chunk;
+    uint64_t tok, states;
+    if (!prod(tok, {batch, nheads, lay.nchunks, chunk}) ||
+        !prod(states, {batch, lay.nchunks, nheads, headdim, dstate}))
+        return fail(SSD_ERR_SHAPE, "workspace size overflows");
+    const size_t hbytes = 4;  // float, or two bf16 planes (head + tail) on the bf16 path
+    lay.off_delta = 0;
+    lay.off_cs = round_up(tok * 4, 256);
+    lay.off_hprev = lay.off_cs + round_up(tok * 8, 256);
+    lay.total = lay.off_hprev + round_up(states * hbytes, 256);
+    return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_version(void) { return 100; }
+
+const char *ssd_status_string(int status) {
+    switch (status) {
+    case SSD_OK: return "SSD_OK";
+    case SSD_ERR_NULL: return "SSD_ERR_NULL";
+    case SSD_ERR_SHAPE: return "SSD_ERR_SHAPE";
+    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED";
+    case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE";
+    case SSD_ERR_ALIGN: return "SSD_ERR_ALIGN";
+    case SSD_ERR_ALIAS: return "SSD_ERR_ALIAS";
+    case SSD_ERR_HIP: return "SSD_ERR_HIP";
+    default: return "SSD_ERR_UNKNOWN";
+    }
+}
+
+const char *ssd_last_error(void) { return g_last_error.c_str(); }
+
+int ssd_set_launch_events(void *const *events, int count) {
+    if (count < 0) return fail(SSD_ERR_SHAPE, "event count %d < 0", count);
+    g_events = events;
+    g_nevents = events ? count : 0;
+    return SSD_OK;
+}
+
+size_t ssd_chunk_scan_workspace_size(int batch, int seqlen, int nheads, int headdim, int dstate,
+                                     int ngroups, int chunk, int dtype) {
+    ScanLayout lay;
+    if (scan_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, lay)) return 0;
+    return lay.total;
+}
+
+int ssd_chunk_scan_workspace_layout(int batch, int seqlen, int nheads, int headdim, int dstate,
+                                    int ngroups, int chunk, int dtype, size_t *off_delta,
+                                    size_t *off_cs, size_t *off_hprev) {
+    ScanLayout lay;
+    int st = scan_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, lay);
+    if (st) return st;
+    if (off_delta) *off_delta = lay.off_delta;
+    if (off_cs) *off_cs = lay.off_cs;
+    if (off_hprev) *off_hprev = lay.off_hprev;
+    return SSD_OK;
+}
+
+int ssd_chunk_scan_fwd(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
+                       int chunk, int dtype, int dt_softplus, const void *x, const void *dt,
+                       const float *A, const void *B, const void *C, const float *D,
+                       const float *initial_state, void *y, float *final_state, void *workspace,
+                       size_t workspace_bytes, void *stream_) {
+    ScanLayout lay;
+    int st = scan_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, lay);
+    if (st) return st;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    const int es = elem_size(dtype);
+    uint64_t n_x, n_dt, n_bc, n_state;
+    prod(n_x, {batch, seqlen, nheads, headdim});
+    prod(n_dt, {batch, seqlen, nheads});
+    prod(n_bc, {batch, seqlen, ngroups, dstate});
+    prod(n_state, {batch, nheads, dstate, headdim});
+
+    if (batch == 0) return SSD_OK;
+    if (seqlen == 0) {
+        // empty sequence: the final state is the initial one
+        if (!final_state) return SSD_OK;
+        if (!aligned(final_state, 16) || (initial_state && !aligned(initial_state, 16)))
+            return fail(SSD_ERR_ALIGN, "state pointers must be 16-byte aligned");
+        st = check_alias({span("final_state", final_state, n_state * 4)},
+                         {span("initial_state", initial_state, n_state * 4)});
+        if (st) return st;
+        hipError_t e = ssd::launch_copy_state(initial_state, final_state, n_state, stream);
+        return e == hipSuccess ? SSD_OK : hip_fail(e, "state copy");
+    }
+    if (!x || !dt || !A || !B || !C || !y)
+        return fail(SSD_ERR_NULL, "x, dt, A, B, C and y are required");
+    const void *ptrs[] = {x, dt, A, B, C, D, initial_state, y, final_state};
+    for (const void *p : ptrs)
+        if (p && !aligned(p, 16)) return fail(SSD_ERR_ALIGN, "tensor pointer %p is not 16-byte aligned", p);
+    if (!workspace || workspace_bytes < lay.total)
+        return fail(SSD_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", lay.total,
+                    workspace_bytes, workspace ? "" : " (NULL)");
+    if (!aligned(workspace, 256)) return fail(SSD_ERR_ALIGN, "workspace must be 256-byte aligned");
+    st = check_alias(
+        {span("y", y, n_x * es), span("final_state", final_state, n_state * 4),
+         span("workspace", workspace, lay.total)},
+        {span("x", x, n_x * es), span("dt", dt, n_dt * es), span("A", A, (uint64_t)nheads * 4),
+         span("B", B, n_bc * es), span("C", C, n_bc * es), span("D", D, D ? (uint64_t)nheads * 4 : 0),
+         span("initial_state", initial_state, initial_state ? n_state * 4 : 0)});
+    if (st) return st;
+
+    char *ws = static_cast<char *>(workspace);
+    float *delta = reinterpret_cast<float *>(ws + lay.off_delta);
+    double *cs = reinterpret_cast<double *>(ws + lay.off_cs);
+    const int K = lay.nchunks;
+
+    LaunchMarks marks(stream);
+    marks.before();
+    hipError_t e = ssd::launch_dt_cumsum(dtype, dt, A, dt_softplus, batch, seqlen, nheads, chunk,
+                                         K, delta, cs, stream);
+    marks.after();
+    if (e != hipSuccess) return hip_fail(e, "dt cumsum launch");
+    if (prefill_uses_mfma(dtype)) {
+        uint16_t *hprev = reinterpret_cast<uint16_t *>(ws + lay.off_hprev);
+        marks.before();
+        e = ssd::launch_state_pass_mfma(x, B, delta, cs, initial_state, batch, seqlen, nheads,
+                                        headdim, dstate, ngroups, chunk, K, hprev, final_state,
+                                        stream);
+        marks.after();
+        if (e != hipSuccess) return hip_fail(e, "state pass launch");
+        marks.before();
+        e = ssd::launch_chunk_output_mfma(x, B, C, D, delta, cs, hprev, batch, seqlen, nheads,
+                                          headdim, dstate, ngroups, chunk, K, y, stream);
+        marks.after();
+        if (e != hipSuccess) return hip_fail(e, "chunk output launch");
+    } else {
+        float *S = reinterpret_cast<float *>(ws + lay.off_hprev);
+        marks.before();
+        e = ssd::launch_chunk_state_valu(dtype, x, B, delta, cs, batch, seqlen, nheads, headdim,
+                                         dstate, ngroups, chunk, K, S, stream);
+        marks.after();
+        if (e != hipSuccess) return hip_fail(e, "chunk state launch");
+        marks.before();
+        e = ssd::launch_state_pass_valu(cs, initial_state, batch, nheads, headdim, dstate, chunk,
+                                        K, S, final_state, stream);
+        marks.after();
+        if (e != hipSuccess) return hip_fail(e, "state pass launch");
+        marks.before();
+        e = ssd::launch_chunk_output_valu(dtype, x, B, C, D, delta, cs, S, batch, seqlen, nheads,
+                                          headdim, dstate, ngroups, chunk, K, y, stream);
+        marks.after();
+        if (e != hipSuccess) return hip_fail(e, "chunk output launch");
+    }
+    return SSD_OK;
+}
+
+int ssd_decode_step(int batch, int nheads, int headdim, int dstate, int ngroups, int dtype,
+                    int dt_softplus, const void *x, const void *dt, const float *A, const void *B,
+                    const void *C, const float *D, float *state, void *y, void *stream_) {
+    if (dtype != SSD_F32 && dtype != SSD_BF16)
+        return fail(SSD_ERR_UNSUPPORTED, "dtype %d is not SSD_F32 or SSD_BF16", dtype);
+    if (batch < 0) return fail(SSD_ERR_SHAPE, "batch (%d) must be >= 0", batch);
+    if (nheads < 1 || headdim < 1 || dstate < 1 || ngroups < 1)
+        return fail(SSD_ERR_SHAPE, "nheads, headdim, dstate and ngroups must be >= 1");
+    if (nheads % ngroups)
+        return fail(SSD_ERR_SHAPE, "ngroups (%d) must divide nheads (%d)", ngroups, nheads);
+    if (headdim != 64) return fail(SSD_ERR_UNSUPPORTED, "headdim %d: only 64 is supported", headdim);
+    if (dstate % 16 || dstate > 256)
+        return fail(SSD_ERR_UNSUPPORTED, "dstate %d: a multiple of 16 up to 256 is required", dstate);
+    uint64_t n_x, n_state, n_bc;
+    if (!prod(n_state, {batch, nheads, dstate, headdim}) || (long long)batch * nheads > (1ll << 31) - 4)
+        return fail(SSD_ERR_SHAPE, "tensor sizes overflow");
+    prod(n_x, {batch, nheads, headdim});
+    prod(n_bc, {batch, ngroups, dstate});
+    if (batch == 0) return SSD_OK;
+    if (!x || !dt || !A || !B || !C || !state || !y)
+        return fail(SSD_ERR_NULL, "x, dt, A, B, C, state and y are required");
+    const void *ptrs[] = {x, dt, A, B, C, D, state, y};
+    for (const void *p : ptrs)
+        if (p && !aligned(p, 16)) return fail(SSD_ERR_ALIGN, "tensor pointer %p is not 16-byte aligned", p);
+    const int es = elem_size(dtype);
+    int st = check_alias(
+        {span("state", state, n_state * 4), span("y", y, n_x * es)},
+        {span("x", x, n_x * es), span("dt", dt, (uint64_t)batch * nheads * es),
+         span("A", A, (uint64_t)nheads * 4), span("B", B, n_bc * es), span("C", C, n_bc * es),
+         span("D", D, D ? (uint64_t)nheads * 4 : 0)});
+    if (st) return st;
+    LaunchMarks marks(static_cast<hipStream_t>(stream_));
+    marks.before();
+    hipError_t e = ssd::launch_decode_step(dtype, x, dt, A, B, C, D, dt_softplus, batch, nheads,
+                                           headdim, dstate, ngroups, state, y,
+                                           static_cast<hipStream_t>(stream_));
+    marks.after();
+    return e == hipSuccess ? SSD_OK : hip_fail(e, "decode launch");
+}
+
+size_t selective_scan_workspace_size(int batch, int seqlen, int dim, int dstate, int dtype) {
+    (void)batch, (void)seqlen, (void)dim, (void)dstate, (void)dtype;
+    return 0;
+}
+
+int selective_scan_fwd(int batch, int seqlen, int dim, int dstate, int dtype, int delta_softplus,
+                       const void *u, const void *delta, const float *A, const void *B,
+                       const void *C, const float *D, const void *z, void *out,
+                       float *final_state, void *workspace, size_t workspace_bytes,
+                       void *stream_) {
+    (void)workspace, (void)workspace_bytes;
+    if (dtype != SSD_F32 && dtype != SSD_BF16)
+        return fail(SSD_ERR_UNSUPPORTED, "dtype %d is not SSD_F32 or SSD_BF16", dtype);
+    if (batch < 0 || seqlen < 0)
+        return fail(SSD_ERR_SHAPE, "batch (%d) and seqlen (%d) must be >= 0", batch, seqlen);
+    if (dim < 1 || dstate < 1) return fail(SSD_ERR_SHAPE, "dim and dstate must be >= 1");
+    if (dstate != 4 && dstate != 8 && dstate != 16)
+        return fail(SSD_ERR_UNSUPPORTED, "dstate %d: only 4, 8 and 16 are supported", dstate);
+    if (dim % 64) return fail(SSD_ERR_UNSUPPORTED, "dim %d must be a multiple of 64", dim);
+    if (batch > 65535) return fail(SSD_ERR_UNSUPPORTED, "batch %d exceeds 65535", batch);
+    uint64_t n_u, n_bc, n_state;
+    if (!prod(n_u, {batch, seqlen, dim}) || !prod(n_bc, {batch, seqlen, dstate}) ||
+        !prod(n_state, {batch, dim, dstate}))
+        return fail(SSD_ERR_SHAPE, "tensor sizes overflow");
+    if (batch == 0) return SSD_OK;
+    if (seqlen > 0 && (!u || !delta || !B || !C || !out))
+        return fail(SSD_ERR_NULL, "u, delta, B, C and out are required");
+    if (!A) return fail(SSD_ERR_NULL, "A is required");
+    const void *ptrs[] = {u, delta, A, B, C, D, z, out, final_state};
+    for (const void *p : ptrs)
+        if (p && !aligned(p, 16)) return fail(SSD_ERR_ALIGN, "tensor pointer %p is not 16-byte aligned", p);
+    const int es = elem_size(dtype);
+    int st = check_alias(
+        {span("out", out, n_u * es), span("final_state", final_state, n_state * 4)},
+        {span("u", u, n_u * es), span("delta", delta, n_u * es),
+         span("A", A, (uint64_t)dim * dstate * 4), span("B", B, n_bc * es),
+         span("C", C, n_bc * es), span("D", D, D ? (uint64_t)dim * 4 : 0),
+         span("z", z, z ? n_u * es : 0)});
+    if (st) return st;
+    if (seqlen == 0 && !final_state) return SSD_OK;
+    LaunchMarks marks(static_cast<hipStream_t>(stream_));
+    marks.before();
+    hipError_t e = ssd::launch_selective_scan(dtype, u, delta, A, B, C, D, z, delta_softplus, batch,
+                                              seqlen, dim, dstate, out, final_state,
+                                              static_cast<hipStream_t>(stream_));
+    marks.after();
+    return e == hipSuccess ? SSD_OK : hip_fail(e, "selective scan launch");
+}
+
+}  // extern "C"

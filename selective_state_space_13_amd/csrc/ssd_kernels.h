@@ -1,0 +1,99 @@
+// Internal declarations shared by the libssd HIP sources (not installed).
+//
+// Device helpers for bf16 storage and the host-side launchers of every kernel.
+// The public C ABI lives in include/ssd.h; api.cpp validates arguments, carves
+// the workspace and calls the launchers below.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace ssd {
+
+// bfloat16 kept as raw bits in memory; arithmetic is always float32.
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) { return __uint_as_float((uint32_t)v.bits << 16); }
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
+    __bf16 b = (__bf16)v;
+    return __builtin_bit_cast(uint16_t, b);
+}
+// two floats -> packed bf16 pair (lo in bits 0..15)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+    bf16x2_t r = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ void store_out(float *p, float v) { *p = v; }
+__device__ __forceinline__ void store_out(bf16_t *p, float v) { p->bits = f32_to_bf16_bits(v); }
+
+// softplus(r) = log(1 + e^r) = max(r, 0) + log1p(e^-|r|), float32
+__device__ __forceinline__ float softplus_f32(float r) {
+    return fmaxf(r, 0.0f) + log1pf(__expf(-fabsf(r)));
+}
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- launchers
+// dtype: 0 = float, 1 = bf16 (matches ssd_dtype in include/ssd.h)
+
+// dt -> Δ (softplus optional) and the within-chunk inclusive cumsum of Δ·A.
+// delta [batch][nheads][nchunks][chunk] float, cs same shape double;
+// Δ = 0 past seqlen (so cs holds its last value there).
+hipError_t launch_dt_cumsum(int dtype, const void *dt, const float *A, int dt_softplus, int batch,
+                            int seqlen, int nheads, int chunk, int nchunks, float *delta, double *cs,
+                            hipStream_t stream);
+
+// float32 vector-ALU path (any dtype): chunk states, state passing, output.
+// S/hprev: [batch][nchunks][nheads][dstate][headdim] float (in place).
+hipError_t launch_chunk_state_valu(int dtype, const void *x, const void *B, const float *delta,
+                                   const double *cs, int batch, int seqlen, int nheads, int headdim,
+                                   int dstate, int ngroups, int chunk, int nchunks, float *S,
+                                   hipStream_t stream);
+hipError_t launch_state_pass_valu(const double *cs, const float *h0, int batch, int nheads,
+                                  int headdim, int dstate, int chunk, int nchunks, float *S_to_hprev,
+                                  float *final_state, hipStream_t stream);
+hipError_t launch_chunk_output_valu(int dtype, const void *x, const void *B, const void *C,
+                                    const float *D, const float *delta, const double *cs,
+                                    const float *hprev, int batch, int seqlen, int nheads,
+                                    int headdim, int dstate, int ngroups, int chunk, int nchunks,
+                                    void *y, hipStream_t stream);
+
+// bf16 matrix-core path (mfma_prefill_enabled says whether it is built in).
+extern const bool mfma_prefill_enabled;
+// hprev: two planes [2][batch][nchunks][nheads][dstate][headdim] bf16 (head, tail).
+hipError_t launch_state_pass_mfma(const void *x, const void *B, const float *delta, const double *cs,
+                                  const float *h0, int batch, int seqlen, int nheads, int headdim,
+                                  int dstate, int ngroups, int chunk, int nchunks, uint16_t *hprev,
+                                  float *final_state, hipStream_t stream);
+hipError_t launch_chunk_output_mfma(const void *x, const void *B, const void *C, const float *D,
+                                    const float *delta, const double *cs, const uint16_t *hprev,
+                                    int batch, int seqlen, int nheads, int headdim, int dstate,
+                                    int ngroups, int chunk, int nchunks, void *y,
+                                    hipStream_t stream);
+
+// decode step, in-place float state
+hipError_t launch_decode_step(int dtype, const void *x, const void *dt, const float *A,
+                              const void *B, const void *C, const float *D, int dt_softplus,
+                              int batch, int nheads, int headdim, int dstate, int ngroups,
+                              float *state, void *y, hipStream_t stream);
+
+// Mamba-1 selective scan
+hipError_t launch_selective_scan(int dtype, const void *u, const void *delta, const float *A,
+                                 const void *B, const void *C, const float *D, const void *z,
+                                 int delta_softplus, int batch, int seqlen, int dim, int dstate,
+                                 void *out, float *final_state, hipStream_t stream);
+
+// copy or zero the state for an empty sequence
+hipError_t launch_copy_state(const float *src, float *dst, size_t n, hipStream_t stream);
+
+}  // namespace ssd
