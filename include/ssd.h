@@ -126,7 +126,7 @@ int ssd_chunk_scan_workspace_layout(int batch, int seqlen, int nheads, int headd
  *   state  [batch][nheads][dstate][headdim] float, read and overwritten in place
  *   y      [batch][nheads][headdim]   dtype, written
  *
- * Supported: headdim == 64; dstate a multiple of 16 in [16, 256].
+ * Supported: headdim == 64; dstate a multiple of 32 in [32, 256].
  * ------------------------------------------------------------------------ */
 int ssd_decode_step(int batch, int nheads, int headdim, int dstate, int ngroups, int dtype,
                     int dt_softplus, const void *x, const void *dt, const float *A,

@@ -298,8 +298,8 @@ int ssd_decode_step(int batch, int nheads, int headdim, int dstate, int ngroups,
     if (nheads % ngroups)
         return fail(SSD_ERR_SHAPE, "ngroups (%d) must divide nheads (%d)", ngroups, nheads);
     if (headdim != 64) return fail(SSD_ERR_UNSUPPORTED, "headdim %d: only 64 is supported", headdim);
-    if (dstate % 16 || dstate > 256)
-        return fail(SSD_ERR_UNSUPPORTED, "dstate %d: a multiple of 16 up to 256 is required", dstate);
+    if (dstate % 32 || dstate > 256)
+        return fail(SSD_ERR_UNSUPPORTED, "dstate %d: a multiple of 32 up to 256 is required", dstate);
     uint64_t n_x, n_state, n_bc;
     if (!prod(n_state, {batch, nheads, dstate, headdim}) || (long long)batch * nheads > (1ll << 31) - 4)
         return fail(SSD_ERR_SHAPE, "tensor sizes overflow");

@@ -9,10 +9,13 @@
 // Pure streaming: every state byte is read once and written once, ~0.6 flop
 // per byte, so HBM bandwidth is the roof.  One wave owns one (b, h) state
 // (dstate x 64 floats).  Lane l covers p = 4·(l % 16) .. +3 with a 16-byte
-// access and rows n ≡ l / 16 (mod 4): each load/store instruction of the wave
-// moves 4 full 256-byte state rows.  The four partial y sums are combined with
-// two cross-lane shuffles.  The loop is unrolled so several row loads are in
-// flight before the first FMA needs its data.
+// access and the contiguous rows n = (l / 16)·dstate/4 + k, so each load/store
+// instruction of the wave moves four full 256-byte state rows and each lane's
+// B and C values are contiguous.  Rows are processed in groups of 8 with the
+// next group's loads issued before the current group is computed (loads and
+// stores of one lane never touch the same row twice, so nothing serialises
+// them); state traffic is non-temporal, it is not reused.  The four partial y
+// sums are combined with two cross-lane shuffles.
 #include "ssd_kernels.h"
 
 namespace ssd {
@@ -44,10 +47,42 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t *p, float4 v) {
 }
 
 template <typename T>
+__device__ __forceinline__ void load_vals(const T *p, float *v, int n);
+template <>
+__device__ __forceinline__ void load_vals<float>(const float *p, float *v, int n) {
+    for (int k = 0; k < n; k += 4) {
+        const float4 q = *reinterpret_cast<const float4 *>(p + k);
+        v[k] = q.x, v[k + 1] = q.y, v[k + 2] = q.z, v[k + 3] = q.w;
+    }
+}
+template <>
+__device__ __forceinline__ void load_vals<bf16_t>(const bf16_t *p, float *v, int n) {
+    for (int k = 0; k < n; k += 8) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(p + k);
+        v[k] = bf16lo(q.x), v[k + 1] = bf16hi(q.x), v[k + 2] = bf16lo(q.y), v[k + 3] = bf16hi(q.y);
+        v[k + 4] = bf16lo(q.z), v[k + 5] = bf16hi(q.z), v[k + 6] = bf16lo(q.w), v[k + 7] = bf16hi(q.w);
+    }
+}
+
+constexpr int kGroup = 8;  // state rows per lane in flight per step of the pipeline
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 nt_load(const float4 *p) {
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void nt_store(float4 s, float4 *p) {
+    const f32x4_t v = {s.x, s.y, s.z, s.w};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t *>(p));
+}
+
+template <typename T, int N>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const T *__restrict__ x, const T *__restrict__ dt, const float *__restrict__ A,
     const T *__restrict__ B, const T *__restrict__ C, const float *__restrict__ D, int dt_softplus,
-    int nbh, int nheads, int N, int ngroups, float *__restrict__ state, T *__restrict__ y) {
+    int nbh, int nheads, int ngroups, float *__restrict__ state, T *__restrict__ y) {
+    constexpr int RPL = N / 4;  // rows per lane
+    constexpr int NG = RPL / kGroup;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int bh = blockIdx.x * (blockDim.x / kWave) + wave;
     if (bh >= nbh) return;
@@ -58,28 +93,44 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     const float d = dt_softplus ? softplus_f32(r) : r;
     const float a = __expf(d * A[h]);
 
-    const int q = lane & 15;  // p = 4q..4q+3
-    const int nq = lane >> 4; // rows n = nq, nq+4, ...
+    const int q = lane & 15;   // p = 4q..4q+3
+    const int n0 = (lane >> 4) * RPL;
     const float4 xv = load4<T>(x + (size_t)bh * P + 4 * q);
-    const T *Bg = B + ((size_t)b * ngroups + g) * N;
-    const T *Cg = C + ((size_t)b * ngroups + g) * N;
-    float4 *st = reinterpret_cast<float4 *>(state + (size_t)bh * N * P) + q;
+    float bn[RPL], cn[RPL];
+    load_vals<T>(B + ((size_t)b * ngroups + g) * N + n0, bn, RPL);
+    load_vals<T>(C + ((size_t)b * ngroups + g) * N + n0, cn, RPL);
+    float4 *st = reinterpret_cast<float4 *>(state + (size_t)bh * N * P) + (size_t)n0 * (P / 4) + q;
 
+    float4 cur[kGroup], nxt[kGroup];
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) cur[k] = nt_load(st + k * (P / 4));
     float4 yacc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-    for (int n = nq; n < N; n += 4) {
-        const float bn = d * to_f32(Bg[n]);
-        const float cn = to_f32(Cg[n]);
-        float4 s = st[n * (P / 4)];
-        s.x = a * s.x + bn * xv.x;
-        s.y = a * s.y + bn * xv.y;
-        s.z = a * s.z + bn * xv.z;
-        s.w = a * s.w + bn * xv.w;
-        st[n * (P / 4)] = s;
-        yacc.x += cn * s.x;
-        yacc.y += cn * s.y;
-        yacc.z += cn * s.z;
-        yacc.w += cn * s.w;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+        if (gi + 1 < NG) {
+#pragma unroll
+            for (int k = 0; k < kGroup; ++k)
+                nxt[k] = nt_load(st + ((gi + 1) * kGroup + k) * (P / 4));
+        }
+#pragma unroll
+        for (int k = 0; k < kGroup; ++k) {
+            const int row = gi * kGroup + k;
+            const float bd = d * bn[row], cc = cn[row];
+            float4 s = cur[k];
+            s.x = a * s.x + bd * xv.x;
+            s.y = a * s.y + bd * xv.y;
+            s.z = a * s.z + bd * xv.z;
+            s.w = a * s.w + bd * xv.w;
+            nt_store(s, st + row * (P / 4));
+            yacc.x += cc * s.x;
+            yacc.y += cc * s.y;
+            yacc.z += cc * s.z;
+            yacc.w += cc * s.w;
+        }
+        if (gi + 1 < NG) {
+#pragma unroll
+            for (int k = 0; k < kGroup; ++k) cur[k] = nxt[k];
+        }
     }
 #pragma unroll
     for (int m = 16; m < kWave; m <<= 1) {
@@ -88,7 +139,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         yacc.z += __shfl_xor(yacc.z, m, kWave);
         yacc.w += __shfl_xor(yacc.w, m, kWave);
     }
-    if (nq == 0) {
+    if (lane < 16) {
         const float Dh = D ? D[h] : 0.0f;
         yacc.x += Dh * xv.x;
         yacc.y += Dh * xv.y;
@@ -98,27 +149,54 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     }
 }
 
+template <typename T, int N>
+void launch_n(unsigned blocks, hipStream_t stream, const void *x, const void *dt, const float *A,
+              const void *B, const void *C, const float *D, int dt_softplus, int nbh, int nheads,
+              int ngroups, float *state, void *y) {
+    decode_step_kernel<T, N><<<dim3(blocks), dim3(256), 0, stream>>>(
+        static_cast<const T *>(x), static_cast<const T *>(dt), A, static_cast<const T *>(B),
+        static_cast<const T *>(C), D, dt_softplus, nbh, nheads, ngroups, state, static_cast<T *>(y));
+}
+
+template <typename T>
+hipError_t launch_t(int dstate, unsigned blocks, hipStream_t stream, const void *x, const void *dt,
+                    const float *A, const void *B, const void *C, const float *D, int dt_softplus,
+                    int nbh, int nheads, int ngroups, float *state, void *y) {
+    switch (dstate) {
+#define SSD_DEC(NN)                                                                                  \
+    case NN:                                                                                         \
+        launch_n<T, NN>(blocks, stream, x, dt, A, B, C, D, dt_softplus, nbh, nheads, ngroups, state, y); \
+        break;
+        SSD_DEC(32)
+        SSD_DEC(64)
+        SSD_DEC(96)
+        SSD_DEC(128)
+        SSD_DEC(160)
+        SSD_DEC(192)
+        SSD_DEC(224)
+        SSD_DEC(256)
+#undef SSD_DEC
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_decode_step(int dtype, const void *x, const void *dt, const float *A,
                               const void *B, const void *C, const float *D, int dt_softplus,
                               int batch, int nheads, int headdim, int dstate, int ngroups,
                               float *state, void *y, hipStream_t stream) {
-    if (headdim != P || dstate % 16) return hipErrorInvalidValue;
+    if (headdim != P || dstate % 32) return hipErrorInvalidValue;
     const long long nbh = (long long)batch * nheads;
     if (nbh == 0) return hipSuccess;
     const unsigned blocks = (unsigned)((nbh + 3) / 4);
     if (dtype == 0)
-        decode_step_kernel<float><<<dim3(blocks), dim3(256), 0, stream>>>(
-            static_cast<const float *>(x), static_cast<const float *>(dt), A,
-            static_cast<const float *>(B), static_cast<const float *>(C), D, dt_softplus,
-            (int)nbh, nheads, dstate, ngroups, state, static_cast<float *>(y));
-    else
-        decode_step_kernel<bf16_t><<<dim3(blocks), dim3(256), 0, stream>>>(
-            static_cast<const bf16_t *>(x), static_cast<const bf16_t *>(dt), A,
-            static_cast<const bf16_t *>(B), static_cast<const bf16_t *>(C), D, dt_softplus,
-            (int)nbh, nheads, dstate, ngroups, state, static_cast<bf16_t *>(y));
-    return hipGetLastError();
+        return launch_t<float>(dstate, blocks, stream, x, dt, A, B, C, D, dt_softplus, (int)nbh,
+                               nheads, ngroups, state, y);
+    return launch_t<bf16_t>(dstate, blocks, stream, x, dt, A, B, C, D, dt_softplus, (int)nbh,
+                            nheads, ngroups, state, y);
 }
 
 }  // namespace ssd

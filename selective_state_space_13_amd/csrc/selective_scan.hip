@@ -10,21 +10,31 @@
 // One lane owns one (batch row, channel) and its dstate-vector state in
 // registers; a 64-lane wave covers 64 consecutive channels, so every u, delta,
 // z and out access of the wave is one contiguous 128-byte (bf16) segment.
-// B_t and C_t are the same for the whole workgroup (one batch row, one t) and
-// are read with scalar loads.  exp(Δ·A) is computed as exp2(Δ·(A·log2 e)) with
-// the scaled A kept in registers: one multiply and one v_exp_f32 per state.
+// Time is processed in tiles of kT steps: while a tile is computed, the next
+// tile's u/delta/z are already in flight into registers, and its B_t/C_t rows
+// (the same for the whole workgroup) are staged once in LDS as float32.
+// exp(Δ·A) is exp2(Δ·(A·log2 e)) with the scaled A in registers: one multiply
+// and one v_exp_f32 per state element and step.
 #include "ssd_kernels.h"
 
 namespace ssd {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kT = 16;  // time steps per tile
 
-template <int N, typename T>
-__device__ __forceinline__ void load_row(const T *p, float (&v)[N]) {
-#pragma unroll
-    for (int n = 0; n < N; ++n) v[n] = to_f32(p[n]);
+// log(1 + e^r) to a few ulps: log1p via log(u)·e/(u - 1) with u = 1 + e
+// (exact where u rounds to 1), e = e^-|r|.
+__device__ __forceinline__ float softplus_fast(float r) {
+    const float e = __builtin_amdgcn_exp2f(-fabsf(r) * kLog2e);
+    const float u = 1.0f + e;
+    const float lp = u == 1.0f ? e : __builtin_amdgcn_logf(u) * kLn2 * e * __builtin_amdgcn_rcpf(u - 1.0f);
+    return fmaxf(r, 0.0f) + lp;
 }
+
+template <typename T>
+__device__ __forceinline__ float ldf(const T *p) { return to_f32(*p); }
 
 template <typename T, int N>
 __global__ __launch_bounds__(256) void selective_scan_kernel(
@@ -32,43 +42,86 @@ __global__ __launch_bounds__(256) void selective_scan_kernel(
     const T *__restrict__ B, const T *__restrict__ C, const float *__restrict__ D,
     const T *__restrict__ z, int delta_softplus, int seqlen, int dim, T *__restrict__ out,
     float *__restrict__ final_state) {
+    __shared__ float bc[2][kT][2 * N];  // double-buffered B_t, C_t rows of a tile
+
     const int d = blockIdx.x * blockDim.x + threadIdx.x;
     const int b = blockIdx.y;
-    if (d >= dim) return;
+    const bool active = d < dim;
+    const int dd = active ? d : dim - 1;  // inactive lanes read a valid address, write nothing
 
     float A2[N], s[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-        A2[n] = A[(size_t)d * N + n] * kLog2e;
+        A2[n] = A[(size_t)dd * N + n] * kLog2e;
         s[n] = 0.0f;
     }
-    const float Dd = D ? D[d] : 0.0f;
-
+    const float Dd = D ? D[dd] : 0.0f;
     const size_t row0 = (size_t)b * seqlen;
-    for (int t = 0; t < seqlen; ++t) {
-        const size_t row = row0 + t;
-        const size_t idx = row * dim + d;
-        const float uv = to_f32(u[idx]);
-        const float r = to_f32(delta[idx]);
-        const float dl = delta_softplus ? softplus_f32(r) : r;
-        const float du = dl * uv;
-        float Bt[N], Ct[N];
-        load_row<N>(B + row * N, Bt);
-        load_row<N>(C + row * N, Ct);
-        float yv = Dd * uv;
+    const int ntiles = (seqlen + kT - 1) / kT;
+
+    // stage B/C of tile k into bc[k & 1]
+    auto stage_bc = [&](int k) {
+        for (int e = threadIdx.x; e < kT * 2 * N; e += blockDim.x) {
+            const int tt = e / (2 * N), j = e % (2 * N);
+            const int t = k * kT + tt;
+            float v = 0.0f;
+            if (t < seqlen) v = j < N ? ldf(B + (row0 + t) * N + j) : ldf(C + (row0 + t) * N + (j - N));
+            bc[k & 1][tt][j] = v;
+        }
+    };
+    float uv[kT], rv[kT], zv[kT];
+    auto load_tile = [&](int k) {
 #pragma unroll
-        for (int n = 0; n < N; ++n) {
-            const float dA = __builtin_amdgcn_exp2f(dl * A2[n]);
-            s[n] = dA * s[n] + du * Bt[n];
-            yv += Ct[n] * s[n];
+        for (int tt = 0; tt < kT; ++tt) {
+            const int t = k * kT + tt;
+            const bool in = t < seqlen;
+            const size_t idx = (row0 + (in ? t : 0)) * dim + dd;
+            uv[tt] = ldf(u + idx);
+            rv[tt] = ldf(delta + idx);
+            zv[tt] = z ? ldf(z + idx) : 0.0f;
         }
-        if (z) {
-            const float zv = to_f32(z[idx]);
-            yv *= zv / (1.0f + __expf(-zv));
-        }
-        store_out(out + idx, yv);
+    };
+
+    if (ntiles > 0) {
+        stage_bc(0);
+        load_tile(0);
     }
-    if (final_state) {
+    for (int k = 0; k < ntiles; ++k) {
+        float cu[kT], cr[kT], cz[kT];
+#pragma unroll
+        for (int tt = 0; tt < kT; ++tt) {
+            cu[tt] = uv[tt];
+            cr[tt] = rv[tt];
+            cz[tt] = zv[tt];
+        }
+        __syncthreads();  // bc[k & 1] staged; bc[(k+1) & 1] free
+        if (k + 1 < ntiles) {
+            stage_bc(k + 1);
+            load_tile(k + 1);
+        }
+        const int nt = min(kT, seqlen - k * kT);
+#pragma unroll
+        for (int tt = 0; tt < kT; ++tt) {
+            if (tt < nt) {
+                const float dl = delta_softplus ? softplus_fast(cr[tt]) : cr[tt];
+                const float du = dl * cu[tt];
+                const float *bt = bc[k & 1][tt];
+                float yv = Dd * cu[tt];
+#pragma unroll
+                for (int n = 0; n < N; ++n) {
+                    const float dA = __builtin_amdgcn_exp2f(dl * A2[n]);
+                    s[n] = dA * s[n] + du * bt[n];
+                    yv += bt[N + n] * s[n];
+                }
+                if (z) {
+                    const float zz = cz[tt];
+                    yv *= zz * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zz * kLog2e));
+                }
+                if (active) store_out(out + (row0 + k * kT + tt) * dim + d, yv);
+            }
+        }
+    }
+    if (final_state && active) {
         float *fs = final_state + ((size_t)b * dim + d) * N;
 #pragma unroll
         for (int n = 0; n < N; ++n) fs[n] = s[n];

@@ -147,7 +147,7 @@ def decode_call(L, b=4, H=8, P=64, N=128, G=1, dtype=BF16, ptrs=None):
 
 
 @pytest.mark.parametrize("kw,status", [(dict(b=-1), SHAPE), (dict(G=3), SHAPE), (dict(P=128), UNSUP),
-                                       (dict(N=24), UNSUP), (dict(N=512), UNSUP),
+                                       (dict(N=24), UNSUP), (dict(N=16), UNSUP), (dict(N=512), UNSUP),
                                        (dict(dtype=2), UNSUP)])
 def test_decode_shape_errors(L, kw, status):
     assert decode_call(L, **kw) == status

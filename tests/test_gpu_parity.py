@@ -221,7 +221,7 @@ def test_config3_long_context_full():
 # ------------------------------------------------------------------- decode
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("N,G,wD", [(128, 1, True), (64, 2, False), (16, 4, True), (256, 1, False)])
+@pytest.mark.parametrize("N,G,wD", [(128, 1, True), (64, 2, False), (32, 4, True), (256, 1, False), (96, 2, True)])
 def test_decode_small_chain(N, G, wD, dtype):
     b, H, P, steps = 5, 8, 64, 6
     A, D = gen.ssd_params(H, seed=N, config_id=110)
