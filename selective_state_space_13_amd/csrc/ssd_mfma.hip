@@ -56,6 +56,7 @@ typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 constexpr int P = 64;
+constexpr int kNumCUs = 256;  // compute units of the target part (MI355X)
 constexpr float kMaxBlockDecay = 60.0f;  // exp(60) ~ 1e26 keeps G·u finite in float32
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -72,11 +73,16 @@ __device__ __forceinline__ bf16x8 cat8(v4i16 a, v4i16 b) {
     return __builtin_bit_cast(bf16x8, r);
 }
 
-__device__ __forceinline__ bf16x8 ld16(const uint16_t *p) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
-}
-
 __device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
+
+// Loads are never predicated: callers clamp the row to a valid one and zero
+// the value afterwards, so the compiler can issue a batch of loads before the
+// first use instead of a branch and a full wait around each of them.
+__device__ __forceinline__ uint4 ld16u(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ uint4 keep_if(bool ok, uint4 v) {
+    return make_uint4(ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u);
+}
+__device__ __forceinline__ bf16x8 as8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ bf16x8 pack8(const float *v) {
     uint4 r;
@@ -110,99 +116,120 @@ __device__ __forceinline__ uint32_t scale_bf16x2(uint32_t w, float s) {
 __device__ __forceinline__ int tr_col(int lane) { return 16 * ((lane >> 4) & 1) + 4 * (lane & 3); }
 __device__ __forceinline__ int tr_row(int lane) { return (lane >> 2) & 3; }
 
+// LDS tiles read with ds_read_b64_tr_b16 hold 64 bf16 columns per row (128 B,
+// no padding).  The 32-byte chunk index of a row is XORed with (row & 3), so
+// the 4 rows x 32 B that one 16-lane group reads fall in distinct banks (and
+// the 4 rows x 64 B of two groups too).
+__device__ __forceinline__ int swz(int row, int col) {
+    return row * 64 + (((col >> 4) ^ (row & 3)) << 4) + (col & 15);
+}
+// same for rows of W bf16 columns (W = 64 or 128)
+template <int W>
+__device__ __forceinline__ int swzn(int row, int col) {
+    return row * W + (((col >> 4) ^ (row & 3)) << 4) + (col & 15);
+}
+
 // =====================================================================
 // state pass
 // =====================================================================
-constexpr int kNT = 64;         // state rows per workgroup
-constexpr int kXP = P + 8;      // LDS pitch (elements) of the x tiles
-constexpr int kBP = kNT + 8;    // LDS pitch of the B tile
-
+// One workgroup (4 waves) per (batch row, head, NW state rows) holds an
+// NW x 64 slab of the state: wave w owns p-tile (w & 1) and the state rows
+// [NW/2 (w >> 1), +NW/2), as NW/64 32x32 accumulators.  NW = 128 reads each x
+// tile once for the whole state; NW = 64 doubles the workgroups for short
+// grids.  Tokens stream through LDS in slices of kKT, double buffered, and
+// through registers two slices ahead (see the main loop).
 // w·x is split into a bf16 head and a bf16 tail (w·x - head, exact in
 // float32), so the product enters the state with ~2^-17 relative error
 // instead of bf16's 2^-9; B and x themselves are exact bf16 inputs.
-template <int Q>
+constexpr int kKT = 64;  // tokens per LDS slice
+
+template <int Q, int N, int NW>
 __global__ __launch_bounds__(256, 2) void state_pass_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ B,
     const float *__restrict__ delta, const double *__restrict__ cs,
-    const float *__restrict__ h0, int seqlen, int nheads, int N, int ngroups, int nchunks,
+    const float *__restrict__ h0, int seqlen, int nheads, int ngroups, int nchunks,
     uint16_t *__restrict__ hprev, size_t plane, float *__restrict__ final_state) {
-    constexpr int KT = Q < 128 ? Q : 128;  // tokens per LDS slice
-    constexpr int SPC = Q / KT;            // slices per chunk
-    constexpr int VPT = KT * 8 / 256;      // 16-byte vectors per thread per tile
-    __shared__ __attribute__((aligned(16))) uint16_t xh[KT * kXP];
-    __shared__ __attribute__((aligned(16))) uint16_t xl[KT * kXP];
-    __shared__ __attribute__((aligned(16))) uint16_t bs[KT * kBP];
+    constexpr int SPC = Q / kKT;         // slices per chunk
+    constexpr int XV = kKT * 8 / 256;    // x vectors (16 B) per thread per slice
+    constexpr int BV = kKT * NW / 8 / 256;  // B vectors per thread per slice
+    constexpr int NTW = NW / 64;         // 32-wide n-tiles per wave
+    __shared__ __attribute__((aligned(16))) uint16_t xh[2][kKT * 64];
+    __shared__ __attribute__((aligned(16))) uint16_t xl[2][kKT * 64];
+    __shared__ __attribute__((aligned(16))) uint16_t bs[2][kKT * NW];
 
-    const int ntiles = N / kNT;
-    int bid = blockIdx.x;
-    const int nt = bid % ntiles;
-    bid /= ntiles;
-    const int h = bid % nheads;
-    const int b = bid / nheads;
+    constexpr int NSLAB = N / NW;
+    const int slab = blockIdx.x % NSLAB;
+    const int h = (blockIdx.x / NSLAB) % nheads;
+    const int b = blockIdx.x / NSLAB / nheads;
     const int g = h / (nheads / ngroups);
-    const int n0 = nt * kNT;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int pt = wave & 1;   // p-tile of this wave (32 columns of headdim)
-    const int ntl = wave >> 1; // n-tile within the workgroup's 64 rows
+    const int pt = wave & 1;             // p-tile (32 columns of headdim)
+    const int nbase = slab * NW + (wave >> 1) * (NW / 2);  // first state row of this wave
     const int l32 = lane & 31, lg = lane >> 5;
-    const int ncol = n0 + ntl * 32 + l32;  // this lane's state row n
 
-    // accumulator = state tile (rows p, cols n); lane holds p = 32pt + 8q + 4lg + 0..3
+    // accumulators: state rows p (C-layout rows), cols n; lane holds p = 32pt + 8q + 4lg + 0..3
     const size_t sbase = ((size_t)b * nheads + h) * (size_t)N * P;
-    f32x16 acc;
+    f32x16 acc[NTW];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (h0) v = *reinterpret_cast<const float4 *>(h0 + sbase + (size_t)ncol * P + pt * 32 + 8 * q + 4 * lg);
-        acc[4 * q + 0] = v.x;
-        acc[4 * q + 1] = v.y;
-        acc[4 * q + 2] = v.z;
-        acc[4 * q + 3] = v.w;
-    }
+    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (h0)
+                v = *reinterpret_cast<const float4 *>(h0 + sbase + (size_t)(nbase + 32 * j + l32) * P + pt * 32 + 8 * q + 4 * lg);
+            acc[j][4 * q + 0] = v.x;
+            acc[j][4 * q + 1] = v.y;
+            acc[j][4 * q + 2] = v.z;
+            acc[j][4 * q + 3] = v.w;
+        }
 
-    // staging geometry: thread -> token row (tid >> 3) + 32k, 16-byte column (tid & 7)
-    const int srow = tid >> 3, scol = (tid & 7) * 8;
-    const uint16_t *xbase = x + (size_t)h * P + scol;
-    const uint16_t *bbase = B + (size_t)g * N + n0 + scol;
+    // staging geometry: x vector k of thread -> token (tid >> 3) + 32k, column 8 (tid & 7);
+    // B vector k -> token (tid / (NW/8)) + (256 / (NW/8)) k, slab column 8 (tid % (NW/8))
+    const int xrow = tid >> 3, xcol = (tid & 7) * 8;
+    constexpr int BPR = NW / 8;  // B vectors per token row of the slab
+    const int brow = tid / BPR, bcol = (tid % BPR) * 8;
+    const uint16_t *xbase = x + (size_t)h * P + xcol;
+    const uint16_t *bbase = B + (size_t)g * N + slab * NW + bcol;
     const size_t xstride = (size_t)nheads * P, bstride = (size_t)ngroups * N;
     const size_t hcs = ((size_t)b * nheads + h) * nchunks;  // (b, h) row of delta / cs
 
-    uint4 xr[VPT], br[VPT];
-    float dl[VPT];
-    double cv[VPT], ce;
-    auto prefetch = [&](int s) {
+    // One slice's worth of inputs in registers; two of them are in flight, so
+    // each load has two slices of work to arrive.  Token rows past the end of
+    // the sequence are clamped to its last row and used as they are: the scan
+    // writes Δ = 0 there, so their weight w is exactly zero (no select on the
+    // loaded value, which would make every load wait at once).
+    struct Slice {
+        uint4 xr[XV], br[BV];
+        float dl[XV];
+        double cv[XV], ce;
+    };
+    auto prefetch = [&](Slice &R, int s) {
         const int c = s / SPC, part = s - c * SPC;
-        const int tk = c * Q + part * KT;
-        const size_t cb = (hcs + c) * Q + part * KT;
-        ce = cs[(hcs + c) * Q + Q - 1];
+        const int tk = c * Q + part * kKT;
+        const size_t cb = (hcs + c) * Q + part * kKT;
+        R.ce = cs[(hcs + c) * Q + Q - 1];
 #pragma unroll
-        for (int k = 0; k < VPT; ++k) {
-            const int i = srow + 32 * k;
+        for (int k = 0; k < XV; ++k) {
+            const int i = xrow + 32 * k;
             const int t = tk + i;
-            const bool in = t < seqlen;
-            const size_t row = (size_t)b * seqlen + t;
-            xr[k] = in ? *reinterpret_cast<const uint4 *>(xbase + row * xstride) : make_uint4(0, 0, 0, 0);
-            br[k] = in ? *reinterpret_cast<const uint4 *>(bbase + row * bstride) : make_uint4(0, 0, 0, 0);
-            cv[k] = cs[cb + i];
-            dl[k] = delta[cb + i];
+            const size_t row = (size_t)b * seqlen + min(t, seqlen - 1);
+            R.xr[k] = ld16u(xbase + row * xstride);
+            R.cv[k] = cs[cb + i];
+            R.dl[k] = delta[cb + i];
+        }
+#pragma unroll
+        for (int k = 0; k < BV; ++k) {
+            const int t = tk + brow + (256 / BPR) * k;
+            const size_t row = (size_t)b * seqlen + min(t, seqlen - 1);
+            R.br[k] = ld16u(bbase + row * bstride);
         }
     };
-
-    const int rrow = tr_row(lane), rcol = tr_col(lane);
-    const uint16_t *xha = xh + pt * 32 + rcol;
-    const uint16_t *xla = xl + pt * 32 + rcol;
-    const uint16_t *ba = bs + ntl * 32 + rcol;
-    const int nslices = nchunks * SPC;
-    prefetch(0);
-    for (int s = 0; s < nslices; ++s) {
-        const int c = s / SPC, part = s - c * SPC;
-        const double cs_end = ce;
-        __syncthreads();  // previous slice's LDS readers are done
+    auto stage = [&](int buf, const Slice &R) {
 #pragma unroll
-        for (int k = 0; k < VPT; ++k) {
-            const float w = __expf((float)(cs_end - cv[k])) * dl[k];
-            const uint32_t in[4] = {xr[k].x, xr[k].y, xr[k].z, xr[k].w};
+        for (int k = 0; k < XV; ++k) {
+            const float w = __expf((float)(R.ce - R.cv[k])) * R.dl[k];
+            const uint32_t in[4] = {R.xr[k].x, R.xr[k].y, R.xr[k].z, R.xr[k].w};
             uint32_t hi[4], lo[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -210,59 +237,109 @@ __global__ __launch_bounds__(256, 2) void state_pass_kernel(
                 hi[e] = pack_bf16x2(f0, f1);
                 lo[e] = pack_bf16x2(f0 - bf16lo(hi[e]), f1 - bf16hi(hi[e]));
             }
-            const int i = srow + 32 * k;
-            *reinterpret_cast<uint4 *>(xh + i * kXP + scol) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-            *reinterpret_cast<uint4 *>(xl + i * kXP + scol) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-            *reinterpret_cast<uint4 *>(bs + i * kBP + scol) = br[k];
+            const int o = swz(xrow + 32 * k, xcol);
+            *reinterpret_cast<uint4 *>(&xh[buf][o]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            *reinterpret_cast<uint4 *>(&xl[buf][o]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
         }
-        if (s + 1 < nslices) prefetch(s + 1);
-        __syncthreads();
-
-        if (part == 0) {
-            // state entering chunk c, then its decay over the chunk
-            uint16_t *hp = hprev + ((((size_t)b * nchunks + c) * nheads + h) * N + ncol) * P + pt * 32 + 4 * lg;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t h01 = pack_bf16x2(acc[4 * q], acc[4 * q + 1]);
-                const uint32_t h23 = pack_bf16x2(acc[4 * q + 2], acc[4 * q + 3]);
-                const uint32_t l01 = pack_bf16x2(acc[4 * q] - bf16lo(h01), acc[4 * q + 1] - bf16hi(h01));
-                const uint32_t l23 = pack_bf16x2(acc[4 * q + 2] - bf16lo(h23), acc[4 * q + 3] - bf16hi(h23));
-                *reinterpret_cast<uint2 *>(hp + 8 * q) = make_uint2(h01, h23);
-                *reinterpret_cast<uint2 *>(hp + plane + 8 * q) = make_uint2(l01, l23);
+        for (int k = 0; k < BV; ++k)
+            *reinterpret_cast<uint4 *>(&bs[buf][swzn<NW>(brow + (256 / BPR) * k, bcol)]) = R.br[k];
+    };
+
+    // per-lane parts of the transposed-read addresses (rows advance in steps of 4)
+    const int rrow = tr_row(lane), rcol = tr_col(lane);
+    const int xoff = swz(rrow, pt * 32 + rcol);
+    int boff[NTW];
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) boff[j] = swzn<NW>(rrow, nbase - slab * NW + 32 * j + rcol);
+
+    // fold slice s (staged in LDS buffer buf) into the state; cs_end closes its chunk
+    auto consume = [&](int s, int buf, double cs_end) {
+        const int c = s / SPC, part = s - c * SPC;
+        if (part == 0) {
+            // state entering chunk c (head and tail planes), then its decay over the chunk
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+                uint16_t *hp = hprev + ((((size_t)b * nchunks + c) * nheads + h) * N + nbase + 32 * j + l32) * P +
+                               pt * 32 + 4 * lg;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t h01 = pack_bf16x2(acc[j][4 * q], acc[j][4 * q + 1]);
+                    const uint32_t h23 = pack_bf16x2(acc[j][4 * q + 2], acc[j][4 * q + 3]);
+                    const uint32_t l01 = pack_bf16x2(acc[j][4 * q] - bf16lo(h01), acc[j][4 * q + 1] - bf16hi(h01));
+                    const uint32_t l23 = pack_bf16x2(acc[j][4 * q + 2] - bf16lo(h23), acc[j][4 * q + 3] - bf16hi(h23));
+                    *reinterpret_cast<uint2 *>(hp + 8 * q) = make_uint2(h01, h23);
+                    *reinterpret_cast<uint2 *>(hp + plane + 8 * q) = make_uint2(l01, l23);
+                }
             }
             const float a = __expf((float)cs_end);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] *= a;
-        }
+            for (int j = 0; j < NTW; ++j)
 #pragma unroll
-        for (int ks = 0; ks < KT / 16; ++ks) {
-            const int row = 16 * ks + 8 * lg + rrow;
-            const bf16x8 bop = cat8(tr4(ba + row * kBP), tr4(ba + (row + 4) * kBP));
-            const bf16x8 ahi = cat8(tr4(xha + row * kXP), tr4(xha + (row + 4) * kXP));
-            const bf16x8 alo = cat8(tr4(xla + row * kXP), tr4(xla + (row + 4) * kXP));
-            acc = mfma(ahi, bop, acc);
-            acc = mfma(alo, bop, acc);
+                for (int r = 0; r < 16; ++r) acc[j][r] *= a;
         }
+        const uint16_t *xhb = xh[buf], *xlb = xl[buf], *bsb = bs[buf];
+#pragma unroll
+        for (int ks = 0; ks < kKT / 16; ++ks) {
+            const int r0 = 16 * ks + 8 * lg;  // multiple of 4: (row & 3) == rrow
+            const bf16x8 ahi = cat8(tr4(xhb + r0 * 64 + xoff), tr4(xhb + (r0 + 4) * 64 + xoff));
+            const bf16x8 alo = cat8(tr4(xlb + r0 * 64 + xoff), tr4(xlb + (r0 + 4) * 64 + xoff));
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+                const bf16x8 bop = cat8(tr4(bsb + r0 * NW + boff[j]), tr4(bsb + (r0 + 4) * NW + boff[j]));
+                acc[j] = mfma(ahi, bop, acc[j]);
+                acc[j] = mfma(alo, bop, acc[j]);
+            }
+        }
+    };
+
+    // Even slices live in LDS buffer 0 and register set RA, odd ones in 1 and RB.
+    // A slice is loaded two slices ahead of its use, staged into LDS right after
+    // the slice before it was consumed, and one barrier per slice separates the
+    // last reads of a buffer from its next staging.  Loads are issued
+    // unconditionally (the slice index is clamped at the end; the extra copies
+    // are never consumed) so that no branch makes the compiler wait for every
+    // outstanding load before staging.
+    const int nslices = nchunks * SPC;
+    const int last = nslices - 1;
+    Slice RA, RB;
+    prefetch(RA, 0);
+    prefetch(RB, min(1, last));
+    stage(0, RA);
+    double ce_staged = RA.ce;
+    for (int s = 0; s < nslices; s += 2) {
+        prefetch(RA, min(s + 2, last));
+        __syncthreads();
+        consume(s, 0, ce_staged);
+        if (s + 1 >= nslices) break;
+        stage(1, RB);
+        ce_staged = RB.ce;
+        prefetch(RB, min(s + 3, last));
+        __syncthreads();
+        consume(s + 1, 1, ce_staged);
+        stage(0, RA);  // buffer 0's last readers passed the barrier above
+        ce_staged = RA.ce;
     }
     if (final_state) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<float4 *>(final_state + sbase + (size_t)ncol * P + pt * 32 + 8 * q + 4 * lg) =
-                make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+        for (int j = 0; j < NTW; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<float4 *>(final_state + sbase + (size_t)(nbase + 32 * j + l32) * P + pt * 32 + 8 * q + 4 * lg) =
+                    make_float4(acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]);
     }
 }
 
 // =====================================================================
 // chunk output
 // =====================================================================
-constexpr int kOP = P + 8;  // LDS pitch (elements) of the x and hprev tiles
 constexpr int kSP = P + 8;  // LDS pitch (floats) of a wave's output staging tile
 
 template <int Q, int N>
 struct OutSmem {
-    uint16_t xs[Q * kOP];              // x of the chunk for the current head [i][p]
-    uint16_t hs[2][N * kOP];           // state entering the chunk [n][p], head and tail
-    float stage[(Q / 64) * 32 * kSP];  // one 32 x 64 output tile per wave
+    uint16_t xs[Q * 64];               // x of the chunk for the current head [i][p] (swizzled)
+    uint16_t hs[2][N * 64];            // state entering the chunk [n][p], head and tail (swizzled)
+    float stage[(Q / 32) * 32 * kSP];  // one 32 x 64 output tile per wave
     float vsh[Q];                      // exp(cs_r - cs_j)·Δ_j, r = end of j's 32-block
     float esh[Q];                      // exp(cs_i)
     float dsh[Q];                      // Δ_j
@@ -278,8 +355,8 @@ struct OutArgs {
     int seqlen, nheads, ngroups, nchunks, HB;
 };
 
-// One 32-token output strip I of one head:
-//   acc = Σ_{J<=I} M_IJ · X_J  +  exp(cs_i) ⊙ (C_I · hprev)
+// One 32-token output strip I of one head, on one wave:
+//   acc = exp(cs_i) ⊙ (C_I · hprev)  +  Σ_{J<=I} M_IJ · X_J
 // then y = acc + D·x through the wave's LDS staging tile (16-byte stores).
 template <int Q, int N, int I>
 __device__ __forceinline__ void out_strip(OutSmem<Q, N> &sm, const OutArgs &a, const f32x16 (&G)[I + 1],
@@ -288,14 +365,36 @@ __device__ __forceinline__ void out_strip(OutSmem<Q, N> &sm, const OutArgs &a, c
     const int l32 = lane & 31, lg = lane >> 5;
     const int rrow = tr_row(lane), rcol = tr_col(lane);
 
-    // C rows of the strip (A operands of C·hprev): issued now, used last
+    // state term first: C rows of the strip (A operands) times the hand-off state
     const int ti = t0 + 32 * I + l32;
-    const uint16_t *cp = a.C + (((size_t)b * a.seqlen + ti) * a.ngroups + g) * N + 8 * lg;
+    const bool iok = ti < a.seqlen;
+    const uint16_t *cp = a.C + (((size_t)b * a.seqlen + min(ti, a.seqlen - 1)) * a.ngroups + g) * N + 8 * lg;
     bf16x8 cop[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) cop[ks] = ti < a.seqlen ? ld16(cp + 16 * ks) : zero8();
-
+    for (int ks = 0; ks < KS; ++ks) cop[ks] = as8(keep_if(iok, ld16u(cp + 16 * ks)));
     f32x16 acc[2] = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+            for (int pt = 0; pt < 2; ++pt) {
+                const int r0 = 16 * ks + 8 * lg + rrow, col = pt * 32 + rcol;
+                acc[pt] = mfma(cop[ks], cat8(tr4(sm.hs[pl] + swz(r0, col)), tr4(sm.hs[pl] + swz(r0 + 4, col))), acc[pt]);
+            }
+    // rows i = 32I + 8q + 4lg + 0..3 scale by exp(cs_i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float4 e4 = *reinterpret_cast<const float4 *>(sm.esh + 32 * I + 8 * q + 4 * lg);
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt) {
+            acc[pt][4 * q + 0] *= e4.x;
+            acc[pt][4 * q + 1] *= e4.y;
+            acc[pt][4 * q + 2] *= e4.z;
+            acc[pt][4 * q + 3] *= e4.w;
+        }
+    }
+
     const double cs_i = sm.csh[32 * I + l32];
 #pragma unroll
     for (int J = 0; J <= I; ++J) {
@@ -331,36 +430,22 @@ __device__ __forceinline__ void out_strip(OutSmem<Q, N> &sm, const OutArgs &a, c
             const int row = 32 * J + 16 * kk + 4 * lg + rrow;
 #pragma unroll
             for (int pt = 0; pt < 2; ++pt) {
-                const uint16_t *p0 = sm.xs + row * kOP + pt * 32 + rcol;
-                const bf16x8 xop = cat8(tr4(p0), tr4(p0 + 8 * kOP));
+                const int col = pt * 32 + rcol;
+                const bf16x8 xop = cat8(tr4(sm.xs + swz(row, col)), tr4(sm.xs + swz(row + 8, col)));
                 acc[pt] = mfma(mh, xop, acc[pt]);
                 acc[pt] = mfma(ml, xop, acc[pt]);
             }
         }
     }
-    f32x16 off[2] = {};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-            for (int pl = 0; pl < 2; ++pl) {
-                const uint16_t *p0 = sm.hs[pl] + (16 * ks + 8 * lg + rrow) * kOP + pt * 32 + rcol;
-                off[pt] = mfma(cop[ks], cat8(tr4(p0), tr4(p0 + 4 * kOP)), off[pt]);
-            }
 
-    // acc += exp(cs_i)·off, rows i = 8q + 4lg + 0..3; stage as [row][p] float
+    // stage as [row][p] float, rows i = 8q + 4lg + 0..3
     float *st = sm.stage + wave * 32 * kSP;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const float4 e4 = *reinterpret_cast<const float4 *>(sm.esh + 32 * I + 8 * q + 4 * lg);
-        const float ev[4] = {e4.x, e4.y, e4.z, e4.w};
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int pt = 0; pt < 2; ++pt)
-                st[(8 * q + 4 * lg + e) * kSP + 32 * pt + l32] = acc[pt][4 * q + e] + ev[e] * off[pt][4 * q + e];
-    }
+            for (int pt = 0; pt < 2; ++pt) st[(8 * q + 4 * lg + e) * kSP + 32 * pt + l32] = acc[pt][4 * q + e];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -372,7 +457,7 @@ __device__ __forceinline__ void out_strip(OutSmem<Q, N> &sm, const OutArgs &a, c
         const int t = t0 + 32 * I + row;
         const float4 v0 = *reinterpret_cast<const float4 *>(st + row * kSP + cq);
         const float4 v1 = *reinterpret_cast<const float4 *>(st + row * kSP + cq + 4);
-        const uint4 xv = *reinterpret_cast<const uint4 *>(sm.xs + (32 * I + row) * kOP + cq);
+        const uint4 xv = *reinterpret_cast<const uint4 *>(sm.xs + swz(32 * I + row, cq));
         uint4 o;
         o.x = pack_bf16x2(v0.x + Dh * bf16lo(xv.x), v0.y + Dh * bf16hi(xv.x));
         o.y = pack_bf16x2(v0.z + Dh * bf16lo(xv.y), v0.w + Dh * bf16hi(xv.y));
@@ -381,9 +466,6 @@ __device__ __forceinline__ void out_strip(OutSmem<Q, N> &sm, const OutArgs &a, c
         if (t < a.seqlen)
             *reinterpret_cast<uint4 *>(a.y + (((size_t)b * a.seqlen + t) * a.nheads + h) * P + cq) = o;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // Gᵀ blocks of strip I: Gt[J] = B_J · C_Iᵀ, rows j of block J, cols i of strip I
@@ -393,41 +475,45 @@ __device__ __forceinline__ void g_blocks(const OutArgs &a, f32x16 (&Gt)[I + 1], 
     constexpr int KS = N / 16;
     const int l32 = lane & 31, lg = lane >> 5;
     const int ti = t0 + 32 * I + l32;
-    const uint16_t *cp = a.C + (((size_t)b * a.seqlen + ti) * a.ngroups + g) * N + 8 * lg;
+    const bool iok = ti < a.seqlen;
+    const uint16_t *cp = a.C + (((size_t)b * a.seqlen + min(ti, a.seqlen - 1)) * a.ngroups + g) * N + 8 * lg;
+    uint4 cr[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) cr[ks] = keep_if(iok, ld16u(cp + 16 * ks));
 #pragma unroll
     for (int J = 0; J <= I; ++J) {
         const int tj = t0 + 32 * J + l32;
-        const uint16_t *bp = a.B + (((size_t)b * a.seqlen + tj) * a.ngroups + g) * N + 8 * lg;
+        const bool jok = tj < a.seqlen;
+        const uint16_t *bp = a.B + (((size_t)b * a.seqlen + min(tj, a.seqlen - 1)) * a.ngroups + g) * N + 8 * lg;
+        uint4 brow[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) brow[ks] = keep_if(jok, ld16u(bp + 16 * ks));
         f32x16 acc = {};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 aop = tj < a.seqlen ? ld16(bp + 16 * ks) : zero8();
-            const bf16x8 bop = ti < a.seqlen ? ld16(cp + 16 * ks) : zero8();
-            acc = mfma(aop, bop, acc);
-        }
+        for (int ks = 0; ks < KS; ++ks) acc = mfma(as8(brow[ks]), as8(cr[ks]), acc);
         Gt[J] = acc;
     }
 }
 
-// Work of wave SA: strips SA and NS-1-SA (equal causal work for every wave).
-template <int Q, int N, int SA>
+// Work of the wave owning strip I.  Every wave of the workgroup runs the same
+// head loop (same barriers); the strips differ only in their causal blocks.
+template <int Q, int N, int I>
 __device__ __forceinline__ void output_wave(OutSmem<Q, N> &sm, const OutArgs &a, int b, int c, int g,
                                             int hbi) {
-    constexpr int NS = Q / 32, SB = NS - 1 - SA;
+    constexpr int NT = Q * 2;  // threads of the workgroup (Q/32 waves)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int t0 = c * Q;
     const int R = a.nheads / a.ngroups;
 
-    f32x16 GA[SA + 1], GB[SB + 1];
-    g_blocks<N, SA>(a, GA, b, g, t0, lane);
-    g_blocks<N, SB>(a, GB, b, g, t0, lane);
+    f32x16 G[I + 1];
+    g_blocks<N, I>(a, G, b, g, t0, lane);
 
     for (int k = 0; k < a.HB; ++k) {
         const int h = g * R + hbi * a.HB + k;
         const size_t cb = (((size_t)b * a.nheads + h) * a.nchunks + c) * Q;
         __syncthreads();  // previous head's LDS readers are done
-        {
-            const int i = tid;  // Q threads, one token each
+        if (tid < Q) {
+            const int i = tid;
             const double csi = a.cs[cb + i];
             const double csr = a.cs[cb + (i | 31)];
             const float di = a.delta[cb + i];
@@ -436,37 +522,52 @@ __device__ __forceinline__ void output_wave(OutSmem<Q, N> &sm, const OutArgs &a,
             sm.vsh[i] = __expf((float)(csr - csi)) * di;
             sm.esh[i] = __expf((float)csi);
         }
+        constexpr int XV = Q * 8 / NT;      // x vectors per thread
+        constexpr int HV = N * 8 / NT;      // hprev vectors per thread and plane
+        uint4 xv[XV], hv[2][HV];
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int v = tid + it * Q;
+        for (int it = 0; it < XV; ++it) {
+            const int v = tid + it * NT;
             const int i = v >> 3, q = v & 7;
             const int t = t0 + i;
-            uint4 raw = make_uint4(0, 0, 0, 0);
-            if (t < a.seqlen)
-                raw = *reinterpret_cast<const uint4 *>(a.x + (((size_t)b * a.seqlen + t) * a.nheads + h) * P + q * 8);
-            *reinterpret_cast<uint4 *>(sm.xs + i * kOP + q * 8) = raw;
+            xv[it] = keep_if(t < a.seqlen,
+                             ld16u(a.x + (((size_t)b * a.seqlen + min(t, a.seqlen - 1)) * a.nheads + h) * P + q * 8));
         }
         const uint16_t *hsrc = a.hprev + (((size_t)b * a.nchunks + c) * a.nheads + h) * (size_t)N * P;
 #pragma unroll
-        for (int it = 0; it < N * 8 / Q; ++it) {
-            const int v = tid + it * Q;
-            const int n = v >> 3, q = v & 7;
+        for (int it = 0; it < HV; ++it) {
+            const int v = tid + it * NT;
+#pragma unroll
+            for (int pl = 0; pl < 2; ++pl) hv[pl][it] = ld16u(hsrc + pl * a.plane + (size_t)(v >> 3) * P + (v & 7) * 8);
+        }
+#pragma unroll
+        for (int it = 0; it < XV; ++it) {
+            const int v = tid + it * NT;
+            *reinterpret_cast<uint4 *>(sm.xs + swz(v >> 3, (v & 7) * 8)) = xv[it];
+        }
+#pragma unroll
+        for (int it = 0; it < HV; ++it) {
+            const int v = tid + it * NT;
 #pragma unroll
             for (int pl = 0; pl < 2; ++pl)
-                *reinterpret_cast<uint4 *>(sm.hs[pl] + n * kOP + q * 8) =
-                    *reinterpret_cast<const uint4 *>(hsrc + pl * a.plane + (size_t)n * P + q * 8);
+                *reinterpret_cast<uint4 *>(sm.hs[pl] + swz(v >> 3, (v & 7) * 8)) = hv[pl][it];
         }
         __syncthreads();
-
         const float Dh = a.D ? a.D[h] : 0.0f;
-        out_strip<Q, N, SA>(sm, a, GA, b, g, h, t0, Dh, lane, wave);
-        out_strip<Q, N, SB>(sm, a, GB, b, g, h, t0, Dh, lane, wave);
+        out_strip<Q, N, I>(sm, a, G, b, g, h, t0, Dh, lane, wave);
     }
 }
 
+// strip owned by wave w: the first half of the waves take strips 0.., the second
+// half the strips from the end, so waves w and w + NS/2 (co-resident on one
+// SIMD) together cover NS + 1 causal blocks.
+template <int NS>
+constexpr int strip_of(int w) { return w < NS / 2 ? w : NS - 1 - (w - NS / 2); }
+
 template <int Q, int N>
-__global__ __launch_bounds__(Q, 1) void chunk_output_kernel(OutArgs a) {
+__global__ __launch_bounds__(2 * Q, 1) void chunk_output_kernel(OutArgs a) {
     __shared__ __attribute__((aligned(16))) OutSmem<Q, N> sm;
+    constexpr int NS = Q / 32;
     const int R = a.nheads / a.ngroups;
     const int nhb = R / a.HB;
     int bid = blockIdx.x;
@@ -477,10 +578,14 @@ __global__ __launch_bounds__(Q, 1) void chunk_output_kernel(OutArgs a) {
     const int c = bid % a.nchunks;
     const int b = bid / a.nchunks;
     switch (threadIdx.x >> 6) {
-    case 0: output_wave<Q, N, 0>(sm, a, b, c, g, hbi); break;
-    case 1: if constexpr (Q >= 128) output_wave<Q, N, 1>(sm, a, b, c, g, hbi); break;
-    case 2: if constexpr (Q >= 256) output_wave<Q, N, 2>(sm, a, b, c, g, hbi); break;
-    case 3: if constexpr (Q >= 256) output_wave<Q, N, 3>(sm, a, b, c, g, hbi); break;
+    case 0: output_wave<Q, N, strip_of<NS>(0)>(sm, a, b, c, g, hbi); break;
+    case 1: output_wave<Q, N, strip_of<NS>(1)>(sm, a, b, c, g, hbi); break;
+    case 2: if constexpr (NS >= 4) output_wave<Q, N, strip_of<NS>(2)>(sm, a, b, c, g, hbi); break;
+    case 3: if constexpr (NS >= 4) output_wave<Q, N, strip_of<NS>(3)>(sm, a, b, c, g, hbi); break;
+    case 4: if constexpr (NS >= 8) output_wave<Q, N, strip_of<NS>(4)>(sm, a, b, c, g, hbi); break;
+    case 5: if constexpr (NS >= 8) output_wave<Q, N, strip_of<NS>(5)>(sm, a, b, c, g, hbi); break;
+    case 6: if constexpr (NS >= 8) output_wave<Q, N, strip_of<NS>(6)>(sm, a, b, c, g, hbi); break;
+    case 7: if constexpr (NS >= 8) output_wave<Q, N, strip_of<NS>(7)>(sm, a, b, c, g, hbi); break;
     default: break;
     }
 }
@@ -499,29 +604,32 @@ hipError_t launch_state_pass_mfma(const void *x, const void *B, const float *del
                                   const float *h0, int batch, int seqlen, int nheads, int headdim,
                                   int dstate, int ngroups, int chunk, int nchunks, uint16_t *hprev,
                                   float *final_state, hipStream_t stream) {
-    if (headdim != P || dstate % kNT) return hipErrorInvalidValue;
-    const long long blocks = (long long)batch * nheads * (dstate / kNT);
-    if (blocks == 0) return hipSuccess;
+    if (headdim != P) return hipErrorInvalidValue;
+    const long long bh = (long long)batch * nheads;
+    if (bh == 0) return hipSuccess;
     const uint16_t *xp = static_cast<const uint16_t *>(x), *bp = static_cast<const uint16_t *>(B);
     const size_t plane = (size_t)batch * nchunks * nheads * dstate * P;  // head -> tail plane
-    dim3 grid((unsigned)blocks), block(256);
-    switch (chunk) {
-    case 64:
-        state_pass_kernel<64><<<grid, block, 0, stream>>>(xp, bp, delta, cs, h0, seqlen, nheads, dstate,
-                                                         ngroups, nchunks, hprev, plane, final_state);
-        break;
-    case 128:
-        state_pass_kernel<128><<<grid, block, 0, stream>>>(xp, bp, delta, cs, h0, seqlen, nheads, dstate,
-                                                          ngroups, nchunks, hprev, plane, final_state);
-        break;
-    case 256:
-        state_pass_kernel<256><<<grid, block, 0, stream>>>(xp, bp, delta, cs, h0, seqlen, nheads, dstate,
-                                                          ngroups, nchunks, hprev, plane, final_state);
-        break;
-    default:
-        return hipErrorInvalidValue;
+    // whole-state slabs while they fill the chip twice over, half slabs otherwise
+    const bool wide = dstate == 128 && bh >= 2 * kNumCUs;
+    const dim3 grid((unsigned)(bh * (wide ? 1 : dstate / 64))), block(256);
+#define SSD_SP(QQ, NN)                                                                                 \
+    if (chunk == QQ && dstate == NN) {                                                                 \
+        if (wide && NN == 128)                                                                         \
+            state_pass_kernel<QQ, NN, (NN == 128 ? 128 : 64)><<<grid, block, 0, stream>>>(             \
+                xp, bp, delta, cs, h0, seqlen, nheads, ngroups, nchunks, hprev, plane, final_state);   \
+        else                                                                                           \
+            state_pass_kernel<QQ, NN, 64><<<grid, block, 0, stream>>>(                                 \
+                xp, bp, delta, cs, h0, seqlen, nheads, ngroups, nchunks, hprev, plane, final_state);   \
+        return hipGetLastError();                                                                      \
     }
-    return hipGetLastError();
+    SSD_SP(64, 64)
+    SSD_SP(64, 128)
+    SSD_SP(128, 64)
+    SSD_SP(128, 128)
+    SSD_SP(256, 64)
+    SSD_SP(256, 128)
+#undef SSD_SP
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_chunk_output_mfma(const void *x, const void *B, const void *C, const float *D,
@@ -540,7 +648,7 @@ hipError_t launch_chunk_output_mfma(const void *x, const void *B, const void *C,
                  (size_t)batch * nchunks * nheads * dstate * P, seqlen, nheads, ngroups, nchunks, HB};
 #define SSD_OUT(QQ, NN)                                                                  \
     if (chunk == QQ && dstate == NN) {                                                   \
-        chunk_output_kernel<QQ, NN><<<grid, dim3(QQ), 0, stream>>>(args);                \
+        chunk_output_kernel<QQ, NN><<<grid, dim3(2 * QQ), 0, stream>>>(args);            \
         return hipGetLastError();                                                        \
     }
     SSD_OUT(64, 64)
