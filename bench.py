@@ -133,8 +133,8 @@ def prefill_work(c):
     b, L, H, P, N, G, Q = (c[k] for k in ("batch", "seqlen", "nheads", "headdim", "dstate",
                                           "ngroups", "chunk"))
     K = (L + Q - 1) // Q
-    x_bytes = b * L * H * P * 2
-    bc_bytes = b * L * G * N * 2
+    x_bytes = b * L * H * P * 2          # x, and likewise y
+    bc_bytes = b * L * G * N * 2         # B, and likewise C
     dt_bytes = b * L * H * 2
     final = b * H * N * P * 4 if c.get("final_state") else 0
     units_h = b * K * H
@@ -142,11 +142,11 @@ def prefill_work(c):
     return {
         "dt_cumsum": dict(bytes=dt_bytes, flops=0),
         # chunk state B^T(w x) and its hand-off: x and B read once (+ final state)
-        "state_pass": dict(bytes=x_bytes + bc_bytes / 2 + final, flops=units_h * 2 * Q * N * P),
+        "state_pass": dict(bytes=x_bytes + bc_bytes + final, flops=units_h * 2 * Q * N * P),
         # intra-chunk C B^T ⊙ mask · X and state -> output: x, B, C read, y written
-        "chunk_output": dict(bytes=2 * x_bytes + bc_bytes,
+        "chunk_output": dict(bytes=2 * x_bytes + 2 * bc_bytes,
                              flops=units_h * (Q * (Q + 1) * P + 2 * Q * N * P) + units_g * Q * (Q + 1) * N),
-        "total": dict(bytes=2 * x_bytes + bc_bytes + dt_bytes + final,
+        "total": dict(bytes=2 * x_bytes + 2 * bc_bytes + dt_bytes + final,
                       flops=units_h * (4 * Q * N * P + Q * (Q + 1) * P) + units_g * Q * (Q + 1) * N),
     }
 
@@ -276,6 +276,9 @@ def main():
     ap.add_argument("--legs", default="decode,long,mamba1",
                     help="extra legs to time besides the prefill step (comma list or 'none')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first copy a MIB-mebibyte device buffer 3 times: a plain copy kernel of "
+                         "known size, against which HBM byte counters are scaled")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU "
@@ -288,6 +291,17 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("no GPU visible: this benchmark needs an MI355X")
     ssd.lib()
+
+    if args.copy_calibration > 0:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 device copies of {nbytes} bytes")
+        del src, dst
 
     legs = [] if args.legs == "none" else [s for s in args.legs.split(",") if s]
     cfg = configs.MAMBA2_LAYER_PREFILL

@@ -6,8 +6,9 @@
 // decay one scalar per token and head, so every decay factor is an exp of a
 // difference of the within-chunk cumsums cs).  Two kernels:
 //
-//  state_pass   one workgroup per (batch row, head, 64 state rows n); walks the
-//               chunks in order with the state tile in MFMA accumulators:
+//  state_pass   one workgroup per (batch row, head, slab of 64 or 128 state
+//               rows n); walks the chunks in order with the state slab in MFMA
+//               accumulators:
 //                 hprev_c  = H_{c-1}                 (written as two bf16 planes)
 //                 H_c      = exp(cs_end)·H_{c-1} + Σ_i B_i (w_i x_i)ᵀ,
 //                 w_i      = exp(cs_end - cs_i)·Δ_i
