@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the selective state-space scan on one MI355X.
 
-One step = one chunked SSD prefill call (dt cumsum -> state pass -> chunk output)
-over the Mamba-2-2.7B-like layer shape: batch 8, seqlen 2048, 80 heads of
+One step = one chunked SSD prefill call (the fused bf16 prefill kernel: Δ cumsum,
+state passing, intra-chunk and state-to-output products in one launch) over the
+Mamba-2-2.7B-like layer shape: batch 8, seqlen 2048, 80 heads of
 headdim 64, dstate 128, one B/C group, chunk 256, bf16 inputs with float32
 accumulation and state.  Inputs are seeded synthetic tensors resident in HBM
 before the timed region.  W untimed warm-up steps, then K steps timed back to
@@ -37,7 +38,11 @@ MFMA_BF16_PEAK = 2.5e15    # dense bf16 flop/s
 VALU_F32_PEAK = 78.6e12    # non-packed fp32 FMA flop/s (256 CU x 64 lanes x 2 x 2.4 GHz)
 METRIC = "SSD prefill tokens/s and decode tokens/s at 2.7B-layer shape; % MFMA/HBM roofline"
 
-PREFILL_KERNELS = ["dt_cumsum", "state_pass", "chunk_output"]
+# kernels of one bf16 prefill call: the fused kernel alone, or, when the call is
+# cut into sequence segments (few (batch, head) pairs, long sequence), the
+# segment-state pass and the segment combine before it
+FUSED_KERNELS = ["ssd_fused"]
+SEGMENTED_KERNELS = ["segment_states", "segment_combine", "ssd_fused"]
 
 
 def log(*a):
@@ -128,8 +133,9 @@ def measured_traffic(kernel, workload, digest):
 
 
 def prefill_work(c):
-    """Algorithmic bytes and flops of each prefill kernel (inputs read once,
-    outputs written once; causal flops of the block decomposition)."""
+    """Algorithmic bytes and flops of a prefill call (inputs read once, outputs
+    written once; causal flops of the block decomposition at the workload's
+    chunk size)."""
     b, L, H, P, N, G, Q = (c[k] for k in ("batch", "seqlen", "nheads", "headdim", "dstate",
                                           "ngroups", "chunk"))
     K = (L + Q - 1) // Q
@@ -139,16 +145,12 @@ def prefill_work(c):
     final = b * H * N * P * 4 if c.get("final_state") else 0
     units_h = b * K * H
     units_g = b * K * G
-    return {
-        "dt_cumsum": dict(bytes=dt_bytes, flops=0),
-        # chunk state B^T(w x) and its hand-off: x and B read once (+ final state)
-        "state_pass": dict(bytes=x_bytes + bc_bytes + final, flops=units_h * 2 * Q * N * P),
-        # intra-chunk C B^T ⊙ mask · X and state -> output: x, B, C read, y written
-        "chunk_output": dict(bytes=2 * x_bytes + 2 * bc_bytes,
-                             flops=units_h * (Q * (Q + 1) * P + 2 * Q * N * P) + units_g * Q * (Q + 1) * N),
-        "total": dict(bytes=2 * x_bytes + 2 * bc_bytes + dt_bytes + final,
-                      flops=units_h * (4 * Q * N * P + Q * (Q + 1) * P) + units_g * Q * (Q + 1) * N),
-    }
+    total = dict(bytes=2 * x_bytes + 2 * bc_bytes + dt_bytes + final,
+                 flops=units_h * (4 * Q * N * P + Q * (Q + 1) * P) + units_g * Q * (Q + 1) * N)
+    # the fused kernel does all of it; the segment passes re-read x, B and dt
+    return {"ssd_fused": total, "total": total,
+            "segment_states": dict(bytes=x_bytes + bc_bytes + dt_bytes, flops=units_h * 2 * Q * N * P),
+            "segment_combine": dict(bytes=0, flops=0)}
 
 
 def bench_prefill(cfg, steps, warmup, seed=0):
@@ -167,15 +169,16 @@ def bench_prefill(cfg, steps, warmup, seed=0):
     y = torch.empty_like(x)
     fs = torch.empty(cfg["batch"], cfg["nheads"], cfg["dstate"], cfg["headdim"], device="cuda") \
         if cfg.get("final_state") else None
+    names = SEGMENTED_KERNELS if ws.numel() > 256 else FUSED_KERNELS
 
     def step():
         ssd.ssd_chunk_scan(x, dt, A, B, C, D, chunk=cfg["chunk"], workspace=ws, out=y,
                            return_final_state=fs is not None, final_state=fs)
 
     log(f"[bench] prefill {cfg['name']}: timing {steps} steps after {warmup} warm-up")
-    ms, per = time_calls(step, 3, steps, warmup)
+    ms, per = time_calls(step, len(names), steps, warmup)
     tokens = cfg["batch"] * cfg["seqlen"]
-    return dict(ms=ms, per_kernel_ms=dict(zip(PREFILL_KERNELS, per)), tokens=tokens,
+    return dict(ms=ms, per_kernel_ms=dict(zip(names, per)), tokens=tokens,
                 work=prefill_work(cfg), final_state=fs, y=y)
 
 
@@ -307,11 +310,11 @@ def main():
     cfg = configs.MAMBA2_LAYER_PREFILL
     workload = f"{cfg['name']}:b{cfg['batch']}L{cfg['seqlen']}H{cfg['nheads']}P{cfg['headdim']}" \
                f"N{cfg['dstate']}G{cfg['ngroups']}Q{cfg['chunk']}"
-    digest = source_digest(["selective_state_space_13_amd/csrc/ssd_mfma.hip",
+    digest = source_digest(["selective_state_space_13_amd/csrc/ssd_fused.hip",
                             "selective_state_space_13_amd/csrc/ssd_kernels.h"])
     pf = bench_prefill(cfg, args.steps, args.warmup)
     per = pf["per_kernel_ms"]
-    dom = max(("state_pass", "chunk_output"), key=lambda k: per[k])
+    dom = max(per, key=lambda k: per[k])
     roof = roofline_entry(dom, per[dom], pf["work"][dom], workload, digest)
     total_work = pf["work"]["total"]
     t_step = pf["ms"] * 1e-3

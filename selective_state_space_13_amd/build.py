@@ -22,7 +22,7 @@ SOURCES = [
     "api.cpp",
     "dt_cumsum.hip",
     "ssd_valu.hip",
-    "ssd_mfma.hip",
+    "ssd_fused.hip",
     "decode.hip",
     "selective_scan.hip",
     "misc.hip",

@@ -103,12 +103,14 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 int elem_size(int dtype) { return dtype == SSD_BF16 ? 2 : 4; }
 
-// bf16 prefill runs on the matrix cores; its hand-off states are bf16.
-bool prefill_uses_mfma(int dtype) { return dtype == SSD_BF16 && ssd::mfma_prefill_enabled; }
+// bf16 prefill runs as the fused matrix-core kernel; float32 inputs take the
+// vector-ALU path, whose stages (Δ, cs, hand-off states) live in the workspace.
+bool prefill_fused(int dtype) { return dtype == SSD_BF16; }
 
 struct ScanLayout {
     int nchunks = 0;
     size_t off_delta = 0, off_cs = 0, off_hprev = 0, total = 0;
+    ssd::FusedPlan plan;  // bf16 only
 };
 
 int check_scan_sizes(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
@@ -137,11 +139,18 @@ int scan_layout(int batch, int seqlen, int nheads, int headdim, int dstate, int 
     int st = check_scan_sizes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype);
     if (st) return st;
     lay.nchunks = (seqlen + chunk - 1) / chunk;
+    if (prefill_fused(dtype)) {
+        // segment buffers of long, narrow calls; otherwise nothing (a minimum of
+        // 256 bytes keeps 0 as the "unsupported" answer of the size query)
+        lay.plan = ssd::fused_plan(batch, seqlen, nheads, dstate);
+        lay.total = lay.plan.ws_bytes > 256 ? lay.plan.ws_bytes : 256;
+        return SSD_OK;
+    }
     uint64_t tok, states;
     if (!prod(tok, {batch, nheads, lay.nchunks, chunk}) ||
         !prod(states, {batch, lay.nchunks, nheads, headdim, dstate}))
         return fail(SSD_ERR_SHAPE, "workspace size overflows");
-    const size_t hbytes = 4;  // float, or two bf16 planes (head + tail) on the bf16 path
+    const size_t hbytes = 4;  // float hand-off states
     lay.off_delta = 0;
     lay.off_cs = round_up(tok * 4, 256);
     lay.off_hprev = lay.off_cs + round_up(tok * 8, 256);
@@ -191,6 +200,9 @@ int ssd_chunk_scan_workspace_layout(int batch, int seqlen, int nheads, int headd
     ScanLayout lay;
     int st = scan_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, lay);
     if (st) return st;
+    if (prefill_fused(dtype))
+        return fail(SSD_ERR_UNSUPPORTED, "the bf16 prefill keeps its stages on chip; only the "
+                                         "float32 path lays them out in the workspace");
     if (off_delta) *off_delta = lay.off_delta;
     if (off_cs) *off_cs = lay.off_cs;
     if (off_hprev) *off_hprev = lay.off_hprev;
@@ -243,30 +255,30 @@ int ssd_chunk_scan_fwd(int batch, int seqlen, int nheads, int headdim, int dstat
     if (st) return st;
 
     char *ws = static_cast<char *>(workspace);
+    LaunchMarks marks(stream);
+    hipError_t e;
+    if (prefill_fused(dtype)) {
+        static const char *what[3] = {"segment state launch", "segment combine launch",
+                                      "fused prefill launch"};
+        for (int phase = lay.plan.nseg > 1 ? 0 : 2; phase < 3; ++phase) {
+            marks.before();
+            e = ssd::launch_ssd_fused(phase, lay.plan, x, dt, A, B, C, D, initial_state, dt_softplus,
+                                      batch, seqlen, nheads, headdim, dstate, ngroups, y,
+                                      final_state, ws, stream);
+            marks.after();
+            if (e != hipSuccess) return hip_fail(e, what[phase]);
+        }
+        return SSD_OK;
+    }
     float *delta = reinterpret_cast<float *>(ws + lay.off_delta);
     double *cs = reinterpret_cast<double *>(ws + lay.off_cs);
     const int K = lay.nchunks;
-
-    LaunchMarks marks(stream);
     marks.before();
-    hipError_t e = ssd::launch_dt_cumsum(dtype, dt, A, dt_softplus, batch, seqlen, nheads, chunk,
-                                         K, delta, cs, stream);
+    e = ssd::launch_dt_cumsum(dtype, dt, A, dt_softplus, batch, seqlen, nheads, chunk, K, delta, cs,
+                              stream);
     marks.after();
     if (e != hipSuccess) return hip_fail(e, "dt cumsum launch");
-    if (prefill_uses_mfma(dtype)) {
-        uint16_t *hprev = reinterpret_cast<uint16_t *>(ws + lay.off_hprev);
-        marks.before();
-        e = ssd::launch_state_pass_mfma(x, B, delta, cs, initial_state, batch, seqlen, nheads,
-                                        headdim, dstate, ngroups, chunk, K, hprev, final_state,
-                                        stream);
-        marks.after();
-        if (e != hipSuccess) return hip_fail(e, "state pass launch");
-        marks.before();
-        e = ssd::launch_chunk_output_mfma(x, B, C, D, delta, cs, hprev, batch, seqlen, nheads,
-                                          headdim, dstate, ngroups, chunk, K, y, stream);
-        marks.after();
-        if (e != hipSuccess) return hip_fail(e, "chunk output launch");
-    } else {
+    {
         float *S = reinterpret_cast<float *>(ws + lay.off_hprev);
         marks.before();
         e = ssd::launch_chunk_state_valu(dtype, x, B, delta, cs, batch, seqlen, nheads, headdim,

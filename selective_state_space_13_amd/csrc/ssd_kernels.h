@@ -68,18 +68,22 @@ hipError_t launch_chunk_output_valu(int dtype, const void *x, const void *B, con
                                     int headdim, int dstate, int ngroups, int chunk, int nchunks,
                                     void *y, hipStream_t stream);
 
-// bf16 matrix-core path (mfma_prefill_enabled says whether it is built in).
-extern const bool mfma_prefill_enabled;
-// hprev: two planes [2][batch][nchunks][nheads][dstate][headdim] bf16 (head, tail).
-hipError_t launch_state_pass_mfma(const void *x, const void *B, const float *delta, const double *cs,
-                                  const float *h0, int batch, int seqlen, int nheads, int headdim,
-                                  int dstate, int ngroups, int chunk, int nchunks, uint16_t *hprev,
-                                  float *final_state, hipStream_t stream);
-hipError_t launch_chunk_output_mfma(const void *x, const void *B, const void *C, const float *D,
-                                    const float *delta, const double *cs, const uint16_t *hprev,
-                                    int batch, int seqlen, int nheads, int headdim, int dstate,
-                                    int ngroups, int chunk, int nchunks, void *y,
-                                    hipStream_t stream);
+// bf16 fused prefill (one kernel walks 64-token chunks per (batch, head) with the
+// state on chip).  Long sequences with few (batch, head) pairs are cut into
+// nseg segments: phase 0 computes each segment's local end state, phase 1
+// chains them into incoming states, phase 2 is the full pass.  With nseg == 1
+// only phase 2 runs and no workspace is used.
+struct FusedPlan {
+    int nchunks = 0, nseg = 1, seg_chunks = 1;
+    size_t state_bytes = 0, ws_bytes = 0;
+};
+FusedPlan fused_plan(int batch, int seqlen, int nheads, int dstate);
+hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const void *dt,
+                            const float *A, const void *B, const void *C, const float *D,
+                            const float *h0, int dt_softplus, int batch, int seqlen, int nheads,
+                            int headdim, int dstate, int ngroups, void *y, float *final_state,
+                            void *workspace, hipStream_t stream);
+
 
 // decode step, in-place float state
 hipError_t launch_decode_step(int dtype, const void *x, const void *dt, const float *A,

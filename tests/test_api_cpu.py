@@ -125,16 +125,29 @@ def test_scan_empty_batch_is_ok_without_pointers(L):
 def test_workspace_size_and_layout(L):
     prev = -1
     for Lq in [1, 63, 64, 65, 256, 257, 1000, 4096]:
-        s = L.ssd_chunk_scan_workspace_size(3, Lq, 8, 64, 128, 2, 64, BF16)
+        s = L.ssd_chunk_scan_workspace_size(3, Lq, 8, 64, 128, 2, 64, F32)
         assert s > 0 and s % 256 == 0 and s >= prev
         prev = s
-        od, oc, oh = ssd.chunk_scan_workspace_layout(3, Lq, 8, 64, 128, 2, 64, BF16)
+        od, oc, oh = ssd.chunk_scan_workspace_layout(3, Lq, 8, 64, 128, 2, 64, F32)
         K = (Lq + 63) // 64
         assert od == 0 and oc >= 3 * 8 * K * 64 * 4 and oh >= oc + 3 * 8 * K * 64 * 4
         assert oh < s and oc % 256 == 0 and oh % 256 == 0
+        assert oh + 3 * K * 8 * 128 * 64 * 4 <= s
     assert L.ssd_chunk_scan_workspace_size(3, 100, 8, 64, 100, 2, 64, BF16) == 0  # unsupported
+    assert L.ssd_chunk_scan_workspace_size(3, 100, 8, 64, 100, 2, 64, F32) == 0
     with pytest.raises(ssd.SSDError):
-        ssd.chunk_scan_workspace_layout(3, 100, 8, 33, 128, 2, 64, BF16)
+        ssd.chunk_scan_workspace_layout(3, 100, 8, 33, 128, 2, 64, F32)
+
+
+def test_bf16_workspace_is_small_or_segment_buffers(L):
+    # the fused bf16 path keeps its stages on chip: 256 bytes unless the call is
+    # cut into segments (few (batch, head) pairs, long sequence)
+    assert L.ssd_chunk_scan_workspace_size(8, 2048, 80, 64, 128, 1, 256, BF16) == 256
+    assert L.ssd_chunk_scan_workspace_size(0, 2048, 80, 64, 128, 1, 256, BF16) == 256
+    big = L.ssd_chunk_scan_workspace_size(1, 65536, 80, 64, 128, 8, 256, BF16)
+    assert big > 2 * 80 * 128 * 64 * 4 and big % 256 == 0
+    with pytest.raises(ssd.SSDError):
+        ssd.chunk_scan_workspace_layout(8, 2048, 80, 64, 128, 1, 256, BF16)
 
 
 def decode_call(L, b=4, H=8, P=64, N=128, G=1, dtype=BF16, ptrs=None):

@@ -83,10 +83,11 @@ def test_config1_tiny_fp32():
 
 
 def test_stages_delta_and_cumsum_from_workspace():
-    """Δ and the within-chunk cumsum read back from the workspace equal the
-    chunked formulation's stages."""
+    """Δ, the within-chunk cumsum and the hand-off states that the float32 path
+    leaves in its workspace equal the chunked formulation's stages (the bf16
+    path keeps them on chip)."""
     b, L, H, P, N, G, Q = 2, 300, 4, 64, 64, 2, 128
-    for dtype in ("f32", "bf16"):
+    for dtype in ("f32",):
         d = gen.ssd_inputs(b, L, H, P, N, G, dtype, seed=5, config_id=101)
         code = ssd.SSD_F32 if dtype == "f32" else ssd.SSD_BF16
         need = ssd.chunk_scan_workspace_size(b, L, H, P, N, G, Q, code)
@@ -106,18 +107,35 @@ def test_stages_delta_and_cumsum_from_workspace():
         assert np.all(delta[~valid] == 0.0)
         # Δ and Δ·A are rounded to float32 per token; the sum itself is float64
         np.testing.assert_allclose(cs[valid], st["cs"][valid], rtol=2e-6, atol=1e-9)
-        # the state entering each chunk, [n][p]: float for f32 inputs, bf16 for bf16
+        # the state entering each chunk, [n][p], float
         ne = b * K * H * P * N
-        if dtype == "f32":
-            hp = ws[oh:oh + 4 * ne].view(torch.float32)
-        else:  # head and tail planes
-            planes = ws[oh:oh + 4 * ne].view(torch.bfloat16).float()
-            hp = planes[:ne] + planes[ne:]
+        hp = ws[oh:oh + 4 * ne].view(torch.float32)
         hp = hp.reshape(b, K, H, N, P).double().cpu().numpy()
         ref = st["Hprev"]
         rms = np.sqrt(np.mean(ref ** 2))
         tol = 1e-4
         assert np.max(np.abs(hp - ref)) <= tol * rms, (dtype, np.max(np.abs(hp - ref)) / rms)
+
+
+SEGMENTED_CASES = [
+    # b, L, H, N, G, with_D, with_h0: few (batch, head) pairs and long sequences,
+    # which the bf16 path cuts into segments scanned in parallel
+    (1, 4096, 2, 128, 1, True, True),
+    (2, 3000, 3, 64, 3, False, True),     # ragged last chunk
+    (1, 8192, 1, 128, 1, True, False),
+]
+
+
+@pytest.mark.parametrize("case", SEGMENTED_CASES, ids=lambda c: "b{}L{}H{}N{}G{}".format(*c[:5]))
+def test_prefill_segmented_bf16(case):
+    b, L, H, N, G, wD, wh = case
+    # more than the 256-byte minimum: the call plans several segments
+    assert ssd.chunk_scan_workspace_size(b, L, H, 64, N, G, 256, ssd.SSD_BF16) > 256
+    d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=L + N, config_id=102, with_h0=wh)
+    y, fs = run_scan(d, 256, "bf16", wD, wh)
+    yo, fo = oracle_scan(d, wD, wh)
+    assert_parity(to_f64(y), yo, TAU_BF16, True, f"segmented y {case}")
+    assert_parity(to_f64(fs), fo, TAU_BF16, False, f"segmented final {case}")
 
 
 def test_prefill_extreme_decay_and_large_steps():
