@@ -93,6 +93,30 @@ __device__ __forceinline__ int swz(int row, int col) {
     return row * W + ((((col >> 3) ^ m)) << 3) + (col & 7);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave in float64, on DPP lane
+// moves (no LDS round trips): shifts by 1, 2, 4, 8 within each row of 16
+// lanes, then row 0's total into row 1 and row 2's into row 3, then lane 31's
+// running total into rows 2 and 3.  Lanes a move cannot reach add zero.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_add(double v) {
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROW_MASK, 0xf, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROW_MASK, 0xf, true);
+    return v + __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double wave_inclusive_scan(double v) {
+    v = dpp_add<0x111, 0xf>(v);  // row_shr:1
+    v = dpp_add<0x112, 0xf>(v);  // row_shr:2
+    v = dpp_add<0x114, 0xf>(v);  // row_shr:4
+    v = dpp_add<0x118, 0xf>(v);  // row_shr:8
+    v = dpp_add<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+    v = dpp_add<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+    return v;
+}
+__device__ __forceinline__ double read_lane(double v, int l) {
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
+                            __builtin_amdgcn_readlane(__double2loint(v), l));
+}
+
 // Lane geometry of ds_read_b64_tr_b16 for a 32x32x16 operand: source lane j
 // of a 16-lane group addresses row (j >> 2) & 3 of a 4-row slab and columns
 // 16·((j >> 4) & 1) + 4·(j & 3)..+3; each lane receives 4 consecutive rows of
@@ -100,23 +124,33 @@ __device__ __forceinline__ int swz(int row, int col) {
 __device__ __forceinline__ int tr_col(int lane) { return 16 * ((lane >> 4) & 1) + 4 * (lane & 3); }
 __device__ __forceinline__ int tr_row(int lane) { return (lane >> 2) & 3; }
 
+// Per-token values of one chunk (index = token), written by one wave.
+struct TokSmem {
+    double cs[kC];  // within-chunk inclusive cumsum of Δ·A_h (cs[63] closes the chunk)
+    float e[kC];    // exp(cs_i)
+    float v[kC];    // exp(cs_r - cs_j)·Δ_j, r = last token of j's 32-block
+    float d[kC];    // Δ
+    float w[kC];    // exp(cs_end - cs_j)·Δ_j, the weight of token j in the chunk's state
+};
+
+// Tiles read as transposed operands (ds_read_b64_tr_b16) are XOR-swizzled
+// (swz); tiles read only as k-contiguous 16-byte operands use a padded row
+// pitch of N + 8 elements instead, so their read offsets are immediates.
 template <int N, bool STATE_ONLY>
 struct FusedSmem {
-    uint16_t xs[2][kC * P];       // raw x, [t][p]; double-buffered (readout of c overlaps staging of c+1)
-    uint16_t xt[2][kC * P];       // w·x head and tail, [t][p]
-    uint16_t bs[kC * N];          // B rows, [t][n]
-    uint16_t cr[kC * N];          // C rows, [t][n]
-    uint16_t hs[2][P * N];        // state entering the chunk, head and tail, [p][n]
-    float stage[2][4][32 * kSt];  // partial outputs: M·X of waves 0-3, C·H of waves 4-7
-    double csh[kC];               // cs
-    float esh[kC];                // exp(cs_i)
-    float vsh[kC];                // exp(cs_r - cs_j)·Δ_j, r = last token of j's 32-block
-    float dsh[kC];                // Δ
+    uint16_t xs[2][kC * P];        // raw x [t][p]; double-buffered (readout of c overlaps staging of c+1)
+    uint16_t xt[2][kC * P];        // w·x head and tail [t][p]
+    uint16_t bs[kC * N];           // B [t][n]
+    uint16_t cr[kC * (N + 8)];     // C [t][n], padded
+    uint16_t hs[2][P * (N + 8)];   // state entering the chunk, head and tail, [p][n], padded
+    float stage[2][4][32 * kSt];   // partial outputs: M·X of waves 0-3, C·H of waves 4-7
+    TokSmem tok[2];                // per-token values of chunks c (even/odd)
 };
 template <int N>
-struct FusedSmem<N, true> {       // state-only pass: w·x and B only
+struct FusedSmem<N, true> {        // state-only pass: w·x and B only
     uint16_t xt[2][kC * P];
     uint16_t bs[kC * N];
+    TokSmem tok[2];
 };
 
 struct FusedArgs {
@@ -144,14 +178,20 @@ struct ChunkRegs {
 };
 
 // Roles of wave w in a workgroup (8 waves):
-//   state tile (32 n x 32 p): n-tile w >> 1, p-tile w & 1 (dstate 64: waves 0-3 only);
 //   output tile (32 tokens x 32 p) of the chunk: token strip (w >> 1) & 1, p-tile w & 1;
-//     waves 0-3 compute its C·Bᵀ blocks and masked M·X, waves 4-7 its C·H_prev.
+//     waves 0-3 compute its C·Bᵀ blocks and masked M·X, waves 4-7 its C·H_prev;
+//   state tiles (32 n x 32 p): waves 4 and 5 own both p-tiles of n-tiles 0 and 1;
+//     for dstate 128, waves 0, 1, 6, 7 own one p-tile each of n-tiles 2 and 3
+//     (waves 2 and 3, whose strip has two C·Bᵀ blocks, own none); the
+//     state-only pass gives every wave one tile (dstate 64: waves 0-3);
+//   one wave (kScanWave) also scans the next chunk's Δ·A while the others multiply.
 template <int N, bool STATE_ONLY>
 __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel(FusedArgs a) {
     constexpr int KS = N / 16;        // k-steps over n
     constexpr int BV = N / 64;
     constexpr int BPR = N / 8;        // 16-byte vectors per B/C row
+    constexpr int NP = N + 8;         // padded pitch of cr and hs
+    constexpr int kScanWave = STATE_ONLY ? (N == 128 ? 0 : 4) : 6;
     __shared__ __attribute__((aligned(16))) FusedSmem<N, STATE_ONLY> sm;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -174,10 +214,24 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
     const float Ah = a.A[h];
     const size_t bh = (size_t)b * a.nheads + h;
 
-    // ---- this wave's state tile: rows n = 32·snt + 8q + 4lg + e, cols p = 32·spt + l32
-    const bool owns_state = N == 128 || wave < 4;
-    const int snt = (wave >> 1) & (N / 32 - 1), spt = wave & 1;
-    f32x16 st;
+    // ---- this wave's state tiles: rows n = 32·snt + 8q + 4lg + e, cols p = 32·spt[j] + l32
+    int nst, snt, spt0;
+    if (STATE_ONLY) {
+        nst = (N == 128 || wave < 4) ? 1 : 0;
+        snt = (wave >> 1) & (N / 32 - 1);
+        spt0 = wave & 1;
+    } else if (wave == 4 || wave == 5) {
+        nst = 2;
+        snt = wave - 4;
+        spt0 = 0;
+    } else {
+        nst = (N == 128 && wave != 2 && wave != 3) ? 1 : 0;
+        snt = wave < 4 ? 2 : 3;
+        spt0 = wave & 1;
+    }
+    const bool owns_state = nst > 0;
+    const int spt1 = nst == 2 ? 1 : spt0;  // second tile (same n-tile), when there is one
+    f32x16 st[2];
     {
         const float *src = nullptr;
         if (seg == 0) {
@@ -186,67 +240,83 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
             src = a.hin + (bh * a.nseg + seg) * N * P;
         }
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            const int n = 32 * snt + 8 * (rr >> 2) + 4 * lg + (rr & 3);
-            st[rr] = (src && owns_state) ? src[n * P + 32 * spt + l32] : 0.0f;
+        for (int j = 0; j < 2; ++j) {
+            const int pc = 32 * (j ? spt1 : spt0) + l32;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int n = 32 * snt + 8 * (rr >> 2) + 4 * lg + (rr & 3);
+                st[j][rr] = (src && j < nst) ? src[n * P + pc] : 0.0f;
+            }
         }
     }
 
-    // ---- per-lane staging geometry
-    const int xrow = tid >> 3, xcol = (tid & 7) * 8;          // x: token, 8 columns of p
-    const int brow = tid / BPR, bcol = (tid % BPR) * 8;       // B/C: token (+ 512/BPR per vector)
+    // ---- per-lane geometry, fixed for the whole walk
+    const int xrow = tid >> 3, xcol = (tid & 7) * 8;          // x staging: token, 8 columns of p
+    const int brow = tid / BPR, bcol = (tid % BPR) * 8;       // B/C staging: token (+ 512/BPR per vector)
+    const int ox = swz<64>(xrow, xcol);                       // x / w·x staging offset
+    const int ob = swz<N>(brow, bcol);                        // B staging offset (+ (512/BPR)·N per vector)
+    const int oc = brow * NP + bcol;                          // C staging offset
+    // state update: transposed reads of rows 8lg + rrow (+4) (+16 per k-step)
+    const int o_sa = swz<N>(8 * lg + rrow, 32 * snt + rcol), o_sb = swz<N>(8 * lg + 4 + rrow, 32 * snt + rcol);
+    const int o_xa0 = swz<64>(8 * lg + rrow, 32 * spt0 + rcol), o_xb0 = swz<64>(8 * lg + 4 + rrow, 32 * spt0 + rcol);
+    const int o_xa1 = swz<64>(8 * lg + rrow, 32 * spt1 + rcol), o_xb1 = swz<64>(8 * lg + 4 + rrow, 32 * spt1 + rcol);
+    // output tile of this wave
+    const int tile = wave & 3, I = tile >> 1, pt = tile & 1;
+    const int o_cop = (32 * I + l32) * NP + 8 * lg;           // C strip rows (+16 per k-step)
+    const int o_hrd = (32 * pt + l32) * NP + 8 * lg;          // state [p][n] rows (+16 per k-step)
+    const int o_hw0 = (32 * spt0 + l32) * NP + 32 * snt + 4 * lg;  // state writes (+8 per q)
+    const int o_hw1 = (32 * spt1 + l32) * NP + 32 * snt + 4 * lg;
+    const int m_g = (((l32 & 3) << 1) | ((l32 >> 2) & 1) | (N == 128 ? ((l32 >> 3) & 1) << 3 : 0)) ^ lg;
+    const int o_ya = swz<64>(4 * lg + rrow, 32 * pt + rcol), o_yb = swz<64>(4 * lg + 8 + rrow, 32 * pt + rcol);
+
     const size_t xstride = (size_t)a.nheads * P, bstride = (size_t)a.ngroups * N;
-    const uint16_t *xbase = a.x + (size_t)h * P + xcol;
-    const uint16_t *bbase = a.B + (size_t)g * N + bcol;
-    const uint16_t *cbase = a.C + (size_t)g * N + bcol;
     const size_t row0 = (size_t)b * a.seqlen;
     const int last = a.seqlen - 1;
 
     ChunkRegs<N> R0;
     auto prefetch = [&](ChunkRegs<N> &Rg, int c) {
-        const int t0 = c * kC;
-        Rg.x = ld16(xbase + (row0 + min(t0 + xrow, last)) * xstride);
+        const int t0 = c * kC, lim = last - t0;  // rows past the end are clamped to the last one
+        const uint16_t *xc = a.x + ((row0 + t0) * a.nheads + h) * P + xcol;
+        Rg.x = ld16(xc + (size_t)min(xrow, lim) * xstride);
+        const uint16_t *bc = a.B + (row0 + t0) * bstride + (size_t)g * N + bcol;
+        const uint16_t *cc = a.C + (row0 + t0) * bstride + (size_t)g * N + bcol;
 #pragma unroll
         for (int k = 0; k < BV; ++k) {
-            const size_t rw = row0 + min(t0 + brow + (kThreads / BPR) * k, last);
-            Rg.b[k] = ld16(bbase + rw * bstride);
-            if constexpr (!STATE_ONLY) Rg.c[k] = ld16(cbase + rw * bstride);
+            const size_t rw = (size_t)min(brow + (kThreads / BPR) * k, lim) * bstride;
+            Rg.b[k] = ld16(bc + rw);
+            if constexpr (!STATE_ONLY) Rg.c[k] = ld16(cc + rw);
         }
-        const uint16_t raw = a.dt[(row0 + min(t0 + lane, last)) * a.nheads + h];
+        const uint16_t raw = a.dt[(row0 + t0 + min(lane, lim)) * a.nheads + h];
         Rg.dt = __uint_as_float((uint32_t)raw << 16);
     };
+    // Δ, the float64 inclusive cumsum of Δ·A over the chunk (lane = token) and
+    // the values derived from it; returns Σ Δ·A over the chunk
+    auto scan_chunk = [&](int c, float raw, TokSmem &T) -> double {
+        const bool ok = c * kC + lane < a.seqlen;
+        const float delta = ok ? (a.dt_softplus ? softplus_f32(raw) : raw) : 0.0f;
+        const double cs = wave_inclusive_scan((double)(delta * Ah));
+        const double cs_end = read_lane(cs, 63);
+        const double cs_r = lane < 32 ? read_lane(cs, 31) : cs_end;
+        T.cs[lane] = cs;
+        T.d[lane] = delta;
+        T.e[lane] = __expf((float)cs);
+        T.v[lane] = __expf((float)(cs_r - cs)) * delta;
+        T.w[lane] = __expf((float)(cs_end - cs)) * delta;
+        return cs_end;
+    };
 
-    prefetch(R0, c0);
     double seg_decay = 0.0;
+    prefetch(R0, c0);
+    if (wave == kScanWave) seg_decay += scan_chunk(c0, R0.dt, sm.tok[c0 & 1]);
+    __syncthreads();
 
     for (int c = c0; c < c1; ++c) {
         const int buf = c & 1;
         const int t0 = c * kC;
-        // ================= S1: scan of Δ·A and staging of chunk c
-        // every wave scans the chunk's 64 tokens (lane = token) in float64
-        const bool tok_ok = t0 + lane < a.seqlen;
-        const float delta = tok_ok ? (a.dt_softplus ? softplus_f32(R0.dt) : R0.dt) : 0.0f;
-        double cs = (double)(delta * Ah);
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const double o = __shfl_up(cs, off, 64);
-            if (lane >= off) cs += o;
-        }
-        const double cs_end = __shfl(cs, 63, 64);
-        const float wtok = __expf((float)(cs_end - cs)) * delta;
-        if constexpr (!STATE_ONLY) {
-            if (wave == 0) {
-                const double cs_r = __shfl(cs, lane | 31, 64);
-                sm.csh[lane] = cs;
-                sm.dsh[lane] = delta;
-                sm.esh[lane] = __expf((float)cs);
-                sm.vsh[lane] = __expf((float)(cs_r - cs)) * delta;
-            }
-        }
-        seg_decay += cs_end;
-        // x raw and w·x head/tail
+        const TokSmem &T = sm.tok[buf];
+        // ================= S1: staging of chunk c
         {
-            const float w = __shfl(wtok, xrow, 64);
+            const float w = T.w[xrow];
             const uint32_t in[4] = {R0.x.x, R0.x.y, R0.x.z, R0.x.w};
             uint32_t hi[4], lo[4];
 #pragma unroll
@@ -255,36 +325,36 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
                 hi[e] = pack_bf16x2(f0, f1);
                 lo[e] = pack_bf16x2(f0 - bf16lo(hi[e]), f1 - bf16hi(hi[e]));
             }
-            const int o = swz<64>(xrow, xcol);
-            if constexpr (!STATE_ONLY) *reinterpret_cast<uint4 *>(&sm.xs[buf][o]) = R0.x;
-            *reinterpret_cast<uint4 *>(&sm.xt[0][o]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-            *reinterpret_cast<uint4 *>(&sm.xt[1][o]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+            if constexpr (!STATE_ONLY) *reinterpret_cast<uint4 *>(&sm.xs[buf][ox]) = R0.x;
+            *reinterpret_cast<uint4 *>(&sm.xt[0][ox]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            *reinterpret_cast<uint4 *>(&sm.xt[1][ox]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
         }
 #pragma unroll
         for (int k = 0; k < BV; ++k) {
-            const int o = swz<N>(brow + (kThreads / BPR) * k, bcol);
-            *reinterpret_cast<uint4 *>(&sm.bs[o]) = R0.b[k];
-            if constexpr (!STATE_ONLY) *reinterpret_cast<uint4 *>(&sm.cr[o]) = R0.c[k];
+            *reinterpret_cast<uint4 *>(&sm.bs[ob + k * (kThreads / BPR) * N]) = R0.b[k];
+            if constexpr (!STATE_ONLY) *reinterpret_cast<uint4 *>(&sm.cr[oc + k * (kThreads / BPR) * NP]) = R0.c[k];
         }
         // state entering the chunk -> LDS as [p][n] head/tail, then its decay over the chunk
         if (owns_state) {
-            if constexpr (!STATE_ONLY) {
-                const int p = 32 * spt + l32;
+            const float dec = __expf((float)T.cs[kC - 1]);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int n = 32 * snt + 8 * q + 4 * lg;
-                    const float v[4] = {st[4 * q], st[4 * q + 1], st[4 * q + 2], st[4 * q + 3]};
-                    const uint32_t h01 = pack_bf16x2(v[0], v[1]), h23 = pack_bf16x2(v[2], v[3]);
-                    const uint32_t l01 = pack_bf16x2(v[0] - bf16lo(h01), v[1] - bf16hi(h01));
-                    const uint32_t l23 = pack_bf16x2(v[2] - bf16lo(h23), v[3] - bf16hi(h23));
-                    const int o = swz<N>(p, n);
-                    *reinterpret_cast<uint2 *>(&sm.hs[0][o]) = make_uint2(h01, h23);
-                    *reinterpret_cast<uint2 *>(&sm.hs[1][o]) = make_uint2(l01, l23);
+            for (int j = 0; j < 2; ++j) {
+                if (j >= nst) break;
+                if constexpr (!STATE_ONLY) {
+                    const int ow = j ? o_hw1 : o_hw0;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float v[4] = {st[j][4 * q], st[j][4 * q + 1], st[j][4 * q + 2], st[j][4 * q + 3]};
+                        const uint32_t h01 = pack_bf16x2(v[0], v[1]), h23 = pack_bf16x2(v[2], v[3]);
+                        const uint32_t l01 = pack_bf16x2(v[0] - bf16lo(h01), v[1] - bf16hi(h01));
+                        const uint32_t l23 = pack_bf16x2(v[2] - bf16lo(h23), v[3] - bf16hi(h23));
+                        *reinterpret_cast<uint2 *>(&sm.hs[0][ow + 8 * q]) = make_uint2(h01, h23);
+                        *reinterpret_cast<uint2 *>(&sm.hs[1][ow + 8 * q]) = make_uint2(l01, l23);
+                    }
                 }
-            }
-            const float dec = __expf((float)cs_end);
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) st[rr] *= dec;
+                for (int rr = 0; rr < 16; ++rr) st[j][rr] *= dec;
+            }
         }
         // next chunk's inputs (clamped to the last chunk: loads stay unconditional)
         prefetch(R0, min(c + 1, c1 - 1));
@@ -295,34 +365,37 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
             // H[n][p] += Σ_t B[t][n]·(w x)[t][p]: A = Bᵀ (rows n, k = t), B = w·x (k = t, cols p)
 #pragma unroll
             for (int ks = 0; ks < kC / 16; ++ks) {
-                const int ra = 16 * ks + 8 * lg + rrow, rb = ra + 4;
-                const int ncol = 32 * snt + rcol, pcol = 32 * spt + rcol;
-                const bf16x8 aop = cat8(tr4(sm.bs + swz<N>(ra, ncol)), tr4(sm.bs + swz<N>(rb, ncol)));
-                const bf16x8 bhi = cat8(tr4(sm.xt[0] + swz<64>(ra, pcol)), tr4(sm.xt[0] + swz<64>(rb, pcol)));
-                const bf16x8 blo = cat8(tr4(sm.xt[1] + swz<64>(ra, pcol)), tr4(sm.xt[1] + swz<64>(rb, pcol)));
-                st = mfma(aop, bhi, st);
-                st = mfma(aop, blo, st);
+                const bf16x8 aop = cat8(tr4(sm.bs + o_sa + 16 * ks * N), tr4(sm.bs + o_sb + 16 * ks * N));
+                {
+                    const bf16x8 bhi = cat8(tr4(sm.xt[0] + o_xa0 + 16 * ks * 64), tr4(sm.xt[0] + o_xb0 + 16 * ks * 64));
+                    const bf16x8 blo = cat8(tr4(sm.xt[1] + o_xa0 + 16 * ks * 64), tr4(sm.xt[1] + o_xb0 + 16 * ks * 64));
+                    st[0] = mfma(aop, bhi, st[0]);
+                    st[0] = mfma(aop, blo, st[0]);
+                }
+                if (nst == 2) {
+                    const bf16x8 bhi = cat8(tr4(sm.xt[0] + o_xa1 + 16 * ks * 64), tr4(sm.xt[0] + o_xb1 + 16 * ks * 64));
+                    const bf16x8 blo = cat8(tr4(sm.xt[1] + o_xa1 + 16 * ks * 64), tr4(sm.xt[1] + o_xb1 + 16 * ks * 64));
+                    st[1] = mfma(aop, bhi, st[1]);
+                    st[1] = mfma(aop, blo, st[1]);
+                }
             }
         }
         if constexpr (!STATE_ONLY) {
-            const int tile = wave & 3;
-            const int I = tile >> 1, pt = tile & 1;
             // C rows of the strip as operands (rows i, k = n)
             bf16x8 cop[KS];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) cop[ks] = as8(ld16(sm.cr + swz<N>(32 * I + l32, 16 * ks + 8 * lg)));
+            for (int ks = 0; ks < KS; ++ks) cop[ks] = as8(ld16(sm.cr + o_cop + 16 * ks));
             f32x16 acc = {};
             if (wave >= 4) {
                 // C·H_prev over all n, rows scaled by exp(cs_i)
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const int o = swz<N>(32 * pt + l32, 16 * ks + 8 * lg);
-                    acc = mfma(cop[ks], as8(ld16(sm.hs[0] + o)), acc);
-                    acc = mfma(cop[ks], as8(ld16(sm.hs[1] + o)), acc);
+                    acc = mfma(cop[ks], as8(ld16(sm.hs[0] + o_hrd + 16 * ks)), acc);
+                    acc = mfma(cop[ks], as8(ld16(sm.hs[1] + o_hrd + 16 * ks)), acc);
                 }
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float4 e4 = *reinterpret_cast<const float4 *>(sm.esh + 32 * I + 8 * q + 4 * lg);
+                    const float4 e4 = *reinterpret_cast<const float4 *>(T.e + 32 * I + 8 * q + 4 * lg);
                     acc[4 * q + 0] *= e4.x;
                     acc[4 * q + 1] *= e4.y;
                     acc[4 * q + 2] *= e4.z;
@@ -330,20 +403,21 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
                 }
             } else {
                 // Gᵀ blocks (rows j of block J, cols i of strip I) and M·X
-                const double cs_i = sm.csh[32 * I + l32];
+                const double cs_i = T.cs[32 * I + l32];
                 for (int J = 0; J <= I; ++J) {
                     f32x16 gt = {};
+                    const uint16_t *brw = sm.bs + (32 * J + l32) * N;
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks)
-                        gt = mfma(as8(ld16(sm.bs + swz<N>(32 * J + l32, 16 * ks + 8 * lg))), cop[ks], gt);
-                    const double cs_r = sm.csh[32 * J + 31];
+                        gt = mfma(as8(ld16(brw + (((2 * ks) ^ m_g) << 3))), cop[ks], gt);
+                    const double cs_r = T.cs[32 * J + 31];
                     float m[16];
-                    const bool exact = J == I && (float)(sm.csh[32 * J] - cs_r) > kMaxBlockDecay;
+                    const bool exact = J == I && (float)(T.cs[32 * J] - cs_r) > kMaxBlockDecay;
                     if (!exact) {
                         const float u = __expf((float)(cs_i - cs_r));
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
-                            const float4 v4 = *reinterpret_cast<const float4 *>(sm.vsh + 32 * J + 8 * q + 4 * lg);
+                            const float4 v4 = *reinterpret_cast<const float4 *>(T.v + 32 * J + 8 * q + 4 * lg);
                             m[4 * q + 0] = gt[4 * q + 0] * (v4.x * u);
                             m[4 * q + 1] = gt[4 * q + 1] * (v4.y * u);
                             m[4 * q + 2] = gt[4 * q + 2] * (v4.z * u);
@@ -353,7 +427,7 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
 #pragma unroll
                         for (int rr = 0; rr < 16; ++rr) {
                             const int j = 32 * J + 8 * (rr >> 2) + 4 * lg + (rr & 3);
-                            m[rr] = gt[rr] * __expf((float)(cs_i - sm.csh[j])) * sm.dsh[j];
+                            m[rr] = gt[rr] * __expf((float)(cs_i - T.cs[j])) * T.d[j];
                         }
                     }
                     if (J == I) {
@@ -363,13 +437,12 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
                     }
                     // A operand slot (lane, k) holds row j = 16kk + 4lg + {0..3, 8..11}; the
                     // x operand is read with the same permutation
+                    const uint16_t *xj = sm.xs[buf] + 32 * J * 64;
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk) {
                         bf16x8 mh, ml;
                         split8(m + 8 * kk, mh, ml);
-                        const int row = 32 * J + 16 * kk + 4 * lg + rrow;
-                        const int col = 32 * pt + rcol;
-                        const bf16x8 xop = cat8(tr4(sm.xs[buf] + swz<64>(row, col)), tr4(sm.xs[buf] + swz<64>(row + 8, col)));
+                        const bf16x8 xop = cat8(tr4(xj + o_ya + 16 * kk * 64), tr4(xj + o_yb + 16 * kk * 64));
                         acc = mfma(mh, xop, acc);
                         acc = mfma(ml, xop, acc);
                     }
@@ -381,25 +454,27 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
 #pragma unroll
                 for (int e = 0; e < 4; ++e) stp[(8 * q + 4 * lg + e) * kSt + l32] = acc[4 * q + e];
         }
+        // the next chunk's per-token values, while the products run
+        if (wave == kScanWave && c + 1 < c1) seg_decay += scan_chunk(c + 1, R0.dt, sm.tok[buf ^ 1]);
         __syncthreads();
 
         // ================= S3: y = partials + D·x, 16-byte bf16 rows
         if constexpr (!STATE_ONLY) {
             const int row = tid >> 3, cq = (tid & 7) * 8;
-            const int I = row >> 5, rl = row & 31, pt = cq >> 5, cl = cq & 31;
-            const float *s0 = sm.stage[0][2 * I + pt] + rl * kSt + cl;
-            const float *s1 = sm.stage[1][2 * I + pt] + rl * kSt + cl;
+            const int Io = row >> 5, rl = row & 31, po = cq >> 5, cl = cq & 31;
+            const float *s0 = sm.stage[0][2 * Io + po] + rl * kSt + cl;
+            const float *s1 = sm.stage[1][2 * Io + po] + rl * kSt + cl;
             const float4 a0 = *reinterpret_cast<const float4 *>(s0), a1 = *reinterpret_cast<const float4 *>(s0 + 4);
             const float4 b0 = *reinterpret_cast<const float4 *>(s1), b1 = *reinterpret_cast<const float4 *>(s1 + 4);
-            const uint4 xv = *reinterpret_cast<const uint4 *>(sm.xs[buf] + swz<64>(row, cq));
+            const uint4 xv = *reinterpret_cast<const uint4 *>(sm.xs[buf] + ox);
             const float Dh = a.D ? a.D[h] : 0.0f;
             uint4 o;
             o.x = pack_bf16x2(a0.x + b0.x + Dh * bf16lo(xv.x), a0.y + b0.y + Dh * bf16hi(xv.x));
             o.y = pack_bf16x2(a0.z + b0.z + Dh * bf16lo(xv.y), a0.w + b0.w + Dh * bf16hi(xv.y));
             o.z = pack_bf16x2(a1.x + b1.x + Dh * bf16lo(xv.z), a1.y + b1.y + Dh * bf16hi(xv.z));
             o.w = pack_bf16x2(a1.z + b1.z + Dh * bf16lo(xv.w), a1.w + b1.w + Dh * bf16hi(xv.w));
-            const int t = t0 + row;
-            if (t < a.seqlen) *reinterpret_cast<uint4 *>(a.y + ((row0 + t) * a.nheads + h) * P + cq) = o;
+            if (t0 + row < a.seqlen)
+                *reinterpret_cast<uint4 *>(a.y + ((row0 + t0) * a.nheads + h) * P + (size_t)row * xstride + cq) = o;
         }
     }
 
@@ -407,14 +482,19 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
     float *dst = nullptr;
     if (STATE_ONLY) {
         dst = a.seg_state + (bh * a.nseg + seg) * N * P;
-        if (tid == 0) a.seg_decay[bh * a.nseg + seg] = seg_decay;
+        if (wave == kScanWave && lane == 0) a.seg_decay[bh * a.nseg + seg] = seg_decay;
     } else if (a.final_state && seg == a.nseg - 1) {
         dst = a.final_state + bh * N * P;
     }
-    if (dst && owns_state) {
+    if (dst) {
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr)
-            dst[(32 * snt + 8 * (rr >> 2) + 4 * lg + (rr & 3)) * P + 32 * spt + l32] = st[rr];
+        for (int j = 0; j < 2; ++j) {
+            if (j >= nst) break;
+            const int pc = 32 * (j ? spt1 : spt0) + l32;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr)
+                dst[(32 * snt + 8 * (rr >> 2) + 4 * lg + (rr & 3)) * P + pc] = st[j][rr];
+        }
     }
 }
 
