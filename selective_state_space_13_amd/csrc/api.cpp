@@ -340,8 +340,11 @@ int ssd_decode_step(int batch, int nheads, int headdim, int dstate, int ngroups,
 }
 
 size_t selective_scan_workspace_size(int batch, int seqlen, int dim, int dstate, int dtype) {
-    (void)batch, (void)seqlen, (void)dim, (void)dstate, (void)dtype;
-    return 0;
+    if ((dtype != SSD_F32 && dtype != SSD_BF16) || batch < 0 || seqlen < 0 || dim < 1 ||
+        (dstate != 4 && dstate != 8 && dstate != 16) || dim % 64)
+        return 0;
+    // segment buffers when the call is cut into time segments; otherwise none
+    return ssd::selective_scan_plan(batch, seqlen, dim, dstate).ws_bytes;
 }
 
 int selective_scan_fwd(int batch, int seqlen, int dim, int dstate, int dtype, int delta_softplus,
@@ -349,7 +352,6 @@ int selective_scan_fwd(int batch, int seqlen, int dim, int dstate, int dtype, in
                        const void *C, const float *D, const void *z, void *out,
                        float *final_state, void *workspace, size_t workspace_bytes,
                        void *stream_) {
-    (void)workspace, (void)workspace_bytes;
     if (dtype != SSD_F32 && dtype != SSD_BF16)
         return fail(SSD_ERR_UNSUPPORTED, "dtype %d is not SSD_F32 or SSD_BF16", dtype);
     if (batch < 0 || seqlen < 0)
@@ -371,21 +373,35 @@ int selective_scan_fwd(int batch, int seqlen, int dim, int dstate, int dtype, in
     for (const void *p : ptrs)
         if (p && !aligned(p, 16)) return fail(SSD_ERR_ALIGN, "tensor pointer %p is not 16-byte aligned", p);
     const int es = elem_size(dtype);
+    const ssd::ScanPlan plan = ssd::selective_scan_plan(batch, seqlen, dim, dstate);
+    if (plan.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < plan.ws_bytes)
+            return fail(SSD_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", plan.ws_bytes,
+                        workspace_bytes, workspace ? "" : " (NULL)");
+        if (!aligned(workspace, 256)) return fail(SSD_ERR_ALIGN, "workspace must be 256-byte aligned");
+    }
     int st = check_alias(
-        {span("out", out, n_u * es), span("final_state", final_state, n_state * 4)},
+        {span("out", out, n_u * es), span("final_state", final_state, n_state * 4),
+         span("workspace", plan.ws_bytes ? workspace : nullptr, plan.ws_bytes)},
         {span("u", u, n_u * es), span("delta", delta, n_u * es),
          span("A", A, (uint64_t)dim * dstate * 4), span("B", B, n_bc * es),
          span("C", C, n_bc * es), span("D", D, D ? (uint64_t)dim * 4 : 0),
          span("z", z, z ? n_u * es : 0)});
     if (st) return st;
     if (seqlen == 0 && !final_state) return SSD_OK;
-    LaunchMarks marks(static_cast<hipStream_t>(stream_));
-    marks.before();
-    hipError_t e = ssd::launch_selective_scan(dtype, u, delta, A, B, C, D, z, delta_softplus, batch,
-                                              seqlen, dim, dstate, out, final_state,
-                                              static_cast<hipStream_t>(stream_));
-    marks.after();
-    return e == hipSuccess ? SSD_OK : hip_fail(e, "selective scan launch");
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    LaunchMarks marks(stream);
+    static const char *what[3] = {"segment state launch", "segment combine launch",
+                                  "selective scan launch"};
+    for (int phase = plan.nseg > 1 ? 0 : 2; phase < 3; ++phase) {
+        marks.before();
+        hipError_t e = ssd::launch_selective_scan(phase, plan, dtype, u, delta, A, B, C, D, z,
+                                                  delta_softplus, batch, seqlen, dim, dstate, out,
+                                                  final_state, workspace, stream);
+        marks.after();
+        if (e != hipSuccess) return hip_fail(e, what[phase]);
+    }
+    return SSD_OK;
 }
 
 }  // extern "C"

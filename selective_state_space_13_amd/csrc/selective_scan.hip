@@ -7,9 +7,15 @@
 //     Δ = softplus(delta);  s[n] <- exp(Δ·A[d][n])·s[n] + Δ·u·B_t[n]
 //     out = (Σ_n C_t[n]·s[n] + D[d]·u) · z·sigmoid(z)
 //
-// One lane owns one (batch row, channel) and its dstate-vector state in
-// registers; a 64-lane wave covers 64 consecutive channels, so every u, delta,
-// z and out access of the wave is one contiguous 128-byte (bf16) segment.
+// One lane owns one (batch row, channel, time segment) and its dstate-vector
+// state in registers; a 64-lane wave covers 64 consecutive channels, so every
+// u, delta, z and out access of the wave is one contiguous 128-byte (bf16)
+// segment.  A batch x channels grid alone gives well under one wave per SIMD,
+// so the sequence is cut into segments scanned in parallel: a state-only pass
+// (MODE 0) gives each segment's end state from a zero start and its Σ Δ, a
+// small combine chains them into each segment's incoming state, and the
+// output pass (MODE 1) runs every segment from that state.  The recurrence is
+// linear in the state, so this is the same computation regrouped.
 // Time is processed in tiles of kT steps: while a tile is computed, the next
 // tile's u/delta/z are already in flight into registers, and its B_t/C_t rows
 // (the same for the whole workgroup) are staged once in LDS as float32.
@@ -36,28 +42,41 @@ __device__ __forceinline__ float softplus_fast(float r) {
 template <typename T>
 __device__ __forceinline__ float ldf(const T *p) { return to_f32(*p); }
 
-template <typename T, int N>
+struct ScanArgs {
+    int delta_softplus, seqlen, dim;
+    int nseg, seg_len;       // segments of seg_len steps (a multiple of kT)
+    float *seg_state;        // [b][S][dim][N] local end state of each segment (MODE 0)
+    float *seg_dsum;         // [b][S][dim] Σ Δ over each segment (MODE 0)
+    const float *hin;        // [b][S][dim][N] state entering each segment s >= 1 (MODE 1)
+};
+
+template <typename T, int N, int MODE>
 __global__ __launch_bounds__(256) void selective_scan_kernel(
     const T *__restrict__ u, const T *__restrict__ delta, const float *__restrict__ A,
     const T *__restrict__ B, const T *__restrict__ C, const float *__restrict__ D,
-    const T *__restrict__ z, int delta_softplus, int seqlen, int dim, T *__restrict__ out,
-    float *__restrict__ final_state) {
+    const T *__restrict__ z, ScanArgs sa, T *__restrict__ out, float *__restrict__ final_state) {
     __shared__ float bc[2][kT][2 * N];  // double-buffered B_t, C_t rows of a tile
+    const int delta_softplus = sa.delta_softplus, seqlen = sa.seqlen, dim = sa.dim;
 
     const int d = blockIdx.x * blockDim.x + threadIdx.x;
     const int b = blockIdx.y;
+    const int seg = blockIdx.z;
     const bool active = d < dim;
     const int dd = active ? d : dim - 1;  // inactive lanes read a valid address, write nothing
+    const size_t sidx = ((size_t)b * sa.nseg + seg) * dim + dd;  // (b, segment, channel)
 
     float A2[N], s[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) {
         A2[n] = A[(size_t)dd * N + n] * kLog2e;
-        s[n] = 0.0f;
+        s[n] = (MODE == 1 && seg > 0) ? sa.hin[sidx * N + n] : 0.0f;
     }
     const float Dd = D ? D[dd] : 0.0f;
-    const size_t row0 = (size_t)b * seqlen;
-    const int ntiles = (seqlen + kT - 1) / kT;
+    const int tbeg = seg * sa.seg_len;
+    const int tend = min(seqlen, tbeg + sa.seg_len);
+    const size_t row0 = (size_t)b * seqlen + tbeg;  // first row of this segment
+    const int ntiles = tend > tbeg ? (tend - tbeg + kT - 1) / kT : 0;
+    float dsum = 0.0f;
 
     // stage B/C of tile k into bc[k & 1]
     auto stage_bc = [&](int k) {
@@ -65,7 +84,7 @@ __global__ __launch_bounds__(256) void selective_scan_kernel(
             const int tt = e / (2 * N), j = e % (2 * N);
             const int t = k * kT + tt;
             float v = 0.0f;
-            if (t < seqlen) v = j < N ? ldf(B + (row0 + t) * N + j) : ldf(C + (row0 + t) * N + (j - N));
+            if (tbeg + t < tend) v = j < N ? ldf(B + (row0 + t) * N + j) : ldf(C + (row0 + t) * N + (j - N));
             bc[k & 1][tt][j] = v;
         }
     };
@@ -74,7 +93,7 @@ __global__ __launch_bounds__(256) void selective_scan_kernel(
 #pragma unroll
         for (int tt = 0; tt < kT; ++tt) {
             const int t = k * kT + tt;
-            const bool in = t < seqlen;
+            const bool in = tbeg + t < tend;
             const size_t idx = (row0 + (in ? t : 0)) * dim + dd;
             uv[tt] = ldf(u + idx);
             rv[tt] = ldf(delta + idx);
@@ -99,79 +118,145 @@ __global__ __launch_bounds__(256) void selective_scan_kernel(
             stage_bc(k + 1);
             load_tile(k + 1);
         }
-        const int nt = min(kT, seqlen - k * kT);
+        const int nt = min(kT, tend - tbeg - k * kT);
 #pragma unroll
         for (int tt = 0; tt < kT; ++tt) {
             if (tt < nt) {
                 const float dl = delta_softplus ? softplus_fast(cr[tt]) : cr[tt];
                 const float du = dl * cu[tt];
                 const float *bt = bc[k & 1][tt];
-                float yv = Dd * cu[tt];
+                if (MODE == 0) {
+                    dsum += dl;
 #pragma unroll
-                for (int n = 0; n < N; ++n) {
-                    const float dA = __builtin_amdgcn_exp2f(dl * A2[n]);
-                    s[n] = dA * s[n] + du * bt[n];
-                    yv += bt[N + n] * s[n];
+                    for (int n = 0; n < N; ++n) s[n] = __builtin_amdgcn_exp2f(dl * A2[n]) * s[n] + du * bt[n];
+                } else {
+                    float yv = Dd * cu[tt];
+#pragma unroll
+                    for (int n = 0; n < N; ++n) {
+                        const float dA = __builtin_amdgcn_exp2f(dl * A2[n]);
+                        s[n] = dA * s[n] + du * bt[n];
+                        yv += bt[N + n] * s[n];
+                    }
+                    if (z) {
+                        const float zz = cz[tt];
+                        yv *= zz * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zz * kLog2e));
+                    }
+                    if (active) store_out(out + (row0 + k * kT + tt) * dim + d, yv);
                 }
-                if (z) {
-                    const float zz = cz[tt];
-                    yv *= zz * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zz * kLog2e));
-                }
-                if (active) store_out(out + (row0 + k * kT + tt) * dim + d, yv);
             }
         }
     }
-    if (final_state && active) {
+    if (!active) return;
+    if (MODE == 0) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) sa.seg_state[sidx * N + n] = s[n];
+        sa.seg_dsum[sidx] = dsum;
+    } else if (final_state && seg == sa.nseg - 1) {
         float *fs = final_state + ((size_t)b * dim + d) * N;
 #pragma unroll
         for (int n = 0; n < N; ++n) fs[n] = s[n];
     }
 }
 
+// State entering segment s >= 1 of each (batch row, channel, state n):
+// h_s = exp(A_n·ΣΔ_{s-1})·h_{s-1} + E_{s-1}, h_0 = 0.
+__global__ __launch_bounds__(256) void scan_combine_kernel(const float *__restrict__ A, ScanArgs sa,
+                                                           int N, long long total) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;  // (b, d, n)
+    if (i >= total) return;
+    const int n = (int)(i % N);
+    const long long bd = i / N;
+    const int d = (int)(bd % sa.dim);
+    const long long b = bd / sa.dim;
+    const float a2 = A[(size_t)d * N + n] * kLog2e;
+    float h = 0.0f;
+    for (int s = 1; s < sa.nseg; ++s) {
+        const size_t prev = ((size_t)b * sa.nseg + (s - 1)) * sa.dim + d;
+        h = __builtin_amdgcn_exp2f(a2 * sa.seg_dsum[prev]) * h + sa.seg_state[prev * N + n];
+        const_cast<float *>(sa.hin)[(((size_t)b * sa.nseg + s) * sa.dim + d) * N + n] = h;
+    }
+}
+
 template <typename T, int N>
-hipError_t launch_n(const void *u, const void *delta, const float *A, const void *B,
-                    const void *C, const float *D, const void *z, int delta_softplus, int batch,
-                    int seqlen, int dim, void *out, float *final_state, hipStream_t stream) {
-    dim3 grid((unsigned)((dim + 255) / 256), (unsigned)batch);
-    selective_scan_kernel<T, N><<<grid, dim3(256), 0, stream>>>(
-        static_cast<const T *>(u), static_cast<const T *>(delta), A, static_cast<const T *>(B),
-        static_cast<const T *>(C), D, static_cast<const T *>(z), delta_softplus, seqlen, dim,
-        static_cast<T *>(out), final_state);
+hipError_t launch_n(int phase, const ScanArgs &sa, const void *u, const void *delta, const float *A,
+                    const void *B, const void *C, const float *D, const void *z, int batch,
+                    void *out, float *final_state, hipStream_t stream) {
+    const dim3 grid((unsigned)((sa.dim + 255) / 256), (unsigned)batch, (unsigned)sa.nseg);
+    const T *up = static_cast<const T *>(u), *dp = static_cast<const T *>(delta);
+    const T *Bp = static_cast<const T *>(B), *Cp = static_cast<const T *>(C), *zp = static_cast<const T *>(z);
+    if (phase == 0) {
+        selective_scan_kernel<T, N, 0><<<grid, dim3(256), 0, stream>>>(up, dp, A, Bp, Cp, D, zp, sa,
+                                                                       static_cast<T *>(out), final_state);
+    } else if (phase == 1) {
+        const long long total = (long long)batch * sa.dim * N;
+        scan_combine_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(A, sa, N, total);
+    } else {
+        selective_scan_kernel<T, N, 1><<<grid, dim3(256), 0, stream>>>(up, dp, A, Bp, Cp, D, zp, sa,
+                                                                       static_cast<T *>(out), final_state);
+    }
     return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_t(const void *u, const void *delta, const float *A, const void *B,
-                    const void *C, const float *D, const void *z, int delta_softplus, int batch,
-                    int seqlen, int dim, int dstate, void *out, float *final_state,
-                    hipStream_t stream) {
+hipError_t launch_t(int phase, const ScanArgs &sa, const void *u, const void *delta, const float *A,
+                    const void *B, const void *C, const float *D, const void *z, int batch,
+                    int dstate, void *out, float *final_state, hipStream_t stream) {
     switch (dstate) {
-    case 4:
-        return launch_n<T, 4>(u, delta, A, B, C, D, z, delta_softplus, batch, seqlen, dim, out,
-                              final_state, stream);
-    case 8:
-        return launch_n<T, 8>(u, delta, A, B, C, D, z, delta_softplus, batch, seqlen, dim, out,
-                              final_state, stream);
-    case 16:
-        return launch_n<T, 16>(u, delta, A, B, C, D, z, delta_softplus, batch, seqlen, dim, out,
-                               final_state, stream);
-    default:
-        return hipErrorInvalidValue;
+    case 4: return launch_n<T, 4>(phase, sa, u, delta, A, B, C, D, z, batch, out, final_state, stream);
+    case 8: return launch_n<T, 8>(phase, sa, u, delta, A, B, C, D, z, batch, out, final_state, stream);
+    case 16: return launch_n<T, 16>(phase, sa, u, delta, A, B, C, D, z, batch, out, final_state, stream);
+    default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-hipError_t launch_selective_scan(int dtype, const void *u, const void *delta, const float *A,
-                                 const void *B, const void *C, const float *D, const void *z,
-                                 int delta_softplus, int batch, int seqlen, int dim, int dstate,
-                                 void *out, float *final_state, hipStream_t stream) {
+ScanPlan selective_scan_plan(int batch, int seqlen, int dim, int dstate) {
+    ScanPlan pl;
+    // about 16 waves per SIMD (1024 SIMDs) to hide the latency of the serial
+    // steps, segments of at least 256 steps
+    const long long waves = (long long)batch * ((dim + 63) / 64);
+    long long s = waves > 0 ? (16384 + waves - 1) / waves : 1;
+    s = s < 1 ? 1 : s;
+    const long long smax = seqlen / 256 > 1 ? seqlen / 256 : 1;
+    s = s > smax ? smax : s;
+    s = s > 64 ? 64 : s;
+    const int tiles = (seqlen + kT - 1) / kT;
+    pl.seg_len = (int)((tiles + s - 1) / s) * kT;
+    pl.nseg = seqlen > 0 ? (seqlen + pl.seg_len - 1) / pl.seg_len : 1;
+    if (pl.seg_len == 0) pl.seg_len = kT;
+    pl.ws_bytes = 0;
+    if (pl.nseg > 1) {
+        const size_t st = (size_t)batch * pl.nseg * dim * dstate * sizeof(float);
+        pl.state_bytes = (st + 255) / 256 * 256;
+        pl.ws_bytes = 2 * pl.state_bytes + ((size_t)batch * pl.nseg * dim * sizeof(float) + 255) / 256 * 256;
+    }
+    return pl;
+}
+
+hipError_t launch_selective_scan(int phase, const ScanPlan &pl, int dtype, const void *u,
+                                 const void *delta, const float *A, const void *B, const void *C,
+                                 const float *D, const void *z, int delta_softplus, int batch,
+                                 int seqlen, int dim, int dstate, void *out, float *final_state,
+                                 void *workspace, hipStream_t stream) {
     if (batch == 0 || dim == 0) return hipSuccess;
+    ScanArgs sa{};
+    sa.delta_softplus = delta_softplus;
+    sa.seqlen = seqlen;
+    sa.dim = dim;
+    sa.nseg = pl.nseg;
+    sa.seg_len = pl.seg_len;
+    if (pl.nseg > 1) {
+        char *ws = static_cast<char *>(workspace);
+        sa.seg_state = reinterpret_cast<float *>(ws);
+        sa.hin = reinterpret_cast<const float *>(ws + pl.state_bytes);
+        sa.seg_dsum = reinterpret_cast<float *>(ws + 2 * pl.state_bytes);
+    } else if (phase != 2) {
+        return hipErrorInvalidValue;
+    }
     if (dtype == 0)
-        return launch_t<float>(u, delta, A, B, C, D, z, delta_softplus, batch, seqlen, dim,
-                               dstate, out, final_state, stream);
-    return launch_t<bf16_t>(u, delta, A, B, C, D, z, delta_softplus, batch, seqlen, dim, dstate,
-                            out, final_state, stream);
+        return launch_t<float>(phase, sa, u, delta, A, B, C, D, z, batch, dstate, out, final_state, stream);
+    return launch_t<bf16_t>(phase, sa, u, delta, A, B, C, D, z, batch, dstate, out, final_state, stream);
 }
 
 }  // namespace ssd

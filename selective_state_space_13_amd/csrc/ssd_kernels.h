@@ -91,11 +91,20 @@ hipError_t launch_decode_step(int dtype, const void *x, const void *dt, const fl
                               int batch, int nheads, int headdim, int dstate, int ngroups,
                               float *state, void *y, hipStream_t stream);
 
-// Mamba-1 selective scan
-hipError_t launch_selective_scan(int dtype, const void *u, const void *delta, const float *A,
-                                 const void *B, const void *C, const float *D, const void *z,
-                                 int delta_softplus, int batch, int seqlen, int dim, int dstate,
-                                 void *out, float *final_state, hipStream_t stream);
+// Mamba-1 selective scan.  The sequence is cut into nseg time segments: phase 0
+// gives each segment's local end state and Σ Δ, phase 1 chains them into
+// incoming states, phase 2 computes the outputs.  With nseg == 1 only phase 2
+// runs and no workspace is used.
+struct ScanPlan {
+    int nseg = 1, seg_len = 0;
+    size_t state_bytes = 0, ws_bytes = 0;
+};
+ScanPlan selective_scan_plan(int batch, int seqlen, int dim, int dstate);
+hipError_t launch_selective_scan(int phase, const ScanPlan &pl, int dtype, const void *u,
+                                 const void *delta, const float *A, const void *B, const void *C,
+                                 const float *D, const void *z, int delta_softplus, int batch,
+                                 int seqlen, int dim, int dstate, void *out, float *final_state,
+                                 void *workspace, hipStream_t stream);
 
 // copy or zero the state for an empty sequence
 hipError_t launch_copy_state(const float *src, float *dst, size_t n, hipStream_t stream);

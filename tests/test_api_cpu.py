@@ -197,7 +197,12 @@ def test_selective_scan_null_align_alias(L):
     assert m1_call(L, ptrs={"out": fake(7)}) == ALIAS
     assert m1_call(L, ptrs={"fs": fake(8)}) == ALIAS
     assert m1_call(L, b=0) == OK
-    assert L.selective_scan_workspace_size(8, 4096, 5120, 16, BF16) == 0
+    # segment buffers when few channels meet a long sequence, none otherwise
+    assert L.selective_scan_workspace_size(8, 4096, 5120, 16, BF16) > 0
+    assert L.selective_scan_workspace_size(64, 4096, 8192, 16, BF16) == 0
+    assert L.selective_scan_workspace_size(8, 100, 5120, 16, BF16) == 0
+    assert L.selective_scan_workspace_size(8, 4096, 5120, 32, BF16) == 0  # unsupported
+    assert m1_call(L, Lq=4096, dim=128) == WS  # a segmented call without its workspace
 
 
 def test_last_error_is_thread_local(L):

@@ -309,6 +309,25 @@ def test_mamba1_small(b, L, dim, N, gate, dskip, dtype):
     assert_parity(to_f64(fs), fo, tau_of(dtype), False, f"mamba1 final {dtype}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("b,L,dim,N", [(1, 2000, 128, 16), (2, 1037, 64, 8), (1, 4096, 192, 4)])
+def test_mamba1_segmented(b, L, dim, N, dtype):
+    """Few channels and a long sequence: the scan is cut into time segments
+    (a state pass, a combine, then the output pass); the ragged lengths end in
+    a short last tile."""
+    code = ssd.SSD_F32 if dtype == "f32" else ssd.SSD_BF16
+    assert ssd.lib().selective_scan_workspace_size(b, L, dim, N, code) > 0
+    d = gen.mamba1_inputs(b, L, dim, N, dtype, seed=L, config_id=122)
+    out, fs = ssd.selective_scan(to_dev(d["u"]), to_dev(d["delta"]), to_dev(d["A"]), to_dev(d["B"]),
+                                 to_dev(d["C"]), to_dev(d["D"]), to_dev(d["z"]),
+                                 return_final_state=True)
+    torch.cuda.synchronize()
+    oo, fo = oracle.selective_scan(d["u"].f64(), d["delta"].f64(), d["A"].f64(), d["B"].f64(),
+                                   d["C"].f64(), d["D"].f64(), d["z"].f64(), return_final_state=True)
+    assert_parity(to_f64(out), oo, tau_of(dtype), dtype == "bf16", f"mamba1 segmented out {dtype}")
+    assert_parity(to_f64(fs), fo, tau_of(dtype), False, f"mamba1 segmented final {dtype}")
+
+
 def test_mamba1_general_A():
     """A not of the -(n+1) form: per-channel, per-state random decay rates."""
     b, L, dim, N = 2, 200, 128, 16
