@@ -199,7 +199,7 @@ def test_selective_scan_null_align_alias(L):
     assert m1_call(L, b=0) == OK
     # segment buffers when few channels meet a long sequence, none otherwise
     assert L.selective_scan_workspace_size(8, 4096, 5120, 16, BF16) > 0
-    assert L.selective_scan_workspace_size(64, 4096, 8192, 16, BF16) == 0
+    assert L.selective_scan_workspace_size(128, 4096, 8192, 16, BF16) == 0
     assert L.selective_scan_workspace_size(8, 100, 5120, 16, BF16) == 0
     assert L.selective_scan_workspace_size(8, 4096, 5120, 32, BF16) == 0  # unsupported
     assert m1_call(L, Lq=4096, dim=128) == WS  # a segmented call without its workspace
