@@ -212,6 +212,7 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
     const int c0 = seg * a.seg_chunks;
     const int c1 = min(c0 + a.seg_chunks, a.nchunks);
     const float Ah = a.A[h];
+    const float Dh = a.D ? a.D[h] : 0.0f;  // loaded before the walk: a load after the prefetch would wait for it
     const size_t bh = (size_t)b * a.nheads + h;
 
     // ---- this wave's state tiles: rows n = 32·snt + 8q + 4lg + e, cols p = 32·spt[j] + l32
@@ -276,6 +277,10 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
     ChunkRegs<N> R0;
     auto prefetch = [&](ChunkRegs<N> &Rg, int c) {
         const int t0 = c * kC, lim = last - t0;  // rows past the end are clamped to the last one
+        // dt first: the scan wave uses it before the rest has arrived, and loads
+        // complete in issue order
+        const uint16_t raw = a.dt[(row0 + t0 + min(lane, lim)) * a.nheads + h];
+        Rg.dt = __uint_as_float((uint32_t)raw << 16);
         const uint16_t *xc = a.x + ((row0 + t0) * a.nheads + h) * P + xcol;
         Rg.x = ld16(xc + (size_t)min(xrow, lim) * xstride);
         const uint16_t *bc = a.B + (row0 + t0) * bstride + (size_t)g * N + bcol;
@@ -286,8 +291,6 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
             Rg.b[k] = ld16(bc + rw);
             if constexpr (!STATE_ONLY) Rg.c[k] = ld16(cc + rw);
         }
-        const uint16_t raw = a.dt[(row0 + t0 + min(lane, lim)) * a.nheads + h];
-        Rg.dt = __uint_as_float((uint32_t)raw << 16);
     };
     // Δ, the float64 inclusive cumsum of Δ·A over the chunk (lane = token) and
     // the values derived from it; returns Σ Δ·A over the chunk
@@ -467,7 +470,6 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
             const float4 a0 = *reinterpret_cast<const float4 *>(s0), a1 = *reinterpret_cast<const float4 *>(s0 + 4);
             const float4 b0 = *reinterpret_cast<const float4 *>(s1), b1 = *reinterpret_cast<const float4 *>(s1 + 4);
             const uint4 xv = *reinterpret_cast<const uint4 *>(sm.xs[buf] + ox);
-            const float Dh = a.D ? a.D[h] : 0.0f;
             uint4 o;
             o.x = pack_bf16x2(a0.x + b0.x + Dh * bf16lo(xv.x), a0.y + b0.y + Dh * bf16hi(xv.x));
             o.y = pack_bf16x2(a0.z + b0.z + Dh * bf16lo(xv.y), a0.w + b0.w + Dh * bf16hi(xv.y));
