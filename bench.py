@@ -237,13 +237,17 @@ def bench_mamba1(steps, warmup):
     u, dl, A, B, C, D, z = (to_dev(d[k]) for k in ("u", "delta", "A", "B", "C", "D", "z"))
     del d
     out = torch.empty_like(u)
+    segmented = ssd.lib().selective_scan_workspace_size(c["batch"], c["seqlen"], c["dim"], c["dstate"],
+                                                        ssd.SSD_BF16) > 0
+    names = ["segment_states", "segment_combine", "selective_scan"] if segmented else ["selective_scan"]
 
     def one():
         ssd.selective_scan(u, dl, A, B, C, D, z, out=out)
 
-    ms, per = time_calls(one, 1, steps, warmup)
+    ms, per = time_calls(one, len(names), steps, warmup)
     n_el = c["batch"] * c["seqlen"] * c["dim"]
-    return dict(ms=ms, kernel_ms=per[0], tokens=c["batch"] * c["seqlen"],
+    return dict(ms=ms, kernel_ms=sum(per), per_kernel_ms=dict(zip(names, per)),
+                tokens=c["batch"] * c["seqlen"],
                 bytes=4 * n_el * 2 + 2 * c["batch"] * c["seqlen"] * c["dstate"] * 2,
                 exps=n_el * c["dstate"])
 
@@ -376,6 +380,7 @@ def main():
         extra["mamba1"] = {"workload": "mamba1_selective_scan:b8L4096D5120N16",
                            "tokens_per_s": round(m1["tokens"] / (m1["ms"] * 1e-3), 1),
                            "ms": round(m1["ms"], 5),
+                           "per_kernel_ms": {k: round(v, 5) for k, v in m1["per_kernel_ms"].items()},
                            "hbm_frac": round(m1["bytes"] / t / HBM_PEAK, 4),
                            "exp_per_s": round(m1["exps"] / t, 1)}
     if extra:

@@ -75,8 +75,12 @@ const char *ssd_last_error(void);
  *
  * Computes, for every batch row b and head h (group g = h / (nheads/ngroups)),
  * the scan above over t = 0..seqlen-1 starting from initial_state (or 0), by
- * the block decomposition with chunks of `chunk` tokens (the last chunk may be
- * shorter).  The chunk length changes rounding only, not the result.
+ * the block decomposition.  The chunk length changes rounding only, not the
+ * result: SSD_F32 uses chunks of `chunk` tokens (the last may be shorter);
+ * SSD_BF16 runs one fused kernel with 64-token chunks whatever `chunk` says,
+ * keeps every intermediate on chip, and for calls with few (batch, head)
+ * pairs and long sequences cuts the sequence into segments scanned in
+ * parallel (their end states are chained through the workspace).
  *
  *   x      [batch][seqlen][nheads][headdim]      dtype
  *   dt     [batch][seqlen][nheads]               dtype  (raw if dt_softplus)
@@ -87,6 +91,8 @@ const char *ssd_last_error(void);
  *   y      [batch][seqlen][nheads][headdim]      dtype, written
  *   final_state   [batch][nheads][dstate][headdim] float or NULL, written
  *   workspace     >= ssd_chunk_scan_workspace_size(...) bytes, 256-byte aligned
+ *                 (SSD_BF16: 256 bytes, unused, unless the call is segmented;
+ *                 SSD_F32: the stages below)
  *
  * Supported: headdim == 64; dstate in {64, 128}; chunk in {64, 128, 256};
  * ngroups >= 1 dividing nheads; batch, seqlen >= 0 (an empty call writes
@@ -102,14 +108,13 @@ int ssd_chunk_scan_fwd(int batch, int seqlen, int nheads, int headdim, int dstat
                        void *y, float *final_state,
                        void *workspace, size_t workspace_bytes, void *stream);
 
-/* Byte offsets of the intermediate stages inside the workspace, for
- * inspection by tests (contents valid after the call has completed):
+/* Byte offsets of the intermediate stages that the SSD_F32 path leaves in the
+ * workspace, for inspection by tests (contents valid after the call):
  *   delta  [batch][nheads][nchunks][chunk] float   Δ per token (0 past the end)
  *   cs     [batch][nheads][nchunks][chunk] double  within-chunk inclusive cumsum of Δ·A
- *   hprev  [batch][nchunks][nheads][dstate][headdim]  the state entering each
- *          chunk: float for SSD_F32; for SSD_BF16 two bf16 planes of that shape,
- *          head then tail, whose sum is the state.
- * Returns SSD_OK, or the status ssd_chunk_scan_fwd would return for the sizes. */
+ *   hprev  [batch][nchunks][nheads][dstate][headdim] float, the state entering each chunk
+ * Returns SSD_OK, SSD_ERR_UNSUPPORTED for SSD_BF16 (whose stages stay on chip),
+ * or the status ssd_chunk_scan_fwd would return for the sizes. */
 int ssd_chunk_scan_workspace_layout(int batch, int seqlen, int nheads, int headdim, int dstate,
                                     int ngroups, int chunk, int dtype, size_t *off_delta,
                                     size_t *off_cs, size_t *off_hprev);
@@ -145,7 +150,9 @@ int ssd_decode_step(int batch, int nheads, int headdim, int dstate, int ngroups,
  *   B, C   [batch][seqlen][dstate]         dtype
  *   D      [dim] float or NULL
  *   final_state [batch][dim][dstate] float or NULL, written
- *   workspace   >= selective_scan_workspace_size(...) bytes (may be 0 -> NULL ok)
+ *   workspace   >= selective_scan_workspace_size(...) bytes, 256-byte aligned; 0
+ *               (NULL ok) unless the call is cut into time segments (few batch x
+ *               channel lanes, long sequence), whose end states it chains
  *
  * Supported: dstate in {4, 8, 16}; dim a multiple of 64.
  * ------------------------------------------------------------------------ */
