@@ -120,6 +120,34 @@ int ssd_chunk_scan_workspace_layout(int batch, int seqlen, int nheads, int headd
                                     size_t *off_cs, size_t *off_hprev);
 
 /* ------------------------------------------------------------------------
+ * Packed variable-length prefill ([TP] §4.3: sequences of different lengths
+ * packed back to back without padding; the recurrence restarts at every
+ * sequence start).  Sequence s occupies rows cu_seqlens[s] .. cu_seqlens[s+1]-1
+ * of the packed tensors and is scanned exactly as ssd_chunk_scan_fwd would
+ * scan it alone (batch 1), from initial_states[s] (or 0).
+ *
+ *   cu_seqlens    [nseq + 1] int32, device memory: 0 = cu[0] <= cu[1] <= ...
+ *                 <= cu[nseq] = total_tokens.  Offsets are clamped to
+ *                 [0, total_tokens] on the device, so other contents give
+ *                 unspecified outputs but never an access out of bounds.
+ *   x      [total_tokens][nheads][headdim]      bf16
+ *   dt     [total_tokens][nheads]               bf16 (raw if dt_softplus)
+ *   A, D   [nheads] float (D may be NULL)
+ *   B, C   [total_tokens][ngroups][dstate]      bf16
+ *   initial_states [nseq][nheads][dstate][headdim] float or NULL (= 0)
+ *   y      [total_tokens][nheads][headdim]      bf16, written
+ *   final_states   [nseq][nheads][dstate][headdim] float or NULL, written
+ *
+ * Supported: dtype SSD_BF16 only; headdim == 64; dstate in {64, 128}; ngroups
+ * dividing nheads.  No workspace: one fused pass per (sequence, head).
+ * ------------------------------------------------------------------------ */
+int ssd_chunk_scan_varlen_fwd(int nseq, int total_tokens, int nheads, int headdim, int dstate,
+                              int ngroups, int dtype, int dt_softplus, const int *cu_seqlens,
+                              const void *x, const void *dt, const float *A, const void *B,
+                              const void *C, const float *D, const float *initial_states, void *y,
+                              float *final_states, void *stream);
+
+/* ------------------------------------------------------------------------
  * One decode step against a cached state ([INF] Abstract; the single step of
  * [TP] §2.1 with the scalar decay of §3.1).  For each (b, h):
  *     a = exp(Δ·A_h);  state <- a·state + Δ·B xᵀ;  y = stateᵀ C + D_h·x

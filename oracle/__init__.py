@@ -92,6 +92,32 @@ def ssd_scan(x, dt, A, B, C, D=None, h0=None, dt_softplus=True, return_final_sta
     return (y, hf) if return_final_state else y
 
 
+def ssd_scan_varlen(x, dt, A, B, C, cu_seqlens, D=None, h0s=None, dt_softplus=True,
+                    return_final_state=False):
+    """Packed variable-length SSD scan (page "5.3 텐서 병렬화(Tensor Parallelism) 지원과
+    대규모 클러스터 학습", §4.3): sequence s is rows cu[s]..cu[s+1]-1 of the packed
+    x [T,H,P], dt [T,H], B, C [T,G,N]; each is scanned on its own by ssd_scan,
+    from h0s[s] [H,N,P] (or 0).  Returns y [T,H,P] (and final states [nseq,H,N,P])."""
+    x, dt, B, C = map(_f64, (x, dt, B, C))
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    T, H, P = x.shape
+    N = B.shape[2]
+    y = np.zeros_like(x)
+    hf = np.zeros((len(cu) - 1, H, N, P))
+    for s in range(len(cu) - 1):
+        a, e = int(cu[s]), int(cu[s + 1])
+        h0 = None if h0s is None else _f64(h0s)[s:s + 1]
+        if e == a:
+            if h0 is not None:
+                hf[s] = h0[0]
+            continue
+        ys, fs = ssd_scan(x[None, a:e], dt[None, a:e], A, B[None, a:e], C[None, a:e], D, h0,
+                          dt_softplus, return_final_state=True)
+        y[a:e] = ys[0]
+        hf[s] = fs[0]
+    return (y, hf) if return_final_state else y
+
+
 def ssd_decode(x, dt, A, B, C, D, state, dt_softplus=True):
     """One fp64 decode step.  x [b,H,P], dt [b,H], B, C [b,G,N], state [b,H,N,P].
     Returns (y, new_state); the input state array is not modified."""

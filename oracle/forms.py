@@ -21,6 +21,11 @@ same result, used to pin it.
 * ``selective_scan_dual``: the Mamba-1 diagonal-A scan of §2.1 written as a
   sum over source tokens, y_t = Σ_{s<=t} Σ_n C_t[n] B_s[n] exp(A[n] Σ_{k=s+1..t} Δ_k) Δ_s u_s.
 
+* ``ssd_packed_reset``: the packing of §4.3 written literally: one sequential
+  recurrence over the packed tokens whose state transition is set to zero at
+  the first token of every sequence (there the previous state is replaced by
+  that sequence's initial state, zero by default).
+
 Only for small inputs (the dual forms build L x L matrices).
 """
 from __future__ import annotations
@@ -145,3 +150,38 @@ def selective_scan_dual(u, delta, A, B, C, D=None, z=None, delta_softplus=True):
                 yy *= zz / (1.0 + np.exp(-zz))
             out[bb, :, d] = yy
     return out, hf
+
+
+def ssd_packed_reset(x, dt, A, B, C, cu_seqlens, D=None, h0s=None, dt_softplus=True):
+    """Returns (y [T,H,P], final states [nseq,H,N,P]) of the packed recurrence."""
+    x = np.asarray(x, np.float64)
+    dt = np.asarray(dt, np.float64)
+    B = np.asarray(B, np.float64)
+    C = np.asarray(C, np.float64)
+    A = np.asarray(A, np.float64)
+    T, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    cu = [int(v) for v in cu_seqlens]
+    nseq = len(cu) - 1
+    start = {}
+    for s_ in range(nseq):
+        if cu[s_ + 1] > cu[s_]:
+            start[cu[s_]] = s_
+    delta = softplus(dt) if dt_softplus else dt
+    y = np.zeros((T, H, P))
+    hf = np.zeros((nseq, H, N, P)) if h0s is None else np.array(h0s, np.float64)
+    for h in range(H):
+        g = h // (H // G)
+        state = np.zeros((N, P))
+        for t in range(T):
+            a_t = np.exp(delta[t, h] * A[h])
+            if t in start:  # transition zeroed: the sequence starts from its own state
+                s_ = start[t]
+                state = np.zeros((N, P)) if h0s is None else np.array(h0s[s_][h], np.float64)
+            state = a_t * state + delta[t, h] * np.outer(B[t, g], x[t, h])
+            y[t, h] = C[t, g] @ state + (0.0 if D is None else D[h] * x[t, h])
+            if t + 1 in cu[1:] or t == T - 1:
+                for s_ in range(nseq):
+                    if cu[s_ + 1] == t + 1 and cu[s_ + 1] > cu[s_]:
+                        hf[s_, h] = state
+    return y, hf

@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
     L.ssd_chunk_scan_workspace_layout.restype = i
     L.ssd_chunk_scan_fwd.argtypes = [i] * 9 + [vp] * 10 + [sz, vp]
     L.ssd_chunk_scan_fwd.restype = i
+    L.ssd_chunk_scan_varlen_fwd.argtypes = [i] * 8 + [vp] * 11
+    L.ssd_chunk_scan_varlen_fwd.restype = i
     L.ssd_decode_step.argtypes = [i] * 7 + [vp] * 9
     L.ssd_decode_step.restype = i
     L.selective_scan_workspace_size.argtypes = [i] * 5
@@ -179,6 +181,48 @@ def ssd_chunk_scan(x, dt, A, B, C, D=None, *, chunk, initial_state=None,
         _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(initial_state),
         _ptr(y), _ptr(fs), _ptr(workspace), workspace.numel(), _stream(dev)))
     return (y, fs) if return_final_state else y
+
+
+def ssd_chunk_scan_varlen(x, dt, A, B, C, D=None, *, cu_seqlens, initial_states=None,
+                          return_final_states=False, dt_softplus=True, out=None,
+                          final_states=None):
+    """Packed variable-length SSD prefill (bf16).  x [T,H,P], dt [T,H], A [H] fp32,
+    B, C [T,G,N], D [H] fp32 or None, cu_seqlens int32 [nseq+1] on the GPU (sequence
+    s is rows cu[s]..cu[s+1]-1, scanned on its own), initial_states [nseq,H,N,P] fp32
+    or None.  Returns y [T,H,P] or (y, final_states fp32 [nseq,H,N,P])."""
+    torch = _torch()
+    x = _req(x, "x", torch.bfloat16)
+    dev = x.device
+    T, H, P = x.shape
+    _req(dt, "dt", x.dtype, dev)
+    _req(B, "B", x.dtype, dev)
+    _req(C, "C", x.dtype, dev)
+    _req(A, "A", torch.float32, dev)
+    _req(D, "D", torch.float32, dev)
+    _req(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    _req(initial_states, "initial_states", torch.float32, dev)
+    G, N = B.shape[1], B.shape[2]
+    nseq = cu_seqlens.numel() - 1
+    if nseq < 0:
+        raise ValueError("cu_seqlens needs at least one entry")
+    if tuple(dt.shape) != (T, H) or tuple(B.shape) != (T, G, N) or C.shape != B.shape:
+        raise ValueError("shape mismatch among x, dt, B, C")
+    if tuple(A.shape) != (H,) or (D is not None and tuple(D.shape) != (H,)):
+        raise ValueError("A and D must have shape [nheads]")
+    if initial_states is not None and tuple(initial_states.shape) != (nseq, H, N, P):
+        raise ValueError("initial_states must be [nseq, nheads, dstate, headdim]")
+    y = out if out is not None else torch.empty_like(x)
+    _req(y, "out", x.dtype, dev)
+    fs = None
+    if return_final_states:
+        fs = final_states if final_states is not None else torch.empty(
+            (nseq, H, N, P), dtype=torch.float32, device=dev)
+        _req(fs, "final_states", torch.float32, dev)
+    check(lib().ssd_chunk_scan_varlen_fwd(
+        nseq, T, H, P, N, G, SSD_BF16, int(bool(dt_softplus)), _ptr(cu_seqlens),
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(initial_states),
+        _ptr(y), _ptr(fs), _stream(dev)))
+    return (y, fs) if return_final_states else y
 
 
 def ssd_decode_step(x, dt, A, B, C, D, state, *, dt_softplus=True, out=None):

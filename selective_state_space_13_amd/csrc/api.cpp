@@ -299,6 +299,48 @@ int ssd_chunk_scan_fwd(int batch, int seqlen, int nheads, int headdim, int dstat
     return SSD_OK;
 }
 
+int ssd_chunk_scan_varlen_fwd(int nseq, int total_tokens, int nheads, int headdim, int dstate,
+                              int ngroups, int dtype, int dt_softplus, const int *cu_seqlens,
+                              const void *x, const void *dt, const float *A, const void *B,
+                              const void *C, const float *D, const float *initial_states, void *y,
+                              float *final_states, void *stream_) {
+    if (dtype != SSD_BF16)
+        return fail(SSD_ERR_UNSUPPORTED, "the packed variable-length prefill takes SSD_BF16 inputs");
+    if (nseq < 0 || total_tokens < 0)
+        return fail(SSD_ERR_SHAPE, "nseq (%d) and total_tokens (%d) must be >= 0", nseq, total_tokens);
+    int st = check_scan_sizes(1, total_tokens, nheads, headdim, dstate, ngroups, 64, dtype);
+    if (st) return st;
+    if ((long long)nseq * nheads > (1ll << 31) - 1) return fail(SSD_ERR_SHAPE, "nseq * nheads overflows");
+    uint64_t n_x, n_dt, n_bc, n_state;
+    prod(n_x, {total_tokens, nheads, headdim});
+    prod(n_dt, {total_tokens, nheads});
+    prod(n_bc, {total_tokens, ngroups, dstate});
+    if (!prod(n_state, {nseq, nheads, dstate, headdim})) return fail(SSD_ERR_SHAPE, "state size overflows");
+    if (nseq == 0) return SSD_OK;
+    if (!cu_seqlens || !A) return fail(SSD_ERR_NULL, "cu_seqlens and A are required");
+    if (total_tokens > 0 && (!x || !dt || !B || !C || !y))
+        return fail(SSD_ERR_NULL, "x, dt, B, C and y are required");
+    const void *ptrs[] = {x, dt, A, B, C, D, initial_states, y, final_states};
+    for (const void *p : ptrs)
+        if (p && !aligned(p, 16)) return fail(SSD_ERR_ALIGN, "tensor pointer %p is not 16-byte aligned", p);
+    if (!aligned(cu_seqlens, 4)) return fail(SSD_ERR_ALIGN, "cu_seqlens must be 4-byte aligned");
+    st = check_alias(
+        {span("y", y, n_x * 2), span("final_states", final_states, final_states ? n_state * 4 : 0)},
+        {span("x", x, n_x * 2), span("dt", dt, n_dt * 2), span("A", A, (uint64_t)nheads * 4),
+         span("B", B, n_bc * 2), span("C", C, n_bc * 2), span("D", D, D ? (uint64_t)nheads * 4 : 0),
+         span("initial_states", initial_states, initial_states ? n_state * 4 : 0),
+         span("cu_seqlens", cu_seqlens, (uint64_t)(nseq + 1) * 4)});
+    if (st) return st;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    LaunchMarks marks(stream);
+    marks.before();
+    hipError_t e = ssd::launch_ssd_fused_varlen(cu_seqlens, nseq, total_tokens, x, dt, A, B, C, D,
+                                                initial_states, dt_softplus, nheads, headdim, dstate,
+                                                ngroups, y, final_states, stream);
+    marks.after();
+    return e == hipSuccess ? SSD_OK : hip_fail(e, "varlen prefill launch");
+}
+
 int ssd_decode_step(int batch, int nheads, int headdim, int dstate, int ngroups, int dtype,
                     int dt_softplus, const void *x, const void *dt, const float *A, const void *B,
                     const void *C, const float *D, float *state, void *y, void *stream_) {

@@ -163,6 +163,10 @@ struct FusedArgs {
     float *seg_state;     // [b][H][S][N][P] local end state of each segment (state-only pass)
     double *seg_decay;    // [b][H][S] Σ Δ·A over each segment (state-only pass)
     int seqlen, nheads, ngroups, dt_softplus;
+    // packed variable-length batch: sequence b covers rows [cu[b], cu[b+1]) of
+    // x, dt, B, C, y (each clamped to [0, total_tokens]); null for equal lengths
+    const int *cu_seqlens;
+    int total_tokens;
     int nchunks;          // 64-token chunks over the sequence
     int seg_chunks;       // chunks per segment
     int nseg;             // S
@@ -209,8 +213,18 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
     const int seg = item / R;
     const int b = bg / a.ngroups, g = bg % a.ngroups;
     const int h = g * R + r;
+    // rows of this sequence: row0.. row0 + seqlen - 1 of the [rows][...] inputs
+    size_t row0 = (size_t)b * a.seqlen;
+    int seqlen = a.seqlen, nchunks = a.nchunks;
+    if (a.cu_seqlens) {
+        const int s0 = min(max(a.cu_seqlens[b], 0), a.total_tokens);
+        const int s1 = min(max(a.cu_seqlens[b + 1], s0), a.total_tokens);
+        row0 = (size_t)s0;
+        seqlen = s1 - s0;
+        nchunks = (seqlen + kC - 1) / kC;
+    }
     const int c0 = seg * a.seg_chunks;
-    const int c1 = min(c0 + a.seg_chunks, a.nchunks);
+    const int c1 = min(c0 + a.seg_chunks, nchunks);
     const float Ah = a.A[h];
     const float Dh = a.D ? a.D[h] : 0.0f;  // loaded before the walk: a load after the prefetch would wait for it
     const size_t bh = (size_t)b * a.nheads + h;
@@ -271,8 +285,7 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
     const int o_ya = swz<64>(4 * lg + rrow, 32 * pt + rcol), o_yb = swz<64>(4 * lg + 8 + rrow, 32 * pt + rcol);
 
     const size_t xstride = (size_t)a.nheads * P, bstride = (size_t)a.ngroups * N;
-    const size_t row0 = (size_t)b * a.seqlen;
-    const int last = a.seqlen - 1;
+    const int last = seqlen - 1;
 
     ChunkRegs<N> R0;
     auto prefetch = [&](ChunkRegs<N> &Rg, int c) {
@@ -295,7 +308,7 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
     // Δ, the float64 inclusive cumsum of Δ·A over the chunk (lane = token) and
     // the values derived from it; returns Σ Δ·A over the chunk
     auto scan_chunk = [&](int c, float raw, TokSmem &T) -> double {
-        const bool ok = c * kC + lane < a.seqlen;
+        const bool ok = c * kC + lane < seqlen;
         const float delta = ok ? (a.dt_softplus ? softplus_f32(raw) : raw) : 0.0f;
         const double cs = wave_inclusive_scan((double)(delta * Ah));
         const double cs_end = read_lane(cs, 63);
@@ -309,8 +322,10 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
     };
 
     double seg_decay = 0.0;
-    prefetch(R0, c0);
-    if (wave == kScanWave) seg_decay += scan_chunk(c0, R0.dt, sm.tok[c0 & 1]);
+    if (c0 < c1) {  // an empty sequence loads nothing and returns its initial state
+        prefetch(R0, c0);
+        if (wave == kScanWave) seg_decay += scan_chunk(c0, R0.dt, sm.tok[c0 & 1]);
+    }
     __syncthreads();
 
     for (int c = c0; c < c1; ++c) {
@@ -475,7 +490,7 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
             o.y = pack_bf16x2(a0.z + b0.z + Dh * bf16lo(xv.y), a0.w + b0.w + Dh * bf16hi(xv.y));
             o.z = pack_bf16x2(a1.x + b1.x + Dh * bf16lo(xv.z), a1.y + b1.y + Dh * bf16hi(xv.z));
             o.w = pack_bf16x2(a1.z + b1.z + Dh * bf16lo(xv.w), a1.w + b1.w + Dh * bf16hi(xv.w));
-            if (t0 + row < a.seqlen)
+            if (t0 + row < seqlen)
                 *reinterpret_cast<uint4 *>(a.y + ((row0 + t0) * a.nheads + h) * P + (size_t)row * xstride + cq) = o;
         }
     }
@@ -597,6 +612,40 @@ hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const
         else
             ssd_fused_kernel<64, false><<<items, kThreads, 0, stream>>>(a);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_ssd_fused_varlen(const int *cu_seqlens, int nseq, int total_tokens, const void *x,
+                                   const void *dt, const float *A, const void *B, const void *C,
+                                   const float *D, const float *h0, int dt_softplus, int nheads,
+                                   int headdim, int dstate, int ngroups, void *y, float *final_state,
+                                   hipStream_t stream) {
+    if (headdim != P || (dstate != 64 && dstate != 128)) return hipErrorInvalidValue;
+    if ((long long)nseq * nheads == 0) return hipSuccess;
+    FusedArgs a{};
+    a.x = static_cast<const uint16_t *>(x);
+    a.dt = static_cast<const uint16_t *>(dt);
+    a.B = static_cast<const uint16_t *>(B);
+    a.C = static_cast<const uint16_t *>(C);
+    a.A = A;
+    a.D = D;
+    a.h0 = h0;
+    a.y = static_cast<uint16_t *>(y);
+    a.final_state = final_state;
+    a.seqlen = 0;
+    a.cu_seqlens = cu_seqlens;
+    a.total_tokens = total_tokens;
+    a.nheads = nheads;
+    a.ngroups = ngroups;
+    a.dt_softplus = dt_softplus;
+    a.nchunks = (total_tokens + kC - 1) / kC;  // bound; each sequence counts its own
+    a.nseg = 1;
+    a.seg_chunks = a.nchunks + 1;
+    const unsigned items = (unsigned)((long long)nseq * nheads);
+    if (dstate == 128)
+        ssd_fused_kernel<128, false><<<items, kThreads, 0, stream>>>(a);
+    else
+        ssd_fused_kernel<64, false><<<items, kThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -83,6 +83,15 @@ hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const
                             const float *h0, int dt_softplus, int batch, int seqlen, int nheads,
                             int headdim, int dstate, int ngroups, void *y, float *final_state,
                             void *workspace, hipStream_t stream);
+// Packed variable-length batch: sequence s covers rows [cu_seqlens[s],
+// cu_seqlens[s+1]) of x [T][H][P], dt [T][H], B, C [T][G][N] and y; each
+// sequence starts from h0[s] (or 0) and writes final_state[s].  One fused pass
+// per (sequence, head), no workspace.
+hipError_t launch_ssd_fused_varlen(const int *cu_seqlens, int nseq, int total_tokens, const void *x,
+                                   const void *dt, const float *A, const void *B, const void *C,
+                                   const float *D, const float *h0, int dt_softplus, int nheads,
+                                   int headdim, int dstate, int ngroups, void *y, float *final_state,
+                                   hipStream_t stream);
 
 
 // decode step, in-place float state

@@ -205,6 +205,32 @@ def test_selective_scan_null_align_alias(L):
     assert m1_call(L, Lq=4096, dim=128) == WS  # a segmented call without its workspace
 
 
+def varlen_call(L, nseq=3, T=500, H=8, P=64, N=128, G=2, dtype=BF16, ptrs=None):
+    p = dict(cu=fake(10), x=fake(1), dt=fake(2), A=fake(3), B=fake(4), C=fake(5), D=fake(6),
+             h0=None, y=fake(7), fs=fake(8))
+    if ptrs:
+        p.update(ptrs)
+    return L.ssd_chunk_scan_varlen_fwd(nseq, T, H, P, N, G, dtype, 1, p["cu"], p["x"], p["dt"],
+                                       p["A"], p["B"], p["C"], p["D"], p["h0"], p["y"], p["fs"], None)
+
+
+@pytest.mark.parametrize("kw,status", [(dict(dtype=F32), UNSUP), (dict(nseq=-1), SHAPE),
+                                       (dict(T=-3), SHAPE), (dict(G=3), SHAPE), (dict(P=32), UNSUP),
+                                       (dict(N=96), UNSUP)])
+def test_varlen_shape_errors(L, kw, status):
+    assert varlen_call(L, **kw) == status
+
+
+def test_varlen_null_align_alias(L):
+    assert varlen_call(L, ptrs={"cu": None}) == NULL
+    assert varlen_call(L, ptrs={"x": None}) == NULL
+    assert varlen_call(L, ptrs={"cu": fake(10, 2)}) == ALIGN
+    assert varlen_call(L, ptrs={"y": fake(1, 8)}) == ALIGN
+    assert varlen_call(L, ptrs={"y": fake(1)}) == ALIAS
+    assert varlen_call(L, ptrs={"fs": fake(10)}) == ALIAS  # final states over cu_seqlens
+    assert varlen_call(L, nseq=0) == OK
+
+
 def test_last_error_is_thread_local(L):
     assert scan_call(L, G=3) == SHAPE
     msg_main = L.ssd_last_error()

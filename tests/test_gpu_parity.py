@@ -138,6 +138,39 @@ def test_prefill_segmented_bf16(case):
     assert_parity(to_f64(fs), fo, TAU_BF16, False, f"segmented final {case}")
 
 
+VARLEN_GPU_CASES = [
+    # lengths, H, N, G, with_D, with_h0
+    ([300, 1, 64, 0, 257, 1000], 8, 128, 2, True, True),
+    ([128, 129, 5], 6, 64, 3, False, False),
+    ([2048, 513, 77, 1536], 4, 128, 1, True, False),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_GPU_CASES, ids=lambda c: "n{}H{}N{}".format(len(c[0]), c[1], c[2]))
+def test_prefill_varlen_packed(case):
+    """Packed sequences (empty, one token, a chunk multiple, ragged tails), each
+    scanned from its own initial state, against the oracle's separate scans."""
+    lengths, H, N, G, wD, wh = case
+    d = gen.ssd_varlen_inputs(lengths, H, 64, N, G, "bf16", seed=len(lengths) + N, config_id=103,
+                              with_D=wD, with_h0=wh)
+    x, dt, B, C, A = (to_dev(d[k]) for k in ("x", "dt", "B", "C", "A"))
+    D = to_dev(d["D"]) if wD else None
+    h0 = to_dev(d["h0"]) if wh else None
+    cu = torch.from_numpy(d["cu_seqlens"]).cuda()
+    y, fs = ssd.ssd_chunk_scan_varlen(x, dt, A, B, C, D, cu_seqlens=cu, initial_states=h0,
+                                      return_final_states=True)
+    torch.cuda.synchronize()
+    yo, fo = oracle.ssd_scan_varlen(d["x"].f64(), d["dt"].f64(), d["A"].f64(), d["B"].f64(),
+                                    d["C"].f64(), d["cu_seqlens"], d["D"].f64() if wD else None,
+                                    d["h0"].f64() if wh else None, return_final_state=True)
+    assert_parity(to_f64(y), yo, TAU_BF16, True, f"varlen y {lengths}")
+    assert_parity(to_f64(fs), fo, TAU_BF16, False, f"varlen final {lengths}")
+    for s, n in enumerate(lengths):  # an empty sequence hands back its initial state exactly
+        if n == 0:
+            ref = h0[s] if wh else torch.zeros_like(fs[s])
+            assert torch.equal(fs[s], ref)
+
+
 def test_prefill_extreme_decay_and_large_steps():
     """Δ up to ~10 with A = -16: chunk decays underflow float32; results stay finite
     and match the oracle."""

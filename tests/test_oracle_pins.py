@@ -319,3 +319,48 @@ def test_mamba1_constant_input_closed_form():
 
 def test_oracle_uses_threads():
     assert oracle.threads() >= 1
+
+
+# ---- packed variable-length batches (page 1 §4.3)
+
+VARLEN_CASES = [
+    # lengths, H, P, N, G, with_D, with_h0
+    ([5, 0, 7, 1, 3], 3, 4, 2, 1, True, True),
+    ([9, 9], 2, 3, 4, 2, False, False),
+    ([1], 1, 2, 2, 1, True, False),
+    ([0, 0, 4, 0], 2, 2, 3, 1, True, True),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=lambda c: "-".join(map(str, c[0])))
+def test_pin_varlen_packed_reset_equals_separate_scans(case):
+    """The packed recurrence with the transition zeroed at every sequence start
+    (the literal §4.3 form) equals independent scans of the sequences."""
+    from workloads import gen
+    lengths, H, P, N, G, wD, wh = case
+    d = gen.ssd_varlen_inputs(lengths, H, P, N, G, "f32", seed=sum(lengths), config_id=90,
+                              with_D=wD, with_h0=wh)
+    args = (d["x"].f64(), d["dt"].f64(), d["A"].f64(), d["B"].f64(), d["C"].f64(), d["cu_seqlens"])
+    D = d["D"].f64() if wD else None
+    h0 = d["h0"].f64() if wh else None
+    y1, f1 = forms.ssd_packed_reset(*args, D, h0)
+    y2, f2 = oracle.ssd_scan_varlen(*args, D, h0, return_final_state=True)
+    scale = max(np.abs(y1).max(), 1e-30)
+    assert np.abs(y1 - y2).max() <= 1e-12 * scale
+    assert np.abs(f1 - f2).max() <= 1e-12 * max(np.abs(f1).max(), 1e-30)
+    # an empty sequence returns its initial state untouched
+    for s, n in enumerate(lengths):
+        if n == 0:
+            np.testing.assert_array_equal(f2[s], h0[s] if wh else 0.0)
+
+
+def test_varlen_reset_is_not_vacuous():
+    """Without the reset, the second sequence sees the first one's state: the
+    packed answer differs from one long scan exactly from the boundary on."""
+    from workloads import gen
+    d = gen.ssd_varlen_inputs([6, 5], 2, 3, 2, 1, "f32", seed=4, config_id=91)
+    x, dt, A, B, C = (d[k].f64() for k in ("x", "dt", "A", "B", "C"))
+    packed = oracle.ssd_scan_varlen(x, dt, A, B, C, d["cu_seqlens"], d["D"].f64())
+    whole = oracle.ssd_scan(x[None], dt[None], A, B[None], C[None], d["D"].f64())[0]
+    np.testing.assert_array_equal(packed[:6], whole[:6])
+    assert np.all(np.abs(packed[6:] - whole[6:]).max(axis=(1, 2)) > 0)

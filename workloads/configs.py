@@ -35,6 +35,15 @@ MAMBA1_SELECTIVE_SCAN = dict(
     batch=8, seqlen=4096, dim=5120, dstate=16, gate=True, dskip=True,
 )
 
+# Packed variable-length prefill at the 2.7B-layer head shape: 8 sequences of
+# mixed lengths (16384 tokens in all, the token count of the batch-8 prefill),
+# each scanned from its own start.
+VARLEN_PREFILL = dict(
+    id=6, name="varlen_packed_prefill", kind="ssd_varlen", dtype="bf16",
+    lengths=[3072, 512, 2048, 1536, 4096, 1024, 2560, 1536],
+    nheads=80, headdim=64, dstate=128, ngroups=1,
+)
+
 ALL = [TINY_SSD_F32, MAMBA2_LAYER_PREFILL, LONG_CONTEXT_PREFILL,
-       DECODE_STATE_CACHE, MAMBA1_SELECTIVE_SCAN]
+       DECODE_STATE_CACHE, MAMBA1_SELECTIVE_SCAN, VARLEN_PREFILL]
 BY_ID = {c["id"]: c for c in ALL}

@@ -113,6 +113,24 @@ def ssd_inputs(batch, seqlen, nheads, headdim, dstate, ngroups, dtype,
     return out
 
 
+def ssd_varlen_inputs(lengths, nheads, headdim, dstate, ngroups, dtype, seed=0, config_id=0,
+                      with_D=True, with_h0=False):
+    """Inputs of one packed variable-length call: the tensors of a batch-1 call of
+    sum(lengths) tokens, flattened to x [T, nheads, headdim], dt [T, nheads],
+    B and C [T, ngroups, dstate]; cu_seqlens int32 [nseq + 1] (0, then the running
+    sum of lengths); h0 [nseq, nheads, dstate, headdim] fp32 per sequence."""
+    T = int(sum(lengths))
+    d = ssd_inputs(1, T, nheads, headdim, dstate, ngroups, dtype, seed, config_id, with_D, False)
+    for k in ("x", "dt", "B", "C"):
+        d[k] = Tensor(d[k].data[0], d[k].dtype)
+    d["cu_seqlens"] = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    d["h0"] = None
+    if with_h0:
+        d["h0"] = _store(_normal(_rng(seed, config_id, _H0), (len(lengths), nheads, dstate, headdim),
+                                 0.05), "f32")
+    return d
+
+
 def decode_inputs(batch, nheads, headdim, dstate, ngroups, dtype, step, seed=0, config_id=0):
     """Per-token inputs of one decode step: x [b, H, P], dt [b, H] (raw), B, C [b, G, N]."""
     return dict(
