@@ -232,6 +232,47 @@ def test_prefill_split_sequence_handoff():
     assert_parity(to_f64(y), yo, TAU_BF16, True, "whole y")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_without_softplus(dtype):
+    """dt_softplus = 0: dt is used as Δ directly (positive steps of the right scale)."""
+    b, L, H, P, N, G, Q = 2, 333, 4, 64, 128, 2, 128
+    d = gen.ssd_inputs(b, L, H, P, N, G, dtype, seed=9, config_id=105, with_h0=True)
+    steps = np.random.default_rng(5).uniform(1e-3, 0.2, (b, L, H)).astype(np.float32)
+    d["dt"] = gen.Tensor(steps if dtype == "f32" else gen.f32_to_bf16_bits(steps), dtype)
+    x, dt, B, C, A, D, h0 = (to_dev(d[k]) for k in ("x", "dt", "B", "C", "A", "D", "h0"))
+    y, fs = ssd.ssd_chunk_scan(x, dt, A, B, C, D, chunk=Q, initial_state=h0, dt_softplus=False,
+                               return_final_state=True)
+    torch.cuda.synchronize()
+    yo, fo = oracle.ssd_scan(d["x"].f64(), d["dt"].f64(), d["A"].f64(), d["B"].f64(), d["C"].f64(),
+                             d["D"].f64(), d["h0"].f64(), dt_softplus=False, return_final_state=True)
+    assert_parity(to_f64(y), yo, tau_of(dtype), dtype == "bf16", f"no softplus y {dtype}")
+    assert_parity(to_f64(fs), fo, tau_of(dtype), False, f"no softplus final {dtype}")
+
+
+def test_prefill_segmented_extreme_decay_no_final_state():
+    """Segmented bf16 call with large steps (chunk decays far below float32) and
+    no final state requested: outputs stay finite and match."""
+    b, L, H, N, G = 1, 3000, 2, 64, 1
+    d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=12, config_id=106)
+    steps = np.random.default_rng(6).uniform(0.5, 8.0, (b, L, H))
+    raw = (steps + np.log(-np.expm1(-steps))).astype(np.float32)
+    d["dt"] = gen.Tensor(gen.f32_to_bf16_bits(raw), "bf16")
+    d["A"] = gen.Tensor(np.full(H, -12.0, np.float32), "f32")
+    assert ssd.chunk_scan_workspace_size(b, L, H, 64, N, G, 64, ssd.SSD_BF16) > 256
+    y = run_scan(d, 64, "bf16", final=False)
+    assert torch.isfinite(y.float()).all()
+    yo = oracle_scan(d)[0]
+    assert_parity(to_f64(y), yo, TAU_BF16, True, "segmented extreme y")
+
+
+def test_prefill_segmented_deterministic():
+    b, L, H, N, G = 1, 4096, 3, 128, 3
+    d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=13, config_id=107, with_h0=True)
+    y1, f1 = run_scan(d, 256, "bf16", with_h0=True)
+    y2, f2 = run_scan(d, 256, "bf16", with_h0=True)
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
 # ---------------------------------------------------------- full-size configs
 
 @pytest.fixture(scope="module")
