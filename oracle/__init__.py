@@ -51,6 +51,10 @@ def _load():
     lib.oracle_ssd_decode.restype = None
     lib.oracle_selective_scan.argtypes = [i] * 5 + [_dp] * 9
     lib.oracle_selective_scan.restype = None
+    lib.oracle_causal_conv1d.argtypes = [i] * 5 + [_dp] * 6
+    lib.oracle_causal_conv1d.restype = None
+    lib.oracle_gated_rmsnorm.argtypes = [i] * 3 + [ctypes.c_double] + [_dp] * 4
+    lib.oracle_gated_rmsnorm.restype = None
     lib.oracle_threads.restype = ctypes.c_int
     lib.oracle_version.restype = ctypes.c_int
     _lib = lib
@@ -153,3 +157,35 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_softplus=True,
                               _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(out), _ptr(hf))
     last_seconds = time.perf_counter() - t0
     return (out, hf) if return_final_state else out
+
+
+def causal_conv1d(x, weight, bias=None, initial_state=None, apply_silu=True,
+                  return_final_state=False):
+    """Causal depthwise conv over time (+ SiLU).  x [b,L,C], weight [C,W],
+    bias [C] or None, initial_state [b,W-1,C] (previous inputs, oldest first) or
+    None.  Returns y [b,L,C] (and the final state [b,W-1,C])."""
+    lib = _load()
+    x, weight, bias, initial_state = map(_f64, (x, weight, bias, initial_state))
+    b, L, C = x.shape
+    W = weight.shape[1]
+    assert weight.shape == (C, W) and W >= 1
+    y = np.empty_like(x)
+    fs = np.empty((b, W - 1, C)) if return_final_state else None
+    lib.oracle_causal_conv1d(b, L, C, W, int(bool(apply_silu)), _ptr(x), _ptr(weight), _ptr(bias),
+                             _ptr(initial_state), _ptr(y), _ptr(fs) if fs is not None and W > 1 else None)
+    if fs is not None and W == 1:
+        fs = np.empty((b, 0, C))
+    return (y, fs) if return_final_state else y
+
+
+def gated_rmsnorm(y, z, weight, ngroups=1, eps=1e-5):
+    """RMSNorm of g = y·silu(z) (g = y when z is None) over ngroups contiguous
+    channel groups of each row.  y, z [..., C], weight [C]."""
+    lib = _load()
+    y, z, weight = map(_f64, (y, z, weight))
+    C = y.shape[-1]
+    rows = int(np.prod(y.shape[:-1]))
+    assert C % ngroups == 0 and weight.shape == (C,)
+    out = np.empty_like(y)
+    lib.oracle_gated_rmsnorm(rows, C, ngroups, float(eps), _ptr(y), _ptr(z), _ptr(weight), _ptr(out))
+    return out

@@ -206,3 +206,80 @@ void oracle_selective_scan(int batch, int seqlen, int dim, int dstate, int delta
         }
     }
 }
+
+/*
+ * Causal depthwise 1-D convolution of the inner activations ([TP] §2.2: the
+ * SSM inputs come out of a 1-D convolution and an activation).  For batch row
+ * b, channel c and time t, with window width W:
+ *     v = bias[c] + Σ_{k=0}^{W-1} w[c][k]·u(t - (W-1) + k),   y = silu(v) or v
+ * where u(s) = x[b][s][c] for s >= 0 and, for s < 0, the carried state
+ * state0[b][W-1+s][c] (zero without one).  The final state holds the last
+ * W-1 inputs, u(L-W+1) .. u(L-1), oldest first.
+ */
+void oracle_causal_conv1d(int batch, int seqlen, int channels, int width, int apply_silu,
+                          const double *x, const double *w, const double *bias,
+                          const double *state0, double *y, double *state_out)
+{
+    const int W1 = width - 1;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) collapse(2)
+#endif
+    for (int b = 0; b < batch; ++b)
+        for (int c = 0; c < channels; ++c) {
+            for (int t = 0; t < seqlen; ++t) {
+                double v = bias ? bias[c] : 0.0;
+                for (int k = 0; k < width; ++k) {
+                    const int s = t - W1 + k;
+                    double u = 0.0;
+                    if (s >= 0)
+                        u = x[((size_t)b * seqlen + s) * channels + c];
+                    else if (state0)
+                        u = state0[((size_t)b * W1 + (W1 + s)) * channels + c];
+                    v += w[(size_t)c * width + k] * u;
+                }
+                y[((size_t)b * seqlen + t) * channels + c] = apply_silu ? v / (1.0 + exp(-v)) : v;
+            }
+            if (state_out)
+                for (int r = 0; r < W1; ++r) {
+                    const int s = seqlen - W1 + r;
+                    double u = 0.0;
+                    if (s >= 0)
+                        u = x[((size_t)b * seqlen + s) * channels + c];
+                    else if (state0)
+                        u = state0[((size_t)b * W1 + (W1 + s)) * channels + c];
+                    state_out[((size_t)b * W1 + r) * channels + c] = u;
+                }
+        }
+}
+
+/*
+ * Gated grouped RMS normalisation of the scan output ([TP] §4.1: the norm
+ * runs over groups of channels, so each group's statistics stay local).  For
+ * row r, the channels split into G contiguous groups of channels/G; with
+ * g = y·silu(z) (g = y without z):
+ *     out[c] = g[c] / sqrt(mean over c's group of g² + eps) · weight[c]
+ */
+void oracle_gated_rmsnorm(int rows, int channels, int ngroups, double eps, const double *y,
+                          const double *z, const double *weight, double *out)
+{
+    const int cg = channels / ngroups;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) collapse(2)
+#endif
+    for (int r = 0; r < rows; ++r)
+        for (int gi = 0; gi < ngroups; ++gi) {
+            const size_t base = (size_t)r * channels + (size_t)gi * cg;
+            double ss = 0.0;
+            for (int c = 0; c < cg; ++c) {
+                double g = y[base + c];
+                if (z) g *= z[base + c] / (1.0 + exp(-z[base + c]));
+                ss += g * g;
+            }
+            const double inv = 1.0 / sqrt(ss / cg + eps);
+            for (int c = 0; c < cg; ++c) {
+                double g = y[base + c];
+                if (z) g *= z[base + c] / (1.0 + exp(-z[base + c]));
+                out[base + c] = g * inv * weight[(size_t)gi * cg + c];
+            }
+        }
+}

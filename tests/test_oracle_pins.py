@@ -364,3 +364,87 @@ def test_varlen_reset_is_not_vacuous():
     whole = oracle.ssd_scan(x[None], dt[None], A, B[None], C[None], d["D"].f64())[0]
     np.testing.assert_array_equal(packed[:6], whole[:6])
     assert np.all(np.abs(packed[6:] - whole[6:]).max(axis=(1, 2)) > 0)
+
+
+# ---- neighbouring ops: causal conv1d (page 1 §2.2) and gated grouped RMSNorm (§4.1)
+
+def test_conv1d_equals_numpy_convolve():
+    """Without the activation, each channel is a full linear convolution cut to
+    the first L outputs (numpy's routine), plus the bias."""
+    rng = np.random.default_rng(21)
+    b, L, C, W = 2, 37, 6, 4
+    x, w, bias = rng.normal(size=(b, L, C)), rng.normal(size=(C, W)), rng.normal(size=C)
+    y = oracle.causal_conv1d(x, w, bias, apply_silu=False)
+    ref = np.empty_like(y)
+    for bi in range(b):
+        for c in range(C):
+            ref[bi, :, c] = np.convolve(x[bi, :, c], w[c, ::-1])[:L] + bias[c]
+    np.testing.assert_allclose(y, ref, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("W", [2, 3, 4])
+def test_conv1d_identity_and_shift_kernels(W):
+    rng = np.random.default_rng(W)
+    x = rng.normal(size=(1, 15, 3))
+    ident = np.zeros((3, W)); ident[:, -1] = 1.0
+    np.testing.assert_array_equal(oracle.causal_conv1d(x, ident, apply_silu=False), x)
+    shift = np.zeros((3, W)); shift[:, 0] = 1.0  # y_t = x_{t-W+1}, zeros before the start
+    y = oracle.causal_conv1d(x, shift, apply_silu=False)
+    np.testing.assert_array_equal(y[:, W - 1:], x[:, :15 - (W - 1)])
+    assert np.all(y[:, :W - 1] == 0.0)
+
+
+def test_conv1d_silu_closed_form():
+    x = np.zeros((1, 3, 2)); x[0, :, 0] = [0.0, math.log(3.0), -2.0]
+    ident = np.zeros((2, 4)); ident[:, -1] = 1.0
+    y = oracle.causal_conv1d(x, ident, apply_silu=True)
+    np.testing.assert_allclose(y[0, :, 0], [0.0, 0.75 * math.log(3.0), -2.0 / (1.0 + math.exp(2.0))],
+                               rtol=1e-15)
+
+
+def test_conv1d_state_handoff():
+    """Convolving a prefix, then the rest from the prefix's final state, equals
+    convolving the whole sequence (and a final state shorter than the window
+    reaches back into the carried state)."""
+    rng = np.random.default_rng(22)
+    b, L, C, W, L1 = 2, 40, 5, 4, 13
+    x, w, bias = rng.normal(size=(b, L, C)), rng.normal(size=(C, W)), rng.normal(size=C)
+    s0 = rng.normal(size=(b, W - 1, C))
+    y, fs = oracle.causal_conv1d(x, w, bias, s0, return_final_state=True)
+    y1, f1 = oracle.causal_conv1d(x[:, :L1], w, bias, s0, return_final_state=True)
+    y2, f2 = oracle.causal_conv1d(x[:, L1:], w, bias, f1, return_final_state=True)
+    np.testing.assert_array_equal(np.concatenate([y1, y2], 1), y)
+    np.testing.assert_array_equal(f2, fs)
+    np.testing.assert_array_equal(fs, x[:, L - (W - 1):])
+    _, f_short = oracle.causal_conv1d(x[:, :1], w, bias, s0, return_final_state=True)
+    np.testing.assert_array_equal(f_short, np.concatenate([s0[:, 1:], x[:, :1]], 1))
+
+
+def test_rmsnorm_unit_rms_closed_form():
+    """Weight 1, no gate: the mean square of each normalised group is m/(m+eps)."""
+    rng = np.random.default_rng(23)
+    y = rng.normal(size=(4, 12)) * 3.0
+    eps = 0.1
+    out = oracle.gated_rmsnorm(y, None, np.ones(12), ngroups=3, eps=eps)
+    for g in range(3):
+        m = np.mean(y[:, 4 * g:4 * g + 4] ** 2, axis=1)
+        np.testing.assert_allclose(np.mean(out[:, 4 * g:4 * g + 4] ** 2, axis=1), m / (m + eps),
+                                   rtol=1e-13)
+
+
+def test_rmsnorm_scale_invariance_groups_and_gate():
+    rng = np.random.default_rng(24)
+    y, z, w = rng.normal(size=(5, 16)), rng.normal(size=(5, 16)), rng.normal(size=16)
+    base = oracle.gated_rmsnorm(y, z, w, ngroups=4, eps=0.0)
+    np.testing.assert_allclose(oracle.gated_rmsnorm(7.5 * y, z, w, ngroups=4, eps=0.0), base,
+                               rtol=1e-13)
+    # groups are independent: each group alone (one group over its channels) gives the same
+    for g in range(4):
+        sl = slice(4 * g, 4 * g + 4)
+        np.testing.assert_allclose(oracle.gated_rmsnorm(y[:, sl], z[:, sl], w[sl], 1, 0.0),
+                                   base[:, sl], rtol=1e-13)
+    # a constant gate z = ln 3 scales g uniformly, which the norm removes
+    np.testing.assert_allclose(oracle.gated_rmsnorm(y, np.full_like(y, math.log(3.0)), w, 4, 0.0),
+                               oracle.gated_rmsnorm(y, None, w, 4, 0.0), rtol=1e-13)
+    # a closed gate (z = 0) gives zeros
+    assert np.all(oracle.gated_rmsnorm(y, np.zeros_like(y), w, 4, 1e-5) == 0.0)
