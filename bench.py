@@ -14,8 +14,10 @@ The same run also times, as separate legs of the JSON line: the single-token
 decode step at batch 256 (state cache of a 2.7B-layer prefill), the 64K-token
 long-context prefill with eight groups, the Mamba-1 selective scan (batch 8,
 seqlen 4096, 5120 channels, dstate 16), and a packed variable-length prefill
-(8 sequences of mixed lengths, 16384 tokens); and the CPU float64 oracle on the
-prefill workload (the `cpu_baseline`, timed on this host's cores).
+(8 sequences of mixed lengths, 16384 tokens), the causal conv1d (width 4 over
+5376 channels) and the gated RMSNorm (5120 channels) of the same layer; and the
+CPU float64 oracle on the prefill workload (the `cpu_baseline`, timed on this
+host's cores).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs ...]
        [--no-cpu-baseline]
@@ -276,6 +278,43 @@ def bench_varlen(steps, warmup):
     return dict(ms=ms, kernel_ms=per[0], tokens=T, bytes=nbytes)
 
 
+def bench_convnorm(steps, warmup):
+    """The causal conv1d and the gated RMSNorm at the 2.7B-layer shape."""
+    import torch
+    import selective_state_space_13_amd as ssd
+    from workloads import configs, gen
+    c = configs.CONV1D_LAYER
+    log("[bench] conv1d: generating inputs")
+    d = gen.conv1d_inputs(c["batch"], c["seqlen"], c["channels"], c["width"], c["dtype"],
+                          config_id=c["id"])
+    x, w, bias, s0 = (to_dev(d[k]) for k in ("x", "weight", "bias", "state"))
+    del d
+    y = torch.empty_like(x)
+    fs = torch.empty_like(s0)
+
+    def conv():
+        ssd.causal_conv1d(x, w, bias, initial_state=s0, return_final_state=True, out=y, final_state=fs)
+
+    ms_c, per_c = time_calls(conv, 1, steps, warmup)
+    n = c["batch"] * c["seqlen"] * c["channels"]
+    conv_bytes = 2 * n * 2 + 2 * s0.numel() * 4 + w.numel() * 4 + bias.numel() * 4
+    del x, y
+    r = configs.GATED_RMSNORM_LAYER
+    log("[bench] rmsnorm: generating inputs")
+    d = gen.rmsnorm_inputs(r["rows"], r["channels"], r["dtype"], config_id=r["id"])
+    yy, z, wn = (to_dev(d[k]) for k in ("y", "z", "weight"))
+    del d
+    out = torch.empty_like(yy)
+
+    def norm():
+        ssd.gated_rmsnorm(yy, z, wn, ngroups=r["ngroups"], out=out)
+
+    ms_n, per_n = time_calls(norm, 1, steps, warmup)
+    norm_bytes = 3 * r["rows"] * r["channels"] * 2 + wn.numel() * 4
+    return dict(conv_ms=per_c[0], conv_bytes=conv_bytes, norm_ms=per_n[0], norm_bytes=norm_bytes,
+                conv_tokens=c["batch"] * c["seqlen"], norm_rows=r["rows"])
+
+
 def cpu_baseline(cfg, seed=0, min_seconds=10.0):
     """The float64 oracle on the prefill workload, on this host's cores."""
     import oracle
@@ -304,7 +343,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="decode,long,mamba1,varlen",
+    ap.add_argument("--legs", default="decode,long,mamba1,varlen,convnorm",
                     help="extra legs to time besides the prefill step (comma list or 'none')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -414,6 +453,15 @@ def main():
                            "tokens_per_s": round(vl["tokens"] / (vl["ms"] * 1e-3), 1),
                            "ms": round(vl["ms"], 5), "kernel_ms": round(vl["kernel_ms"], 5),
                            "hbm_frac": round(vl["bytes"] / t / HBM_PEAK, 4)}
+    if "convnorm" in legs:
+        cn = bench_convnorm(args.steps, args.warmup)
+        for key, wl in (("conv", "conv1d_layer:b8L2048C5376W4"), ("norm", "gated_rmsnorm_layer:rows16384C5120G1")):
+            t = cn[key + "_ms"] * 1e-3
+            extra[{"conv": "conv1d", "norm": "gated_rmsnorm"}[key]] = {
+                "workload": wl, "kernel_ms": round(cn[key + "_ms"], 5),
+                "roofline": {"bound": "hbm", "achieved": round(cn[key + "_bytes"] / t / 1e9, 2),
+                             "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                             "frac": round(cn[key + "_bytes"] / t / HBM_PEAK, 4)}}
     if extra:
         result["legs"] = extra
     if not args.no_cpu_baseline:

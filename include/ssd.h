@@ -148,6 +148,39 @@ int ssd_chunk_scan_varlen_fwd(int nseq, int total_tokens, int nheads, int headdi
                               float *final_states, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Causal depthwise 1-D convolution with SiLU, the short convolution whose
+ * outputs feed the scan ([TP] §2.2).  For batch row b, channel c, time t and
+ * window width W:
+ *     v = bias[c] + Σ_{k<W} weight[c][k]·u(t-W+1+k);  y = silu(v) if apply_silu, else v
+ * with u(s) = x[b][s][c] for s >= 0 and initial_state[b][W-1+s][c] (or 0) for
+ * s < 0.  final_state receives the last W-1 inputs u(L-W+1 .. L-1), oldest
+ * first, so a sequence can be continued (or decoded) where it stopped.
+ *
+ *   x, y    [batch][seqlen][channels]  dtype
+ *   weight  [channels][width] float;  bias [channels] float or NULL
+ *   initial_state, final_state  [batch][width-1][channels] float or NULL
+ *
+ * Supported: width 1..4; channels a multiple of 8; batch <= 65535.
+ * ------------------------------------------------------------------------ */
+int ssd_causal_conv1d_fwd(int batch, int seqlen, int channels, int width, int dtype,
+                          int apply_silu, const void *x, const float *weight, const float *bias,
+                          const float *initial_state, void *y, float *final_state, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Gated grouped RMS normalisation of the scan output ([TP] §4.1: the norm
+ * runs over channel groups so their statistics stay local).  Each row's
+ * channels split into ngroups contiguous groups; with g = y·silu(z) (g = y
+ * when z is NULL):
+ *     out[c] = g[c] / sqrt(mean over c's group of g² + eps) · weight[c]
+ *
+ *   y, z, out  [rows][channels] dtype (z may be NULL); weight [channels] float
+ *
+ * Supported: channels/ngroups a multiple of 8, at most 8192.
+ * ------------------------------------------------------------------------ */
+int ssd_gated_rmsnorm_fwd(int rows, int channels, int ngroups, int dtype, float eps, const void *y,
+                          const void *z, const float *weight, void *out, void *stream);
+
+/* ------------------------------------------------------------------------
  * One decode step against a cached state ([INF] Abstract; the single step of
  * [TP] §2.1 with the scalar decay of §3.1).  For each (b, h):
  *     a = exp(Δ·A_h);  state <- a·state + Δ·B xᵀ;  y = stateᵀ C + D_h·x

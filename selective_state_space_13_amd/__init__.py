@@ -62,6 +62,10 @@ def lib() -> ctypes.CDLL:
     L.ssd_chunk_scan_fwd.restype = i
     L.ssd_chunk_scan_varlen_fwd.argtypes = [i] * 8 + [vp] * 11
     L.ssd_chunk_scan_varlen_fwd.restype = i
+    L.ssd_causal_conv1d_fwd.argtypes = [i] * 6 + [vp] * 7
+    L.ssd_causal_conv1d_fwd.restype = i
+    L.ssd_gated_rmsnorm_fwd.argtypes = [i] * 4 + [ctypes.c_float] + [vp] * 5
+    L.ssd_gated_rmsnorm_fwd.restype = i
     L.ssd_decode_step.argtypes = [i] * 7 + [vp] * 9
     L.ssd_decode_step.restype = i
     L.selective_scan_workspace_size.argtypes = [i] * 5
@@ -223,6 +227,59 @@ def ssd_chunk_scan_varlen(x, dt, A, B, C, D=None, *, cu_seqlens, initial_states=
         _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(initial_states),
         _ptr(y), _ptr(fs), _stream(dev)))
     return (y, fs) if return_final_states else y
+
+
+def causal_conv1d(x, weight, bias=None, *, initial_state=None, apply_silu=True,
+                  return_final_state=False, out=None, final_state=None):
+    """Causal depthwise conv over time (+ SiLU).  x [b,L,C] float32 or bf16,
+    weight [C,W] fp32, bias [C] fp32 or None, initial_state [b,W-1,C] fp32 or None.
+    Returns y [b,L,C] or (y, final_state fp32 [b,W-1,C])."""
+    torch = _torch()
+    x = _req(x, "x")
+    dev = x.device
+    code = _dtype_code(x)
+    b, L, Cc = x.shape
+    _req(weight, "weight", torch.float32, dev)
+    _req(bias, "bias", torch.float32, dev)
+    _req(initial_state, "initial_state", torch.float32, dev)
+    W = weight.shape[1]
+    if tuple(weight.shape) != (Cc, W) or (bias is not None and tuple(bias.shape) != (Cc,)):
+        raise ValueError("weight must be [channels, width] and bias [channels]")
+    if initial_state is not None and tuple(initial_state.shape) != (b, W - 1, Cc):
+        raise ValueError("initial_state must be [batch, width-1, channels]")
+    y = out if out is not None else torch.empty_like(x)
+    _req(y, "out", x.dtype, dev)
+    fs = None
+    if return_final_state:
+        fs = final_state if final_state is not None else torch.empty(
+            (b, W - 1, Cc), dtype=torch.float32, device=dev)
+        _req(fs, "final_state", torch.float32, dev)
+    check(lib().ssd_causal_conv1d_fwd(b, L, Cc, W, code, int(bool(apply_silu)), _ptr(x),
+                                      _ptr(weight), _ptr(bias), _ptr(initial_state), _ptr(y),
+                                      _ptr(fs), _stream(dev)))
+    return (y, fs) if return_final_state else y
+
+
+def gated_rmsnorm(y, z, weight, *, ngroups=1, eps=1e-5, out=None):
+    """RMSNorm of y·silu(z) (y alone when z is None) over ngroups contiguous
+    channel groups of each row.  y, z [..., C] float32 or bf16, weight [C] fp32."""
+    torch = _torch()
+    y = _req(y, "y")
+    dev = y.device
+    code = _dtype_code(y)
+    _req(z, "z", y.dtype, dev)
+    _req(weight, "weight", torch.float32, dev)
+    Cc = y.shape[-1]
+    if z is not None and z.shape != y.shape:
+        raise ValueError("z must have the shape of y")
+    if tuple(weight.shape) != (Cc,):
+        raise ValueError("weight must be [channels]")
+    o = out if out is not None else torch.empty_like(y)
+    _req(o, "out", y.dtype, dev)
+    rows = y.numel() // Cc if Cc else 0
+    check(lib().ssd_gated_rmsnorm_fwd(rows, Cc, ngroups, code, float(eps), _ptr(y), _ptr(z),
+                                      _ptr(weight), _ptr(o), _stream(dev)))
+    return o
 
 
 def ssd_decode_step(x, dt, A, B, C, D, state, *, dt_softplus=True, out=None):

@@ -446,4 +446,81 @@ int selective_scan_fwd(int batch, int seqlen, int dim, int dstate, int dtype, in
     return SSD_OK;
 }
 
+int ssd_causal_conv1d_fwd(int batch, int seqlen, int channels, int width, int dtype,
+                          int apply_silu, const void *x, const float *weight, const float *bias,
+                          const float *initial_state, void *y, float *final_state, void *stream_) {
+    if (dtype != SSD_F32 && dtype != SSD_BF16)
+        return fail(SSD_ERR_UNSUPPORTED, "dtype %d is not SSD_F32 or SSD_BF16", dtype);
+    if (batch < 0 || seqlen < 0 || channels < 1)
+        return fail(SSD_ERR_SHAPE, "batch, seqlen must be >= 0 and channels >= 1");
+    if (width < 1 || width > 4) return fail(SSD_ERR_UNSUPPORTED, "width %d: 1 to 4 supported", width);
+    if (channels % 8) return fail(SSD_ERR_UNSUPPORTED, "channels %d must be a multiple of 8", channels);
+    if (batch > 65535 || seqlen / 64 > 65535)
+        return fail(SSD_ERR_UNSUPPORTED, "batch <= 65535 and seqlen < 4194304 are supported");
+    uint64_t n_x, n_state;
+    if (!prod(n_x, {batch, seqlen, channels}) || !prod(n_state, {batch, width - 1, channels}))
+        return fail(SSD_ERR_SHAPE, "tensor sizes overflow");
+    if (batch == 0) return SSD_OK;
+    if (!weight) return fail(SSD_ERR_NULL, "weight is required");
+    if (seqlen > 0 && (!x || !y)) return fail(SSD_ERR_NULL, "x and y are required");
+    if ((x && !aligned(x, 16)) || (y && !aligned(y, 16)))
+        return fail(SSD_ERR_ALIGN, "x and y must be 16-byte aligned");
+    const void *fptrs[] = {weight, bias, initial_state, final_state};
+    for (const void *p : fptrs)
+        if (p && !aligned(p, 4)) return fail(SSD_ERR_ALIGN, "float pointer %p is not 4-byte aligned", p);
+    const int es = elem_size(dtype);
+    int st = check_alias(
+        {span("y", y, n_x * es), span("final_state", final_state, final_state ? n_state * 4 : 0)},
+        {span("x", x, n_x * es), span("weight", weight, (uint64_t)channels * width * 4),
+         span("bias", bias, bias ? (uint64_t)channels * 4 : 0),
+         span("initial_state", initial_state, initial_state ? n_state * 4 : 0)});
+    if (st) return st;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    LaunchMarks marks(stream);
+    marks.before();
+    hipError_t e;
+    if (seqlen == 0)  // the carried state passes through unchanged
+        e = final_state && width > 1 ? ssd::launch_copy_state(initial_state, final_state, n_state, stream)
+                                     : hipSuccess;
+    else
+        e = ssd::launch_causal_conv1d(dtype, x, weight, bias, initial_state, batch, seqlen, channels,
+                                      width, apply_silu, y, final_state, stream);
+    marks.after();
+    return e == hipSuccess ? SSD_OK : hip_fail(e, "conv1d launch");
+}
+
+int ssd_gated_rmsnorm_fwd(int rows, int channels, int ngroups, int dtype, float eps, const void *y,
+                          const void *z, const float *weight, void *out, void *stream_) {
+    if (dtype != SSD_F32 && dtype != SSD_BF16)
+        return fail(SSD_ERR_UNSUPPORTED, "dtype %d is not SSD_F32 or SSD_BF16", dtype);
+    if (rows < 0 || channels < 1 || ngroups < 1)
+        return fail(SSD_ERR_SHAPE, "rows must be >= 0, channels and ngroups >= 1");
+    if (channels % ngroups)
+        return fail(SSD_ERR_SHAPE, "ngroups (%d) must divide channels (%d)", ngroups, channels);
+    const int cg = channels / ngroups;
+    if (cg % 8 || cg > 8192)
+        return fail(SSD_ERR_UNSUPPORTED, "group size %d: a multiple of 8 up to 8192 is supported", cg);
+    if (!(eps >= 0.0f) || eps == __builtin_inff()) return fail(SSD_ERR_SHAPE, "eps must be finite and >= 0");
+    uint64_t n;
+    if (!prod(n, {rows, channels})) return fail(SSD_ERR_SHAPE, "tensor sizes overflow");
+    if (rows == 0) return SSD_OK;
+    if (!y || !weight || !out) return fail(SSD_ERR_NULL, "y, weight and out are required");
+    const void *ptrs[] = {y, z, out};
+    for (const void *p : ptrs)
+        if (p && !aligned(p, 16)) return fail(SSD_ERR_ALIGN, "tensor pointer %p is not 16-byte aligned", p);
+    if (!aligned(weight, 4)) return fail(SSD_ERR_ALIGN, "weight must be 4-byte aligned");
+    const int es = elem_size(dtype);
+    int st = check_alias({span("out", out, n * es)},
+                         {span("y", y, n * es), span("z", z, z ? n * es : 0),
+                          span("weight", weight, (uint64_t)channels * 4)});
+    if (st) return st;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    LaunchMarks marks(stream);
+    marks.before();
+    hipError_t e = ssd::launch_gated_rmsnorm(dtype, y, z, weight, rows, channels, ngroups, eps, out,
+                                             stream);
+    marks.after();
+    return e == hipSuccess ? SSD_OK : hip_fail(e, "gated rmsnorm launch");
+}
+
 }  // extern "C"

@@ -118,4 +118,17 @@ hipError_t launch_selective_scan(int phase, const ScanPlan &pl, int dtype, const
 // copy or zero the state for an empty sequence
 hipError_t launch_copy_state(const float *src, float *dst, size_t n, hipStream_t stream);
 
+// Causal depthwise conv1d (+ SiLU) over [batch][seqlen][channels], window
+// width 1..4, weight [channels][width] float, carried state [batch][width-1]
+// [channels] float (oldest first); channels a multiple of 8.
+hipError_t launch_causal_conv1d(int dtype, const void *x, const float *weight, const float *bias,
+                                const float *initial_state, int batch, int seqlen, int channels,
+                                int width, int apply_silu, void *y, float *final_state,
+                                hipStream_t stream);
+
+// Gated grouped RMSNorm of [rows][channels]: ngroups contiguous groups per row.
+hipError_t launch_gated_rmsnorm(int dtype, const void *y, const void *z, const float *weight,
+                                long long rows, int channels, int ngroups, float eps, void *out,
+                                hipStream_t stream);
+
 }  // namespace ssd

@@ -231,6 +231,55 @@ def test_varlen_null_align_alias(L):
     assert varlen_call(L, nseq=0) == OK
 
 
+def conv_call(L, b=2, Lq=100, C=64, W=4, dtype=BF16, ptrs=None):
+    p = dict(x=fake(1), w=fake(2), bias=fake(3), s0=None, y=fake(4), fs=fake(5))
+    if ptrs:
+        p.update(ptrs)
+    return L.ssd_causal_conv1d_fwd(b, Lq, C, W, dtype, 1, p["x"], p["w"], p["bias"], p["s0"],
+                                   p["y"], p["fs"], None)
+
+
+@pytest.mark.parametrize("kw,status", [(dict(b=-1), SHAPE), (dict(Lq=-1), SHAPE), (dict(C=0), SHAPE),
+                                       (dict(C=12), UNSUP), (dict(W=5), UNSUP), (dict(W=0), UNSUP),
+                                       (dict(dtype=3), UNSUP), (dict(b=70000), UNSUP)])
+def test_conv1d_shape_errors(L, kw, status):
+    assert conv_call(L, **kw) == status
+
+
+def test_conv1d_null_align_alias(L):
+    assert conv_call(L, ptrs={"w": None}) == NULL
+    assert conv_call(L, ptrs={"x": None}) == NULL
+    assert conv_call(L, ptrs={"x": fake(1, 8)}) == ALIGN
+    assert conv_call(L, ptrs={"w": fake(2, 2)}) == ALIGN
+    assert conv_call(L, ptrs={"y": fake(1)}) == ALIAS
+    assert conv_call(L, ptrs={"fs": fake(2)}) == ALIAS
+    assert conv_call(L, b=0) == OK
+
+
+def norm_call(L, rows=10, C=256, G=2, dtype=BF16, eps=1e-5, ptrs=None):
+    p = dict(y=fake(1), z=fake(2), w=fake(3), out=fake(4))
+    if ptrs:
+        p.update(ptrs)
+    return L.ssd_gated_rmsnorm_fwd(rows, C, G, dtype, ctypes.c_float(eps), p["y"], p["z"], p["w"],
+                                   p["out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [(dict(rows=-1), SHAPE), (dict(C=0), SHAPE), (dict(G=3), SHAPE),
+                                       (dict(C=264, G=2), UNSUP), (dict(C=16384 * 2, G=1), UNSUP),
+                                       (dict(eps=-1.0), SHAPE), (dict(dtype=4), UNSUP)])
+def test_rmsnorm_shape_errors(L, kw, status):
+    assert norm_call(L, **kw) == status
+
+
+def test_rmsnorm_null_align_alias(L):
+    assert norm_call(L, ptrs={"y": None}) == NULL
+    assert norm_call(L, ptrs={"w": None}) == NULL
+    assert norm_call(L, ptrs={"z": fake(2, 4)}) == ALIGN
+    assert norm_call(L, ptrs={"out": fake(1)}) == ALIAS
+    assert norm_call(L, ptrs={"out": fake(3)}) == ALIAS
+    assert norm_call(L, rows=0) == OK
+
+
 def test_last_error_is_thread_local(L):
     assert scan_call(L, G=3) == SHAPE
     msg_main = L.ssd_last_error()

@@ -273,6 +273,86 @@ def test_prefill_segmented_deterministic():
     assert torch.equal(y1, y2) and torch.equal(f1, f2)
 
 
+# ---------------------------------------------- conv1d and gated RMSNorm
+
+CONV_CASES = [
+    # b, L, C, W, silu, with state
+    (2, 200, 64, 4, True, True),    # 4 token tiles, ragged tail of 8
+    (1, 1, 16, 4, True, True),      # one token: the final state is mostly the old state
+    (3, 130, 256, 3, False, False),
+    (1, 70, 8, 2, True, True),
+    (2, 65, 40, 1, True, False),    # width 1: no state at all
+    (1, 2, 24, 4, False, True),     # shorter than the window
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", CONV_CASES, ids=lambda c: "b{}L{}C{}W{}s{}h{}".format(
+    c[0], c[1], c[2], c[3], int(c[4]), int(c[5])))
+def test_conv1d(case, dtype):
+    """Causal depthwise conv (+ SiLU) with a carried state, across token tiles
+    of 64 and sequences shorter than the window."""
+    b, L, Cc, W, silu, st = case
+    d = gen.conv1d_inputs(b, L, Cc, W, dtype, seed=L + W, config_id=110, with_state=st)
+    y, fs = ssd.causal_conv1d(to_dev(d["x"]), to_dev(d["weight"]), to_dev(d["bias"]),
+                              initial_state=to_dev(d["state"]), apply_silu=silu,
+                              return_final_state=True)
+    torch.cuda.synchronize()
+    yo, fo = oracle.causal_conv1d(d["x"].f64(), d["weight"].f64(), d["bias"].f64(),
+                                  d["state"].f64() if st else None, apply_silu=silu,
+                                  return_final_state=True)
+    assert_parity(to_f64(y), yo, tau_of(dtype), dtype == "bf16", f"conv1d {case} {dtype}")
+    np.testing.assert_array_equal(to_f64(fs), fo)  # the window holds exact copies of inputs
+
+
+def test_conv1d_state_handoff():
+    """Two calls joined by the returned state equal one call over the whole
+    sequence (split inside a token tile)."""
+    d = gen.conv1d_inputs(2, 300, 96, 4, "f32", seed=5, config_id=111)
+    x = to_dev(d["x"])
+    w, bias, s0 = to_dev(d["weight"]), to_dev(d["bias"]), to_dev(d["state"])
+    y, fs = ssd.causal_conv1d(x, w, bias, initial_state=s0, return_final_state=True)
+    y1, f1 = ssd.causal_conv1d(x[:, :137].contiguous(), w, bias, initial_state=s0,
+                               return_final_state=True)
+    y2, f2 = ssd.causal_conv1d(x[:, 137:].contiguous(), w, bias, initial_state=f1,
+                               return_final_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([y1, y2], 1), y)
+    assert torch.equal(f2, fs)
+
+
+def test_conv1d_empty_sequence_copies_state():
+    d = gen.conv1d_inputs(2, 0, 32, 4, "bf16", seed=1, config_id=112)
+    x = torch.empty((2, 0, 32), dtype=torch.bfloat16, device="cuda")
+    s0 = to_dev(d["state"])
+    y, fs = ssd.causal_conv1d(x, to_dev(d["weight"]), None, initial_state=s0, return_final_state=True)
+    torch.cuda.synchronize()
+    assert y.shape == (2, 0, 32) and torch.equal(fs, s0)
+
+
+NORM_CASES = [
+    # rows, C, ngroups, gate
+    (7, 5120, 1, True),      # 640 vectors per group: 10 per lane
+    (33, 512, 4, True),
+    (5, 64, 8, False),       # groups of 8 channels: one vector
+    (3, 8192, 1, True),      # the largest group: 16 vectors per lane
+    (9, 1024, 2, False),
+    (4, 5120, 8, True),      # the 2.7B layer with 8 groups
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", NORM_CASES, ids=lambda c: "r{}C{}G{}z{}".format(
+    c[0], c[1], c[2], int(c[3])))
+def test_gated_rmsnorm(case, dtype):
+    rows, Cc, G, gate = case
+    d = gen.rmsnorm_inputs(rows, Cc, dtype, seed=rows + G, config_id=120, gate=gate)
+    out = ssd.gated_rmsnorm(to_dev(d["y"]), to_dev(d["z"]), to_dev(d["weight"]), ngroups=G, eps=1e-5)
+    torch.cuda.synchronize()
+    ref = oracle.gated_rmsnorm(d["y"].f64(), d["z"].f64() if gate else None, d["weight"].f64(), G, 1e-5)
+    assert_parity(to_f64(out), ref, tau_of(dtype), dtype == "bf16", f"rmsnorm {case} {dtype}")
+
+
 # ---------------------------------------------------------- full-size configs
 
 @pytest.fixture(scope="module")

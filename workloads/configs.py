@@ -44,6 +44,20 @@ VARLEN_PREFILL = dict(
     nheads=80, headdim=64, dstate=128, ngroups=1,
 )
 
+# The ops on either side of the scan in the same 2.7B layer: the causal conv over
+# x, B and C together (5120 + 2·128 channels, width 4) and the gated RMSNorm of
+# the scan output (5120 channels, one group) on the batch-8 prefill's tokens.
+CONV1D_LAYER = dict(
+    id=7, name="conv1d_layer", kind="conv1d", dtype="bf16",
+    batch=8, seqlen=2048, channels=5376, width=4,
+)
+
+GATED_RMSNORM_LAYER = dict(
+    id=8, name="gated_rmsnorm_layer", kind="rmsnorm", dtype="bf16",
+    rows=16384, channels=5120, ngroups=1,
+)
+
 ALL = [TINY_SSD_F32, MAMBA2_LAYER_PREFILL, LONG_CONTEXT_PREFILL,
-       DECODE_STATE_CACHE, MAMBA1_SELECTIVE_SCAN, VARLEN_PREFILL]
+       DECODE_STATE_CACHE, MAMBA1_SELECTIVE_SCAN, VARLEN_PREFILL,
+       CONV1D_LAYER, GATED_RMSNORM_LAYER]
 BY_ID = {c["id"]: c for c in ALL}

@@ -164,3 +164,26 @@ def mamba1_inputs(batch, seqlen, dim, dstate, dtype, seed=0, config_id=0,
         z=_store(_normal(_rng(seed, config_id, _Z), (batch, seqlen, dim)), dtype) if gate else None,
     )
 
+
+
+def conv1d_inputs(batch, seqlen, channels, width, dtype, seed=0, config_id=0, with_state=True):
+    """Inputs of one causal depthwise conv: x [b, L, C] (dtype), weight [C, W] fp32
+    scaled by 1/sqrt(W), bias [C] fp32, state [b, W-1, C] fp32 (previous inputs)."""
+    w = _normal(_rng(seed, config_id, _A), (channels, width), 1.0 / math.sqrt(width))
+    return dict(
+        x=_store(_normal(_rng(seed, config_id, _X), (batch, seqlen, channels)), dtype),
+        weight=Tensor(w, "f32"),
+        bias=Tensor(_normal(_rng(seed, config_id, _D), (channels,), 0.1), "f32"),
+        state=Tensor(_normal(_rng(seed, config_id, _H0), (batch, width - 1, channels)), "f32")
+        if with_state else None,
+    )
+
+
+def rmsnorm_inputs(rows, channels, dtype, seed=0, config_id=0, gate=True):
+    """Inputs of one gated grouped RMSNorm: y and z [rows, C] (dtype), weight [C]
+    fp32 around 1.  y has the scale of a scan output (RMS about 2)."""
+    return dict(
+        y=_store(_normal(_rng(seed, config_id, _X), (rows, channels), 2.0), dtype),
+        z=_store(_normal(_rng(seed, config_id, _Z), (rows, channels)), dtype) if gate else None,
+        weight=Tensor(1.0 + _normal(_rng(seed, config_id, _D), (channels,), 0.1), "f32"),
+    )
