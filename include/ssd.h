@@ -161,6 +161,9 @@ int ssd_chunk_scan_varlen_fwd(int nseq, int total_tokens, int nheads, int headdi
  *   initial_state, final_state  [batch][width-1][channels] float or NULL
  *
  * Supported: width 1..4; channels a multiple of 8; batch <= 65535.
+ * Alignment: x, y and final_state 16 bytes; weight, bias, initial_state 4.
+ * seqlen == 0 copies initial_state (or zeros) to final_state.  The caller
+ * owns every buffer; nothing is retained after the call returns.
  * ------------------------------------------------------------------------ */
 int ssd_causal_conv1d_fwd(int batch, int seqlen, int channels, int width, int dtype,
                           int apply_silu, const void *x, const float *weight, const float *bias,
@@ -175,7 +178,9 @@ int ssd_causal_conv1d_fwd(int batch, int seqlen, int channels, int width, int dt
  *
  *   y, z, out  [rows][channels] dtype (z may be NULL); weight [channels] float
  *
- * Supported: channels/ngroups a multiple of 8, at most 8192.
+ * Supported: channels/ngroups a multiple of 8, at most 8192; eps finite and
+ * >= 0.  Alignment: y, z, out and weight 16 bytes.  out may not overlap an
+ * input.  The caller owns every buffer.
  * ------------------------------------------------------------------------ */
 int ssd_gated_rmsnorm_fwd(int rows, int channels, int ngroups, int dtype, float eps, const void *y,
                           const void *z, const float *weight, void *out, void *stream);

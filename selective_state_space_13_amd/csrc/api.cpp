@@ -455,17 +455,16 @@ int ssd_causal_conv1d_fwd(int batch, int seqlen, int channels, int width, int dt
         return fail(SSD_ERR_SHAPE, "batch, seqlen must be >= 0 and channels >= 1");
     if (width < 1 || width > 4) return fail(SSD_ERR_UNSUPPORTED, "width %d: 1 to 4 supported", width);
     if (channels % 8) return fail(SSD_ERR_UNSUPPORTED, "channels %d must be a multiple of 8", channels);
-    if (batch > 65535 || seqlen / 64 > 65535)
-        return fail(SSD_ERR_UNSUPPORTED, "batch <= 65535 and seqlen < 4194304 are supported");
+    if (batch > 65535) return fail(SSD_ERR_UNSUPPORTED, "batch %d exceeds 65535", batch);
     uint64_t n_x, n_state;
     if (!prod(n_x, {batch, seqlen, channels}) || !prod(n_state, {batch, width - 1, channels}))
         return fail(SSD_ERR_SHAPE, "tensor sizes overflow");
     if (batch == 0) return SSD_OK;
     if (!weight) return fail(SSD_ERR_NULL, "weight is required");
     if (seqlen > 0 && (!x || !y)) return fail(SSD_ERR_NULL, "x and y are required");
-    if ((x && !aligned(x, 16)) || (y && !aligned(y, 16)))
-        return fail(SSD_ERR_ALIGN, "x and y must be 16-byte aligned");
-    const void *fptrs[] = {weight, bias, initial_state, final_state};
+    if ((x && !aligned(x, 16)) || (y && !aligned(y, 16)) || (final_state && !aligned(final_state, 16)))
+        return fail(SSD_ERR_ALIGN, "x, y and final_state must be 16-byte aligned");
+    const void *fptrs[] = {weight, bias, initial_state};
     for (const void *p : fptrs)
         if (p && !aligned(p, 4)) return fail(SSD_ERR_ALIGN, "float pointer %p is not 4-byte aligned", p);
     const int es = elem_size(dtype);
@@ -505,10 +504,9 @@ int ssd_gated_rmsnorm_fwd(int rows, int channels, int ngroups, int dtype, float 
     if (!prod(n, {rows, channels})) return fail(SSD_ERR_SHAPE, "tensor sizes overflow");
     if (rows == 0) return SSD_OK;
     if (!y || !weight || !out) return fail(SSD_ERR_NULL, "y, weight and out are required");
-    const void *ptrs[] = {y, z, out};
+    const void *ptrs[] = {y, z, out, weight};
     for (const void *p : ptrs)
         if (p && !aligned(p, 16)) return fail(SSD_ERR_ALIGN, "tensor pointer %p is not 16-byte aligned", p);
-    if (!aligned(weight, 4)) return fail(SSD_ERR_ALIGN, "weight must be 4-byte aligned");
     const int es = elem_size(dtype);
     int st = check_alias({span("out", out, n * es)},
                          {span("y", y, n * es), span("z", z, z ? n * es : 0),

@@ -251,6 +251,7 @@ def test_conv1d_null_align_alias(L):
     assert conv_call(L, ptrs={"x": None}) == NULL
     assert conv_call(L, ptrs={"x": fake(1, 8)}) == ALIGN
     assert conv_call(L, ptrs={"w": fake(2, 2)}) == ALIGN
+    assert conv_call(L, ptrs={"fs": fake(5, 4)}) == ALIGN
     assert conv_call(L, ptrs={"y": fake(1)}) == ALIAS
     assert conv_call(L, ptrs={"fs": fake(2)}) == ALIAS
     assert conv_call(L, b=0) == OK
@@ -275,6 +276,7 @@ def test_rmsnorm_null_align_alias(L):
     assert norm_call(L, ptrs={"y": None}) == NULL
     assert norm_call(L, ptrs={"w": None}) == NULL
     assert norm_call(L, ptrs={"z": fake(2, 4)}) == ALIGN
+    assert norm_call(L, ptrs={"w": fake(3, 4)}) == ALIGN
     assert norm_call(L, ptrs={"out": fake(1)}) == ALIAS
     assert norm_call(L, ptrs={"out": fake(3)}) == ALIAS
     assert norm_call(L, rows=0) == OK

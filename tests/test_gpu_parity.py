@@ -338,6 +338,8 @@ NORM_CASES = [
     (3, 8192, 1, True),      # the largest group: 16 vectors per lane
     (9, 1024, 2, False),
     (4, 5120, 8, True),      # the 2.7B layer with 8 groups
+    (7, 1536, 1, True),      # two waves per unit, last block half used
+    (5, 4096, 1, False),     # four waves per unit, 2 vectors a lane
 ]
 
 
