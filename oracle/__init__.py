@@ -47,6 +47,7 @@ def _load():
     i = ctypes.c_int
     lib.oracle_ssd_scan.argtypes = [i] * 7 + [_dp] * 9
     lib.oracle_ssd_scan.restype = None
+    lib.oracle_ssd_scan_bwd.argtypes = [i] * 7 + [_dp] * 16
     lib.oracle_ssd_decode.argtypes = [i] * 6 + [_dp] * 8
     lib.oracle_ssd_decode.restype = None
     lib.oracle_selective_scan.argtypes = [i] * 5 + [_dp] * 9
@@ -94,6 +95,36 @@ def ssd_scan(x, dt, A, B, C, D=None, h0=None, dt_softplus=True, return_final_sta
                         _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y), _ptr(hf))
     last_seconds = time.perf_counter() - t0
     return (y, hf) if return_final_state else y
+
+
+def ssd_scan_bwd(x, dt, A, B, C, dy, D=None, h0=None, dhfinal=None, dt_softplus=True):
+    """Gradient of ssd_scan for the loss Σ dy·y + Σ dhfinal·h_final, by the
+    reverse-time adjoint recurrence in fp64.  Returns a dict with dx [b,L,H,P],
+    ddt [b,L,H] (w.r.t. the raw dt), dA [H], dB, dC [b,L,G,N], dD [H] and
+    dh0 [b,H,N,P].  Memory: the forward states of one (b, h) at a time,
+    (L+1)·N·P doubles per thread."""
+    global last_seconds
+    lib = _load()
+    x, dt, A, B, C, dy, D, h0, dhfinal = map(_f64, (x, dt, A, B, C, dy, D, h0, dhfinal))
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert dt.shape == (b, L, H) and A.shape == (H,) and dy.shape == x.shape
+    assert B.shape == (b, L, G, N) and C.shape == B.shape and H % G == 0
+    dx = np.empty_like(x)
+    ddt = np.empty_like(dt)
+    dA = np.empty((b, H))
+    dD = np.empty((b, H))
+    dBh = np.empty((b, L, H, N))
+    dCh = np.empty((b, L, H, N))
+    dh0 = np.empty((b, H, N, P))
+    t0 = time.perf_counter()
+    lib.oracle_ssd_scan_bwd(b, L, H, P, N, G, int(bool(dt_softplus)), _ptr(x), _ptr(dt), _ptr(A),
+                            _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(dy), _ptr(dhfinal), _ptr(dx),
+                            _ptr(ddt), _ptr(dA), _ptr(dBh), _ptr(dCh), _ptr(dD), _ptr(dh0))
+    last_seconds = time.perf_counter() - t0
+    R = H // G
+    return dict(dx=dx, ddt=ddt, dA=dA.sum(0), dB=dBh.reshape(b, L, G, R, N).sum(3),
+                dC=dCh.reshape(b, L, G, R, N).sum(3), dD=dD.sum(0), dh0=dh0)
 
 
 def ssd_scan_varlen(x, dt, A, B, C, cu_seqlens, D=None, h0s=None, dt_softplus=True,

@@ -26,6 +26,24 @@ same result, used to pin it.
   the first token of every sequence (there the previous state is replaced by
   that sequence's initial state, zero by default).
 
+* ``ssd_chunked_bwd``: the gradient of ``ssd_chunked`` in the same block
+  form, derived by hand from the chunk equations above (not from the
+  sequential adjoint).  With G_out the gradient w.r.t. the state leaving a
+  chunk (dL/dh_final for the last), K = X dYᵀ (K[s,u] = x_s·dy_u) and the
+  anti-causal decay E[s,u] = exp(cs_u - cs_s) for u >= s:
+      dxr_s = Σ_u (C_u·B_s) E[s,u] dy_u + exp(cs_end - cs_s) B_sᵀ G_out
+      dx    = Δ·dxr + D dy
+      dB_s  = Δ_s Σ_u K[s,u] E[s,u] C_u + Δ_s exp(cs_end - cs_s) G_out x_s
+      dC_u  = Σ_s K[s,u] E[s,u] Δ_s B_s + exp(cs_u) h_in dy_u
+      G_in  = exp(cs_end) G_out + Σ_u exp(cs_u) C_u dy_uᵀ   (= G_out of the chunk before)
+  and for the decays, with cs taken as free variables inside the chunk,
+  Z[u,s] = M[u,s] K[s,u] (M the forward's intra-chunk matrix) and
+  q_s = Δ_s exp(cs_end - cs_s) x_s·(B_sᵀ G_out):
+      dcs_u += Σ_s Z[u,s] + exp(cs_u) dy_u·(h_inᵀ C_u);   dcs_s -= Σ_u Z[u,s] + q_s
+      dcs_end += exp(cs_end) <G_out, h_in> + Σ_s q_s
+      dℓ_t   = Σ_{v >= t in the chunk} dcs_v   (cs_v = Σ_{k<=v} ℓ_k, ℓ = Δ·A)
+      dΔ     = A·dℓ + x·dxr;  dA = Σ Δ·dℓ;  dD = Σ x·dy;  dh0 = G_in of chunk 0
+
 Only for small inputs (the dual forms build L x L matrices).
 """
 from __future__ import annotations
@@ -185,3 +203,68 @@ def ssd_packed_reset(x, dt, A, B, C, cu_seqlens, D=None, h0s=None, dt_softplus=T
                     if cu[s_ + 1] == t + 1 and cu[s_ + 1] > cu[s_]:
                         hf[s_, h] = state
     return y, hf
+
+
+def ssd_chunked_bwd(x, dt, A, B, C, dy, D=None, h0=None, dhfinal=None, chunk=64, dt_softplus=True):
+    """Gradient of the chunked SSD scan (see the module notes), chunk by chunk:
+    states entering each chunk forward, then the adjoint backwards.  Returns the
+    dict of ``oracle.ssd_scan_bwd``."""
+    x, dt, B, C, dy = (np.asarray(v, np.float64) for v in (x, dt, B, C, dy))
+    A = np.asarray(A, np.float64)
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    R = H // G
+    out = dict(dx=np.zeros_like(x), ddt=np.zeros_like(dt), dA=np.zeros(H), dB=np.zeros_like(B),
+               dC=np.zeros_like(C), dD=np.zeros(H), dh0=np.zeros((b, H, N, P)))
+    starts = list(range(0, L, chunk))
+    for bi in range(b):
+        for h in range(H):
+            g = h // R
+            raw = dt[bi, :, h]
+            delta = softplus(raw) if dt_softplus else raw.copy()
+            ell = delta * A[h]
+            # forward: the state entering every chunk
+            hin = []
+            Hs = np.zeros((N, P)) if h0 is None else np.asarray(h0, np.float64)[bi, h].copy()
+            for t0 in starts:
+                sl = slice(t0, min(t0 + chunk, L))
+                cs = np.cumsum(ell[sl])
+                hin.append(Hs.copy())
+                w = np.exp(cs[-1] - cs) * delta[sl]
+                Hs = np.exp(cs[-1]) * Hs + B[bi, sl, g].T @ (w[:, None] * x[bi, sl, h])
+            # backward over chunks
+            Gout = np.zeros((N, P)) if dhfinal is None else np.asarray(dhfinal, np.float64)[bi, h].copy()
+            for c in range(len(starts) - 1, -1, -1):
+                t0 = starts[c]
+                sl = slice(t0, min(t0 + chunk, L))
+                Xc, dYc, Bc, Cc, dl = x[bi, sl, h], dy[bi, sl, h], B[bi, sl, g], C[bi, sl, g], delta[sl]
+                cs = np.cumsum(ell[sl])
+                Hin = hin[c]
+                Ecaus = np.exp(cs[:, None] - cs[None, :])           # [u, s] = exp(cs_u - cs_s)
+                mask = np.tril(np.ones((len(cs), len(cs)), bool))     # s <= u
+                Ecaus = np.where(mask, Ecaus, 0.0)
+                Gm = Cc @ Bc.T                                        # [u, s] = C_u·B_s
+                M = Gm * Ecaus * dl[None, :]                          # forward intra-chunk matrix
+                K = Xc @ dYc.T                                        # [s, u] = x_s·dy_u
+                einter = np.exp(cs[-1] - cs)                          # exp(cs_end - cs_s)
+                dxr_inter = einter[:, None] * (Bc @ Gout)
+                dxr = (Gm * Ecaus).T @ dYc + dxr_inter
+                out["dx"][bi, sl, h] = dl[:, None] * dxr + (0.0 if D is None else D[h]) * dYc
+                dBc = (dl[:, None] * (K * Ecaus.T)) @ Cc + (dl * einter)[:, None] * (Xc @ Gout.T)
+                dC_off = np.exp(cs)[:, None] * (dYc @ Hin.T)
+                dCc = (K.T * Ecaus * dl[None, :]) @ Bc + dC_off
+                out["dB"][bi, sl, g] += dBc
+                out["dC"][bi, sl, g] += dCc
+                # decays
+                Z = M * K.T                                           # [u, s]
+                q = dl * einter * np.sum(Xc * (Bc @ Gout), axis=1)
+                dcs = Z.sum(axis=1) - Z.sum(axis=0) + np.sum(Cc * dC_off, axis=1) - q
+                dcs[-1] += np.exp(cs[-1]) * np.sum(Gout * Hin) + q.sum()
+                dell = np.cumsum(dcs[::-1])[::-1]
+                ddelta = A[h] * dell + np.sum(Xc * dxr, axis=1)
+                out["ddt"][bi, sl, h] = ddelta / (1.0 + np.exp(-raw[sl])) if dt_softplus else ddelta
+                out["dA"][h] += np.sum(dl * dell)
+                out["dD"][h] += np.sum(Xc * dYc)
+                Gout = np.exp(cs[-1]) * Gout + Cc.T @ (np.exp(cs)[:, None] * dYc)
+            out["dh0"][bi, h] = Gout
+    return out

@@ -111,6 +111,117 @@ void oracle_ssd_scan(int batch, int seqlen, int nheads, int headdim, int dstate,
 }
 
 /*
+ * Gradient of the SSD scan above (reverse-mode, the chain rule taken one time
+ * step at a time).  The forward states h_t of one (b, h) are kept, then the
+ * adjoint g = dL/dh_t runs backwards from g = dL/dh_final (or 0):
+ *     g      += C_t dy_tᵀ                      (y_t reads h_t)
+ *     dC_t   += h_tᵀ-contract dy_t = Σ_p h_t[n,p] dy_t[p]
+ *     dD     += x_t · dy_t;       dx_t = D·dy_t + Δ_t Σ_n B_t[n] g[n,:]
+ *     dB_t   += Δ_t Σ_p g[n,p] x_t[p]
+ *     dΔ_t    = Σ g[n,p] B_t[n] x_t[p]  +  A·a_t·Σ g[n,p] h_{t-1}[n,p]
+ *     dA     += Δ_t·a_t·Σ g h_{t-1};     ddt_t = dΔ_t·σ(raw) when Δ = softplus(raw)
+ *     g       = a_t·g                          (h_t = a_t h_{t-1} + Δ_t B_t x_tᵀ)
+ * and dh0 = g after t = 0.  dB and dC are returned per head, [b][L][H][N]
+ * (the caller sums the heads of a group); dA, dD are [b][H] per batch row.
+ * dy [b][L][H][P]; dhfinal [b][H][N][P] or NULL; every output is written.
+ */
+void oracle_ssd_scan_bwd(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
+                         int dt_softplus, const double *x, const double *dt, const double *A,
+                         const double *B, const double *C, const double *D, const double *h0,
+                         const double *dy, const double *dhfinal, double *dx, double *ddt,
+                         double *dA, double *dB_head, double *dC_head, double *dD, double *dh0)
+{
+    const int P = headdim, N = dstate, H = nheads, G = ngroups, L = seqlen;
+    const int R = H / G;
+    const size_t NP = (size_t)N * P;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int b = 0; b < batch; ++b) {
+        for (int h = 0; h < H; ++h) {
+            const int g = h / R;
+            const size_t soff = ((size_t)b * H + h) * NP;
+            /* hs[t+1] = state after token t; hs[0] = state before the sequence */
+            double *hs = (double *)malloc(sizeof(double) * NP * (size_t)(L + 1));
+            double *adj = (double *)malloc(sizeof(double) * NP);
+            if (h0)
+                memcpy(hs, h0 + soff, sizeof(double) * NP);
+            else
+                memset(hs, 0, sizeof(double) * NP);
+            for (int t = 0; t < L; ++t) {
+                const size_t row = (size_t)b * L + t;
+                const double *xt = x + (row * H + h) * P;
+                const double *Bt = B + (row * G + g) * N;
+                const double raw = dt[row * H + h];
+                const double delta = dt_softplus ? softplus(raw) : raw;
+                const double a = exp(delta * A[h]);
+                const double *prev = hs + (size_t)t * NP;
+                double *cur = hs + (size_t)(t + 1) * NP;
+                for (int n = 0; n < N; ++n)
+                    for (int p = 0; p < P; ++p)
+                        cur[(size_t)n * P + p] = a * prev[(size_t)n * P + p] + delta * Bt[n] * xt[p];
+            }
+            if (dhfinal)
+                memcpy(adj, dhfinal + soff, sizeof(double) * NP);
+            else
+                memset(adj, 0, sizeof(double) * NP);
+            double dA_acc = 0.0, dD_acc = 0.0;
+            const double Dh = D ? D[h] : 0.0;
+            for (int t = L - 1; t >= 0; --t) {
+                const size_t row = (size_t)b * L + t;
+                const double *xt = x + (row * H + h) * P;
+                const double *dyt = dy + (row * H + h) * P;
+                const double *Bt = B + (row * G + g) * N;
+                const double *Ct = C + (row * G + g) * N;
+                const double raw = dt[row * H + h];
+                const double delta = dt_softplus ? softplus(raw) : raw;
+                const double a = exp(delta * A[h]);
+                const double *ht = hs + (size_t)(t + 1) * NP;
+                const double *hprev = hs + (size_t)t * NP;
+                double *dxt = dx + (row * H + h) * P;
+                double *dBt = dB_head + (row * H + h) * N;
+                double *dCt = dC_head + (row * H + h) * N;
+                /* output read: y_t = h_tᵀ C_t + D x_t */
+                for (int n = 0; n < N; ++n) {
+                    double s = 0.0;
+                    for (int p = 0; p < P; ++p) {
+                        adj[(size_t)n * P + p] += Ct[n] * dyt[p];
+                        s += ht[(size_t)n * P + p] * dyt[p];
+                    }
+                    dCt[n] = s;
+                }
+                for (int p = 0; p < P; ++p) {
+                    dD_acc += xt[p] * dyt[p];
+                    dxt[p] = Dh * dyt[p];
+                }
+                /* state update: h_t = a h_{t-1} + Δ B_t x_tᵀ */
+                double gin = 0.0, gprev = 0.0;
+                for (int n = 0; n < N; ++n) {
+                    double sb = 0.0;
+                    for (int p = 0; p < P; ++p) {
+                        const double gv = adj[(size_t)n * P + p];
+                        dxt[p] += delta * Bt[n] * gv;
+                        sb += gv * xt[p];
+                        gprev += gv * hprev[(size_t)n * P + p];
+                    }
+                    dBt[n] = delta * sb;
+                    gin += Bt[n] * sb;
+                }
+                const double ddelta = gin + A[h] * a * gprev;
+                dA_acc += delta * a * gprev;
+                ddt[row * H + h] = dt_softplus ? ddelta / (1.0 + exp(-raw)) : ddelta;
+                for (size_t i = 0; i < NP; ++i)
+                    adj[i] *= a;
+            }
+            dA[(size_t)b * H + h] = dA_acc;
+            dD[(size_t)b * H + h] = dD_acc;
+            if (dh0)
+                memcpy(dh0 + soff, adj, sizeof(double) * NP);
+            free(adj);
+            free(hs);
+        }
+    }
+}
+
+/*
  * One decode step against a cached state ([INF] Abstract: the state cache
  * carried from prefill into decode; the update is the same single step of
  * [TP] §2.1 as above).  state [b][H][N][P] is read and overwritten;

@@ -448,3 +448,98 @@ def test_rmsnorm_scale_invariance_groups_and_gate():
                                oracle.gated_rmsnorm(y, None, w, 4, 0.0), rtol=1e-13)
     # a closed gate (z = 0) gives zeros
     assert np.all(oracle.gated_rmsnorm(y, np.zeros_like(y), w, 4, 1e-5) == 0.0)
+
+
+# ------------------------------------------------------------------ backward
+# The gradient of the scan (the chunked backward of page "5.3 텐서 병렬화(Tensor
+# Parallelism) 지원과 대규모 클러스터 학습", §3.2 decomposition differentiated) is
+# pinned to central finite differences of the sequential forward, to the
+# hand-derived block form, and to a closed form at A = 0.
+
+GRAD_KEYS = {"x": "dx", "dt": "ddt", "A": "dA", "B": "dB", "C": "dC", "D": "dD", "h0": "dh0"}
+
+
+def _bwd_case(seed, b, L, H, P, N, G, softplus=True):
+    rng = np.random.default_rng(seed)
+    x, dt, A, B, C, D, h0 = rand_ssd(rng, b, L, H, P, N, G, dt_scale=0.5)
+    if not softplus:
+        dt = rng.uniform(0.01, 0.6, dt.shape)
+    dy = rng.standard_normal(x.shape)
+    dhf = rng.standard_normal((b, H, N, P))
+    return dict(x=x, dt=dt, A=A, B=B, C=C, D=D, h0=h0), dy, dhf
+
+
+@pytest.mark.parametrize("softplus", [True, False])
+@pytest.mark.parametrize("shape", [(1, 6, 2, 3, 4, 1), (2, 5, 4, 2, 3, 2)])
+def test_pin13_backward_equals_finite_differences(shape, softplus):
+    """Every gradient against central differences of the loss Σ dy·y + Σ dhf·h_final."""
+    args, dy, dhf = _bwd_case(31, *shape, softplus=softplus)
+
+    def loss(**kw):
+        a = dict(args, **kw)
+        y, hf = oracle.ssd_scan(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["h0"],
+                                dt_softplus=softplus, return_final_state=True)
+        return float(np.sum(y * dy) + np.sum(hf * dhf))
+
+    g = oracle.ssd_scan_bwd(args["x"], args["dt"], args["A"], args["B"], args["C"], dy, args["D"],
+                            args["h0"], dhf, dt_softplus=softplus)
+    eps = 1e-6
+    for k, v in args.items():
+        fd = np.zeros_like(v)
+        for i in np.ndindex(v.shape):
+            vp, vm = v.copy(), v.copy()
+            vp[i] += eps
+            vm[i] -= eps
+            fd[i] = (loss(**{k: vp}) - loss(**{k: vm})) / (2 * eps)
+        assert rel_err(g[GRAD_KEYS[k]], fd) < 1e-6, k
+
+
+@pytest.mark.parametrize("Q", [1, 3, 16, 64, 97])
+def test_pin14_backward_block_form_equals_adjoint(Q):
+    """The hand-derived chunk form (what the GPU computes) = the sequential adjoint,
+    with G > 1, a ragged last chunk, D, h0 and a final-state gradient."""
+    args, dy, dhf = _bwd_case(32, 2, 150, 4, 5, 6, 2)
+    ref = oracle.ssd_scan_bwd(args["x"], args["dt"], args["A"], args["B"], args["C"], dy, args["D"],
+                              args["h0"], dhf)
+    got = forms.ssd_chunked_bwd(args["x"], args["dt"], args["A"], args["B"], args["C"], dy, args["D"],
+                                args["h0"], dhf, chunk=Q)
+    for k in ref:
+        assert rel_err(got[k], ref[k]) < 1e-11, k
+
+
+def test_backward_zero_decay_closed_form():
+    """A = 0: y = tril(C Bᵀ)(Δ x) + C h0 + D x, so dx = Δ·(tril(C Bᵀ)ᵀ dy) + D dy,
+    dD = Σ x·dy and dh0 = Σ_t C_t dy_tᵀ, with library products only."""
+    args, dy, _ = _bwd_case(33, 1, 20, 2, 3, 4, 1, softplus=False)
+    args["A"] = np.zeros(2)
+    g = oracle.ssd_scan_bwd(args["x"], args["dt"], args["A"], args["B"], args["C"], dy, args["D"],
+                            args["h0"], None, dt_softplus=False)
+    Bm, Cm = args["B"][0, :, 0], args["C"][0, :, 0]
+    T = np.tril(Cm @ Bm.T)
+    for h in range(2):
+        dlt = args["dt"][0, :, h]
+        dx = dlt[:, None] * (T.T @ dy[0, :, h]) + args["D"][h] * dy[0, :, h]
+        np.testing.assert_allclose(g["dx"][0, :, h], dx, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(g["dD"][h], np.sum(args["x"][0, :, h] * dy[0, :, h]), rtol=1e-12)
+        np.testing.assert_allclose(g["dh0"][0, h], Cm.T @ dy[0, :, h], rtol=1e-12, atol=1e-12)
+
+
+def test_backward_directional_derivative_medium():
+    """At a size where full differences are too slow: the derivative along a
+    random direction of all inputs equals the gradients' inner product with it."""
+    args, dy, dhf = _bwd_case(34, 1, 300, 3, 8, 16, 1)
+    g = oracle.ssd_scan_bwd(args["x"], args["dt"], args["A"], args["B"], args["C"], dy, args["D"],
+                            args["h0"], dhf)
+    rng = np.random.default_rng(35)
+    dirs = {k: rng.standard_normal(v.shape) for k, v in args.items()}
+
+    def loss(s):
+        a = {k: v + s * dirs[k] for k, v in args.items()}
+        y, hf = oracle.ssd_scan(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["h0"],
+                                return_final_state=True)
+        return float(np.sum(y * dy) + np.sum(hf * dhf))
+
+    eps = 1e-5
+    fd = (loss(eps) - loss(-eps)) / (2 * eps)
+    an = sum(float(np.sum(g[GRAD_KEYS[k]] * dirs[k])) for k in args)
+    assert abs(fd - an) <= 1e-6 * max(abs(an), 1.0)
