@@ -120,6 +120,42 @@ int ssd_chunk_scan_workspace_layout(int batch, int seqlen, int nheads, int headd
                                     size_t *off_cs, size_t *off_hprev);
 
 /* ------------------------------------------------------------------------
+ * Gradient of the chunked SSD prefill: the block decomposition of [TP] §3.2
+ * (scalar decay of §3.1) differentiated chunk by chunk, for training at the
+ * scales the page describes.  For the loss L with dL/dy = dy and
+ * dL/d(final state) = dfinal_state (NULL = 0), every gradient of
+ * ssd_chunk_scan_fwd's inputs is written:
+ *
+ *   dx    [batch][seqlen][nheads][headdim]   dtype  dL/dx
+ *   ddt   [batch][seqlen][nheads]            dtype  dL/d(raw dt) (through the
+ *                                                   softplus when dt_softplus)
+ *   dA    [nheads] float                            dL/dA (summed over batch)
+ *   dB,dC [batch][seqlen][ngroups][dstate]   dtype  summed over a group's heads
+ *   dD    [nheads] float or NULL                    dL/dD = Σ x·dy
+ *   dinitial_state [batch][nheads][dstate][headdim] float or NULL
+ *
+ * Inputs are those of the forward (x, dt, A, B, C, D, initial_state) plus
+ * dy [batch][seqlen][nheads][headdim] dtype.  The forward is recomputed: the
+ * call stores the state entering every 64-token chunk and the adjoint of the
+ * state leaving it in the workspace (2 · batch · nheads · ceil(seqlen/64) ·
+ * dstate · headdim floats, plus small partial sums), sized by
+ * ssd_chunk_scan_bwd_workspace_size (0 = unsupported), 256-byte aligned.
+ * dA and dD are reduced in a fixed order, so results are deterministic.
+ *
+ * Supported: dtype SSD_BF16 only; headdim == 64; dstate in {64, 128}; ngroups
+ * dividing nheads.  seqlen == 0 or batch == 0: dA = dD = 0 and
+ * dinitial_state = dfinal_state (or 0), no workspace needed.
+ * ------------------------------------------------------------------------ */
+size_t ssd_chunk_scan_bwd_workspace_size(int batch, int seqlen, int nheads, int headdim, int dstate,
+                                         int ngroups, int dtype);
+int ssd_chunk_scan_bwd(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
+                       int dtype, int dt_softplus, const void *x, const void *dt, const float *A,
+                       const void *B, const void *C, const float *D, const float *initial_state,
+                       const void *dy, const float *dfinal_state, void *dx, void *ddt, float *dA,
+                       void *dB, void *dC, float *dD, float *dinitial_state, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * Packed variable-length prefill ([TP] §4.3: sequences of different lengths
  * packed back to back without padding; the recurrence restarts at every
  * sequence start).  Sequence s occupies rows cu_seqlens[s] .. cu_seqlens[s+1]-1

@@ -60,6 +60,10 @@ def lib() -> ctypes.CDLL:
     L.ssd_chunk_scan_workspace_layout.restype = i
     L.ssd_chunk_scan_fwd.argtypes = [i] * 9 + [vp] * 10 + [sz, vp]
     L.ssd_chunk_scan_fwd.restype = i
+    L.ssd_chunk_scan_bwd_workspace_size.argtypes = [i] * 7
+    L.ssd_chunk_scan_bwd_workspace_size.restype = sz
+    L.ssd_chunk_scan_bwd.argtypes = [i] * 8 + [vp] * 17 + [sz, vp]
+    L.ssd_chunk_scan_bwd.restype = i
     L.ssd_chunk_scan_varlen_fwd.argtypes = [i] * 8 + [vp] * 11
     L.ssd_chunk_scan_varlen_fwd.restype = i
     L.ssd_causal_conv1d_fwd.argtypes = [i] * 6 + [vp] * 7
@@ -185,6 +189,52 @@ def ssd_chunk_scan(x, dt, A, B, C, D=None, *, chunk, initial_state=None,
         _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(initial_state),
         _ptr(y), _ptr(fs), _ptr(workspace), workspace.numel(), _stream(dev)))
     return (y, fs) if return_final_state else y
+
+
+def ssd_chunk_scan_bwd(x, dt, A, B, C, dy, D=None, *, initial_state=None, dfinal_state=None,
+                       dt_softplus=True, want_dD=True, want_dinitial_state=True, workspace=None):
+    """Gradients of ssd_chunk_scan (bf16 inputs) for dL/dy = dy and
+    dL/d(final state) = dfinal_state (None = 0).  Returns a dict with dx, ddt,
+    dB, dC (dtype of x), dA [H] fp32, and dD [H], dinitial_state [b,H,N,P] fp32
+    (None when not wanted)."""
+    torch = _torch()
+    x = _req(x, "x")
+    dev = x.device
+    code = _dtype_code(x)
+    b, L, H, P = x.shape
+    for t, n in ((dt, "dt"), (B, "B"), (C, "C"), (dy, "dy")):
+        _req(t, n, x.dtype, dev)
+    _req(A, "A", torch.float32, dev)
+    _req(D, "D", torch.float32, dev)
+    _req(initial_state, "initial_state", torch.float32, dev)
+    _req(dfinal_state, "dfinal_state", torch.float32, dev)
+    G, N = B.shape[2], B.shape[3]
+    if tuple(dt.shape) != (b, L, H) or tuple(B.shape) != (b, L, G, N) or C.shape != B.shape:
+        raise ValueError("shape mismatch among x, dt, B, C")
+    if dy.shape != x.shape:
+        raise ValueError("dy must have the shape of x")
+    if tuple(A.shape) != (H,) or (D is not None and tuple(D.shape) != (H,)):
+        raise ValueError("A and D must have shape [nheads]")
+    for t, n in ((initial_state, "initial_state"), (dfinal_state, "dfinal_state")):
+        if t is not None and tuple(t.shape) != (b, H, N, P):
+            raise ValueError(f"{n} must be [batch, nheads, dstate, headdim]")
+    out = dict(dx=torch.empty_like(x), ddt=torch.empty_like(dt), dB=torch.empty_like(B),
+               dC=torch.empty_like(C), dA=torch.empty(H, dtype=torch.float32, device=dev),
+               dD=torch.empty(H, dtype=torch.float32, device=dev) if want_dD else None,
+               dinitial_state=torch.empty((b, H, N, P), dtype=torch.float32, device=dev)
+               if want_dinitial_state else None)
+    need = lib().ssd_chunk_scan_bwd_workspace_size(b, L, H, P, N, G, code)
+    if need == 0:
+        raise SSDError(-3, "unsupported backward configuration (bf16, headdim 64, dstate 64 or 128)")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    check(lib().ssd_chunk_scan_bwd(
+        b, L, H, P, N, G, code, int(bool(dt_softplus)),
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(initial_state), _ptr(dy),
+        _ptr(dfinal_state), _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA"]), _ptr(out["dB"]),
+        _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dinitial_state"]), _ptr(workspace),
+        workspace.numel(), _stream(dev)))
+    return out
 
 
 def ssd_chunk_scan_varlen(x, dt, A, B, C, D=None, *, cu_seqlens, initial_states=None,

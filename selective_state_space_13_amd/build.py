@@ -23,6 +23,7 @@ SOURCES = [
     "dt_cumsum.hip",
     "ssd_valu.hip",
     "ssd_fused.hip",
+    "ssd_bwd.hip",
     "conv_norm.hip",
     "decode.hip",
     "selective_scan.hip",

@@ -299,6 +299,90 @@ int ssd_chunk_scan_fwd(int batch, int seqlen, int nheads, int headdim, int dstat
     return SSD_OK;
 }
 
+size_t ssd_chunk_scan_bwd_workspace_size(int batch, int seqlen, int nheads, int headdim, int dstate,
+                                         int ngroups, int dtype) {
+    if (dtype != SSD_BF16) return 0;
+    if (check_scan_sizes(batch, seqlen, nheads, headdim, dstate, ngroups, 64, dtype)) return 0;
+    uint64_t states;
+    const int K = (seqlen + 63) / 64;
+    if (!prod(states, {batch, nheads, K, dstate, headdim, 4})) return 0;
+    const ssd::BwdPlan pl = ssd::bwd_plan(batch, seqlen, nheads, dstate);
+    return pl.ws_bytes > 256 ? pl.ws_bytes : 256;
+}
+
+int ssd_chunk_scan_bwd(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
+                       int dtype, int dt_softplus, const void *x, const void *dt, const float *A,
+                       const void *B, const void *C, const float *D, const float *initial_state,
+                       const void *dy, const float *dfinal_state, void *dx, void *ddt, float *dA,
+                       void *dB, void *dC, float *dD, float *dinitial_state, void *workspace,
+                       size_t workspace_bytes, void *stream_) {
+    int st = check_scan_sizes(batch, seqlen, nheads, headdim, dstate, ngroups, 64, dtype);
+    if (st) return st;
+    if (dtype != SSD_BF16)
+        return fail(SSD_ERR_UNSUPPORTED, "the backward runs on the matrix cores: bf16 inputs only");
+    const size_t need = ssd_chunk_scan_bwd_workspace_size(batch, seqlen, nheads, headdim, dstate,
+                                                          ngroups, dtype);
+    if (need == 0) return fail(SSD_ERR_SHAPE, "workspace size overflows");
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    const int es = elem_size(dtype);
+    uint64_t n_x, n_dt, n_bc, n_state;
+    prod(n_x, {batch, seqlen, nheads, headdim});
+    prod(n_dt, {batch, seqlen, nheads});
+    prod(n_bc, {batch, seqlen, ngroups, dstate});
+    prod(n_state, {batch, nheads, dstate, headdim});
+    if (!dA) return fail(SSD_ERR_NULL, "dA is required");
+    const void *ptrs[] = {x, dt, A, B, C, D, initial_state, dy, dfinal_state, dx, ddt, dA, dB, dC, dD,
+                          dinitial_state};
+    for (const void *p : ptrs)
+        if (p && !aligned(p, 16)) return fail(SSD_ERR_ALIGN, "tensor pointer %p is not 16-byte aligned", p);
+    LaunchMarks marks(stream);
+    hipError_t e;
+    if (batch == 0 || seqlen == 0) {
+        // no tokens: dA = dD = 0 and the initial state's gradient is the final state's
+        st = check_alias({span("dA", dA, (uint64_t)nheads * 4), span("dD", dD, dD ? (uint64_t)nheads * 4 : 0),
+                          span("dinitial_state", dinitial_state, dinitial_state ? n_state * 4 : 0)},
+                         {span("dfinal_state", dfinal_state, dfinal_state ? n_state * 4 : 0)});
+        if (st) return st;
+        marks.before();
+        e = ssd::launch_copy_state(nullptr, dA, (size_t)nheads, stream);
+        if (e == hipSuccess && dD) e = ssd::launch_copy_state(nullptr, dD, (size_t)nheads, stream);
+        if (e == hipSuccess && dinitial_state)
+            e = ssd::launch_copy_state(dfinal_state, dinitial_state, n_state, stream);
+        marks.after();
+        return e == hipSuccess ? SSD_OK : hip_fail(e, "empty-sequence gradients");
+    }
+    if (!x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dB || !dC)
+        return fail(SSD_ERR_NULL, "x, dt, A, B, C, dy, dx, ddt, dA, dB and dC are required");
+    if (!workspace || workspace_bytes < need)
+        return fail(SSD_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need,
+                    workspace_bytes, workspace ? "" : " (NULL)");
+    if (!aligned(workspace, 256)) return fail(SSD_ERR_ALIGN, "workspace must be 256-byte aligned");
+    st = check_alias(
+        {span("dx", dx, n_x * es), span("ddt", ddt, n_dt * es), span("dA", dA, (uint64_t)nheads * 4),
+         span("dB", dB, n_bc * es), span("dC", dC, n_bc * es),
+         span("dD", dD, dD ? (uint64_t)nheads * 4 : 0),
+         span("dinitial_state", dinitial_state, dinitial_state ? n_state * 4 : 0),
+         span("workspace", workspace, need)},
+        {span("x", x, n_x * es), span("dt", dt, n_dt * es), span("A", A, (uint64_t)nheads * 4),
+         span("B", B, n_bc * es), span("C", C, n_bc * es), span("D", D, D ? (uint64_t)nheads * 4 : 0),
+         span("initial_state", initial_state, initial_state ? n_state * 4 : 0),
+         span("dy", dy, n_x * es), span("dfinal_state", dfinal_state, dfinal_state ? n_state * 4 : 0)});
+    if (st) return st;
+    const ssd::BwdPlan pl = ssd::bwd_plan(batch, seqlen, nheads, dstate);
+    static const char *what[6] = {"segment state launch", "segment combine launch",
+                                  "chunk state launch", "adjoint walk launch",
+                                  "chunk gradient launch", "dA/dD reduction launch"};
+    for (int phase = pl.fwd.nseg > 1 ? 0 : 2; phase < 6; ++phase) {
+        marks.before();
+        e = ssd::launch_ssd_bwd(phase, pl, x, dt, A, B, C, D, initial_state, dy, dfinal_state,
+                                dt_softplus, batch, seqlen, nheads, headdim, dstate, ngroups, dx, ddt,
+                                dA, dB, dC, dD, dinitial_state, workspace, stream);
+        marks.after();
+        if (e != hipSuccess) return hip_fail(e, what[phase]);
+    }
+    return SSD_OK;
+}
+
 int ssd_chunk_scan_varlen_fwd(int nseq, int total_tokens, int nheads, int headdim, int dstate,
                               int ngroups, int dtype, int dt_softplus, const int *cu_seqlens,
                               const void *x, const void *dt, const float *A, const void *B,

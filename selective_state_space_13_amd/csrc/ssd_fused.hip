@@ -38,91 +38,16 @@
 // x, B, C are exact bf16 and enter unsplit.  cs is summed in float64 so that
 // exp of a difference of nearby cs values keeps float32 accuracy.  A_h <= 0
 // is assumed (cs non-increasing within a chunk).
-#include "ssd_kernels.h"
+#include "mfma_tile.h"
 
 namespace ssd {
 namespace {
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef short v8i16 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 constexpr int P = 64;            // headdim
 constexpr int kC = 64;           // tokens per internal chunk
 constexpr int kThreads = 512;    // 8 waves
 constexpr int kSt = 36;          // row pitch (floats) of the 32x32 output staging tiles
 constexpr float kMaxBlockDecay = 60.0f;  // above this, a diagonal block uses the exact mask
-
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ v4i16 tr4(const uint16_t *p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p));
-}
-__device__ __forceinline__ bf16x8 cat8(v4i16 a, v4i16 b) {
-    v8i16 r = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8, r);
-}
-__device__ __forceinline__ bf16x8 as8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
-__device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
-
-// v = head + tail, head = bf16(v), tail = bf16(v - head)
-__device__ __forceinline__ void split8(const float *v, bf16x8 &head, bf16x8 &tail) {
-    uint32_t hw[4], tw[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        hw[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
-        tw[e] = pack_bf16x2(v[2 * e] - bf16lo(hw[e]), v[2 * e + 1] - bf16hi(hw[e]));
-    }
-    head = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-    tail = __builtin_bit_cast(bf16x8, make_uint4(tw[0], tw[1], tw[2], tw[3]));
-}
-
-// LDS tiles of W bf16 columns (W = 64 or 128), no padding.  The 16-byte chunk
-// index of a row is XORed with a row mask whose bits 1-2 are (row & 3) and
-// whose bits 0 and 3 are bits 2 and 3 of the row.  Then the 4 rows x 32 bytes
-// one 16-lane group reads with ds_read_b64_tr_b16 fall in distinct banks, and
-// so do the 16-byte reads of 16 (W = 128) or 8 (W = 64) consecutive rows at
-// one column, the pattern of the k-contiguous operand reads.
-template <int W>
-__device__ __forceinline__ int swz(int row, int col) {
-    int m = ((row & 3) << 1) | ((row >> 2) & 1);
-    if (W == 128) m |= ((row >> 3) & 1) << 3;
-    return row * W + ((((col >> 3) ^ m)) << 3) + (col & 7);
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave in float64, on DPP lane
-// moves (no LDS round trips): shifts by 1, 2, 4, 8 within each row of 16
-// lanes, then row 0's total into row 1 and row 2's into row 3, then lane 31's
-// running total into rows 2 and 3.  Lanes a move cannot reach add zero.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ double dpp_add(double v) {
-    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROW_MASK, 0xf, true);
-    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROW_MASK, 0xf, true);
-    return v + __hiloint2double(hi, lo);
-}
-__device__ __forceinline__ double wave_inclusive_scan(double v) {
-    v = dpp_add<0x111, 0xf>(v);  // row_shr:1
-    v = dpp_add<0x112, 0xf>(v);  // row_shr:2
-    v = dpp_add<0x114, 0xf>(v);  // row_shr:4
-    v = dpp_add<0x118, 0xf>(v);  // row_shr:8
-    v = dpp_add<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
-    v = dpp_add<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
-    return v;
-}
-__device__ __forceinline__ double read_lane(double v, int l) {
-    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
-                            __builtin_amdgcn_readlane(__double2loint(v), l));
-}
-
-// Lane geometry of ds_read_b64_tr_b16 for a 32x32x16 operand: source lane j
-// of a 16-lane group addresses row (j >> 2) & 3 of a 4-row slab and columns
-// 16·((j >> 4) & 1) + 4·(j & 3)..+3; each lane receives 4 consecutive rows of
-// column (lane & 31).
-__device__ __forceinline__ int tr_col(int lane) { return 16 * ((lane >> 4) & 1) + 4 * (lane & 3); }
-__device__ __forceinline__ int tr_row(int lane) { return (lane >> 2) & 3; }
 
 // Per-token values of one chunk (index = token), written by one wave.
 struct TokSmem {
@@ -170,6 +95,10 @@ struct FusedArgs {
     int nchunks;          // 64-token chunks over the sequence
     int seg_chunks;       // chunks per segment
     int nseg;             // S
+    // state-only pass: when set, the state entering every chunk c is stored at
+    // chunk_states[(b·H + h)·nchunks + c] ([N][P] float) and segment s >= 1
+    // starts from hin (the true incoming state) instead of zero
+    float *chunk_states;
 };
 
 // Inputs of one chunk, loaded into registers one chunk ahead of their use.
@@ -251,7 +180,7 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
         const float *src = nullptr;
         if (seg == 0) {
             if (a.h0) src = a.h0 + bh * N * P;
-        } else if (!STATE_ONLY) {
+        } else if (!STATE_ONLY || a.chunk_states) {
             src = a.hin + (bh * a.nseg + seg) * N * P;
         }
 #pragma unroll
@@ -358,6 +287,12 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 if (j >= nst) break;
+                if (STATE_ONLY && a.chunk_states) {
+                    float *cst = a.chunk_states + (bh * a.nchunks + c) * N * P + 32 * (j ? spt1 : spt0) + l32;
+#pragma unroll
+                    for (int rr = 0; rr < 16; ++rr)
+                        cst[(32 * snt + 8 * (rr >> 2) + 4 * lg + (rr & 3)) * P] = st[j][rr];
+                }
                 if constexpr (!STATE_ONLY) {
                     const int ow = j ? o_hw1 : o_hw0;
 #pragma unroll
@@ -498,8 +433,10 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
     // ---- end of the segment
     float *dst = nullptr;
     if (STATE_ONLY) {
-        dst = a.seg_state + (bh * a.nseg + seg) * N * P;
-        if (wave == kScanWave && lane == 0) a.seg_decay[bh * a.nseg + seg] = seg_decay;
+        if (!a.chunk_states) {
+            dst = a.seg_state + (bh * a.nseg + seg) * N * P;
+            if (wave == kScanWave && lane == 0) a.seg_decay[bh * a.nseg + seg] = seg_decay;
+        }
     } else if (a.final_state && seg == a.nseg - 1) {
         dst = a.final_state + bh * N * P;
     }
@@ -612,6 +549,42 @@ hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const
         else
             ssd_fused_kernel<64, false><<<items, kThreads, 0, stream>>>(a);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_ssd_chunk_states(int phase, const FusedPlan &pl, const void *x, const void *dt,
+                                  const float *A, const void *B, const float *h0, int dt_softplus,
+                                  int batch, int seqlen, int nheads, int headdim, int dstate,
+                                  int ngroups, float *chunk_states, void *workspace,
+                                  hipStream_t stream) {
+    if (headdim != P || (dstate != 64 && dstate != 128)) return hipErrorInvalidValue;
+    if ((long long)batch * nheads == 0 || seqlen == 0) return hipSuccess;
+    // phases 0 and 1 (segments only) are those of the forward; phase 2 is the
+    // state-only walk that stores every chunk's incoming state
+    if (phase != 2) {
+        return launch_ssd_fused(phase, pl, x, dt, A, B, nullptr, nullptr, h0, dt_softplus, batch, seqlen,
+                                nheads, headdim, dstate, ngroups, nullptr, nullptr, workspace, stream);
+    }
+    FusedArgs a{};
+    a.x = static_cast<const uint16_t *>(x);
+    a.dt = static_cast<const uint16_t *>(dt);
+    a.B = static_cast<const uint16_t *>(B);
+    a.A = A;
+    a.h0 = h0;
+    a.seqlen = seqlen;
+    a.nheads = nheads;
+    a.ngroups = ngroups;
+    a.dt_softplus = dt_softplus;
+    a.nchunks = pl.nchunks;
+    a.nseg = pl.nseg;
+    a.seg_chunks = pl.seg_chunks;
+    a.chunk_states = chunk_states;
+    if (pl.nseg > 1) a.hin = reinterpret_cast<const float *>(static_cast<char *>(workspace) + pl.state_bytes);
+    const unsigned items = (unsigned)((long long)batch * nheads * pl.nseg);
+    if (dstate == 128)
+        ssd_fused_kernel<128, true><<<items, kThreads, 0, stream>>>(a);
+    else
+        ssd_fused_kernel<64, true><<<items, kThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -83,6 +83,31 @@ hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const
                             const float *h0, int dt_softplus, int batch, int seqlen, int nheads,
                             int headdim, int dstate, int ngroups, void *y, float *final_state,
                             void *workspace, hipStream_t stream);
+// State-only forward pass that stores the state entering every 64-token
+// chunk, [b][H][nchunks][N][P] float.  Phases 0 and 1 are the segment passes
+// of launch_ssd_fused (plan.nseg > 1 only); phase 2 is the storing walk.
+hipError_t launch_ssd_chunk_states(int phase, const FusedPlan &pl, const void *x, const void *dt,
+                                  const float *A, const void *B, const float *h0, int dt_softplus,
+                                  int batch, int seqlen, int nheads, int headdim, int dstate,
+                                  int ngroups, float *chunk_states, void *workspace,
+                                  hipStream_t stream);
+
+// Chunked backward (bf16).  Workspace: the forward plan's, then the chunk
+// states, the chunk adjoints and the per-(b, h, chunk) dA, dD partials.
+struct BwdPlan {
+    FusedPlan fwd;
+    size_t states_bytes = 0, part_bytes = 0, ws_bytes = 0;
+};
+BwdPlan bwd_plan(int batch, int seqlen, int nheads, int dstate);
+// phase 0..2: forward chunk states (0, 1 only when segmented); 3: adjoint walk;
+// 4: per-chunk gradients; 5: dA, dD reduction
+hipError_t launch_ssd_bwd(int phase, const BwdPlan &pl, const void *x, const void *dt, const float *A,
+                          const void *B, const void *C, const float *D, const float *h0,
+                          const void *dy, const float *dfinal, int dt_softplus, int batch, int seqlen,
+                          int nheads, int headdim, int dstate, int ngroups, void *dx, void *ddt,
+                          float *dA, void *dB, void *dC, float *dD, float *dh0, void *workspace,
+                          hipStream_t stream);
+
 // Packed variable-length batch: sequence s covers rows [cu_seqlens[s],
 // cu_seqlens[s+1]) of x [T][H][P], dt [T][H], B, C [T][G][N] and y; each
 // sequence starts from h0[s] (or 0) and writes final_state[s].  One fused pass

@@ -37,7 +37,8 @@ def test_header_declares_expected_entry_points():
     for n in ["ssd_chunk_scan_fwd", "ssd_decode_step", "selective_scan_fwd",
               "ssd_chunk_scan_workspace_size", "ssd_chunk_scan_workspace_layout",
               "selective_scan_workspace_size", "ssd_status_string", "ssd_last_error",
-              "ssd_version"]:
+              "ssd_version", "ssd_chunk_scan_bwd", "ssd_chunk_scan_bwd_workspace_size",
+              "ssd_chunk_scan_varlen_fwd", "ssd_causal_conv1d_fwd", "ssd_gated_rmsnorm_fwd"]:
         assert n in names
 
 
@@ -229,6 +230,54 @@ def test_varlen_null_align_alias(L):
     assert varlen_call(L, ptrs={"y": fake(1)}) == ALIAS
     assert varlen_call(L, ptrs={"fs": fake(10)}) == ALIAS  # final states over cu_seqlens
     assert varlen_call(L, nseq=0) == OK
+
+
+BWD_NAMES = "x dt A B C D h0 dy dfs dx ddt dA dB dC dD dh0".split()
+
+
+def bwd_call(L, b=2, Lq=300, H=8, P=64, N=128, G=2, dtype=BF16, ptrs=None, ws_bytes=None, ws=None):
+    p = {n: fake(i + 1) for i, n in enumerate(BWD_NAMES)}
+    if ptrs:
+        p.update(ptrs)
+    need = L.ssd_chunk_scan_bwd_workspace_size(b, Lq, H, P, N, G, dtype)
+    return L.ssd_chunk_scan_bwd(b, Lq, H, P, N, G, dtype, 1, *[p[n] for n in BWD_NAMES],
+                                ws if ws is not None else fake(20),
+                                need if ws_bytes is None else ws_bytes, None)
+
+
+def test_bwd_workspace_size(L):
+    b, Lq, H, N = 2, 300, 8, 128
+    need = L.ssd_chunk_scan_bwd_workspace_size(b, Lq, H, 64, N, 2, BF16)
+    states = b * H * 5 * N * 64 * 4          # 5 chunks of 64 tokens
+    assert 2 * states <= need <= 2 * states + 4096
+    assert L.ssd_chunk_scan_bwd_workspace_size(b, Lq, H, 64, N, 2, F32) == 0  # bf16 only
+    assert L.ssd_chunk_scan_bwd_workspace_size(b, Lq, H, 32, N, 2, BF16) == 0
+    assert L.ssd_chunk_scan_bwd_workspace_size(b, Lq, H, 64, 96, 2, BF16) == 0
+
+
+@pytest.mark.parametrize("kw,status", [(dict(b=-1), SHAPE), (dict(G=3), SHAPE), (dict(P=32), UNSUP),
+                                       (dict(N=96), UNSUP), (dict(dtype=F32), UNSUP)])
+def test_bwd_shape_errors(L, kw, status):
+    assert bwd_call(L, **kw) == status
+
+
+@pytest.mark.parametrize("name", ["x", "dt", "A", "B", "C", "dy", "dx", "ddt", "dA", "dB", "dC"])
+def test_bwd_null(L, name):
+    assert bwd_call(L, ptrs={name: None}) == NULL
+
+
+@pytest.mark.parametrize("name", ["dy", "dfs", "dx", "dD", "dh0"])
+def test_bwd_misaligned(L, name):
+    assert bwd_call(L, ptrs={name: fake(BWD_NAMES.index(name) + 1, 8)}) == ALIGN
+
+
+def test_bwd_workspace_and_alias(L):
+    assert bwd_call(L, ws_bytes=1000) == WS
+    assert bwd_call(L, ws=fake(20, 64)) == ALIGN
+    assert bwd_call(L, ptrs={"dx": fake(1)}) == ALIAS     # dx over x
+    assert bwd_call(L, ptrs={"dB": fake(5)}) == ALIAS     # dB over C
+    assert bwd_call(L, ptrs={"dh0": fake(9)}) == ALIAS    # dinitial_state over dfinal_state
+    assert bwd_call(L, ws=fake(10)) == ALIAS              # workspace over dx
 
 
 def conv_call(L, b=2, Lq=100, C=64, W=4, dtype=BF16, ptrs=None):

@@ -273,6 +273,74 @@ def test_prefill_segmented_deterministic():
     assert torch.equal(y1, y2) and torch.equal(f1, f2)
 
 
+# ------------------------------------------------------------------ backward
+
+BWD_CASES = [
+    # b, L, H, N, G, with_D, with_h0, with_dfinal
+    (2, 200, 4, 128, 2, True, True, True),     # 4 chunks, ragged tail of 8
+    (1, 64, 2, 128, 1, False, False, False),   # exactly one chunk, no optional inputs
+    (1, 1, 4, 64, 1, True, True, True),        # single token, dstate 64
+    (2, 300, 6, 64, 3, True, False, True),     # dstate 64, 3 groups
+    (1, 1024, 8, 128, 1, True, True, True),    # 16 chunks, long enough for forward segments
+    (3, 129, 10, 128, 2, False, True, False),  # 5 heads per group, tail of 1
+]
+
+
+def run_bwd(case, softplus=True, seed=0):
+    b, L, H, N, G, wD, wh, wf = case
+    d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=seed + L + H, config_id=130, with_h0=wh)
+    gr = gen.ssd_grad_inputs(b, L, H, 64, N, "bf16", seed=seed + L + H, config_id=130, with_dfinal=wf)
+    if not softplus:  # raw dt as Δ: keep it positive and in range
+        d["dt"] = gen.Tensor(gen.f32_to_bf16_bits(np.abs(d["dt"].f32()) * 0.05 + 0.01), "bf16")
+    dev = lambda k: to_dev(d[k]) if d[k] is not None else None
+    out = ssd.ssd_chunk_scan_bwd(dev("x"), dev("dt"), dev("A"), dev("B"), dev("C"), to_dev(gr["dy"]),
+                                 dev("D") if wD else None, initial_state=dev("h0") if wh else None,
+                                 dfinal_state=to_dev(gr["dfinal"]) if wf else None, dt_softplus=softplus)
+    torch.cuda.synchronize()
+    ref = oracle.ssd_scan_bwd(d["x"].f64(), d["dt"].f64(), d["A"].f64(), d["B"].f64(), d["C"].f64(),
+                              gr["dy"].f64(), d["D"].f64() if wD else None,
+                              d["h0"].f64() if wh else None, gr["dfinal"].f64() if wf else None,
+                              dt_softplus=softplus)
+    return out, ref
+
+
+def check_bwd(out, ref, what):
+    for k, rk, bf in (("dx", "dx", True), ("ddt", "ddt", True), ("dB", "dB", True), ("dC", "dC", True),
+                      ("dA", "dA", False), ("dD", "dD", False), ("dinitial_state", "dh0", False)):
+        assert_parity(to_f64(out[k]), ref[rk], TAU_BF16, bf, f"{what} {k}")
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "b{}L{}H{}N{}G{}D{}h{}f{}".format(
+    c[0], c[1], c[2], c[3], c[4], int(c[5]), int(c[6]), int(c[7])))
+def test_backward(case):
+    out, ref = run_bwd(case)
+    check_bwd(out, ref, f"bwd {case}")
+
+
+def test_backward_without_softplus():
+    out, ref = run_bwd((2, 150, 4, 128, 1, True, True, True), softplus=False)
+    check_bwd(out, ref, "bwd raw dt")
+
+
+def test_backward_deterministic():
+    a1, _ = run_bwd(BWD_CASES[0])
+    a2, _ = run_bwd(BWD_CASES[0])
+    for k in a1:
+        assert torch.equal(a1[k], a2[k]), k
+
+
+def test_backward_empty_sequence():
+    x = torch.empty((2, 0, 4, 64), dtype=torch.bfloat16, device="cuda")
+    dt = torch.empty((2, 0, 4), dtype=torch.bfloat16, device="cuda")
+    B = torch.empty((2, 0, 1, 128), dtype=torch.bfloat16, device="cuda")
+    A = torch.full((4,), -1.0, device="cuda")
+    dfs = torch.randn(2, 4, 128, 64, device="cuda")
+    out = ssd.ssd_chunk_scan_bwd(x, dt, A, B, B.clone(), x.clone(), dfinal_state=dfs)
+    torch.cuda.synchronize()
+    assert torch.equal(out["dinitial_state"], dfs)
+    assert torch.count_nonzero(out["dA"]) == 0 and torch.count_nonzero(out["dD"]) == 0
+
+
 # ---------------------------------------------- conv1d and gated RMSNorm
 
 CONV_CASES = [

@@ -17,7 +17,7 @@ from dataclasses import dataclass
 import numpy as np
 
 # tensor ids of the per-tensor streams
-_X, _DT, _A, _B, _C, _D, _H0, _Z = range(8)
+_X, _DT, _A, _B, _C, _D, _H0, _Z, _DY, _DHF = range(10)
 
 
 @dataclass
@@ -186,4 +186,15 @@ def rmsnorm_inputs(rows, channels, dtype, seed=0, config_id=0, gate=True):
         y=_store(_normal(_rng(seed, config_id, _X), (rows, channels), 2.0), dtype),
         z=_store(_normal(_rng(seed, config_id, _Z), (rows, channels)), dtype) if gate else None,
         weight=Tensor(1.0 + _normal(_rng(seed, config_id, _D), (channels,), 0.1), "f32"),
+    )
+
+
+def ssd_grad_inputs(batch, seqlen, nheads, headdim, dstate, dtype, seed=0, config_id=0,
+                    with_dfinal=True):
+    """Upstream gradients of one chunked-scan call: dy [b, L, H, P] (dtype),
+    N(0, 1), and dL/d(final state) [b, H, N, P] fp32, 0.1·N(0, 1) (or None)."""
+    return dict(
+        dy=_store(_normal(_rng(seed, config_id, _DY), (batch, seqlen, nheads, headdim)), dtype),
+        dfinal=_store(_normal(_rng(seed, config_id, _DHF), (batch, nheads, dstate, headdim), 0.1), "f32")
+        if with_dfinal else None,
     )
