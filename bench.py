@@ -15,7 +15,8 @@ decode step at batch 256 (state cache of a 2.7B-layer prefill), the 64K-token
 long-context prefill with eight groups, the Mamba-1 selective scan (batch 8,
 seqlen 4096, 5120 channels, dstate 16), and a packed variable-length prefill
 (8 sequences of mixed lengths, 16384 tokens), the causal conv1d (width 4 over
-5376 channels) and the gated RMSNorm (5120 channels) of the same layer; and the
+5376 channels) and the gated RMSNorm (5120 channels) of the same layer, the
+chunked backward at the prefill shape; and the
 CPU float64 oracle on the prefill workload (the `cpu_baseline`, timed on this
 host's cores).
 
@@ -278,6 +279,42 @@ def bench_varlen(steps, warmup):
     return dict(ms=ms, kernel_ms=per[0], tokens=T, bytes=nbytes)
 
 
+BWD_KERNELS = ["chunk_states", "adjoint_walk", "chunk_gradients", "dA_dD_reduce"]
+BWD_SEGMENTED = ["segment_states", "segment_combine"] + BWD_KERNELS
+
+
+def bench_backward(cfg, steps, warmup, seed=0):
+    """The chunked backward at the prefill workload's shape (dL/dy random, dL/dh_final = 0)."""
+    import torch
+    import selective_state_space_13_amd as ssd
+    from workloads import gen
+    log(f"[bench] backward {cfg['name']}: generating inputs")
+    d = gen.ssd_inputs(cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["headdim"], cfg["dstate"],
+                       cfg["ngroups"], cfg["dtype"], seed=seed, config_id=cfg["id"])
+    gr = gen.ssd_grad_inputs(cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["headdim"], cfg["dstate"],
+                             cfg["dtype"], seed=seed, config_id=cfg["id"], with_dfinal=False)
+    x, dt, B, C, A, D = (to_dev(d[k]) for k in ("x", "dt", "B", "C", "A", "D"))
+    dy = to_dev(gr["dy"])
+    del d, gr
+    b, L, H, P, N, G = (cfg[k] for k in ("batch", "seqlen", "nheads", "headdim", "dstate", "ngroups"))
+    ws = torch.empty(ssd.lib().ssd_chunk_scan_bwd_workspace_size(b, L, H, P, N, G, ssd.SSD_BF16),
+                     dtype=torch.uint8, device="cuda")
+    nchunks = (L + 63) // 64
+    # the plan cuts the forward state pass into segments exactly when the forward does
+    fwd_ws = ssd.chunk_scan_workspace_size(b, L, H, P, N, G, cfg["chunk"], ssd.SSD_BF16)
+    names = BWD_SEGMENTED if fwd_ws > 256 else BWD_KERNELS
+
+    def step():
+        ssd.ssd_chunk_scan_bwd(x, dt, A, B, C, dy, D, workspace=ws)
+
+    log(f"[bench] backward: timing {steps} steps after {warmup} warm-up")
+    ms, per = time_calls(step, len(names), steps, warmup)
+    alg = 3 * b * L * H * P * 2 + 2 * b * L * H * 2 + 4 * b * L * G * N * 2
+    states = 2 * b * H * nchunks * N * P * 4
+    return dict(ms=ms, per_kernel_ms=dict(zip(names, per)), tokens=b * L, alg_bytes=alg,
+                state_bytes=states)
+
+
 def bench_convnorm(steps, warmup):
     """The causal conv1d and the gated RMSNorm at the 2.7B-layer shape."""
     import torch
@@ -343,7 +380,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="decode,long,mamba1,varlen,convnorm",
+    ap.add_argument("--legs", default="decode,long,mamba1,varlen,convnorm,backward",
                     help="extra legs to time besides the prefill step (comma list or 'none')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -453,6 +490,16 @@ def main():
                            "tokens_per_s": round(vl["tokens"] / (vl["ms"] * 1e-3), 1),
                            "ms": round(vl["ms"], 5), "kernel_ms": round(vl["kernel_ms"], 5),
                            "hbm_frac": round(vl["bytes"] / t / HBM_PEAK, 4)}
+    if "backward" in legs:
+        bw = bench_backward(cfg, max(3, args.steps // 2), 2)
+        t = bw["ms"] * 1e-3
+        extra["backward"] = {
+            "workload": workload + " (dL/dy random; dx, ddt, dA, dB, dC, dD)",
+            "tokens_per_s": round(bw["tokens"] / t, 1), "ms": round(bw["ms"], 5),
+            "per_kernel_ms": {k: round(v, 5) for k, v in bw["per_kernel_ms"].items()},
+            "alg_bytes": bw["alg_bytes"], "state_bytes_written_and_read": bw["state_bytes"],
+            "hbm_frac_algorithmic": round(bw["alg_bytes"] / t / HBM_PEAK, 4),
+            "hbm_frac_with_states": round((bw["alg_bytes"] + 2 * bw["state_bytes"]) / t / HBM_PEAK, 4)}
     if "convnorm" in legs:
         cn = bench_convnorm(args.steps, args.warmup)
         for key, wl in (("conv", "conv1d_layer:b8L2048C5376W4"), ("norm", "gated_rmsnorm_layer:rows16384C5120G1")):

@@ -307,6 +307,27 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
     const int dst_ = wave >> 1, dpt = wave & 1; // dxr tile (waves 0-3)
     f32x16 dBacc = {}, dCacc = {};
 
+    // inputs of one head, loaded into registers a head ahead of their use
+    constexpr int GV = N * P / (4 * kThreads);  // float4 of G_out per thread
+    struct HeadRegs {
+        uint4 x, y;
+        float4 g[GV];
+        float dt;
+    } R0;
+    auto prefetch = [&](int h) {
+        const int srow = tid >> 3, scol = (tid & 7) * 8;
+        R0.x = ld16(a.x + (row0 + min(srow, lim)) * xstride + (size_t)h * P + scol);
+        R0.y = ld16(a.dy + (row0 + min(srow, lim)) * xstride + (size_t)h * P + scol);
+        const float4 *go = reinterpret_cast<const float4 *>(a.gst + (((size_t)b * a.nheads + h) * a.nchunks + c) * N * P);
+#pragma unroll
+        for (int k = 0; k < GV / 2; ++k) {  // 8 consecutive floats at (tid + k·512)·8, as staged
+            R0.g[2 * k] = go[(tid + k * kThreads) * 2];
+            R0.g[2 * k + 1] = go[(tid + k * kThreads) * 2 + 1];
+        }
+        R0.dt = __uint_as_float((uint32_t)a.dt[(row0 + min(lane, lim)) * a.nheads + h] << 16);
+    };
+    prefetch(g * R);
+
     for (int r = 0; r < R; ++r) {
         // lane-derived offsets are recomputed per head (an opaque copy of the
         // thread index), which keeps them out of the registers live across the loop
@@ -317,12 +338,11 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
         const int h = g * R + r;
         const size_t bh = (size_t)b * a.nheads + h;
         const size_t bhc = bh * a.nchunks + c;
-        // ================= staging of head h
+        // ================= staging of head h (from the registers loaded a head ahead)
         {
             const bool ok = srow <= lim;
-            const uint4 xv = ld16(a.x + (row0 + min(srow, lim)) * xstride + (size_t)h * P + scol);
-            uint4 yv = ld16(a.dy + (row0 + min(srow, lim)) * xstride + (size_t)h * P + scol);
-            if (!ok) yv = make_uint4(0, 0, 0, 0);
+            const uint4 xv = R0.x;
+            const uint4 yv = ok ? R0.y : make_uint4(0, 0, 0, 0);
             *reinterpret_cast<uint4 *>(&sm.xs[srow * PQ + scol]) = xv;
             *reinterpret_cast<uint4 *>(&sm.ys[srow * PQ + scol]) = yv;
             const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, yw[4] = {yv.x, yv.y, yv.z, yv.w};
@@ -335,13 +355,11 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
             if ((tdv & 7) == 0) sm.xdy[srow] = dot;
         }
         {
-            const float *go = a.gst + bhc * N * P;
 #pragma unroll
-            for (int k = 0; k < N * P / (8 * kThreads); ++k) {
+            for (int k = 0; k < GV / 2; ++k) {
                 const int idx = (tdv + k * kThreads) * 8;
                 const int n = idx / P, p = idx % P;
-                const float4 v0 = *reinterpret_cast<const float4 *>(go + idx);
-                const float4 v1 = *reinterpret_cast<const float4 *>(go + idx + 4);
+                const float4 v0 = R0.g[2 * k], v1 = R0.g[2 * k + 1];
                 const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
                 bf16x8 hi, lo;
                 split8(v, hi, lo);
@@ -351,7 +369,7 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
         }
         if (wave == 7) {
             const bool ok = lane <= lim;
-            const float raw = __uint_as_float((uint32_t)a.dt[(row0 + min(lane, lim)) * a.nheads + h] << 16);
+            const float raw = R0.dt;
             const float delta = ok ? (a.dt_softplus ? softplus_f32(raw) : raw) : 0.0f;
             const double cs = wave_inclusive_scan((double)(delta * a.A[h]));
             const double cs_end = read_lane(cs, 63);
@@ -362,6 +380,7 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
             sm.sg[lane] = a.dt_softplus ? 1.0f / (1.0f + __expf(-raw)) : 1.0f;
         }
         __syncthreads();
+        prefetch(g * R + min(r + 1, R - 1));  // next head (the last one again at the end)
 
         // ================= products that need no decayed blocks
         f32x16 inter = {};
