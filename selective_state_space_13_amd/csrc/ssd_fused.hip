@@ -48,6 +48,7 @@ constexpr int kC = 64;           // tokens per internal chunk
 constexpr int kThreads = 512;    // 8 waves
 constexpr int kSt = 36;          // row pitch (floats) of the 32x32 output staging tiles
 constexpr float kMaxBlockDecay = 60.0f;  // above this, a diagonal block uses the exact mask
+constexpr int kMaxRankedSeq = 256;       // packed batches up to this many sequences run longest first
 
 // Per-token values of one chunk (index = token), written by one wave.
 struct TokSmem {
@@ -131,17 +132,48 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
     const int l32 = lane & 31, lg = lane >> 5;
     const int rrow = tr_row(lane), rcol = tr_col(lane);
 
-    // work item: (b, g) varies fastest so that all heads of one B/C group run
-    // on the same XCD (workgroups are dealt to the 8 XCDs round robin)
     const int R = a.nheads / a.ngroups;
-    const int nbg = (int)(gridDim.x / (unsigned)(R * a.nseg));
-    int item = blockIdx.x;
-    const int bg = item % nbg;
-    item /= nbg;
-    const int r = item % R;
-    const int seg = item / R;
-    const int b = bg / a.ngroups, g = bg % a.ngroups;
-    const int h = g * R + r;
+    int b = 0, g = 0, h = 0, seg = 0;
+    bool ranked = false;
+    if constexpr (!STATE_ONLY) {
+      if (a.cu_seqlens && gridDim.x <= (unsigned)(kMaxRankedSeq * a.nheads)) {
+        // packed batch: the work items of the longest sequence first, all heads of a
+        // sequence together, so that long sequences never start in the last round
+        // of workgroups (list scheduling, longest first).  Ranks break ties by index.
+        const int nseq = (int)(gridDim.x / (unsigned)a.nheads);
+        int *len = reinterpret_cast<int *>(&sm.stage[0][0][0]);
+        int *order = len + kMaxRankedSeq;
+        for (int s = tid; s < nseq; s += kThreads) {
+            const int s0 = min(max(a.cu_seqlens[s], 0), a.total_tokens);
+            len[s] = min(max(a.cu_seqlens[s + 1], s0), a.total_tokens) - s0;
+        }
+        __syncthreads();
+        for (int s = tid; s < nseq; s += kThreads) {
+            const int ls = len[s];
+            int rank = 0;
+            for (int t = 0; t < nseq; ++t) rank += (len[t] > ls) || (len[t] == ls && t < s);
+            order[rank] = s;
+        }
+        __syncthreads();
+        b = order[blockIdx.x / a.nheads];
+        h = blockIdx.x % a.nheads;
+        g = h / R;
+        ranked = true;
+      }
+    }
+    if (!ranked) {
+        // work item: (b, g) varies fastest so that all heads of one B/C group run
+        // on the same XCD (workgroups are dealt to the 8 XCDs round robin)
+        const int nbg = (int)(gridDim.x / (unsigned)(R * a.nseg));
+        int item = blockIdx.x;
+        const int bg = item % nbg;
+        item /= nbg;
+        const int r = item % R;
+        seg = item / R;
+        b = bg / a.ngroups;
+        g = bg % a.ngroups;
+        h = g * R + r;
+    }
     // rows of this sequence: row0.. row0 + seqlen - 1 of the [rows][...] inputs
     size_t row0 = (size_t)b * a.seqlen;
     int seqlen = a.seqlen, nchunks = a.nchunks;

@@ -143,6 +143,9 @@ VARLEN_GPU_CASES = [
     ([300, 1, 64, 0, 257, 1000], 8, 128, 2, True, True),
     ([128, 129, 5], 6, 64, 3, False, False),
     ([2048, 513, 77, 1536], 4, 128, 1, True, False),
+    # up to 256 sequences run longest first, more in their own order: both, with ties
+    ([(7 * i) % 97 for i in range(256)], 2, 64, 1, True, True),
+    ([(5 * i) % 41 for i in range(300)], 2, 64, 1, False, True),
 ]
 
 
