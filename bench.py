@@ -47,6 +47,8 @@ METRIC = "SSD prefill tokens/s and decode tokens/s at 2.7B-layer shape; % MFMA/H
 # segment-state pass and the segment combine before it
 FUSED_KERNELS = ["ssd_fused"]
 SEGMENTED_KERNELS = ["segment_states", "segment_combine", "ssd_fused"]
+# when only the last round of (batch, head) pairs is cut in halves: the state at the cut first
+CUT_KERNELS = ["cut_states", "ssd_fused"]
 
 
 def log(*a):
@@ -136,7 +138,7 @@ def measured_traffic(kernel, workload, digest):
     return e.get("bytes_per_launch")
 
 
-def prefill_work(c):
+def prefill_work(c, cut_pairs=0):
     """Algorithmic bytes and flops of a prefill call (inputs read once, outputs
     written once; causal flops of the block decomposition at the workload's
     chunk size)."""
@@ -152,9 +154,13 @@ def prefill_work(c):
     total = dict(bytes=2 * x_bytes + 2 * bc_bytes + dt_bytes + final,
                  flops=units_h * (4 * Q * N * P + Q * (Q + 1) * P) + units_g * Q * (Q + 1) * N)
     # the fused kernel does all of it; the segment passes re-read x, B and dt
+    # a cut of the last round's pairs re-reads the first halves of those pairs
+    cut = cut_pairs / (b * H) * 0.5
     return {"ssd_fused": total, "total": total,
             "segment_states": dict(bytes=x_bytes + bc_bytes + dt_bytes, flops=units_h * 2 * Q * N * P),
-            "segment_combine": dict(bytes=0, flops=0)}
+            "segment_combine": dict(bytes=0, flops=0),
+            "cut_states": dict(bytes=int(cut * (x_bytes + dt_bytes) + 0.5 * bc_bytes),
+                               flops=int(cut * units_h * 2 * Q * N * P))}
 
 
 def bench_prefill(cfg, steps, warmup, seed=0):
@@ -173,7 +179,9 @@ def bench_prefill(cfg, steps, warmup, seed=0):
     y = torch.empty_like(x)
     fs = torch.empty(cfg["batch"], cfg["nheads"], cfg["dstate"], cfg["headdim"], device="cuda") \
         if cfg.get("final_state") else None
-    names = SEGMENTED_KERNELS if ws.numel() > 256 else FUSED_KERNELS
+    launches, _, cut_pairs = ssd.chunk_scan_plan(cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["headdim"],
+                                         cfg["dstate"], cfg["ngroups"], cfg["chunk"], code)
+    names = {3: SEGMENTED_KERNELS, 2: CUT_KERNELS}.get(launches, FUSED_KERNELS)
 
     def step():
         ssd.ssd_chunk_scan(x, dt, A, B, C, D, chunk=cfg["chunk"], workspace=ws, out=y,
@@ -183,7 +191,7 @@ def bench_prefill(cfg, steps, warmup, seed=0):
     ms, per = time_calls(step, len(names), steps, warmup)
     tokens = cfg["batch"] * cfg["seqlen"]
     return dict(ms=ms, per_kernel_ms=dict(zip(names, per)), tokens=tokens,
-                work=prefill_work(cfg), final_state=fs, y=y)
+                work=prefill_work(cfg, cut_pairs), final_state=fs, y=y)
 
 
 def roofline_entry(kernel, ms, work, workload, digest):
@@ -300,9 +308,9 @@ def bench_backward(cfg, steps, warmup, seed=0):
     ws = torch.empty(ssd.lib().ssd_chunk_scan_bwd_workspace_size(b, L, H, P, N, G, ssd.SSD_BF16),
                      dtype=torch.uint8, device="cuda")
     nchunks = (L + 63) // 64
-    # the plan cuts the forward state pass into segments exactly when the forward does
-    fwd_ws = ssd.chunk_scan_workspace_size(b, L, H, P, N, G, cfg["chunk"], ssd.SSD_BF16)
-    names = BWD_SEGMENTED if fwd_ws > 256 else BWD_KERNELS
+    # the forward state pass is cut into segments exactly when the forward's is
+    _, nseg, _ = ssd.chunk_scan_plan(b, L, H, P, N, G, cfg["chunk"], ssd.SSD_BF16)
+    names = BWD_SEGMENTED if nseg > 1 else BWD_KERNELS
 
     def step():
         ssd.ssd_chunk_scan_bwd(x, dt, A, B, C, dy, D, workspace=ws)

@@ -115,6 +115,17 @@ int ssd_chunk_scan_fwd(int batch, int seqlen, int nheads, int headdim, int dstat
  *   hprev  [batch][nchunks][nheads][dstate][headdim] float, the state entering each chunk
  * Returns SSD_OK, SSD_ERR_UNSUPPORTED for SSD_BF16 (whose stages stay on chip),
  * or the status ssd_chunk_scan_fwd would return for the sizes. */
+/* How ssd_chunk_scan_fwd will run a call of this shape (host query, no GPU
+ * work): *launches = kernel launches per call (bf16: 1 for the fused pass
+ * alone; 2 when the last round of (batch, head) pairs is cut in halves, after
+ * a state pass that computes the state at the cut; 3 when every sequence is
+ * cut into *segments parallel segments, with a state pass and a combine;
+ * float32: 4 stages; 1 for an empty sequence's state copy).  *cut_pairs =
+ * pairs cut in halves.  Any pointer may be NULL.  Same validation and return
+ * codes as ssd_chunk_scan_workspace_size's shape checks. */
+int ssd_chunk_scan_plan(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
+                        int chunk, int dtype, int *launches, int *segments, int *cut_pairs);
+
 int ssd_chunk_scan_workspace_layout(int batch, int seqlen, int nheads, int headdim, int dstate,
                                     int ngroups, int chunk, int dtype, size_t *off_delta,
                                     size_t *off_cs, size_t *off_hprev);

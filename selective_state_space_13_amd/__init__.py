@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
     L.ssd_chunk_scan_workspace_size.restype = sz
     L.ssd_chunk_scan_workspace_layout.argtypes = [i] * 8 + [ctypes.POINTER(sz)] * 3
     L.ssd_chunk_scan_workspace_layout.restype = i
+    L.ssd_chunk_scan_plan.argtypes = [i] * 8 + [ctypes.POINTER(i)] * 3
+    L.ssd_chunk_scan_plan.restype = i
     L.ssd_chunk_scan_fwd.argtypes = [i] * 9 + [vp] * 10 + [sz, vp]
     L.ssd_chunk_scan_fwd.restype = i
     L.ssd_chunk_scan_bwd_workspace_size.argtypes = [i] * 7
@@ -147,6 +149,14 @@ def chunk_scan_workspace_layout(batch, seqlen, nheads, headdim, dstate, ngroups,
 
 
 # ---------------------------------------------------------------- functions
+
+def chunk_scan_plan(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype):
+    """(launches per call, segments, pairs cut in halves) of ssd_chunk_scan_fwd."""
+    v = [ctypes.c_int(), ctypes.c_int(), ctypes.c_int()]
+    check(lib().ssd_chunk_scan_plan(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype,
+                                    *[ctypes.byref(t) for t in v]))
+    return tuple(t.value for t in v)
+
 
 def ssd_chunk_scan(x, dt, A, B, C, D=None, *, chunk, initial_state=None,
                    return_final_state=False, dt_softplus=True, workspace=None,

@@ -194,6 +194,24 @@ size_t ssd_chunk_scan_workspace_size(int batch, int seqlen, int nheads, int head
     return lay.total;
 }
 
+int ssd_chunk_scan_plan(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
+                        int chunk, int dtype, int *launches, int *segments, int *cut_pairs) {
+    ScanLayout lay;
+    int st = scan_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, lay);
+    if (st) return st;
+    int nl = 4, ns = 1, nc = 0;  // float32: cumsum, chunk states, state passing, outputs
+    if (prefill_fused(dtype)) {
+        ns = lay.plan.nseg;
+        nc = lay.plan.tail_from >= 0 ? batch * nheads - lay.plan.tail_from : 0;
+        nl = ns > 1 ? 3 : nc > 0 ? 2 : 1;
+    }
+    if (batch == 0 || seqlen == 0) nl = seqlen == 0 && batch > 0 ? 1 : 0;
+    if (launches) *launches = nl;
+    if (segments) *segments = ns;
+    if (cut_pairs) *cut_pairs = nc;
+    return SSD_OK;
+}
+
 int ssd_chunk_scan_workspace_layout(int batch, int seqlen, int nheads, int headdim, int dstate,
                                     int ngroups, int chunk, int dtype, size_t *off_delta,
                                     size_t *off_cs, size_t *off_hprev) {
@@ -258,9 +276,11 @@ int ssd_chunk_scan_fwd(int batch, int seqlen, int nheads, int headdim, int dstat
     LaunchMarks marks(stream);
     hipError_t e;
     if (prefill_fused(dtype)) {
-        static const char *what[3] = {"segment state launch", "segment combine launch",
+        static const char *what[3] = {"state pass launch", "segment combine launch",
                                       "fused prefill launch"};
-        for (int phase = lay.plan.nseg > 1 ? 0 : 2; phase < 3; ++phase) {
+        const bool cut = lay.plan.nseg > 1 || lay.plan.tail_from >= 0;
+        for (int phase = cut ? 0 : 2; phase < 3; ++phase) {
+            if (phase == 1 && lay.plan.nseg <= 1) continue;  // a tail cut needs no combine
             marks.before();
             e = ssd::launch_ssd_fused(phase, lay.plan, x, dt, A, B, C, D, initial_state, dt_softplus,
                                       batch, seqlen, nheads, headdim, dstate, ngroups, y,

@@ -100,6 +100,13 @@ struct FusedArgs {
     // chunk_states[(b·H + h)·nchunks + c] ([N][P] float) and segment s >= 1
     // starts from hin (the true incoming state) instead of zero
     float *chunk_states;
+    // pairs (b, h): items < npairs·nseg are (pair, segment); when tail_from >= 0
+    // the pairs from tail_from on are each cut at chunk tail_mid into two halves,
+    // the second half starting from tail_state[pair - tail_from] ([N][P] float),
+    // which the state-only pass (grid = npairs - tail_from) writes from h0
+    int npairs;
+    int tail_from, tail_mid;
+    float *tail_state;
 };
 
 // Inputs of one chunk, loaded into registers one chunk ahead of their use.
@@ -161,15 +168,22 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
         ranked = true;
       }
     }
+    int pair = 0, half = -1;  // half: 0 / 1 for the two halves of a cut pair, -1 otherwise
     if (!ranked) {
-        // work item: (b, g) varies fastest so that all heads of one B/C group run
-        // on the same XCD (workgroups are dealt to the 8 XCDs round robin)
-        const int nbg = (int)(gridDim.x / (unsigned)(R * a.nseg));
-        int item = blockIdx.x;
-        const int bg = item % nbg;
-        item /= nbg;
-        const int r = item % R;
-        seg = item / R;
+        // pair q = (b, g) fastest, then the head within the group, so that all heads
+        // of one B/C group run on the same XCD (workgroups are dealt to the 8 XCDs
+        // round robin)
+        if (a.tail_from >= 0 && (STATE_ONLY || (int)blockIdx.x >= a.tail_from)) {
+            const int ntail = a.npairs - a.tail_from;
+            const int k = STATE_ONLY ? (int)blockIdx.x : (int)blockIdx.x - a.tail_from;
+            pair = a.tail_from + k % ntail;
+            half = STATE_ONLY ? 0 : k / ntail;
+        } else {
+            pair = (int)blockIdx.x % a.npairs;
+            seg = (int)blockIdx.x / a.npairs;
+        }
+        const int nbg = a.npairs / R;
+        const int bg = pair % nbg, r = pair / nbg;
         b = bg / a.ngroups;
         g = bg % a.ngroups;
         h = g * R + r;
@@ -184,8 +198,11 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
         seqlen = s1 - s0;
         nchunks = (seqlen + kC - 1) / kC;
     }
-    const int c0 = seg * a.seg_chunks;
-    const int c1 = min(c0 + a.seg_chunks, nchunks);
+    int c0 = seg * a.seg_chunks, c1 = min(c0 + a.seg_chunks, nchunks);
+    if (half >= 0) {
+        c0 = half ? a.tail_mid : 0;
+        c1 = half ? nchunks : min(a.tail_mid, nchunks);
+    }
     const float Ah = a.A[h];
     const float Dh = a.D ? a.D[h] : 0.0f;  // loaded before the walk: a load after the prefetch would wait for it
     const size_t bh = (size_t)b * a.nheads + h;
@@ -210,7 +227,9 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
     f32x16 st[2];
     {
         const float *src = nullptr;
-        if (seg == 0) {
+        if (half == 1) {
+            src = a.tail_state + (size_t)(pair - a.tail_from) * N * P;
+        } else if (seg == 0) {
             if (a.h0) src = a.h0 + bh * N * P;
         } else if (!STATE_ONLY || a.chunk_states) {
             src = a.hin + (bh * a.nseg + seg) * N * P;
@@ -465,11 +484,13 @@ __global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel
     // ---- end of the segment
     float *dst = nullptr;
     if (STATE_ONLY) {
-        if (!a.chunk_states) {
+        if (half == 0) {
+            dst = a.tail_state + (size_t)(pair - a.tail_from) * N * P;
+        } else if (!a.chunk_states) {
             dst = a.seg_state + (bh * a.nseg + seg) * N * P;
             if (wave == kScanWave && lane == 0) a.seg_decay[bh * a.nseg + seg] = seg_decay;
         }
-    } else if (a.final_state && seg == a.nseg - 1) {
+    } else if (a.final_state && half != 0 && seg == a.nseg - 1) {
         dst = a.final_state + bh * N * P;
     }
     if (dst) {
@@ -529,6 +550,18 @@ FusedPlan fused_plan(int batch, int seqlen, int nheads, int dstate) {
         const size_t st = (size_t)bh * pl.nseg * dstate * P * sizeof(float);
         pl.state_bytes = (st + 255) / 256 * 256;
         pl.ws_bytes = 2 * pl.state_bytes + ((size_t)bh * pl.nseg * sizeof(double) + 255) / 256 * 256;
+    } else {
+        // Whole pairs in rounds of 256 workgroups: when the last round is at most
+        // half full, its pairs are cut in two halves, so that it takes about half
+        // the time.  The second halves start from the state at the cut, which a
+        // state-only pass over the first halves computes beforehand.
+        const long long rounds = (bh + 255) / 256;
+        const long long rem = bh - 256 * (rounds - 1);
+        if (rounds >= 2 && rem <= 128 && pl.nchunks >= 16) {
+            pl.tail_from = (int)(bh - rem);
+            pl.tail_mid = pl.nchunks / 2;
+            pl.ws_bytes = ((size_t)rem * dstate * P * sizeof(float) + 255) / 256 * 256;
+        }
     }
     return pl;
 }
@@ -557,15 +590,24 @@ hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const
     a.nchunks = pl.nchunks;
     a.nseg = pl.nseg;
     a.seg_chunks = pl.seg_chunks;
+    a.npairs = batch * nheads;
+    a.tail_from = pl.tail_from;
+    a.tail_mid = pl.tail_mid;
+    unsigned items = (unsigned)((long long)batch * nheads * pl.nseg);
     if (pl.nseg > 1) {
         char *ws = static_cast<char *>(workspace);
         a.seg_state = reinterpret_cast<float *>(ws);
         a.hin = reinterpret_cast<const float *>(ws + pl.state_bytes);
         a.seg_decay = reinterpret_cast<double *>(ws + 2 * pl.state_bytes);
+    } else if (pl.tail_from >= 0) {
+        // phase 0: the state at the cut of every tail pair; phase 2: whole pairs and halves
+        if (phase == 1) return hipErrorInvalidValue;
+        a.tail_state = static_cast<float *>(workspace);
+        const unsigned ntail = (unsigned)(a.npairs - pl.tail_from);
+        items = phase == 0 ? ntail : (unsigned)pl.tail_from + 2 * ntail;
     } else if (phase != 2) {
         return hipErrorInvalidValue;
     }
-    const unsigned items = (unsigned)((long long)batch * nheads * pl.nseg);
     if (phase == 0) {
         if (dstate == 128)
             ssd_fused_kernel<128, true><<<items, kThreads, 0, stream>>>(a);
@@ -594,6 +636,7 @@ hipError_t launch_ssd_chunk_states(int phase, const FusedPlan &pl, const void *x
     // phases 0 and 1 (segments only) are those of the forward; phase 2 is the
     // state-only walk that stores every chunk's incoming state
     if (phase != 2) {
+        if (pl.nseg <= 1) return hipErrorInvalidValue;  // segment passes only
         return launch_ssd_fused(phase, pl, x, dt, A, B, nullptr, nullptr, h0, dt_softplus, batch, seqlen,
                                 nheads, headdim, dstate, ngroups, nullptr, nullptr, workspace, stream);
     }
@@ -611,6 +654,8 @@ hipError_t launch_ssd_chunk_states(int phase, const FusedPlan &pl, const void *x
     a.nseg = pl.nseg;
     a.seg_chunks = pl.seg_chunks;
     a.chunk_states = chunk_states;
+    a.npairs = batch * nheads;
+    a.tail_from = -1;  // the walk stores every chunk's state: whole pairs (or segments) only
     if (pl.nseg > 1) a.hin = reinterpret_cast<const float *>(static_cast<char *>(workspace) + pl.state_bytes);
     const unsigned items = (unsigned)((long long)batch * nheads * pl.nseg);
     if (dstate == 128)
@@ -646,6 +691,8 @@ hipError_t launch_ssd_fused_varlen(const int *cu_seqlens, int nseq, int total_to
     a.nchunks = (total_tokens + kC - 1) / kC;  // bound; each sequence counts its own
     a.nseg = 1;
     a.seg_chunks = a.nchunks + 1;
+    a.npairs = nseq * nheads;
+    a.tail_from = -1;
     const unsigned items = (unsigned)((long long)nseq * nheads);
     if (dstate == 128)
         ssd_fused_kernel<128, false><<<items, kThreads, 0, stream>>>(a);

@@ -38,7 +38,8 @@ def test_header_declares_expected_entry_points():
               "ssd_chunk_scan_workspace_size", "ssd_chunk_scan_workspace_layout",
               "selective_scan_workspace_size", "ssd_status_string", "ssd_last_error",
               "ssd_version", "ssd_chunk_scan_bwd", "ssd_chunk_scan_bwd_workspace_size",
-              "ssd_chunk_scan_varlen_fwd", "ssd_causal_conv1d_fwd", "ssd_gated_rmsnorm_fwd"]:
+              "ssd_chunk_scan_varlen_fwd", "ssd_causal_conv1d_fwd", "ssd_gated_rmsnorm_fwd",
+              "ssd_chunk_scan_plan"]:
         assert n in names
 
 
@@ -142,8 +143,10 @@ def test_workspace_size_and_layout(L):
 
 def test_bf16_workspace_is_small_or_segment_buffers(L):
     # the fused bf16 path keeps its stages on chip: 256 bytes unless the call is
-    # cut into segments (few (batch, head) pairs, long sequence)
-    assert L.ssd_chunk_scan_workspace_size(8, 2048, 80, 64, 128, 1, 256, BF16) == 256
+    # cut into segments (few (batch, head) pairs, long sequence) or the last
+    # round's pairs are cut in halves (their states at the cut)
+    assert L.ssd_chunk_scan_workspace_size(8, 2048, 96, 64, 128, 1, 256, BF16) == 256
+    assert L.ssd_chunk_scan_workspace_size(8, 2048, 80, 64, 128, 1, 256, BF16) == 128 * 128 * 64 * 4
     assert L.ssd_chunk_scan_workspace_size(0, 2048, 80, 64, 128, 1, 256, BF16) == 256
     big = L.ssd_chunk_scan_workspace_size(1, 65536, 80, 64, 128, 8, 256, BF16)
     assert big > 2 * 80 * 128 * 64 * 4 and big % 256 == 0
@@ -243,6 +246,26 @@ def bwd_call(L, b=2, Lq=300, H=8, P=64, N=128, G=2, dtype=BF16, ptrs=None, ws_by
     return L.ssd_chunk_scan_bwd(b, Lq, H, P, N, G, dtype, 1, *[p[n] for n in BWD_NAMES],
                                 ws if ws is not None else fake(20),
                                 need if ws_bytes is None else ws_bytes, None)
+
+
+def _plan(L, *args):
+    v = [ctypes.c_int(), ctypes.c_int(), ctypes.c_int()]
+    st = L.ssd_chunk_scan_plan(*args, *[ctypes.byref(t) for t in v])
+    return st, tuple(t.value for t in v)
+
+
+def test_chunk_scan_plan(L):
+    # 640 pairs: two full rounds of 256, the last 128 pairs cut in halves
+    assert _plan(L, 8, 2048, 80, 64, 128, 1, 256, BF16) == (OK, (2, 1, 128))
+    # 80 pairs of 64K tokens: 16 segments
+    assert _plan(L, 1, 65536, 80, 64, 128, 8, 256, BF16) == (OK, (3, 16, 0))
+    # three full rounds: nothing to cut
+    assert _plan(L, 8, 2048, 96, 64, 128, 1, 256, BF16) == (OK, (1, 1, 0))
+    # float32: four stages
+    assert _plan(L, 1, 512, 8, 64, 64, 1, 64, F32) == (OK, (4, 1, 0))
+    assert _plan(L, 1, 512, 8, 64, 96, 1, 64, BF16)[0] == UNSUP
+    # the cut pairs' state lives in the workspace
+    assert L.ssd_chunk_scan_workspace_size(8, 2048, 80, 64, 128, 1, 256, BF16) >= 128 * 128 * 64 * 4
 
 
 def test_bwd_workspace_size(L):

@@ -138,6 +138,21 @@ def test_prefill_segmented_bf16(case):
     assert_parity(to_f64(fs), fo, TAU_BF16, False, f"segmented final {case}")
 
 
+@pytest.mark.parametrize("case", [(3, 1100, 100, 128, 4, True, True), (5, 1024, 60, 64, 1, False, False)],
+                         ids=["b3L1100H100N128G4", "b5L1024H60N64G1"])
+def test_prefill_tail_cut(case):
+    """Two full rounds of 256 (batch, head) pairs and a short last round, whose
+    pairs are cut in halves (the second half starting from the state at the cut)."""
+    b, L, H, N, G, wD, wh = case
+    launches, nseg, cut = ssd.chunk_scan_plan(b, L, H, 64, N, G, 256, ssd.SSD_BF16)
+    assert launches == 2 and nseg == 1 and cut == b * H - 256
+    d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=L + H, config_id=104, with_h0=wh)
+    y, fs = run_scan(d, 256, "bf16", wD, wh)
+    yo, fo = oracle_scan(d, wD, wh)
+    assert_parity(to_f64(y), yo, TAU_BF16, True, f"tail cut y {case}")
+    assert_parity(to_f64(fs), fo, TAU_BF16, False, f"tail cut final {case}")
+
+
 VARLEN_GPU_CASES = [
     # lengths, H, N, G, with_D, with_h0
     ([300, 1, 64, 0, 257, 1000], 8, 128, 2, True, True),
@@ -286,6 +301,7 @@ BWD_CASES = [
     (2, 300, 6, 64, 3, True, False, True),     # dstate 64, 3 groups
     (1, 1024, 8, 128, 1, True, True, True),    # 16 chunks, long enough for forward segments
     (3, 129, 10, 128, 2, False, True, False),  # 5 heads per group, tail of 1
+    (5, 1024, 60, 64, 1, True, True, True),    # the forward plan cuts its last round's pairs
 ]
 
 
