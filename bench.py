@@ -287,7 +287,7 @@ def bench_varlen(steps, warmup):
     return dict(ms=ms, kernel_ms=per[0], tokens=T, bytes=nbytes)
 
 
-BWD_KERNELS = ["chunk_states", "adjoint_walk", "chunk_gradients", "dA_dD_reduce"]
+BWD_KERNELS = ["state_and_adjoint_walks", "chunk_gradients", "dA_dD_reduce"]
 BWD_SEGMENTED = ["segment_states", "segment_combine"] + BWD_KERNELS
 
 
@@ -423,6 +423,7 @@ def main():
     workload = f"{cfg['name']}:b{cfg['batch']}L{cfg['seqlen']}H{cfg['nheads']}P{cfg['headdim']}" \
                f"N{cfg['dstate']}G{cfg['ngroups']}Q{cfg['chunk']}"
     digest = source_digest(["selective_state_space_13_amd/csrc/ssd_fused.hip",
+                            "selective_state_space_13_amd/csrc/ssd_fused_walk.h",
                             "selective_state_space_13_amd/csrc/mfma_tile.h",
                             "selective_state_space_13_amd/csrc/ssd_kernels.h"])
     pf = bench_prefill(cfg, args.steps, args.warmup)

@@ -389,10 +389,10 @@ int ssd_chunk_scan_bwd(int batch, int seqlen, int nheads, int headdim, int dstat
          span("dy", dy, n_x * es), span("dfinal_state", dfinal_state, dfinal_state ? n_state * 4 : 0)});
     if (st) return st;
     const ssd::BwdPlan pl = ssd::bwd_plan(batch, seqlen, nheads, dstate);
-    static const char *what[6] = {"segment state launch", "segment combine launch",
-                                  "chunk state launch", "adjoint walk launch",
-                                  "chunk gradient launch", "dA/dD reduction launch"};
-    for (int phase = pl.fwd.nseg > 1 ? 0 : 2; phase < 6; ++phase) {
+    static const char *what[5] = {"segment state launch", "segment combine launch",
+                                  "state and adjoint walk launch", "chunk gradient launch",
+                                  "dA/dD reduction launch"};
+    for (int phase = pl.fwd.nseg > 1 ? 0 : 2; phase < 5; ++phase) {
         marks.before();
         e = ssd::launch_ssd_bwd(phase, pl, x, dt, A, B, C, D, initial_state, dy, dfinal_state,
                                 dt_softplus, batch, seqlen, nheads, headdim, dstate, ngroups, dx, ddt,

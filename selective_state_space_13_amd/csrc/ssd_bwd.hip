@@ -19,11 +19,14 @@
 //   dcs_end += exp(cs_end) <G_out, h_in> + Σ_s q_s
 //   dℓ_t    = Σ_{v >= t} dcs_v,  dΔ = A·dℓ + x·dxr,  dA = Σ Δ·dℓ,  dD = Σ x·dy
 //
-// Three launches after the forward state pass (which stores h_in of every
-// chunk):
-//   ssd_bwd_adjoint_kernel   one workgroup per (b, h) walks the chunks in
-//                            reverse with the N x P adjoint in MFMA
-//                            accumulators and stores G_out of every chunk;
+// Three launches (after the forward's segment passes, when it has any):
+//   ssd_bwd_walks_kernel     the forward's state-only walk, storing h_in of every
+//                            chunk, and in the same launch the adjoint walk: one
+//                            workgroup per (b, h) walks the chunks in reverse
+//                            with the N x P adjoint in MFMA accumulators and
+//                            stores G_out of every chunk (the two are
+//                            independent; one launch packs them into fewer
+//                            rounds of the chip);
 //   ssd_bwd_chunk_kernel     one workgroup per (b, group, chunk) loops over
 //                            the group's heads: every product above on the
 //                            matrix cores, dB and dC summed over the heads in
@@ -32,14 +35,10 @@
 //
 // Precision as in the forward: computed bf16 operands (e·dy, the decayed
 // C·Bᵀ and K blocks, the states) enter as a bf16 head and tail; cs is float64.
-#include "mfma_tile.h"
+#include "ssd_fused_walk.h"  // the forward walk; P, kC, kThreads
 
 namespace ssd {
 namespace {
-
-constexpr int P = 64;           // headdim
-constexpr int kC = 64;          // tokens per chunk
-constexpr int kThreads = 512;   // 8 waves
 
 struct BwdArgs {
     const uint16_t *x, *dt, *B, *C, *dy;
@@ -67,7 +66,7 @@ struct AdjSmem {
 // (dstate 64: waves 0-3).  Wave 7 scans the next chunk's Δ·A while the others
 // multiply.
 template <int N>
-__global__ __launch_bounds__(kThreads, 2) void ssd_bwd_adjoint_kernel(BwdArgs a) {
+__device__ __forceinline__ void adjoint_walk(const BwdArgs &a, unsigned blk, unsigned nblk) {
     constexpr int BV = N / 64, BPR = N / 8;
     constexpr int kScanWave = 7;
     __shared__ __attribute__((aligned(16))) AdjSmem<N> sm;
@@ -76,8 +75,8 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_adjoint_kernel(BwdArgs a)
     const int rrow = tr_row(lane), rcol = tr_col(lane);
 
     const int R = a.nheads / a.ngroups;
-    const int nbg = (int)(gridDim.x / (unsigned)R);
-    const int bg = blockIdx.x % nbg, r = blockIdx.x / nbg;
+    const int nbg = (int)(nblk / (unsigned)R);
+    const int bg = (int)(blk % (unsigned)nbg), r = (int)(blk / (unsigned)nbg);
     const int b = bg / a.ngroups, g = bg % a.ngroups, h = g * R + r;
     const size_t bh = (size_t)b * a.nheads + h;
     const size_t row0 = (size_t)b * a.seqlen;
@@ -168,6 +167,16 @@ __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_adjoint_kernel(BwdArgs a)
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) dst[(32 * snt + 8 * (rr >> 2) + 4 * lg + (rr & 3)) * P] = st[rr];
     }
+}
+
+// Workgroups [0, nfwd) run the forward walk that stores every chunk's incoming
+// state; the rest run the adjoint walk.
+template <int N>
+__global__ __launch_bounds__(kThreads, 2) void ssd_bwd_walks_kernel(FusedArgs fa, BwdArgs ba, unsigned nfwd) {
+    if (blockIdx.x < nfwd)
+        fused_walk<N, true>(fa, blockIdx.x, nfwd);
+    else
+        adjoint_walk<N>(ba, blockIdx.x - nfwd, gridDim.x - nfwd);
 }
 
 // ============================================================ per-chunk gradients
@@ -651,9 +660,12 @@ hipError_t launch_ssd_bwd(int phase, const BwdPlan &pl, const void *x, const voi
     float *gst = reinterpret_cast<float *>(ws + pl.fwd.ws_bytes + pl.states_bytes);
     float *dA_part = reinterpret_cast<float *>(ws + pl.fwd.ws_bytes + 2 * pl.states_bytes);
     float *dD_part = reinterpret_cast<float *>(ws + pl.fwd.ws_bytes + 2 * pl.states_bytes + pl.part_bytes);
-    if (phase <= 2)  // forward: the state entering every chunk (segment passes first when cut)
-        return launch_ssd_chunk_states(phase, pl.fwd, x, dt, A, B, h0, dt_softplus, batch, seqlen,
-                                       nheads, headdim, dstate, ngroups, hst, workspace, stream);
+    if (phase <= 1) {  // the forward's segment passes, when it is cut into segments
+        if (pl.fwd.nseg <= 1) return hipErrorInvalidValue;
+        return launch_ssd_fused(phase, pl.fwd, x, dt, A, B, nullptr, nullptr, h0, dt_softplus, batch,
+                                seqlen, nheads, headdim, dstate, ngroups, nullptr, nullptr, workspace,
+                                stream);
+    }
     BwdArgs a{};
     a.x = static_cast<const uint16_t *>(x);
     a.dt = static_cast<const uint16_t *>(dt);
@@ -677,19 +689,39 @@ hipError_t launch_ssd_bwd(int phase, const BwdPlan &pl, const void *x, const voi
     a.ngroups = ngroups;
     a.dt_softplus = dt_softplus;
     a.nchunks = pl.fwd.nchunks;
-    if (phase == 3) {
-        const unsigned items = (unsigned)((long long)batch * nheads);
+    if (phase == 2) {
+        // the forward walk storing every chunk's incoming state (segment s >= 1
+        // starting from the combined state of the segment passes), and the adjoint walk
+        FusedArgs f{};
+        f.x = static_cast<const uint16_t *>(x);
+        f.dt = static_cast<const uint16_t *>(dt);
+        f.B = static_cast<const uint16_t *>(B);
+        f.A = A;
+        f.h0 = h0;
+        f.seqlen = seqlen;
+        f.nheads = nheads;
+        f.ngroups = ngroups;
+        f.dt_softplus = dt_softplus;
+        f.nchunks = pl.fwd.nchunks;
+        f.nseg = pl.fwd.nseg;
+        f.seg_chunks = pl.fwd.seg_chunks;
+        f.chunk_states = hst;
+        f.npairs = batch * nheads;
+        f.tail_from = -1;
+        if (pl.fwd.nseg > 1) f.hin = reinterpret_cast<const float *>(ws + pl.fwd.state_bytes);
+        const unsigned nfwd = (unsigned)((long long)batch * nheads * pl.fwd.nseg);
+        const unsigned items = nfwd + (unsigned)((long long)batch * nheads);
         if (dstate == 128)
-            ssd_bwd_adjoint_kernel<128><<<items, kThreads, 0, stream>>>(a);
+            ssd_bwd_walks_kernel<128><<<items, kThreads, 0, stream>>>(f, a, nfwd);
         else
-            ssd_bwd_adjoint_kernel<64><<<items, kThreads, 0, stream>>>(a);
-    } else if (phase == 4) {
+            ssd_bwd_walks_kernel<64><<<items, kThreads, 0, stream>>>(f, a, nfwd);
+    } else if (phase == 3) {
         const unsigned items = (unsigned)((long long)batch * ngroups * pl.fwd.nchunks);
         if (dstate == 128)
             ssd_bwd_chunk_kernel<128><<<items, kThreads, 0, stream>>>(a);
         else
             ssd_bwd_chunk_kernel<64><<<items, kThreads, 0, stream>>>(a);
-    } else if (phase == 5) {
+    } else if (phase == 4) {
         bwd_reduce_kernel<<<(unsigned)nheads, 64, 0, stream>>>(dA_part, dD_part, batch, nheads,
                                                              pl.fwd.nchunks, dA, dD);
     } else {

@@ -84,15 +84,6 @@ hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const
                             const float *h0, int dt_softplus, int batch, int seqlen, int nheads,
                             int headdim, int dstate, int ngroups, void *y, float *final_state,
                             void *workspace, hipStream_t stream);
-// State-only forward pass that stores the state entering every 64-token
-// chunk, [b][H][nchunks][N][P] float.  Phases 0 and 1 are the segment passes
-// of launch_ssd_fused (plan.nseg > 1 only); phase 2 is the storing walk.
-hipError_t launch_ssd_chunk_states(int phase, const FusedPlan &pl, const void *x, const void *dt,
-                                  const float *A, const void *B, const float *h0, int dt_softplus,
-                                  int batch, int seqlen, int nheads, int headdim, int dstate,
-                                  int ngroups, float *chunk_states, void *workspace,
-                                  hipStream_t stream);
-
 // Chunked backward (bf16).  Workspace: the forward plan's, then the chunk
 // states, the chunk adjoints and the per-(b, h, chunk) dA, dD partials.
 struct BwdPlan {
@@ -100,8 +91,9 @@ struct BwdPlan {
     size_t states_bytes = 0, part_bytes = 0, ws_bytes = 0;
 };
 BwdPlan bwd_plan(int batch, int seqlen, int nheads, int dstate);
-// phase 0..2: forward chunk states (0, 1 only when segmented); 3: adjoint walk;
-// 4: per-chunk gradients; 5: dA, dD reduction
+// phase 0, 1: the forward's segment passes (only when it is cut into segments);
+// 2: the forward walk storing every chunk's state and the adjoint walk, in one
+// launch; 3: per-chunk gradients; 4: dA, dD reduction
 hipError_t launch_ssd_bwd(int phase, const BwdPlan &pl, const void *x, const void *dt, const float *A,
                           const void *B, const void *C, const float *D, const float *h0,
                           const void *dy, const float *dfinal, int dt_softplus, int batch, int seqlen,
