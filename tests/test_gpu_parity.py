@@ -464,6 +464,26 @@ def test_config2_prefill_full(config2):
         assert_parity(to_f64(fs), fo, TAU_BF16, False, f"C2 final D={wD}")
 
 
+def test_config2_backward_full(config2):
+    """Every gradient at the 2.7B-layer shape (the forward plan cuts its last round
+    of pairs here), element by element against the fp64 adjoint oracle."""
+    c, d = config2
+    gr = gen.ssd_grad_inputs(c["batch"], c["seqlen"], c["nheads"], c["headdim"], c["dstate"], "bf16",
+                             config_id=c["id"])
+    say("C2 backward: GPU run")
+    dev = lambda k: to_dev(d[k])
+    out = ssd.ssd_chunk_scan_bwd(dev("x"), dev("dt"), dev("A"), dev("B"), dev("C"), to_dev(gr["dy"]),
+                                 dev("D"), dfinal_state=to_dev(gr["dfinal"]))
+    torch.cuda.synchronize()
+    out = {k: to_f64(v) for k, v in out.items()}
+    say("C2 backward: oracle")
+    ref = oracle.ssd_scan_bwd(d["x"].f64(), d["dt"].f64(), d["A"].f64(), d["B"].f64(), d["C"].f64(),
+                              gr["dy"].f64(), d["D"].f64(), None, gr["dfinal"].f64())
+    for k, rk, bf in (("dx", "dx", True), ("ddt", "ddt", True), ("dB", "dB", True), ("dC", "dC", True),
+                      ("dA", "dA", False), ("dD", "dD", False), ("dinitial_state", "dh0", False)):
+        assert_parity(out[k], ref[rk], TAU_BF16, bf, f"C2 backward {k}")
+
+
 def test_config3_long_context_full():
     c = configs.LONG_CONTEXT_PREFILL
     say("C3: generating inputs")
