@@ -74,6 +74,8 @@ struct Vec8<float> {
 // the limits (σ -> 0 through rcp(inf) = 0, σ -> 1 through exp(-v) -> 0).
 __device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcpf(1.0f + __expf(-v)); }
 
+constexpr int kXcds = 8;  // MI355X: workgroups are dealt to the 8 XCDs round robin
+
 // Tokens per conv lane: every row of a tile (and the W-1 rows before it) is
 // loaded before the first output is formed, so the tile is sized to the
 // registers of one raw row (4 VGPRs for bf16, 8 for float32).
@@ -83,25 +85,33 @@ constexpr int conv_tile() {
 }
 
 // One lane: 8 channels of one batch row over one tile of tokens.  Lanes are
-// numbered channel-vector fastest, so a wave reads whole 1 KiB runs of a row
-// and no lane of a block is idle except in the last block of a batch row.
+// numbered channel-vector fastest, then tile, then batch row, so a wave reads
+// whole 1 KiB runs of a row and only the last block has idle lanes.
+// Workgroups are dealt to the 8 XCDs round robin; each XCD is given one
+// contiguous range of that numbering, so the W-1 rows a tile reads again from
+// the tile before it were loaded into the same XCD's L2 shortly before.
 template <typename T, int W>
 __global__ __launch_bounds__(256) void causal_conv1d_kernel(const T *__restrict__ x,
                                                             const float *__restrict__ w,
                                                             const float *__restrict__ bias,
                                                             const float *__restrict__ s0,
                                                             int seqlen, int channels, int ntiles,
-                                                            int apply_silu, T *__restrict__ y,
+                                                            long long lanes, int apply_silu,
+                                                            T *__restrict__ y,
                                                             float *__restrict__ sfinal) {
     constexpr int TT = conv_tile<T>();
     constexpr int R = TT + W - 1;  // rows read: t0-W+1 .. t0+TT-1
     const int nvec = channels / 8;
-    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= (long long)nvec * ntiles) return;
-    const int v = (int)(idx % nvec);
-    const int t0 = (int)(idx / nvec) * TT;
+    const long long per_xcd = gridDim.x / kXcds;  // the grid is a multiple of kXcds blocks
+    const long long blk = (long long)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    const long long idx = blk * blockDim.x + threadIdx.x;
+    if (idx >= lanes) return;
+    const long long per_row = (long long)nvec * ntiles;
+    const int b = (int)(idx / per_row);
+    const long long in_row = idx - (long long)b * per_row;
+    const int v = (int)(in_row % nvec);
+    const int t0 = (int)(in_row / nvec) * TT;
     const int c0 = 8 * v;
-    const int b = blockIdx.y;
     const T *xb = x + (size_t)b * seqlen * channels + c0;
 
     // rows outside [0, seqlen) are clamped and never used as x
@@ -250,16 +260,17 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(const T *__restrict_
 }
 
 template <typename T>
-hipError_t conv_t(int width, dim3 grid, hipStream_t stream, const void *x, const float *w,
+hipError_t conv_t(int width, unsigned blocks, hipStream_t stream, const void *x, const float *w,
                   const float *bias, const float *s0, int seqlen, int channels, int ntiles,
-                  int apply_silu, void *y, float *sfinal) {
+                  long long lanes, int apply_silu, void *y, float *sfinal) {
     const T *xp = static_cast<const T *>(x);
     T *yp = static_cast<T *>(y);
     switch (width) {
-#define SSD_CONV(WW)                                                                              \
-    case WW:                                                                                      \
-        causal_conv1d_kernel<T, WW><<<grid, 256, 0, stream>>>(xp, w, bias, s0, seqlen, channels, \
-                                                              ntiles, apply_silu, yp, sfinal);    \
+#define SSD_CONV(WW)                                                                               \
+    case WW:                                                                                       \
+        causal_conv1d_kernel<T, WW><<<blocks, 256, 0, stream>>>(xp, w, bias, s0, seqlen, channels, \
+                                                                ntiles, lanes, apply_silu, yp,     \
+                                                                sfinal);                           \
         break;
         SSD_CONV(1)
         SSD_CONV(2)
@@ -305,13 +316,15 @@ hipError_t launch_causal_conv1d(int dtype, const void *x, const float *weight, c
     if (batch == 0 || channels == 0 || seqlen == 0) return hipSuccess;
     const int tt = dtype == 0 ? conv_tile<float>() : conv_tile<bf16_t>();
     const int ntiles = (seqlen + tt - 1) / tt;
-    const long long lanes = (long long)(channels / 8) * ntiles;
-    const dim3 grid((unsigned)((lanes + 255) / 256), (unsigned)batch);
+    const long long lanes = (long long)batch * (channels / 8) * ntiles;
+    // a multiple of the XCD count, so that each XCD's share is one contiguous range
+    const long long blocks = ((lanes + 255) / 256 + kXcds - 1) / kXcds * kXcds;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     if (dtype == 0)
-        return conv_t<float>(width, grid, stream, x, weight, bias, initial_state, seqlen, channels,
-                             ntiles, apply_silu, y, final_state);
-    return conv_t<bf16_t>(width, grid, stream, x, weight, bias, initial_state, seqlen, channels, ntiles,
-                          apply_silu, y, final_state);
+        return conv_t<float>(width, (unsigned)blocks, stream, x, weight, bias, initial_state, seqlen,
+                             channels, ntiles, lanes, apply_silu, y, final_state);
+    return conv_t<bf16_t>(width, (unsigned)blocks, stream, x, weight, bias, initial_state, seqlen,
+                          channels, ntiles, lanes, apply_silu, y, final_state);
 }
 
 hipError_t launch_gated_rmsnorm(int dtype, const void *y, const void *z, const float *weight,
