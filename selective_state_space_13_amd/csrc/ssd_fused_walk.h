@@ -90,14 +90,16 @@ struct ChunkRegs {
 //     for dstate 128, waves 0, 1, 6, 7 own one p-tile each of n-tiles 2 and 3
 //     (waves 2 and 3, whose strip has two C·Bᵀ blocks, own none); the
 //     state-only pass gives every wave one tile (dstate 64: waves 0-3);
-//   one wave (kScanWave) also scans the next chunk's Δ·A while the others multiply.
+//   one wave (kScanWave) also scans the next chunk's Δ·A: in the full pass wave 2,
+//     which owns no state tile, during the staging phase (its Δ is loaded two chunks
+//     ahead); in the state-only pass while the others multiply.
 template <int N, bool STATE_ONLY>
 __device__ __forceinline__ void fused_walk(const FusedArgs &a, unsigned blk, unsigned nblk) {
     constexpr int KS = N / 16;        // k-steps over n
     constexpr int BV = N / 64;
     constexpr int BPR = N / 8;        // 16-byte vectors per B/C row
     constexpr int NP = N + 8;         // padded pitch of cr and hs
-    constexpr int kScanWave = STATE_ONLY ? (N == 128 ? 0 : 4) : 6;
+    constexpr int kScanWave = STATE_ONLY ? (N == 128 ? 0 : 4) : 2;
     __shared__ __attribute__((aligned(16))) FusedSmem<N, STATE_ONLY> sm;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -233,11 +235,13 @@ __device__ __forceinline__ void fused_walk(const FusedArgs &a, unsigned blk, uns
     const int last = seqlen - 1;
 
     ChunkRegs<N> R0;
-    auto prefetch = [&](ChunkRegs<N> &Rg, int c) {
+    // x, B, C of chunk c and the raw Δ of chunk cd (c, or the chunk after it)
+    auto prefetch = [&](ChunkRegs<N> &Rg, int c, int cd) {
         const int t0 = c * kC, lim = last - t0;  // rows past the end are clamped to the last one
-        // dt first: the scan wave uses it before the rest has arrived, and loads
+        // dt first: the scan wave may use it before the rest has arrived, and loads
         // complete in issue order
-        const uint16_t raw = a.dt[(row0 + t0 + min(lane, lim)) * a.nheads + h];
+        const int td = cd * kC;
+        const uint16_t raw = a.dt[(row0 + td + min(lane, last - td)) * a.nheads + h];
         Rg.dt = __uint_as_float((uint32_t)raw << 16);
         const uint16_t *xc = a.x + ((row0 + t0) * a.nheads + h) * P + xcol;
         Rg.x = ld16(xc + (size_t)min(xrow, lim) * xstride);
@@ -268,8 +272,12 @@ __device__ __forceinline__ void fused_walk(const FusedArgs &a, unsigned blk, uns
 
     double seg_decay = 0.0;
     if (c0 < c1) {  // an empty sequence loads nothing and returns its initial state
-        prefetch(R0, c0);
+        prefetch(R0, c0, c0);
         if (wave == kScanWave) seg_decay += scan_chunk(c0, R0.dt, sm.tok[c0 & 1]);
+        if constexpr (!STATE_ONLY) {  // the full pass scans one chunk ahead during staging
+            const int td = min(c0 + 1, c1 - 1) * kC;
+            R0.dt = __uint_as_float((uint32_t)a.dt[(row0 + td + min(lane, last - td)) * a.nheads + h] << 16);
+        }
     }
     __syncthreads();
 
@@ -325,8 +333,13 @@ __device__ __forceinline__ void fused_walk(const FusedArgs &a, unsigned blk, uns
                 for (int rr = 0; rr < 16; ++rr) st[j][rr] *= dec;
             }
         }
+        // the next chunk's per-token values (its tok buffer was last read before the
+        // previous barrier)
+        if constexpr (!STATE_ONLY) {
+            if (wave == kScanWave && c + 1 < c1) seg_decay += scan_chunk(c + 1, R0.dt, sm.tok[buf ^ 1]);
+        }
         // next chunk's inputs (clamped to the last chunk: loads stay unconditional)
-        prefetch(R0, min(c + 1, c1 - 1));
+        prefetch(R0, min(c + 1, c1 - 1), min(STATE_ONLY ? c + 1 : c + 2, c1 - 1));
         __syncthreads();
 
         // ================= S2: products
@@ -423,8 +436,8 @@ __device__ __forceinline__ void fused_walk(const FusedArgs &a, unsigned blk, uns
 #pragma unroll
                 for (int e = 0; e < 4; ++e) stp[(8 * q + 4 * lg + e) * kSt + l32] = acc[4 * q + e];
         }
-        // the next chunk's per-token values, while the products run
-        if (wave == kScanWave && c + 1 < c1) seg_decay += scan_chunk(c + 1, R0.dt, sm.tok[buf ^ 1]);
+        // state-only pass: the next chunk's per-token values, while the products run
+        if (STATE_ONLY && wave == kScanWave && c + 1 < c1) seg_decay += scan_chunk(c + 1, R0.dt, sm.tok[buf ^ 1]);
         __syncthreads();
 
         // ================= S3: y = partials + D·x, 16-byte bf16 rows
