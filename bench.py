@@ -423,6 +423,7 @@ def main():
     workload = f"{cfg['name']}:b{cfg['batch']}L{cfg['seqlen']}H{cfg['nheads']}P{cfg['headdim']}" \
                f"N{cfg['dstate']}G{cfg['ngroups']}Q{cfg['chunk']}"
     digest = source_digest(["selective_state_space_13_amd/csrc/ssd_fused.hip",
+                            "selective_state_space_13_amd/csrc/ssd_fused_roles.h",
                             "selective_state_space_13_amd/csrc/ssd_fused_walk.h",
                             "selective_state_space_13_amd/csrc/mfma_tile.h",
                             "selective_state_space_13_amd/csrc/ssd_kernels.h"])

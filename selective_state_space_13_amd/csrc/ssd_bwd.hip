@@ -35,7 +35,7 @@
 //
 // Precision as in the forward: computed bf16 operands (e·dy, the decayed
 // C·Bᵀ and K blocks, the states) enter as a bf16 head and tail; cs is float64.
-#include "ssd_fused_walk.h"  // the forward walk; P, kC, kThreads
+#include "ssd_fused_walk.h"  // the state-only walk; P, kC, kThreads
 
 namespace ssd {
 namespace {
@@ -174,7 +174,7 @@ __device__ __forceinline__ void adjoint_walk(const BwdArgs &a, unsigned blk, uns
 template <int N>
 __global__ __launch_bounds__(kThreads, 2) void ssd_bwd_walks_kernel(FusedArgs fa, BwdArgs ba, unsigned nfwd) {
     if (blockIdx.x < nfwd)
-        fused_walk<N, true>(fa, blockIdx.x, nfwd);
+        state_walk<N>(fa, blockIdx.x, nfwd);
     else
         adjoint_walk<N>(ba, blockIdx.x - nfwd, gridDim.x - nfwd);
 }

@@ -17,16 +17,17 @@
 // same result up to rounding, and 64 keeps the quadratic intra-chunk work
 // small next to the state products.
 //
-// Work split inside a workgroup (8 waves, 512 lanes), per chunk: every wave
-// updates one 32 x 32 tile of the state; the 64 x 64 output is four 32 x 32
-// tiles, and for each tile one of waves 0-3 computes the causal blocks of
-// Gᵀ = (C Bᵀ)ᵀ and the masked M·X while one of waves 4-7 computes C·H_prev.
-// The two partial outputs meet in LDS and are summed, skip-added and stored
-// by all lanes as 16-byte bf16 rows.  Two barriers per chunk: after staging,
-// and after the products.
+// Work split inside a workgroup (8 waves, 512 lanes), by role
+// (ssd_fused_roles.h): waves 0-3 hold the state in MFMA accumulators, each one
+// half of n for one 32-wide tile of headdim, and multiply C by it straight
+// from those registers; they also decay and update it and produce the 64 x 64
+// outputs as four 32 x 32 quarters.  Waves 4-7 form the three causal blocks of
+// (C Bᵀ)ᵀ with the decay mask, scan the next chunk's Δ·A, and stage the next
+// chunk into LDS while the state waves finish the outputs.  Two barriers per
+// chunk.
 //
 // Long sequences with few (batch, head) pairs are cut into S segments that
-// run in parallel.  A state-only pass (the same kernel, STATE_ONLY = true)
+// run in parallel.  A state-only pass (ssd_state_kernel, ssd_fused_walk.h)
 // gives each segment's end state from a zero start and its total log-decay;
 // a small combine kernel chains them into each segment's incoming state; the
 // full pass then starts segment s from that state.  The recurrence is linear
@@ -38,14 +39,21 @@
 // x, B, C are exact bf16 and enter unsplit.  cs is summed in float64 so that
 // exp of a difference of nearby cs values keeps float32 accuracy.  A_h <= 0
 // is assumed (cs non-increasing within a chunk).
-#include "ssd_fused_walk.h"
+#include "ssd_fused_roles.h"
 
 namespace ssd {
 namespace {
 
-template <int N, bool STATE_ONLY>
-__global__ __launch_bounds__(kThreads, STATE_ONLY ? 2 : 1) void ssd_fused_kernel(FusedArgs a) {
-    fused_walk<N, STATE_ONLY>(a, blockIdx.x, gridDim.x);
+// The state-only pass (segment end states, states at the cut of a pair).
+template <int N>
+__global__ __launch_bounds__(kThreads, 2) void ssd_state_kernel(FusedArgs a) {
+    state_walk<N>(a, blockIdx.x, gridDim.x);
+}
+
+// The full pass: states and outputs.
+template <int N>
+__global__ __launch_bounds__(kThreads, 1) void ssd_prefill_kernel(FusedArgs a) {
+    fused_roles_walk<N>(a, blockIdx.x, gridDim.x);
 }
 
 // State entering each segment s >= 1: H_s = exp(decay_{s-1})·H_{s-1} + E_{s-1},
@@ -153,18 +161,18 @@ hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const
     }
     if (phase == 0) {
         if (dstate == 128)
-            ssd_fused_kernel<128, true><<<items, kThreads, 0, stream>>>(a);
+            ssd_state_kernel<128><<<items, kThreads, 0, stream>>>(a);
         else
-            ssd_fused_kernel<64, true><<<items, kThreads, 0, stream>>>(a);
+            ssd_state_kernel<64><<<items, kThreads, 0, stream>>>(a);
     } else if (phase == 1) {
         const long long total = (long long)batch * nheads * dstate * P;
         segment_combine_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(
             a.h0, a.seg_state, a.seg_decay, const_cast<float *>(a.hin), a.nseg, dstate * P, total);
     } else {
         if (dstate == 128)
-            ssd_fused_kernel<128, false><<<items, kThreads, 0, stream>>>(a);
+            ssd_prefill_kernel<128><<<items, kThreads, 0, stream>>>(a);
         else
-            ssd_fused_kernel<64, false><<<items, kThreads, 0, stream>>>(a);
+            ssd_prefill_kernel<64><<<items, kThreads, 0, stream>>>(a);
     }
     return hipGetLastError();
 }
@@ -199,9 +207,9 @@ hipError_t launch_ssd_fused_varlen(const int *cu_seqlens, int nseq, int total_to
     a.tail_from = -1;
     const unsigned items = (unsigned)((long long)nseq * nheads);
     if (dstate == 128)
-        ssd_fused_kernel<128, false><<<items, kThreads, 0, stream>>>(a);
+        ssd_prefill_kernel<128><<<items, kThreads, 0, stream>>>(a);
     else
-        ssd_fused_kernel<64, false><<<items, kThreads, 0, stream>>>(a);
+        ssd_prefill_kernel<64><<<items, kThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 
