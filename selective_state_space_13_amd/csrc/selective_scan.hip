@@ -17,10 +17,17 @@
 // output pass (MODE 1) runs every segment from that state.  The recurrence is
 // linear in the state, so this is the same computation regrouped.
 // Time is processed in tiles of kT steps: while a tile is computed, the next
-// tile's u/delta/z are already in flight into registers, and its B_t/C_t rows
-// (the same for the whole workgroup) are staged once in LDS as float32.
+// tile's u/delta/z are already in flight into a second set of registers.
+// B_t and C_t are the same for every lane of the workgroup: they are read as
+// dwords through the scalar cache into SGPRs, one step ahead, and feed the
+// vector ALU as scalar operands (no LDS staging, no barrier).  Every per-lane
+// load is unconditional and lands in a register of its own (bf16 values are
+// widened at their use), because a combine or a branch right after a load
+// would wait there for all loads in flight, the prefetch included.
 // exp(Δ·A) is exp2(Δ·(A·log2 e)) with the scaled A in registers: one multiply
-// and one v_exp_f32 per state element and step.
+// and one v_exp_f32 per state element and step; v_exp_f32 issues at about a
+// quarter of the FMA rate, so the 16 exponentials per step and lane bound the
+// kernel.
 #include "ssd_kernels.h"
 
 namespace ssd {
@@ -28,7 +35,7 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kT = 16;  // time steps per tile
+constexpr int kT = 8;  // time steps per tile
 
 // log(1 + e^r) to a few ulps: log1p via log(u)·e/(u - 1) with u = 1 + e
 // (exact where u rounds to 1), e = e^-|r|.
@@ -41,6 +48,54 @@ __device__ __forceinline__ float softplus_fast(float r) {
 
 template <typename T>
 __device__ __forceinline__ float ldf(const T *p) { return to_f32(*p); }
+
+// Per-lane u, Δ, z of kT consecutive steps (bf16: raw bits, widened on use).
+template <typename T>
+struct StepTile {
+    float u[kT], r[kT], z[kT];
+    __device__ __forceinline__ void load(const T *up, const T *rp, const T *zp, size_t base, size_t stride, int nvalid) {
+#pragma unroll
+        for (int tt = 0; tt < kT; ++tt) {
+            const size_t idx = base + (size_t)(tt < nvalid ? tt : 0) * stride;
+            u[tt] = ldf(up + idx);
+            r[tt] = ldf(rp + idx);
+            z[tt] = ldf(zp + idx);
+        }
+    }
+    __device__ __forceinline__ float gu(int tt) const { return u[tt]; }
+    __device__ __forceinline__ float gr(int tt) const { return r[tt]; }
+    __device__ __forceinline__ float gz(int tt) const { return z[tt]; }
+};
+template <>
+struct StepTile<bf16_t> {
+    uint32_t u[kT], r[kT], z[kT];  // one 16-bit load per register
+    __device__ __forceinline__ void load(const bf16_t *up, const bf16_t *rp, const bf16_t *zp, size_t base, size_t stride, int nvalid) {
+#pragma unroll
+        for (int tt = 0; tt < kT; ++tt) {
+            const size_t idx = base + (size_t)(tt < nvalid ? tt : 0) * stride;
+            u[tt] = up[idx].bits;
+            r[tt] = rp[idx].bits;
+            z[tt] = zp[idx].bits;
+        }
+    }
+    __device__ __forceinline__ float gu(int tt) const { return __uint_as_float(u[tt] << 16); }
+    __device__ __forceinline__ float gr(int tt) const { return __uint_as_float(r[tt] << 16); }
+    __device__ __forceinline__ float gz(int tt) const { return __uint_as_float(z[tt] << 16); }
+};
+
+// B_t, C_t of one step: the same for every lane, read as dwords (through the
+// scalar cache) one step ahead of their use.
+template <typename T, int N>
+struct StepRows {
+    static constexpr int W = (int)sizeof(T) * N / 4;
+    uint32_t b[W], c[W];
+    __device__ __forceinline__ float gb(int n) const { return get(b, n); }
+    __device__ __forceinline__ float gc(int n) const { return get(c, n); }
+    static __device__ __forceinline__ float get(const uint32_t *w, int n) {
+        if (sizeof(T) == 2) return (n & 1) ? bf16hi(w[n >> 1]) : bf16lo(w[n >> 1]);
+        return __uint_as_float(w[n]);
+    }
+};
 
 struct ScanArgs {
     int delta_softplus, seqlen, dim;
@@ -55,7 +110,7 @@ __global__ __launch_bounds__(256) void selective_scan_kernel(
     const T *__restrict__ u, const T *__restrict__ delta, const float *__restrict__ A,
     const T *__restrict__ B, const T *__restrict__ C, const float *__restrict__ D,
     const T *__restrict__ z, ScanArgs sa, T *__restrict__ out, float *__restrict__ final_state) {
-    __shared__ float bc[2][kT][2 * N];  // double-buffered B_t, C_t rows of a tile
+    constexpr int W = StepRows<T, N>::W;
     const int delta_softplus = sa.delta_softplus, seqlen = sa.seqlen, dim = sa.dim;
 
     const int d = blockIdx.x * blockDim.x + threadIdx.x;
@@ -74,76 +129,73 @@ __global__ __launch_bounds__(256) void selective_scan_kernel(
     const float Dd = D ? D[dd] : 0.0f;
     const int tbeg = seg * sa.seg_len;
     const int tend = min(seqlen, tbeg + sa.seg_len);
+    const int len = tend - tbeg;
     const size_t row0 = (size_t)b * seqlen + tbeg;  // first row of this segment
-    const int ntiles = tend > tbeg ? (tend - tbeg + kT - 1) / kT : 0;
+    const int ntiles = len > 0 ? (len + kT - 1) / kT : 0;
+    const uint32_t *Bw = reinterpret_cast<const uint32_t *>(B) + row0 * W;
+    const uint32_t *Cw = reinterpret_cast<const uint32_t *>(C) + row0 * W;
     float dsum = 0.0f;
 
-    // stage B/C of tile k into bc[k & 1]
-    auto stage_bc = [&](int k) {
-        for (int e = threadIdx.x; e < kT * 2 * N; e += blockDim.x) {
-            const int tt = e / (2 * N), j = e % (2 * N);
-            const int t = k * kT + tt;
-            float v = 0.0f;
-            if (tbeg + t < tend) v = j < N ? ldf(B + (row0 + t) * N + j) : ldf(C + (row0 + t) * N + (j - N));
-            bc[k & 1][tt][j] = v;
+    StepRows<T, N> cur;
+    auto load_rows = [&](StepRows<T, N> &R, int t) {
+#pragma unroll
+        for (int j = 0; j < W; ++j) {
+            R.b[j] = Bw[(size_t)t * W + j];
+            if (MODE == 1) R.c[j] = Cw[(size_t)t * W + j];
         }
     };
-    float uv[kT], rv[kT], zv[kT];
-    auto load_tile = [&](int k) {
-#pragma unroll
-        for (int tt = 0; tt < kT; ++tt) {
-            const int t = k * kT + tt;
-            const bool in = tbeg + t < tend;
-            const size_t idx = (row0 + (in ? t : 0)) * dim + dd;
-            uv[tt] = ldf(u + idx);
-            rv[tt] = ldf(delta + idx);
-            zv[tt] = z ? ldf(z + idx) : 0.0f;
-        }
+    // z is read unconditionally (u stands in when there is no gate): a load under a
+    // branch would make the join wait for every load in flight, the prefetch included
+    const T *zsrc = z ? z : u;
+    auto load_tile = [&](StepTile<T> &tl, int k) {
+        tl.load(u, delta, zsrc, (row0 + (size_t)k * kT) * dim + dd, (size_t)dim, len - k * kT);
     };
-
-    if (ntiles > 0) {
-        stage_bc(0);
-        load_tile(0);
-    }
-    for (int k = 0; k < ntiles; ++k) {
-        float cu[kT], cr[kT], cz[kT];
-#pragma unroll
-        for (int tt = 0; tt < kT; ++tt) {
-            cu[tt] = uv[tt];
-            cr[tt] = rv[tt];
-            cz[tt] = zv[tt];
-        }
-        __syncthreads();  // bc[k & 1] staged; bc[(k+1) & 1] free
-        if (k + 1 < ntiles) {
-            stage_bc(k + 1);
-            load_tile(k + 1);
-        }
-        const int nt = min(kT, tend - tbeg - k * kT);
+    auto run_tile = [&](const StepTile<T> &tl, int k) {
+        const int nt = min(kT, len - k * kT);
 #pragma unroll
         for (int tt = 0; tt < kT; ++tt) {
             if (tt < nt) {
-                const float dl = delta_softplus ? softplus_fast(cr[tt]) : cr[tt];
-                const float du = dl * cu[tt];
-                const float *bt = bc[k & 1][tt];
+                const int t = k * kT + tt;
+                StepRows<T, N> nxt;
+                load_rows(nxt, min(t + 1, len - 1));
+                const float dl = delta_softplus ? softplus_fast(tl.gr(tt)) : tl.gr(tt);
+                const float du = dl * tl.gu(tt);
                 if (MODE == 0) {
                     dsum += dl;
 #pragma unroll
-                    for (int n = 0; n < N; ++n) s[n] = __builtin_amdgcn_exp2f(dl * A2[n]) * s[n] + du * bt[n];
+                    for (int n = 0; n < N; ++n) s[n] = __builtin_amdgcn_exp2f(dl * A2[n]) * s[n] + du * cur.gb(n);
                 } else {
-                    float yv = Dd * cu[tt];
+                    float yp[4] = {Dd * tl.gu(tt), 0.0f, 0.0f, 0.0f};
 #pragma unroll
                     for (int n = 0; n < N; ++n) {
                         const float dA = __builtin_amdgcn_exp2f(dl * A2[n]);
-                        s[n] = dA * s[n] + du * bt[n];
-                        yv += bt[N + n] * s[n];
+                        s[n] = dA * s[n] + du * cur.gb(n);
+                        yp[n & 3] += cur.gc(n) * s[n];
                     }
+                    float yv = (yp[0] + yp[1]) + (yp[2] + yp[3]);
                     if (z) {
-                        const float zz = cz[tt];
+                        const float zz = tl.gz(tt);
                         yv *= zz * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zz * kLog2e));
                     }
-                    if (active) store_out(out + (row0 + k * kT + tt) * dim + d, yv);
+                    if (active) store_out(out + (row0 + t) * dim + d, yv);
                 }
+                cur = nxt;
             }
+        }
+    };
+
+    StepTile<T> ta, tb;
+    if (ntiles > 0) {
+        load_rows(cur, 0);
+        load_tile(ta, 0);
+    }
+    // two register sets: tile k+1 loads while tile k runs
+    for (int k = 0; k < ntiles; k += 2) {
+        if (k + 1 < ntiles) load_tile(tb, k + 1);
+        run_tile(ta, k);
+        if (k + 1 < ntiles) {
+            if (k + 2 < ntiles) load_tile(ta, k + 2);
+            run_tile(tb, k + 1);
         }
     }
     if (!active) return;
