@@ -339,9 +339,13 @@ __device__ __forceinline__ void fused_roles_walk(const FusedArgs &a, unsigned bl
                     *reinterpret_cast<uint4 *>(a.y + (row0 + t) * xstride + (size_t)h * P + 32 * pt + cq) = v;
             }
         } else if (c + 1 < c1) {
+            // the staging waves go first while they stage (wave priority within the
+            // SIMD): the next chunk's phase A waits on all of it
+            __builtin_amdgcn_s_setprio(2);
             stage(c + 1);
             load_dt(min(c + 2, c1 - 1));
             prefetch(min(c + 2, c1 - 1));
+            __builtin_amdgcn_s_setprio(0);
         }
         __syncthreads();
     }
