@@ -418,6 +418,19 @@ def main():
         log(f"[bench] copy calibration: 3 device copies of {nbytes} bytes")
         del src, dst
 
+    # practical reference for the HBM fractions: a device copy of 1 GiB (read + write bytes)
+    src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_tbs = 2 * 5 * src.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del src, dst
+
     legs = [] if args.legs == "none" else [s for s in args.legs.split(",") if s]
     cfg = configs.MAMBA2_LAYER_PREFILL
     workload = f"{cfg['name']}:b{cfg['batch']}L{cfg['seqlen']}H{cfg['nheads']}P{cfg['headdim']}" \
@@ -454,6 +467,9 @@ def main():
                           "mfma_frac": round(total_work["flops"] / t_step / MFMA_BF16_PEAK, 4),
                           "alg_bytes": total_work["bytes"], "alg_flops": total_work["flops"]},
         "per_kernel_ms": {k: round(v, 5) for k, v in per.items()},
+        "hbm_copy_reference": {"value": round(copy_tbs, 3), "unit": "TB/s",
+                               "what": "torch device copy of a 1 GiB buffer, read + write bytes, 5 copies; "
+                                       "context for the HBM fractions, which are against the 8 TB/s peak"},
     }
     del pf
     extra = {}
