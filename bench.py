@@ -209,7 +209,7 @@ def roofline_entry(kernel, ms, work, workload, digest):
             "avg_launch_ms": round(ms, 5)}
 
 
-def bench_decode(steps, warmup, prefill_state):
+def bench_decode(steps, warmup, prefill_state, bf16_state=False):
     import torch
     import selective_state_space_13_amd as ssd
     from workloads import configs, gen
@@ -217,6 +217,8 @@ def bench_decode(steps, warmup, prefill_state):
     c2 = configs.MAMBA2_LAYER_PREFILL
     reps = c["batch"] // c2["batch"]
     state = prefill_state.repeat(reps, 1, 1, 1).contiguous()  # state cache of the 2.7B-layer prefill
+    if bf16_state:
+        state = state.to(torch.bfloat16)
     A, D = (to_dev(t) for t in gen.ssd_params(c["nheads"], config_id=c2["id"]))
     log("[bench] decode: generating per-step inputs")
     steps_in = []
@@ -226,14 +228,15 @@ def bench_decode(steps, warmup, prefill_state):
         steps_in.append(tuple(to_dev(s[n]) for n in ("x", "dt", "B", "C")))
     y = torch.empty_like(steps_in[0][0])
     it = [0]
+    step_fn = ssd.ssd_decode_step_bf16_state if bf16_state else ssd.ssd_decode_step
 
     def one():
         x, dt, B, C = steps_in[it[0] % len(steps_in)]
         it[0] += 1
-        ssd.ssd_decode_step(x, dt, A, B, C, D, state, out=y)
+        step_fn(x, dt, A, B, C, D, state, out=y)
 
     ms, per = time_calls(one, 1, c["steps"], warmup)
-    state_bytes = c["batch"] * c["nheads"] * c["dstate"] * c["headdim"] * 4
+    state_bytes = c["batch"] * c["nheads"] * c["dstate"] * c["headdim"] * (2 if bf16_state else 4)
     io = c["batch"] * (c["nheads"] * c["headdim"] * 2 * 2 + c["nheads"] * 2 + 2 * c["ngroups"] * c["dstate"] * 2)
     return dict(ms=ms, kernel_ms=per[0], tokens=c["batch"], bytes=2 * state_bytes + io,
                 flops=c["batch"] * c["nheads"] * c["dstate"] * c["headdim"] * 5)
@@ -482,14 +485,16 @@ def main():
         del d
         _, fs8 = ssd.ssd_chunk_scan(x, dt, A, B, C, D, chunk=cfg["chunk"], return_final_state=True)
         del x, dt, B, C
-        dec = bench_decode(args.steps, args.warmup, fs8)
-        t = dec["kernel_ms"] * 1e-3
-        extra["decode"] = {"workload": "decode_state_cache:b256H80P64N128G1, 64 single-token steps",
-                           "tokens_per_s": round(dec["tokens"] / (dec["ms"] * 1e-3), 1),
-                           "ms_per_step": round(dec["ms"], 5), "kernel_ms": round(dec["kernel_ms"], 5),
-                           "roofline": {"bound": "hbm", "achieved": round(dec["bytes"] / t / 1e9, 2),
-                                        "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                                        "frac": round(dec["bytes"] / t / HBM_PEAK, 4)}}
+        for key, lp in (("decode", False), ("decode_bf16_state", True)):
+            dec = bench_decode(args.steps, args.warmup, fs8, bf16_state=lp)
+            t = dec["kernel_ms"] * 1e-3
+            extra[key] = {"workload": "decode_state_cache:b256H80P64N128G1, 64 single-token steps, "
+                                      + ("bf16" if lp else "float32") + " state cache",
+                          "tokens_per_s": round(dec["tokens"] / (dec["ms"] * 1e-3), 1),
+                          "ms_per_step": round(dec["ms"], 5), "kernel_ms": round(dec["kernel_ms"], 5),
+                          "roofline": {"bound": "hbm", "achieved": round(dec["bytes"] / t / 1e9, 2),
+                                       "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                                       "frac": round(dec["bytes"] / t / HBM_PEAK, 4)}}
     if "long" in legs:
         c3 = configs.LONG_CONTEXT_PREFILL
         lp = bench_prefill(c3, max(3, args.steps // 4), 2)

@@ -252,6 +252,25 @@ int ssd_decode_step(int batch, int nheads, int headdim, int dstate, int ngroups,
                     void *stream);
 
 /* ------------------------------------------------------------------------
+ * The same decode step against a bf16 state cache: half the state bytes,
+ * which are nearly all of the step's memory traffic (reduced precision as in
+ * [TP] §5.1, applied to the stored state).  Arguments and layouts are those of
+ * ssd_decode_step except
+ *
+ *   state  [batch][nheads][dstate][headdim] bf16 (16-bit patterns), read and
+ *          overwritten in place
+ *
+ * Each state value is widened to float32, updated in float32, and summed into
+ * y before rounding; the new state is stored rounded to the nearest bf16, ties
+ * to even.  Supported shapes, alignment (16 bytes), aliasing rules and error
+ * codes are those of ssd_decode_step.
+ * ------------------------------------------------------------------------ */
+int ssd_decode_step_bf16_state(int batch, int nheads, int headdim, int dstate, int ngroups,
+                               int dtype, int dt_softplus, const void *x, const void *dt,
+                               const float *A, const void *B, const void *C, const float *D,
+                               void *state, void *y, void *stream);
+
+/* ------------------------------------------------------------------------
  * Mamba-1 selective scan with a diagonal state matrix per channel ([TP] §2.1).
  * For batch row b and channel d, state s[n] (zero at t = 0):
  *     Δ = softplus(delta) if delta_softplus, else delta

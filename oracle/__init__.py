@@ -8,6 +8,9 @@ links or calls it, and the two share no code.
   recurrences in ``ssd_oracle.c`` (the definition of what the scan computes).
 * ``forms``: independent numpy float64 formulations used to pin the sequential
   oracle -- the quadratic "dual" form and the chunked block decomposition.
+* ``round_bf16``, ``ssd_decode_bf16_state``: the decode step against a bf16
+  state cache -- the float64 step of ``ssd_decode`` on the stored values, the
+  new state then rounded to the nearest bf16 (ties to even).
 
 Parity status: every function is pinned by the CPU tests in
 ``tests/test_oracle_pins.py`` (closed forms, the dual form, the block
@@ -169,6 +172,28 @@ def ssd_decode(x, dt, A, B, C, D, state, dt_softplus=True):
                           _ptr(B), _ptr(C), _ptr(D), _ptr(st), _ptr(y))
     last_seconds = time.perf_counter() - t0
     return y, st
+
+
+def round_bf16(v):
+    """Each value rounded to the nearest bfloat16 (8 significant bits, the
+    float32 exponent range), ties to even; returned as float64.  Magnitudes
+    below the smallest normal bfloat16 keep 8 significant bits (a flush or
+    gradual underflow there is far below any tolerance used with this)."""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)                      # v = m·2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.round(m * 256.0) / 256.0, e)   # np.round: half to even
+
+
+def ssd_decode_bf16_state(x, dt, A, B, C, D, state, dt_softplus=True):
+    """One decode step against a bf16 state cache (reduced precision applied to
+    the stored state; page "5.3 텐서 병렬화(Tensor Parallelism) 지원과 대규모
+    클러스터 학습", §5.1, on low-precision arithmetic for SSD).  ``state`` holds
+    the cached values (bf16-representable).  The step itself is the float64 step
+    of ``ssd_decode`` (single step of §2.1 with the decay of §3.1); y uses the
+    updated state before rounding; the returned state is that updated state
+    rounded to the nearest bf16, ties to even.  Returns (y, new_state)."""
+    y, st = ssd_decode(x, dt, A, B, C, D, state, dt_softplus)
+    return y, round_bf16(st)
 
 
 def selective_scan(u, delta, A, B, C, D=None, z=None, delta_softplus=True,

@@ -11,6 +11,8 @@ Functions (names as in the C ABI):
     ssd_chunk_scan(x, dt, A, B, C, D=None, *, chunk, initial_state=None,
                    return_final_state=False, dt_softplus=True)  -> y | (y, final_state)
     ssd_decode_step(x, dt, A, B, C, D, state, *, dt_softplus=True) -> y  (state updated)
+    ssd_decode_step_bf16_state(x, dt, A, B, C, D, state, *, dt_softplus=True) -> y
+                   (bf16 state cache, updated in place)
     selective_scan(u, delta, A, B, C, D=None, z=None, *, delta_softplus=True,
                    return_final_state=False) -> out | (out, final_state)
 """
@@ -74,6 +76,8 @@ def lib() -> ctypes.CDLL:
     L.ssd_gated_rmsnorm_fwd.restype = i
     L.ssd_decode_step.argtypes = [i] * 7 + [vp] * 9
     L.ssd_decode_step.restype = i
+    L.ssd_decode_step_bf16_state.argtypes = [i] * 7 + [vp] * 9
+    L.ssd_decode_step_bf16_state.restype = i
     L.selective_scan_workspace_size.argtypes = [i] * 5
     L.selective_scan_workspace_size.restype = sz
     L.selective_scan_fwd.argtypes = [i] * 6 + [vp] * 10 + [sz, vp]
@@ -342,9 +346,7 @@ def gated_rmsnorm(y, z, weight, *, ngroups=1, eps=1e-5, out=None):
     return o
 
 
-def ssd_decode_step(x, dt, A, B, C, D, state, *, dt_softplus=True, out=None):
-    """One decode step.  x [b,H,P], dt [b,H], A [H], B, C [b,G,N], D [H] or None,
-    state [b,H,N,P] fp32 (updated in place).  Returns y [b,H,P]."""
+def _decode(fn, state_dtype, x, dt, A, B, C, D, state, dt_softplus, out):
     torch = _torch()
     x = _req(x, "x")
     dev = x.device
@@ -355,7 +357,7 @@ def ssd_decode_step(x, dt, A, B, C, D, state, *, dt_softplus=True, out=None):
     _req(C, "C", x.dtype, dev)
     _req(A, "A", torch.float32, dev)
     _req(D, "D", torch.float32, dev)
-    _req(state, "state", torch.float32, dev)
+    _req(state, "state", state_dtype, dev)
     G, N = B.shape[1], B.shape[2]
     if tuple(dt.shape) != (b, H) or tuple(B.shape) != (b, G, N) or C.shape != B.shape:
         raise ValueError("shape mismatch among x, dt, B, C")
@@ -363,10 +365,22 @@ def ssd_decode_step(x, dt, A, B, C, D, state, *, dt_softplus=True, out=None):
         raise ValueError("state must be [batch, nheads, dstate, headdim]")
     y = out if out is not None else torch.empty_like(x)
     _req(y, "out", x.dtype, dev)
-    check(lib().ssd_decode_step(b, H, P, N, G, code, int(bool(dt_softplus)), _ptr(x), _ptr(dt),
-                                _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(state), _ptr(y),
-                                _stream(dev)))
+    check(fn(b, H, P, N, G, code, int(bool(dt_softplus)), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+             _ptr(C), _ptr(D), _ptr(state), _ptr(y), _stream(dev)))
     return y
+
+
+def ssd_decode_step(x, dt, A, B, C, D, state, *, dt_softplus=True, out=None):
+    """One decode step.  x [b,H,P], dt [b,H], A [H], B, C [b,G,N], D [H] or None,
+    state [b,H,N,P] fp32 (updated in place).  Returns y [b,H,P]."""
+    return _decode(lib().ssd_decode_step, _torch().float32, x, dt, A, B, C, D, state, dt_softplus, out)
+
+
+def ssd_decode_step_bf16_state(x, dt, A, B, C, D, state, *, dt_softplus=True, out=None):
+    """One decode step against a bf16 state cache: as ssd_decode_step, with
+    state [b,H,N,P] bfloat16 (updated in place, rounded to nearest even)."""
+    return _decode(lib().ssd_decode_step_bf16_state, _torch().bfloat16, x, dt, A, B, C, D, state,
+                   dt_softplus, out)
 
 
 def selective_scan(u, delta, A, B, C, D=None, z=None, *, delta_softplus=True,

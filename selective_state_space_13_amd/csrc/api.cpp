@@ -158,6 +158,47 @@ int scan_layout(int batch, int seqlen, int nheads, int headdim, int dstate, int 
     return SSD_OK;
 }
 
+// Shared by the float32 and bf16 state caches: validation, then one launch.
+int decode_step(int batch, int nheads, int headdim, int dstate, int ngroups, int dtype,
+                int dt_softplus, const void *x, const void *dt, const float *A, const void *B,
+                const void *C, const float *D, void *state, int state_bf16, void *y, void *stream_) {
+    if (dtype != SSD_F32 && dtype != SSD_BF16)
+        return fail(SSD_ERR_UNSUPPORTED, "dtype %d is not SSD_F32 or SSD_BF16", dtype);
+    if (batch < 0) return fail(SSD_ERR_SHAPE, "batch (%d) must be >= 0", batch);
+    if (nheads < 1 || headdim < 1 || dstate < 1 || ngroups < 1)
+        return fail(SSD_ERR_SHAPE, "nheads, headdim, dstate and ngroups must be >= 1");
+    if (nheads % ngroups)
+        return fail(SSD_ERR_SHAPE, "ngroups (%d) must divide nheads (%d)", ngroups, nheads);
+    if (headdim != 64) return fail(SSD_ERR_UNSUPPORTED, "headdim %d: only 64 is supported", headdim);
+    if (dstate % 32 || dstate > 256)
+        return fail(SSD_ERR_UNSUPPORTED, "dstate %d: a multiple of 32 up to 256 is required", dstate);
+    uint64_t n_x, n_state, n_bc;
+    if (!prod(n_state, {batch, nheads, dstate, headdim}) || (long long)batch * nheads > (1ll << 31) - 4)
+        return fail(SSD_ERR_SHAPE, "tensor sizes overflow");
+    prod(n_x, {batch, nheads, headdim});
+    prod(n_bc, {batch, ngroups, dstate});
+    if (batch == 0) return SSD_OK;
+    if (!x || !dt || !A || !B || !C || !state || !y)
+        return fail(SSD_ERR_NULL, "x, dt, A, B, C, state and y are required");
+    const void *ptrs[] = {x, dt, A, B, C, D, state, y};
+    for (const void *p : ptrs)
+        if (p && !aligned(p, 16)) return fail(SSD_ERR_ALIGN, "tensor pointer %p is not 16-byte aligned", p);
+    const int es = elem_size(dtype);
+    int st = check_alias(
+        {span("state", state, n_state * (state_bf16 ? 2 : 4)), span("y", y, n_x * es)},
+        {span("x", x, n_x * es), span("dt", dt, (uint64_t)batch * nheads * es),
+         span("A", A, (uint64_t)nheads * 4), span("B", B, n_bc * es), span("C", C, n_bc * es),
+         span("D", D, D ? (uint64_t)nheads * 4 : 0)});
+    if (st) return st;
+    LaunchMarks marks(static_cast<hipStream_t>(stream_));
+    marks.before();
+    hipError_t e = ssd::launch_decode_step(dtype, state_bf16, x, dt, A, B, C, D, dt_softplus, batch,
+                                           nheads, headdim, dstate, ngroups, state, y,
+                                           static_cast<hipStream_t>(stream_));
+    marks.after();
+    return e == hipSuccess ? SSD_OK : hip_fail(e, "decode launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -448,41 +489,16 @@ int ssd_chunk_scan_varlen_fwd(int nseq, int total_tokens, int nheads, int headdi
 int ssd_decode_step(int batch, int nheads, int headdim, int dstate, int ngroups, int dtype,
                     int dt_softplus, const void *x, const void *dt, const float *A, const void *B,
                     const void *C, const float *D, float *state, void *y, void *stream_) {
-    if (dtype != SSD_F32 && dtype != SSD_BF16)
-        return fail(SSD_ERR_UNSUPPORTED, "dtype %d is not SSD_F32 or SSD_BF16", dtype);
-    if (batch < 0) return fail(SSD_ERR_SHAPE, "batch (%d) must be >= 0", batch);
-    if (nheads < 1 || headdim < 1 || dstate < 1 || ngroups < 1)
-        return fail(SSD_ERR_SHAPE, "nheads, headdim, dstate and ngroups must be >= 1");
-    if (nheads % ngroups)
-        return fail(SSD_ERR_SHAPE, "ngroups (%d) must divide nheads (%d)", ngroups, nheads);
-    if (headdim != 64) return fail(SSD_ERR_UNSUPPORTED, "headdim %d: only 64 is supported", headdim);
-    if (dstate % 32 || dstate > 256)
-        return fail(SSD_ERR_UNSUPPORTED, "dstate %d: a multiple of 32 up to 256 is required", dstate);
-    uint64_t n_x, n_state, n_bc;
-    if (!prod(n_state, {batch, nheads, dstate, headdim}) || (long long)batch * nheads > (1ll << 31) - 4)
-        return fail(SSD_ERR_SHAPE, "tensor sizes overflow");
-    prod(n_x, {batch, nheads, headdim});
-    prod(n_bc, {batch, ngroups, dstate});
-    if (batch == 0) return SSD_OK;
-    if (!x || !dt || !A || !B || !C || !state || !y)
-        return fail(SSD_ERR_NULL, "x, dt, A, B, C, state and y are required");
-    const void *ptrs[] = {x, dt, A, B, C, D, state, y};
-    for (const void *p : ptrs)
-        if (p && !aligned(p, 16)) return fail(SSD_ERR_ALIGN, "tensor pointer %p is not 16-byte aligned", p);
-    const int es = elem_size(dtype);
-    int st = check_alias(
-        {span("state", state, n_state * 4), span("y", y, n_x * es)},
-        {span("x", x, n_x * es), span("dt", dt, (uint64_t)batch * nheads * es),
-         span("A", A, (uint64_t)nheads * 4), span("B", B, n_bc * es), span("C", C, n_bc * es),
-         span("D", D, D ? (uint64_t)nheads * 4 : 0)});
-    if (st) return st;
-    LaunchMarks marks(static_cast<hipStream_t>(stream_));
-    marks.before();
-    hipError_t e = ssd::launch_decode_step(dtype, x, dt, A, B, C, D, dt_softplus, batch, nheads,
-                                           headdim, dstate, ngroups, state, y,
-                                           static_cast<hipStream_t>(stream_));
-    marks.after();
-    return e == hipSuccess ? SSD_OK : hip_fail(e, "decode launch");
+    return decode_step(batch, nheads, headdim, dstate, ngroups, dtype, dt_softplus, x, dt, A, B, C,
+                       D, state, 0, y, stream_);
+}
+
+int ssd_decode_step_bf16_state(int batch, int nheads, int headdim, int dstate, int ngroups,
+                               int dtype, int dt_softplus, const void *x, const void *dt,
+                               const float *A, const void *B, const void *C, const float *D,
+                               void *state, void *y, void *stream_) {
+    return decode_step(batch, nheads, headdim, dstate, ngroups, dtype, dt_softplus, x, dt, A, B, C,
+                       D, state, 1, y, stream_);
 }
 
 size_t selective_scan_workspace_size(int batch, int seqlen, int dim, int dstate, int dtype) {

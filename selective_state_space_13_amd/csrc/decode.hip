@@ -1,4 +1,4 @@
-// One decode step against a cached float32 state.
+// One decode step against a cached state, float32 or bf16.
 //
 // The state cache carried from prefill into decode (page "Scaling State-Space
 // Models on Multiple GPUs with Tensor Parallelism", Abstract) advanced by the
@@ -16,6 +16,15 @@
 // stores of one lane never touch the same row twice, so nothing serialises
 // them); state traffic is non-temporal, it is not reused.  The four partial y
 // sums are combined with two cross-lane shuffles.
+//
+// The bf16 state cache halves the state bytes, which are nearly all of the
+// traffic: the reduced-precision direction of page "5.3 텐서 병렬화(Tensor
+// Parallelism) 지원과 대규모 클러스터 학습", §5.1 (low-precision tensor-core
+// arithmetic as a lever for SSD), applied to the stored state.  The state is widened to float32 at its use, updated and summed
+// into y in float32 (y sees the updated state before rounding), and stored
+// rounded to the nearest bf16, ties to even.  Its raw 8-byte rows stay raw in
+// the prefetch registers until their use: widening them right after the loads
+// would make the compiler wait for the loads there.
 #include "ssd_kernels.h"
 
 namespace ssd {
@@ -67,20 +76,44 @@ __device__ __forceinline__ void load_vals<bf16_t>(const bf16_t *p, float *v, int
 constexpr int kGroup = 8;  // state rows per lane in flight per step of the pipeline
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ float4 nt_load(const float4 *p) {
-    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
-    return make_float4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ void nt_store(float4 s, float4 *p) {
-    const f32x4_t v = {s.x, s.y, s.z, s.w};
-    __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t *>(p));
-}
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
-template <typename T, int N>
+// Non-temporal access to one lane's 4 consecutive state values of a row.
+template <typename S>
+struct StateIO;
+template <>
+struct StateIO<float> {
+    typedef f32x4_t Raw;
+    static __device__ __forceinline__ Raw load(const float *p) {
+        return __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
+    }
+    static __device__ __forceinline__ float4 widen(Raw v) { return make_float4(v.x, v.y, v.z, v.w); }
+    static __device__ __forceinline__ void store(float *p, float4 s) {
+        const f32x4_t v = {s.x, s.y, s.z, s.w};
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t *>(p));
+    }
+};
+template <>
+struct StateIO<bf16_t> {
+    typedef u32x2_t Raw;
+    static __device__ __forceinline__ Raw load(const bf16_t *p) {
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+    }
+    static __device__ __forceinline__ float4 widen(Raw v) {
+        return make_float4(bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y));
+    }
+    static __device__ __forceinline__ void store(bf16_t *p, float4 s) {
+        const u32x2_t v = {pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w)};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t *>(p));
+    }
+};
+
+template <typename T, typename S, int N>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const T *__restrict__ x, const T *__restrict__ dt, const float *__restrict__ A,
     const T *__restrict__ B, const T *__restrict__ C, const float *__restrict__ D, int dt_softplus,
-    int nbh, int nheads, int ngroups, float *__restrict__ state, T *__restrict__ y) {
+    int nbh, int nheads, int ngroups, S *__restrict__ state, T *__restrict__ y) {
+    typedef StateIO<S> IO;
     constexpr int RPL = N / 4;  // rows per lane
     constexpr int NG = RPL / kGroup;
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -99,29 +132,29 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     float bn[RPL], cn[RPL];
     load_vals<T>(B + ((size_t)b * ngroups + g) * N + n0, bn, RPL);
     load_vals<T>(C + ((size_t)b * ngroups + g) * N + n0, cn, RPL);
-    float4 *st = reinterpret_cast<float4 *>(state + (size_t)bh * N * P) + (size_t)n0 * (P / 4) + q;
+    S *st = state + (size_t)bh * N * P + (size_t)n0 * P + 4 * q;  // row r of this lane at st + r·P
 
-    float4 cur[kGroup], nxt[kGroup];
+    typename IO::Raw cur[kGroup], nxt[kGroup];
 #pragma unroll
-    for (int k = 0; k < kGroup; ++k) cur[k] = nt_load(st + k * (P / 4));
+    for (int k = 0; k < kGroup; ++k) cur[k] = IO::load(st + k * P);
     float4 yacc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
         if (gi + 1 < NG) {
 #pragma unroll
             for (int k = 0; k < kGroup; ++k)
-                nxt[k] = nt_load(st + ((gi + 1) * kGroup + k) * (P / 4));
+                nxt[k] = IO::load(st + ((gi + 1) * kGroup + k) * P);
         }
 #pragma unroll
         for (int k = 0; k < kGroup; ++k) {
             const int row = gi * kGroup + k;
             const float bd = d * bn[row], cc = cn[row];
-            float4 s = cur[k];
+            float4 s = IO::widen(cur[k]);
             s.x = a * s.x + bd * xv.x;
             s.y = a * s.y + bd * xv.y;
             s.z = a * s.z + bd * xv.z;
             s.w = a * s.w + bd * xv.w;
-            nt_store(s, st + row * (P / 4));
+            IO::store(st + row * P, s);
             yacc.x += cc * s.x;
             yacc.y += cc * s.y;
             yacc.z += cc * s.z;
@@ -149,23 +182,24 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     }
 }
 
-template <typename T, int N>
+template <typename T, typename S, int N>
 void launch_n(unsigned blocks, hipStream_t stream, const void *x, const void *dt, const float *A,
               const void *B, const void *C, const float *D, int dt_softplus, int nbh, int nheads,
-              int ngroups, float *state, void *y) {
-    decode_step_kernel<T, N><<<dim3(blocks), dim3(256), 0, stream>>>(
+              int ngroups, void *state, void *y) {
+    decode_step_kernel<T, S, N><<<dim3(blocks), dim3(256), 0, stream>>>(
         static_cast<const T *>(x), static_cast<const T *>(dt), A, static_cast<const T *>(B),
-        static_cast<const T *>(C), D, dt_softplus, nbh, nheads, ngroups, state, static_cast<T *>(y));
+        static_cast<const T *>(C), D, dt_softplus, nbh, nheads, ngroups, static_cast<S *>(state),
+        static_cast<T *>(y));
 }
 
-template <typename T>
+template <typename T, typename S>
 hipError_t launch_t(int dstate, unsigned blocks, hipStream_t stream, const void *x, const void *dt,
                     const float *A, const void *B, const void *C, const float *D, int dt_softplus,
-                    int nbh, int nheads, int ngroups, float *state, void *y) {
+                    int nbh, int nheads, int ngroups, void *state, void *y) {
     switch (dstate) {
 #define SSD_DEC(NN)                                                                                  \
     case NN:                                                                                         \
-        launch_n<T, NN>(blocks, stream, x, dt, A, B, C, D, dt_softplus, nbh, nheads, ngroups, state, y); \
+        launch_n<T, S, NN>(blocks, stream, x, dt, A, B, C, D, dt_softplus, nbh, nheads, ngroups, state, y); \
         break;
         SSD_DEC(32)
         SSD_DEC(64)
@@ -184,19 +218,20 @@ hipError_t launch_t(int dstate, unsigned blocks, hipStream_t stream, const void 
 
 }  // namespace
 
-hipError_t launch_decode_step(int dtype, const void *x, const void *dt, const float *A,
+hipError_t launch_decode_step(int dtype, int state_bf16, const void *x, const void *dt, const float *A,
                               const void *B, const void *C, const float *D, int dt_softplus,
                               int batch, int nheads, int headdim, int dstate, int ngroups,
-                              float *state, void *y, hipStream_t stream) {
+                              void *state, void *y, hipStream_t stream) {
     if (headdim != P || dstate % 32) return hipErrorInvalidValue;
     const long long nbh = (long long)batch * nheads;
     if (nbh == 0) return hipSuccess;
     const unsigned blocks = (unsigned)((nbh + 3) / 4);
+    const int n = (int)nbh;
     if (dtype == 0)
-        return launch_t<float>(dstate, blocks, stream, x, dt, A, B, C, D, dt_softplus, (int)nbh,
-                               nheads, ngroups, state, y);
-    return launch_t<bf16_t>(dstate, blocks, stream, x, dt, A, B, C, D, dt_softplus, (int)nbh,
-                            nheads, ngroups, state, y);
+        return state_bf16 ? launch_t<float, bf16_t>(dstate, blocks, stream, x, dt, A, B, C, D, dt_softplus, n, nheads, ngroups, state, y)
+                          : launch_t<float, float>(dstate, blocks, stream, x, dt, A, B, C, D, dt_softplus, n, nheads, ngroups, state, y);
+    return state_bf16 ? launch_t<bf16_t, bf16_t>(dstate, blocks, stream, x, dt, A, B, C, D, dt_softplus, n, nheads, ngroups, state, y)
+                      : launch_t<bf16_t, float>(dstate, blocks, stream, x, dt, A, B, C, D, dt_softplus, n, nheads, ngroups, state, y);
 }
 
 }  // namespace ssd

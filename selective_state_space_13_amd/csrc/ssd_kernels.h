@@ -112,11 +112,11 @@ hipError_t launch_ssd_fused_varlen(const int *cu_seqlens, int nseq, int total_to
                                    hipStream_t stream);
 
 
-// decode step, in-place float state
-hipError_t launch_decode_step(int dtype, const void *x, const void *dt, const float *A,
+// decode step, in-place state: float, or bf16 when state_bf16
+hipError_t launch_decode_step(int dtype, int state_bf16, const void *x, const void *dt, const float *A,
                               const void *B, const void *C, const float *D, int dt_softplus,
                               int batch, int nheads, int headdim, int dstate, int ngroups,
-                              float *state, void *y, hipStream_t stream);
+                              void *state, void *y, hipStream_t stream);
 
 // Mamba-1 selective scan.  The sequence is cut into nseg time segments: phase 0
 // gives each segment's local end state and Σ Δ, phase 1 chains them into

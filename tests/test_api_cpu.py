@@ -39,7 +39,7 @@ def test_header_declares_expected_entry_points():
               "selective_scan_workspace_size", "ssd_status_string", "ssd_last_error",
               "ssd_version", "ssd_chunk_scan_bwd", "ssd_chunk_scan_bwd_workspace_size",
               "ssd_chunk_scan_varlen_fwd", "ssd_causal_conv1d_fwd", "ssd_gated_rmsnorm_fwd",
-              "ssd_chunk_scan_plan"]:
+              "ssd_chunk_scan_plan", "ssd_decode_step_bf16_state"]:
         assert n in names
 
 
@@ -154,28 +154,43 @@ def test_bf16_workspace_is_small_or_segment_buffers(L):
         ssd.chunk_scan_workspace_layout(8, 2048, 80, 64, 128, 1, 256, BF16)
 
 
-def decode_call(L, b=4, H=8, P=64, N=128, G=1, dtype=BF16, ptrs=None):
+def decode_call(L, b=4, H=8, P=64, N=128, G=1, dtype=BF16, ptrs=None, bf16_state=False):
     p = dict(x=fake(1), dt=fake(2), A=fake(3), B=fake(4), C=fake(5), D=fake(6), st=fake(7),
              y=fake(8))
     if ptrs:
         p.update(ptrs)
-    return L.ssd_decode_step(b, H, P, N, G, dtype, 1, p["x"], p["dt"], p["A"], p["B"], p["C"],
-                             p["D"], p["st"], p["y"], None)
+    fn = L.ssd_decode_step_bf16_state if bf16_state else L.ssd_decode_step
+    return fn(b, H, P, N, G, dtype, 1, p["x"], p["dt"], p["A"], p["B"], p["C"], p["D"], p["st"],
+              p["y"], None)
 
 
+@pytest.mark.parametrize("bf16_state", [False, True])
 @pytest.mark.parametrize("kw,status", [(dict(b=-1), SHAPE), (dict(G=3), SHAPE), (dict(P=128), UNSUP),
                                        (dict(N=24), UNSUP), (dict(N=16), UNSUP), (dict(N=512), UNSUP),
                                        (dict(dtype=2), UNSUP)])
-def test_decode_shape_errors(L, kw, status):
-    assert decode_call(L, **kw) == status
+def test_decode_shape_errors(L, kw, status, bf16_state):
+    assert decode_call(L, bf16_state=bf16_state, **kw) == status
 
 
-def test_decode_null_align_alias(L):
-    assert decode_call(L, ptrs={"st": None}) == NULL
-    assert decode_call(L, ptrs={"y": fake(8, 4)}) == ALIGN
-    assert decode_call(L, ptrs={"y": fake(1)}) == ALIAS
-    assert decode_call(L, ptrs={"st": fake(8)}) == ALIAS
-    assert decode_call(L, b=0) == OK
+@pytest.mark.parametrize("bf16_state", [False, True])
+def test_decode_null_align_alias(L, bf16_state):
+    call = lambda **kw: decode_call(L, bf16_state=bf16_state, **kw)  # noqa: E731
+    assert call(ptrs={"st": None}) == NULL
+    assert call(ptrs={"y": fake(8, 4)}) == ALIGN
+    assert call(ptrs={"st": fake(7, 8)}) == ALIGN
+    assert call(ptrs={"y": fake(1)}) == ALIAS
+    assert call(ptrs={"st": fake(8)}) == ALIAS
+    assert call(b=0) == OK
+
+
+def test_decode_bf16_state_span_is_two_bytes_per_value(L):
+    # y placed right after a bf16 state of b·H·N·P values: disjoint at 2 bytes a value,
+    # overlapping at 4
+    b, H, N = 4, 8, 128
+    n = b * H * N * 64
+    st, y = fake(7), fake(7, 2 * n)
+    assert decode_call(L, ptrs={"st": st, "y": y}, bf16_state=True) != ALIAS
+    assert decode_call(L, ptrs={"st": st, "y": y}, bf16_state=False) == ALIAS
 
 
 def m1_call(L, b=2, Lq=100, dim=128, N=16, dtype=BF16, ptrs=None):

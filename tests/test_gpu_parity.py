@@ -551,6 +551,108 @@ def test_config4_decode_chain_full(config2):
     say(f"C4 worst step excess/RMS {worst:.3e}")
 
 
+# ------------------------------------------------- decode against a bf16 state cache
+# The cached state has bf16 precision whatever the input dtype, so y is held to
+# the bf16 bar.  The kernel rounds its float32 update and the oracle its float64
+# one: where the two straddle a rounding boundary they round to neighbouring bf16
+# values, and in a chain such a one-unit difference persists.  So each step is
+# checked from the kernel's own cached values (every stored value within one bf16
+# unit of the oracle's rounding, y to the bar), and the independent chains are
+# compared with the bound that follows: at most one unit (2^-7 of the largest
+# magnitude) per step, and an RMS-relative difference of at most 1e-3.
+
+def bf16_units(got, ref):
+    """|got - ref| in units of the bf16 spacing at |ref| (ref bf16-representable)."""
+    ref = np.asarray(ref, np.float64)
+    e = np.frexp(np.abs(ref))[1]
+    unit = np.where(ref != 0, np.ldexp(1.0, e - 8), np.ldexp(1.0, -133))
+    return np.abs(np.asarray(got, np.float64) - ref) / unit
+
+
+def bf16_state_tensor(values):
+    return torch.from_numpy(np.asarray(values, np.float32)).to(torch.bfloat16).cuda()
+
+
+def check_bf16_step(state_after, ref_after, before, what):
+    """Every stored value within one bf16 unit of the oracle's rounding, plus the
+    float32 arithmetic of the update: where a·h and Δ·B·x nearly cancel, its error,
+    relative to those terms (about |before| + |ref|), can exceed a unit of the small
+    result.  1e-5 of them is well above float32 and fast-exp error."""
+    g = to_f64(state_after)
+    units = bf16_units(g, ref_after)
+    slack = 1e-5 * (np.abs(before) + np.abs(ref_after))
+    e = np.frexp(np.abs(ref_after))[1]
+    unit = np.where(ref_after != 0, np.ldexp(1.0, e - 8), np.ldexp(1.0, -133))
+    say(f"{what}: max {units.max():.2f} bf16 units, {np.mean(units > 0):.2e} of values off")
+    assert np.all(np.abs(g - ref_after) <= unit + slack), what
+
+
+def check_bf16_chain(state, ref, steps, what):
+    g = to_f64(state)
+    err = np.abs(g - ref)
+    rms = np.sqrt(np.mean(ref * ref))
+    say(f"{what}: max err {err.max():.3e} (bound {steps * 2.0**-7 * np.abs(ref).max():.3e}), "
+        f"RMS err / RMS {np.sqrt(np.mean(err * err)) / rms:.3e}")
+    assert err.max() <= steps * 2.0**-7 * np.abs(ref).max(), what
+    assert np.sqrt(np.mean(err * err)) <= 1e-3 * rms, what
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N,G,wD", [(128, 1, True), (64, 2, False), (256, 1, False), (96, 2, True)])
+def test_decode_bf16_state_small_chain(N, G, wD, dtype):
+    b, H, P, steps = 5, 8, 64, 6
+    A, D = gen.ssd_params(H, seed=N + 1000, config_id=110)
+    Dn = D.f64() if wD else None
+    rng = np.random.default_rng(N + G + 1000)
+    ost = oracle.round_bf16(rng.standard_normal((b, H, N, P)) * 0.05)
+    state = bf16_state_tensor(ost)
+    Ad, Dd = to_dev(A), (to_dev(D) if wD else None)
+    for k in range(steps):
+        s = gen.decode_inputs(b, H, P, N, G, dtype, step=k, seed=N + 1000, config_id=110)
+        ins = (s["x"].f64(), s["dt"].f64(), A.f64(), s["B"].f64(), s["C"].f64(), Dn)
+        before = to_f64(state)
+        y = ssd.ssd_decode_step_bf16_state(to_dev(s["x"]), to_dev(s["dt"]), Ad, to_dev(s["B"]),
+                                           to_dev(s["C"]), Dd, state)
+        torch.cuda.synchronize()
+        ys, ss = oracle.ssd_decode_bf16_state(*ins, before)   # from the kernel's cached values
+        check_bf16_step(state, ss, before, f"bf16-state step {k}")
+        assert_parity(to_f64(y), ys, TAU_BF16, dtype == "bf16", f"bf16-state decode y step {k}")
+        yo, ost = oracle.ssd_decode_bf16_state(*ins, ost)    # the oracle's own chain
+        assert_parity(to_f64(y), yo, TAU_BF16, dtype == "bf16", f"bf16-state decode y (chain) step {k}")
+    check_bf16_chain(state, ost, steps, "bf16-state chain")
+
+
+def test_config4_decode_bf16_state_chain_full(config2):
+    """The 64-step chain of the decode workload (batch 256) against a bf16 state
+    cache, from the 2.7B-layer prefill's final states rounded to bf16: the first
+    step from identical cached values, every y of the chain, the final state."""
+    c2, d2 = config2
+    c = configs.DECODE_STATE_CACHE
+    say("C4 bf16 state: oracle prefill for the initial state")
+    _, f8 = oracle_scan(d2, True)
+    reps = c["batch"] // c2["batch"]
+    ost = oracle.round_bf16(np.tile(f8, (reps, 1, 1, 1)))
+    state = bf16_state_tensor(ost)
+    first = ost
+    A, D = gen.ssd_params(c["nheads"], config_id=c2["id"])
+    Ad, Dd = to_dev(A), to_dev(D)
+    worst = 0.0
+    for k in range(c["steps"]):
+        s = gen.decode_inputs(c["batch"], c["nheads"], c["headdim"], c["dstate"], c["ngroups"],
+                              c["dtype"], step=k, config_id=c["id"])
+        y = ssd.ssd_decode_step_bf16_state(to_dev(s["x"]), to_dev(s["dt"]), Ad, to_dev(s["B"]),
+                                           to_dev(s["C"]), Dd, state)
+        torch.cuda.synchronize()
+        yo, ost = oracle.ssd_decode_bf16_state(s["x"].f64(), s["dt"].f64(), A.f64(), s["B"].f64(),
+                                               s["C"].f64(), D.f64(), ost)
+        if k == 0:
+            check_bf16_step(state, ost, first, "C4 bf16 state, first step")
+        r = assert_parity(to_f64(y), yo, TAU_BF16, True, f"C4 bf16-state y step {k}")
+        worst = max(worst, r["excess_over_rms"])
+    check_bf16_chain(state, ost, c["steps"], "C4 bf16 state after 64 steps")
+    say(f"C4 bf16 state: worst step excess/RMS {worst:.3e}")
+
+
 # ------------------------------------------------------------------ Mamba-1
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -9,7 +9,8 @@ in the decay product, a wrong head-to-group map, a transposed operand -- fails.
 
 Page cited: "5.3 텐서 병렬화(Tensor Parallelism) 지원과 대규모 클러스터 학습"
 (§2.1 recurrence, §3/§3.1 duality and scalar-identity A, §3.2 block
-decomposition, §4.2 state hand-off, §4.3 reset by a zero transition) and
+decomposition, §4.2 state hand-off, §4.3 reset by a zero transition, §5.1
+reduced precision for the bf16 state cache) and
 "Scaling State-Space Models on Multiple GPUs with Tensor Parallelism"
 (Abstract: prefill-to-decode state cache).
 """
@@ -543,3 +544,57 @@ def test_backward_directional_derivative_medium():
     fd = (loss(eps) - loss(-eps)) / (2 * eps)
     an = sum(float(np.sum(g[GRAD_KEYS[k]] * dirs[k])) for k in args)
     assert abs(fd - an) <= 1e-6 * max(abs(an), 1.0)
+
+
+# ---- bf16 state cache for decode (reduced precision of page 1 §5.1 on the cached
+# state of the INF page's Abstract)
+
+def test_pin15_round_bf16_matches_torch_round_to_nearest_even():
+    """round_bf16 against torch's float32 -> bfloat16 conversion (nearest, ties to
+    even) on float32-exact values: many binades, exact ties, signed zeros."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(15)
+    v = (rng.standard_normal(50000) * np.exp2(rng.integers(-60, 60, 50000))).astype(np.float32)
+    ties = np.array([1 + 2.0**-8, 1 + 3 * 2.0**-8, 2 + 2.0**-7, -(1 + 2.0**-8), 0.0, -0.0,
+                     2.0**-100, 3.0 * 2.0**90], np.float32)
+    v = np.concatenate([v, ties])
+    want = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.round_bf16(v.astype(np.float64))
+    assert np.array_equal(got, want)
+    assert np.array_equal(oracle.round_bf16(got), got)  # idempotent
+    nz = v != 0
+    assert np.max(np.abs(got[nz] - v[nz]) / np.abs(v[nz])) <= 2.0**-8  # unit roundoff of 8 significant bits
+
+
+def test_pin16_bf16_state_decode_exact_case_and_rounding_bound():
+    """With a decay of exactly 1 (A = 0) and an update exact in bf16 (Δ = 1/2 without
+    softplus, small integer B, x and state), the bf16-state step returns the float64
+    step's y and state unchanged.  In general it returns the float64 step's y and
+    that step's state within the bf16 unit roundoff (2^-8 relative), bf16-representable,
+    and the rounding does act."""
+    b, H, P, N, G = 2, 4, 64, 32, 2
+    rng = np.random.default_rng(16)
+    x = rng.integers(-3, 4, (b, H, P)).astype(np.float64)
+    dt = np.full((b, H), 0.5)
+    A = np.zeros(H)
+    B = rng.integers(-2, 3, (b, G, N)).astype(np.float64)
+    C = rng.standard_normal((b, G, N))
+    D = rng.standard_normal(H)
+    st0 = rng.integers(-8, 9, (b, H, N, P)).astype(np.float64)
+    y16, s16 = oracle.ssd_decode_bf16_state(x, dt, A, B, C, D, st0, dt_softplus=False)
+    y64, s64 = oracle.ssd_decode(x, dt, A, B, C, D, st0, dt_softplus=False)
+    assert np.array_equal(s16, s64) and np.array_equal(y16, y64)
+    assert np.array_equal(s64, st0 + 0.5 * np.repeat(B, H // G, axis=1)[..., None] * x[:, :, None, :])
+
+    x = rng.standard_normal((b, H, P))
+    dt = rng.uniform(-4.0, 1.0, (b, H))
+    A = -np.exp(rng.uniform(0.0, math.log(16.0), H))
+    B = rng.standard_normal((b, G, N)) / math.sqrt(N)
+    st0 = oracle.round_bf16(rng.standard_normal((b, H, N, P)))
+    y16, s16 = oracle.ssd_decode_bf16_state(x, dt, A, B, C, D, st0)
+    y64, s64 = oracle.ssd_decode(x, dt, A, B, C, D, st0)
+    assert np.array_equal(y16, y64)
+    nz = s64 != 0
+    assert np.max(np.abs(s16[nz] - s64[nz]) / np.abs(s64[nz])) <= 2.0**-8
+    assert np.array_equal(oracle.round_bf16(s16), s16)
+    assert not np.array_equal(s16, s64)
