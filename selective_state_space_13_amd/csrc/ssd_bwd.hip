@@ -196,12 +196,14 @@ struct ChunkSmem {
     uint16_t mb[2][kC * PQ];   // Mb[s][u] = (C_u·B_s)·E[s,u], head and tail
     uint16_t kd[2][kC * PQ];   // Kd[s][u] = K[s,u]·E[s,u]·Δ_s, head and tail
     uint16_t dxs[kC * PQ];     // dx of the current head, for 16-byte row stores
-    double cst[kC];            // within-chunk cumsum of Δ·A_h
-    float d[kC];               // Δ (0 past the end)
-    float ee[kC];              // exp(cs_end - cs_s), 0 past the end
-    float eu[kC];              // exp(cs_u), 0 past the end
-    float sg[kC];              // dΔ/d(raw dt)
-    float xdy[kC];             // x_t·dy_t
+    // per-token values of a head, double-buffered by head parity: head r + 1's are
+    // scanned while head r's are still read
+    double cst[2][kC];         // within-chunk cumsum of Δ·A_h
+    float d[2][kC];            // Δ (0 past the end)
+    float ee[2][kC];           // exp(cs_end - cs_s), 0 past the end
+    float eu[2][kC];           // exp(cs_u), 0 past the end
+    float sg[2][kC];           // dΔ/d(raw dt)
+    float xdy[2][kC];          // x_t·dy_t
     float zrow[3][32];         // Σ_s Z[u,s] per u, per causal 32 x 32 block
     float zcol[3][32];         // Σ_u Z[u,s] per s, per causal block
     float dcsa[N / 32][kC];    // exp(cs_u) dy_u·(h_inᵀ C_u), per n-tile
@@ -335,7 +337,21 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
         }
         R0.dt = __uint_as_float((uint32_t)a.dt[(row0 + min(lane, lim)) * a.nheads + h] << 16);
     };
+    // per-token values of head hh (its Δ in R0.dt) into buffer tb (one wave)
+    auto scan_head = [&](int hh, int tb) {
+        const bool ok = lane <= lim;
+        const float raw = R0.dt;
+        const float delta = ok ? (a.dt_softplus ? softplus_f32(raw) : raw) : 0.0f;
+        const double cs = wave_inclusive_scan((double)(delta * a.A[hh]));
+        const double cs_end = read_lane(cs, 63);
+        sm.cst[tb][lane] = cs;
+        sm.d[tb][lane] = delta;
+        sm.ee[tb][lane] = ok ? __expf((float)(cs_end - cs)) : 0.0f;
+        sm.eu[tb][lane] = ok ? __expf((float)cs) : 0.0f;
+        sm.sg[tb][lane] = a.dt_softplus ? 1.0f / (1.0f + __expf(-raw)) : 1.0f;
+    };
     prefetch(g * R);
+    if (wave == 6) scan_head(g * R, 0);
 
     for (int r = 0; r < R; ++r) {
         // lane-derived offsets are recomputed per head (an opaque copy of the
@@ -345,6 +361,7 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
         const int ln = tdv & 63, l32 = ln & 31, lg = ln >> 5;
         const int srow = tdv >> 3, scol = (tdv & 7) * 8;   // x / dy staging: token, 8 columns of p
         const int h = g * R + r;
+        const int rb = r & 1;  // this head's per-token buffer
         const size_t bh = (size_t)b * a.nheads + h;
         const size_t bhc = bh * a.nchunks + c;
         // ================= staging of head h (from the registers loaded a head ahead)
@@ -361,7 +378,7 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
             dot += __shfl_xor(dot, 1, 64);
             dot += __shfl_xor(dot, 2, 64);
             dot += __shfl_xor(dot, 4, 64);
-            if ((tdv & 7) == 0) sm.xdy[srow] = dot;
+            if ((tdv & 7) == 0) sm.xdy[rb][srow] = dot;
         }
         {
 #pragma unroll
@@ -375,18 +392,6 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
                 *reinterpret_cast<bf16x8 *>(&sm.gs[0][n * PQ + p]) = hi;
                 *reinterpret_cast<bf16x8 *>(&sm.gs[1][n * PQ + p]) = lo;
             }
-        }
-        if (wave == 7) {
-            const bool ok = lane <= lim;
-            const float raw = R0.dt;
-            const float delta = ok ? (a.dt_softplus ? softplus_f32(raw) : raw) : 0.0f;
-            const double cs = wave_inclusive_scan((double)(delta * a.A[h]));
-            const double cs_end = read_lane(cs, 63);
-            sm.cst[lane] = cs;
-            sm.d[lane] = delta;
-            sm.ee[lane] = ok ? __expf((float)(cs_end - cs)) : 0.0f;
-            sm.eu[lane] = ok ? __expf((float)cs) : 0.0f;
-            sm.sg[lane] = a.dt_softplus ? 1.0f / (1.0f + __expf(-raw)) : 1.0f;
         }
         __syncthreads();
         prefetch(g * R + min(r + 1, R - 1));  // next head (the last one again at the end)
@@ -413,15 +418,15 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
             for (int ks = 0; ks < P / 16; ++ks)
                 kt = mfma(rop<PQ>(sm.ys, 32 * ub, 16 * ks, ln), rop<PQ>(sm.xs, 32 * sb, 16 * ks, ln), kt);
             const int s = 32 * sb + l32;
-            const double cs_s = sm.cst[s];
-            const float d_s = sm.d[s];
+            const double cs_s = sm.cst[rb][s];
+            const float d_s = sm.d[rb][s];
             f32x16 z;
             float mbv[16], kdv[16];
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
                 const int u = 32 * ub + 8 * (rr >> 2) + 4 * lg + (rr & 3);
                 const bool on = u >= s;
-                const float E = on ? __expf((float)(sm.cst[u] - cs_s)) : 0.0f;
+                const float E = on ? __expf((float)(sm.cst[rb][u] - cs_s)) : 0.0f;
                 mbv[rr] = gm[rr] * E;
                 kdv[rr] = kt[rr] * E * d_s;
                 z[rr] = mbv[rr] * d_s * kt[rr];
@@ -490,8 +495,8 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
                 const int row = 32 * bt + 8 * (rr >> 2) + 4 * lg + (rr & 3);
-                dBacc[rr] += sm.d[row] * sm.ee[row] * t2[rr];
-                const float v = sm.eu[row] * t3[rr];
+                dBacc[rr] += sm.d[rb][row] * sm.ee[rb][row] * t2[rr];
+                const float v = sm.eu[rb][row] * t3[rr];
                 dCacc[rr] += v;
                 cc[rr] = v * __uint_as_float((uint32_t)sm.cs[row * PN + 32 * nt + l32] << 16);
             }
@@ -520,11 +525,11 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
                 const int p = 32 * dpt + l32;
                 const float xv = __uint_as_float((uint32_t)sm.xs[s * PQ + p] << 16);
                 const float yv = __uint_as_float((uint32_t)sm.ys[s * PQ + p] << 16);
-                const float iv = sm.ee[s] * inter[rr];
+                const float iv = sm.ee[rb][s] * inter[rr];
                 const float dxr = intra[rr] + iv;
                 dd[rr] = xv * dxr;
-                qq[rr] = sm.d[s] * xv * iv;
-                sm.dxs[s * PQ + p] = f32_to_bf16_bits(sm.d[s] * dxr + Dh * yv);
+                qq[rr] = sm.d[rb][s] * xv * iv;
+                sm.dxs[s * PQ + p] = f32_to_bf16_bits(sm.d[rb][s] * dxr + Dh * yv);
             }
             int rw;
             const float sd = row_sums(dd, ln, rw);
@@ -550,6 +555,9 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
                 }
             }
         }
+        // the next head's per-token values, on a wave that is otherwise idle here
+        // (its Δ arrived with the prefetch after the first barrier)
+        if (wave == 6 && r + 1 < R) scan_head(h + 1, rb ^ 1);
         __syncthreads();
 
         // ================= dx rows; per-token decay gradients (wave 7)
@@ -570,23 +578,25 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
             for (int k = 0; k < NT; ++k) gh += sm.gh[k];
             const float qsum = wave_sum(q);
             double dcs = (double)zr - (double)zc + (double)dcsa - (double)q;
-            if (t == kC - 1) dcs += (double)__expf((float)sm.cst[kC - 1]) * (double)gh + (double)qsum;
+            if (t == kC - 1) dcs += (double)__expf((float)sm.cst[rb][kC - 1]) * (double)gh + (double)qsum;
             // dℓ_t = Σ_{v >= t} dcs_v: an inclusive scan over the reversed lanes
             const double rev = wave_inclusive_scan(shfl_d(dcs, 63 - t));
             const double dl = shfl_d(rev, 63 - t);
             const float dlf = (float)dl;
             const float ddelta = a.A[h] * dlf + ddirect;
             const bool ok = t <= lim;
-            if (ok) a.ddt[(row0 + t) * a.nheads + h] = f32_to_bf16_bits(ddelta * sm.sg[t]);
-            const float dA = wave_sum(ok ? sm.d[t] * dlf : 0.0f);
-            const float dD = wave_sum(ok ? sm.xdy[t] : 0.0f);
+            if (ok) a.ddt[(row0 + t) * a.nheads + h] = f32_to_bf16_bits(ddelta * sm.sg[rb][t]);
+            const float dA = wave_sum(ok ? sm.d[rb][t] * dlf : 0.0f);
+            const float dD = wave_sum(ok ? sm.xdy[rb][t] : 0.0f);
             if (ln == 0) {
                 a.dA_part[bhc] = dA;
                 a.dD_part[bhc] = dD;
             }
         }
-        __syncthreads();
+        // no barrier: wave 7 finishes this head while the others stage the next one
+        // (every value it reads is rewritten only after the next head's first barrier)
     }
+    __syncthreads();
 
     // ---- dB and dC of the chunk, through LDS (the G_out planes are free now)
     uint16_t *ob = sm.gs[0], *oc = sm.gs[1];
