@@ -54,22 +54,23 @@ struct BwdArgs {
 
 // ============================================================ adjoint walk
 
+// (every array double-buffered by chunk parity)
 template <int N>
 struct AdjSmem {
-    uint16_t cs[kC * N];      // C [u][n], swizzled
-    uint16_t ey[2][kC * P];   // e_u·dy_u head and tail [u][p], swizzled
-    double cst[2][kC];        // within-chunk cumsum (double-buffered by chunk parity)
-    float e[2][kC];           // exp(cs_u), 0 past the end of the sequence
+    uint16_t cs[2][kC * N];      // C [u][n], swizzled
+    uint16_t ey[2][2][kC * P];   // e_u·dy_u [parity][head, tail][u][p], swizzled
+    double cst[2][kC];           // within-chunk cumsum
+    float e[2][kC];              // exp(cs_u), 0 past the end of the sequence
 };
 
 // Roles: wave w owns the 32 x 32 adjoint tile (n-tile w >> 1, p-tile w & 1)
-// (dstate 64: waves 0-3).  Wave 7 scans the next chunk's Δ·A while the others
-// multiply.
+// (dstate 64: waves 0-3).  Wave 7 scans the next chunk's Δ·A during the
+// staging; one barrier per chunk (the staged tiles alternate between two
+// buffers, as in the forward state-only walk).
 template <int N>
-__device__ __forceinline__ void adjoint_walk(const BwdArgs &a, unsigned blk, unsigned nblk) {
+__device__ __forceinline__ void adjoint_walk(const BwdArgs &a, unsigned blk, unsigned nblk, AdjSmem<N> &sm) {
     constexpr int BV = N / 64, BPR = N / 8;
     constexpr int kScanWave = 7;
-    __shared__ __attribute__((aligned(16))) AdjSmem<N> sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, lg = lane >> 5;
     const int rrow = tr_row(lane), rcol = tr_col(lane);
@@ -91,6 +92,9 @@ __device__ __forceinline__ void adjoint_walk(const BwdArgs &a, unsigned blk, uns
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) st[rr] = src[(32 * snt + 8 * (rr >> 2) + 4 * lg + (rr & 3)) * P];
     }
+    // vmcnt(0) once here, before any prefetch: otherwise the first use of st
+    // inside the chunk loop waits for every outstanding load in every chunk
+    __builtin_amdgcn_s_waitcnt(0x0f70);
     const int yrow = tid >> 3, ycol = (tid & 7) * 8;
     const int brow = tid / BPR, bcol = (tid % BPR) * 8;
     const int oy = swz<64>(yrow, ycol);
@@ -99,17 +103,19 @@ __device__ __forceinline__ void adjoint_walk(const BwdArgs &a, unsigned blk, uns
     const int o_ya = swz<64>(8 * lg + rrow, 32 * spt + rcol), o_yb = swz<64>(8 * lg + 4 + rrow, 32 * spt + rcol);
     const size_t xstride = (size_t)a.nheads * P, bstride = (size_t)a.ngroups * N;
 
-    uint4 ry, rc[BV];
-    float rdt;
-    auto prefetch = [&](int c) {
+    // dy, C and Δ of one chunk, loaded two chunks ahead of their use into one of
+    // two register sets that the loop alternates
+    struct Loads { uint4 y, c[BV]; uint16_t dt; };  // dt: raw bf16 bits, widened at the scan
+    auto prefetch = [&](Loads &L, int c) {
         const int t0 = c * kC, lim = last - t0;
-        rdt = __uint_as_float((uint32_t)a.dt[(row0 + t0 + min(lane, lim)) * a.nheads + h] << 16);
-        ry = ld16(a.dy + ((row0 + t0) * a.nheads + h) * P + ycol + (size_t)min(yrow, lim) * xstride);
+        L.dt = a.dt[(row0 + t0 + min(lane, lim)) * a.nheads + h];
+        L.y = ld16(a.dy + ((row0 + t0) * a.nheads + h) * P + ycol + (size_t)min(yrow, lim) * xstride);
         const uint16_t *cc = a.C + (row0 + t0) * bstride + (size_t)g * N + bcol;
 #pragma unroll
-        for (int k = 0; k < BV; ++k) rc[k] = ld16(cc + (size_t)min(brow + (kThreads / BPR) * k, lim) * bstride);
+        for (int k = 0; k < BV; ++k) L.c[k] = ld16(cc + (size_t)min(brow + (kThreads / BPR) * k, lim) * bstride);
     };
-    auto scan = [&](int c, int pb) {
+    auto scan = [&](int c, int pb, uint16_t bits) {
+        const float rdt = __uint_as_float((uint32_t)bits << 16);
         const bool ok = c * kC + lane < a.seqlen;
         const float delta = ok ? (a.dt_softplus ? softplus_f32(rdt) : rdt) : 0.0f;
         const double cs = wave_inclusive_scan((double)(delta * Ah));
@@ -118,14 +124,22 @@ __device__ __forceinline__ void adjoint_walk(const BwdArgs &a, unsigned blk, uns
     };
 
     const int c_last = a.nchunks - 1;
-    prefetch(c_last);
-    if (wave == kScanWave) scan(c_last, c_last & 1);
+    Loads la, lb;
+    prefetch(la, c_last);
+    prefetch(lb, max(c_last - 1, 0));
+    if (wave == kScanWave) scan(c_last, c_last & 1, la.dt);
     __syncthreads();
-    for (int c = c_last; c >= 0; --c) {
+    // chunk c from the register set cur, which is then refilled with chunk c - 2;
+    // nxt holds chunk c - 1, whose Δ·A is scanned during the staging.  Buffer
+    // c & 1 of the tiles was last read by the update of chunk c + 2, which every
+    // wave finished before the barrier of chunk c + 1; token buffer (c - 1) & 1
+    // was last read by the staging of chunk c + 1, before that same barrier.
+    auto step = [&](int c, Loads &cur, const Loads &nxt) {
         const int pb = c & 1;
+        uint16_t *eyh = sm.ey[pb][0], *eyl = sm.ey[pb][1], *cs = sm.cs[pb];
         {
             const float e = sm.e[pb][yrow];
-            const uint32_t in[4] = {ry.x, ry.y, ry.z, ry.w};
+            const uint32_t in[4] = {cur.y.x, cur.y.y, cur.y.z, cur.y.w};
             uint32_t hi[4], lo[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -133,11 +147,11 @@ __device__ __forceinline__ void adjoint_walk(const BwdArgs &a, unsigned blk, uns
                 hi[q] = pack_bf16x2(f0, f1);
                 lo[q] = pack_bf16x2(f0 - bf16lo(hi[q]), f1 - bf16hi(hi[q]));
             }
-            *reinterpret_cast<uint4 *>(&sm.ey[0][oy]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-            *reinterpret_cast<uint4 *>(&sm.ey[1][oy]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+            *reinterpret_cast<uint4 *>(&eyh[oy]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            *reinterpret_cast<uint4 *>(&eyl[oy]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
         }
 #pragma unroll
-        for (int k = 0; k < BV; ++k) *reinterpret_cast<uint4 *>(&sm.cs[ob + k * (kThreads / BPR) * N]) = rc[k];
+        for (int k = 0; k < BV; ++k) *reinterpret_cast<uint4 *>(&cs[ob + k * (kThreads / BPR) * N]) = cur.c[k];
         if (owns) {
             float *dst = a.gst + (bh * a.nchunks + c) * N * P + 32 * spt + l32;
 #pragma unroll
@@ -146,22 +160,30 @@ __device__ __forceinline__ void adjoint_walk(const BwdArgs &a, unsigned blk, uns
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) st[rr] *= dec;
         }
-        prefetch(max(c - 1, 0));
+        prefetch(cur, max(c - 2, 0));
+        if (wave == kScanWave && c > 0) scan(c - 1, pb ^ 1, nxt.dt);
         __syncthreads();
         if (owns) {
             // G[n][p] += Σ_u C[u][n]·(e·dy)[u][p]: A = Cᵀ (rows n, k = u), B = e·dy (k = u, cols p)
 #pragma unroll
             for (int ks = 0; ks < kC / 16; ++ks) {
-                const bf16x8 aop = cat8(tr4(sm.cs + o_sa + 16 * ks * N), tr4(sm.cs + o_sb + 16 * ks * N));
-                const bf16x8 bhi = cat8(tr4(sm.ey[0] + o_ya + 16 * ks * 64), tr4(sm.ey[0] + o_yb + 16 * ks * 64));
-                const bf16x8 blo = cat8(tr4(sm.ey[1] + o_ya + 16 * ks * 64), tr4(sm.ey[1] + o_yb + 16 * ks * 64));
+                const bf16x8 aop = cat8(tr4(cs + o_sa + 16 * ks * N), tr4(cs + o_sb + 16 * ks * N));
+                const bf16x8 bhi = cat8(tr4(eyh + o_ya + 16 * ks * 64), tr4(eyh + o_yb + 16 * ks * 64));
+                const bf16x8 blo = cat8(tr4(eyl + o_ya + 16 * ks * 64), tr4(eyl + o_yb + 16 * ks * 64));
                 st = mfma(aop, bhi, st);
                 st = mfma(aop, blo, st);
             }
         }
-        if (wave == kScanWave && c > 0) scan(c - 1, pb ^ 1);
-        __syncthreads();
+    };
+    // two chunks per iteration and a last odd chunk after the loop: every path to
+    // the loop head then comes after the second step, so that the compiler does
+    // not wait there for the loads the first step has just issued
+    int c = c_last;
+    for (; c >= 1; c -= 2) {
+        step(c, la, lb);
+        step(c - 1, lb, la);
     }
+    if (c >= 0) step(c, la, lb);
     if (owns && a.dh0) {
         float *dst = a.dh0 + bh * N * P + 32 * spt + l32;
 #pragma unroll
@@ -172,11 +194,17 @@ __device__ __forceinline__ void adjoint_walk(const BwdArgs &a, unsigned blk, uns
 // Workgroups [0, nfwd) run the forward walk that stores every chunk's incoming
 // state; the rest run the adjoint walk.
 template <int N>
-__global__ __launch_bounds__(kThreads, 2) void ssd_bwd_walks_kernel(FusedArgs fa, BwdArgs ba, unsigned nfwd) {
+// two workgroups of 8 waves per CU: 4 waves per SIMD (at most 128 VGPRs)
+__global__ __launch_bounds__(kThreads, 4) void ssd_bwd_walks_kernel(FusedArgs fa, BwdArgs ba, unsigned nfwd) {
+    // the two walks run in different workgroups and share one LDS allocation
+    __shared__ __attribute__((aligned(16))) union {
+        StateSmem<N> fwd;
+        AdjSmem<N> adj;
+    } sm;
     if (blockIdx.x < nfwd)
-        state_walk<N>(fa, blockIdx.x, nfwd);
+        state_walk<N, true>(fa, blockIdx.x, nfwd, sm.fwd);
     else
-        adjoint_walk<N>(ba, blockIdx.x - nfwd, gridDim.x - nfwd);
+        adjoint_walk<N>(ba, blockIdx.x - nfwd, gridDim.x - nfwd, sm.adj);
 }
 
 // ============================================================ per-chunk gradients

@@ -46,8 +46,10 @@ namespace {
 
 // The state-only pass (segment end states, states at the cut of a pair).
 template <int N>
-__global__ __launch_bounds__(kThreads, 2) void ssd_state_kernel(FusedArgs a) {
-    state_walk<N>(a, blockIdx.x, gridDim.x);
+// two workgroups of 8 waves per CU: 4 waves per SIMD (at most 128 VGPRs)
+__global__ __launch_bounds__(kThreads, 4) void ssd_state_kernel(FusedArgs a) {
+    __shared__ __attribute__((aligned(16))) StateSmem<N> sm;
+    state_walk<N, false>(a, blockIdx.x, gridDim.x, sm);
 }
 
 // The full pass: states and outputs.

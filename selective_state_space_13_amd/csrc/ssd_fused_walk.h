@@ -137,27 +137,34 @@ __device__ __forceinline__ WalkItem map_walk_item(const FusedArgs &a, unsigned b
 }
 
 // LDS of the state-only walk: w·x head/tail [t][p] (swz<64>) and B [t][n]
-// (swz<N>), both read as transposed operands, and the per-token values.
+// (swz<N>), both read as transposed operands, and the per-token values, each
+// double-buffered by chunk parity.
+struct StateTok {
+    float w[kC];  // exp(cs_end - cs_j)·Δ_j, the weight of token j in the chunk's state
+    float dec;    // exp(cs_end), the decay of the state over the chunk
+};
 template <int N>
 struct StateSmem {
-    uint16_t xt[2][kC * P];
-    uint16_t bs[kC * N];
-    TokSmem tok[2];
+    uint16_t xt[2][2][kC * P];  // [chunk parity][head, tail]
+    uint16_t bs[2][kC * N];
+    StateTok tok[2];
 };
 
 // The state-only walk: H = exp(cs_end)·H + Bᵀ(w·x) over the chunks of the work
 // item, no outputs.  Every wave owns one 32 x 32 state tile (dstate 64: waves
 // 0-3): n-tile (w >> 1) mod N/32, p-tile w & 1.  Per chunk: staging (w·x split
-// head/tail, B), then the tile update while one wave scans the next chunk's Δ·A.
+// head/tail, B) while one wave also scans the next chunk's Δ·A, one barrier,
+// then the tile update.  The staged tiles alternate between two buffers, so
+// the next chunk's staging never overwrites a tile that a slower wave may
+// still be reading, and the chunk needs no second barrier.
 // It writes the end state of a segment (and its total log-decay) or of the
 // first half of a cut pair, or, for the backward, the state entering every
-// chunk.
-template <int N>
-__device__ __forceinline__ void state_walk(const FusedArgs &a, unsigned blk, unsigned nblk) {
+// chunk (kStoreStates; a.chunk_states must then be set).
+template <int N, bool kStoreStates>
+__device__ __forceinline__ void state_walk(const FusedArgs &a, unsigned blk, unsigned nblk, StateSmem<N> &sm) {
     constexpr int BV = N / 64;        // 16-byte vectors of B per lane
     constexpr int BPR = N / 8;        // 16-byte vectors per B row
     constexpr int kScanWave = N == 128 ? 0 : 4;
-    __shared__ __attribute__((aligned(16))) StateSmem<N> sm;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, lg = lane >> 5;
@@ -188,6 +195,10 @@ __device__ __forceinline__ void state_walk(const FusedArgs &a, unsigned blk, uns
             const int n = 32 * snt + 8 * (rr >> 2) + 4 * lg + (rr & 3);
             st[rr] = (src && owns_state) ? src[n * P + 32 * spt + l32] : 0.0f;
         }
+        // vmcnt(0) once here, before any prefetch: otherwise the first use of st
+        // inside the chunk loop waits for every outstanding load, the prefetch of
+        // the next chunks included, in every chunk
+        __builtin_amdgcn_s_waitcnt(0x0f70);
     }
 
     // ---- per-lane geometry, fixed for the whole walk
@@ -202,49 +213,55 @@ __device__ __forceinline__ void state_walk(const FusedArgs &a, unsigned blk, uns
     const size_t xstride = (size_t)a.nheads * P, bstride = (size_t)a.ngroups * N;
     const int last = seqlen - 1;
 
-    uint4 rx, rb[BV];
-    float rdt;
-    auto prefetch = [&](int c) {  // x, B and Δ of chunk c
+    // x, B and Δ of one chunk, loaded two chunks ahead of their use into one of
+    // two register sets that the loop alternates (a load one chunk ahead
+    // arrived after the short update phase, and every chunk waited for it)
+    struct Loads { uint4 x, b[BV]; uint16_t dt; };  // dt: raw bf16 bits, widened at the scan
+    auto prefetch = [&](Loads &L, int c) {
         const int t0 = c * kC, lim = last - t0;  // rows past the end are clamped to the last one
         // dt first: the scan wave uses it before the rest has arrived, and loads
         // complete in issue order
-        const uint16_t raw = a.dt[(row0 + t0 + min(lane, lim)) * a.nheads + h];
-        rdt = __uint_as_float((uint32_t)raw << 16);
-        rx = ld16(a.x + ((row0 + t0) * a.nheads + h) * P + xcol + (size_t)min(xrow, lim) * xstride);
+        L.dt = a.dt[(row0 + t0 + min(lane, lim)) * a.nheads + h];
+        L.x = ld16(a.x + ((row0 + t0) * a.nheads + h) * P + xcol + (size_t)min(xrow, lim) * xstride);
         const uint16_t *bc = a.B + (row0 + t0) * bstride + (size_t)g * N + bcol;
 #pragma unroll
-        for (int k = 0; k < BV; ++k) rb[k] = ld16(bc + (size_t)min(brow + (kThreads / BPR) * k, lim) * bstride);
+        for (int k = 0; k < BV; ++k) L.b[k] = ld16(bc + (size_t)min(brow + (kThreads / BPR) * k, lim) * bstride);
     };
-    // Δ, the float64 inclusive cumsum of Δ·A over the chunk (lane = token) and
-    // the values derived from it; returns Σ Δ·A over the chunk
-    auto scan_chunk = [&](int c, float raw, TokSmem &T) -> double {
+    // Δ and the float64 inclusive cumsum of Δ·A over the chunk (lane = token),
+    // the token weights and the chunk's decay; returns Σ Δ·A over the chunk
+    auto scan_chunk = [&](int c, uint16_t bits, StateTok &T) -> double {
+        const float raw = __uint_as_float((uint32_t)bits << 16);
         const bool ok = c * kC + lane < seqlen;
         const float delta = ok ? (a.dt_softplus ? softplus_f32(raw) : raw) : 0.0f;
         const double cs = wave_inclusive_scan((double)(delta * Ah));
         const double cs_end = read_lane(cs, 63);
-        const double cs_r = lane < 32 ? read_lane(cs, 31) : cs_end;
-        T.cs[lane] = cs;
-        T.d[lane] = delta;
-        T.e[lane] = __expf((float)cs);
-        T.v[lane] = __expf((float)(cs_r - cs)) * delta;
         T.w[lane] = __expf((float)(cs_end - cs)) * delta;
+        if (lane == 0) T.dec = __expf((float)cs_end);
         return cs_end;
     };
 
     double seg_decay = 0.0;
+    Loads la, lb;
     if (c0 < c1) {  // an empty sequence loads nothing and returns its initial state
-        prefetch(c0);
-        if (wave == kScanWave) seg_decay += scan_chunk(c0, rdt, sm.tok[c0 & 1]);
+        prefetch(la, c0);
+        prefetch(lb, min(c0 + 1, c1 - 1));
+        if (wave == kScanWave) seg_decay += scan_chunk(c0, la.dt, sm.tok[c0 & 1]);
     }
     __syncthreads();
 
-    for (int c = c0; c < c1; ++c) {
+    // chunk c from the register set cur, which is then refilled with chunk c + 2;
+    // nxt holds chunk c + 1, whose Δ·A is scanned during the staging.  Buffer
+    // c & 1 of the tiles was last read by the update of chunk c - 2, which every
+    // wave finished before the barrier of chunk c - 1; token buffer (c + 1) & 1
+    // was last read by the staging of chunk c - 1, before that same barrier.
+    auto step = [&](int c, Loads &cur, const Loads &nxt) {
         const int buf = c & 1;
-        const TokSmem &T = sm.tok[buf];
+        const StateTok &T = sm.tok[buf];
+        uint16_t *xh = sm.xt[buf][0], *xl = sm.xt[buf][1], *bs = sm.bs[buf];
         // ================= staging of chunk c
         {
             const float w = T.w[xrow];
-            const uint32_t in[4] = {rx.x, rx.y, rx.z, rx.w};
+            const uint32_t in[4] = {cur.x.x, cur.x.y, cur.x.z, cur.x.w};
             uint32_t hi[4], lo[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -252,15 +269,15 @@ __device__ __forceinline__ void state_walk(const FusedArgs &a, unsigned blk, uns
                 hi[e] = pack_bf16x2(f0, f1);
                 lo[e] = pack_bf16x2(f0 - bf16lo(hi[e]), f1 - bf16hi(hi[e]));
             }
-            *reinterpret_cast<uint4 *>(&sm.xt[0][ox]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-            *reinterpret_cast<uint4 *>(&sm.xt[1][ox]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+            *reinterpret_cast<uint4 *>(&xh[ox]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            *reinterpret_cast<uint4 *>(&xl[ox]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
         }
 #pragma unroll
-        for (int k = 0; k < BV; ++k) *reinterpret_cast<uint4 *>(&sm.bs[ob + k * (kThreads / BPR) * N]) = rb[k];
+        for (int k = 0; k < BV; ++k) *reinterpret_cast<uint4 *>(&bs[ob + k * (kThreads / BPR) * N]) = cur.b[k];
         // the state entering the chunk (stored for the backward), then its decay over the chunk
         if (owns_state) {
-            const float dec = __expf((float)T.cs[kC - 1]);
-            if (a.chunk_states) {
+            const float dec = T.dec;
+            if constexpr (kStoreStates) {
                 float *cst = a.chunk_states + (bh * a.nchunks + c) * N * P + 32 * spt + l32;
 #pragma unroll
                 for (int rr = 0; rr < 16; ++rr) cst[(32 * snt + 8 * (rr >> 2) + 4 * lg + (rr & 3)) * P] = st[rr];
@@ -268,25 +285,33 @@ __device__ __forceinline__ void state_walk(const FusedArgs &a, unsigned blk, uns
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) st[rr] *= dec;
         }
-        // next chunk's inputs (clamped to the last chunk: loads stay unconditional)
-        prefetch(min(c + 1, c1 - 1));
+        // the inputs of chunk c + 2 (clamped to the last chunk: loads stay unconditional)
+        prefetch(cur, min(c + 2, c1 - 1));
+        // the next chunk's per-token values
+        if (wave == kScanWave && c + 1 < c1) seg_decay += scan_chunk(c + 1, nxt.dt, sm.tok[buf ^ 1]);
         __syncthreads();
 
         // ================= tile update H += Σ_t B[t][n]·(w x)[t][p]: A = Bᵀ (rows n, k = t), B = w·x
         if (owns_state) {
 #pragma unroll
             for (int ks = 0; ks < kC / 16; ++ks) {
-                const bf16x8 aop = cat8(tr4(sm.bs + o_sa + 16 * ks * N), tr4(sm.bs + o_sb + 16 * ks * N));
-                const bf16x8 bhi = cat8(tr4(sm.xt[0] + o_xa + 16 * ks * 64), tr4(sm.xt[0] + o_xb + 16 * ks * 64));
-                const bf16x8 blo = cat8(tr4(sm.xt[1] + o_xa + 16 * ks * 64), tr4(sm.xt[1] + o_xb + 16 * ks * 64));
+                const bf16x8 aop = cat8(tr4(bs + o_sa + 16 * ks * N), tr4(bs + o_sb + 16 * ks * N));
+                const bf16x8 bhi = cat8(tr4(xh + o_xa + 16 * ks * 64), tr4(xh + o_xb + 16 * ks * 64));
+                const bf16x8 blo = cat8(tr4(xl + o_xa + 16 * ks * 64), tr4(xl + o_xb + 16 * ks * 64));
                 st = mfma(aop, bhi, st);
                 st = mfma(aop, blo, st);
             }
         }
-        // the next chunk's per-token values, while the tiles update
-        if (wave == kScanWave && c + 1 < c1) seg_decay += scan_chunk(c + 1, rdt, sm.tok[buf ^ 1]);
-        __syncthreads();
+    };
+    // two chunks per iteration and a last odd chunk after the loop: every path to
+    // the loop head then comes after the second step, so that the compiler does
+    // not wait there for the loads the first step has just issued
+    int c = c0;
+    for (; c + 1 < c1; c += 2) {
+        step(c, la, lb);
+        step(c + 1, lb, la);
     }
+    if (c < c1) step(c, la, lb);
 
     // ---- end of the walk
     float *dst = nullptr;
