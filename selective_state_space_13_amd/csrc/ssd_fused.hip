@@ -113,7 +113,13 @@ FusedPlan fused_plan(int batch, int seqlen, int nheads, int dstate) {
         if (rounds >= 2 && rem <= 128 && pl.nchunks >= 16) {
             pl.tail_from = (int)(bh - rem);
             pl.tail_mid = pl.nchunks / 2;
-            pl.ws_bytes = ((size_t)rem * dstate * P * sizeof(float) + 255) / 256 * 256;
+            // the state pass over the first halves is as long as its parts: up to
+            // 4 parts of at least 4 chunks, within one round of two workgroups per CU
+            int parts = 1;
+            while (parts < 4 && rem * parts * 2 <= 512 && pl.tail_mid / (parts * 2) >= 4) parts *= 2;  // at most 4: the fused pass chains up to 4
+            pl.tail_parts = parts;
+            pl.state_bytes = ((size_t)rem * parts * dstate * P * sizeof(float) + 255) / 256 * 256;
+            pl.ws_bytes = pl.state_bytes + ((size_t)rem * parts * sizeof(double) + 255) / 256 * 256;
         }
     }
     return pl;
@@ -146,6 +152,8 @@ hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const
     a.npairs = batch * nheads;
     a.tail_from = pl.tail_from;
     a.tail_mid = pl.tail_mid;
+    a.tail_parts = pl.tail_parts;
+    a.tail_decay = nullptr;
     unsigned items = (unsigned)((long long)batch * nheads * pl.nseg);
     if (pl.nseg > 1) {
         char *ws = static_cast<char *>(workspace);
@@ -156,8 +164,9 @@ hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const
         // phase 0: the state at the cut of every tail pair; phase 2: whole pairs and halves
         if (phase == 1) return hipErrorInvalidValue;
         a.tail_state = static_cast<float *>(workspace);
+        a.tail_decay = reinterpret_cast<double *>(static_cast<char *>(workspace) + pl.state_bytes);
         const unsigned ntail = (unsigned)(a.npairs - pl.tail_from);
-        items = phase == 0 ? ntail : (unsigned)pl.tail_from + 2 * ntail;
+        items = phase == 0 ? ntail * (unsigned)pl.tail_parts : (unsigned)pl.tail_from + 2 * ntail;
     } else if (phase != 2) {
         return hipErrorInvalidValue;
     }
@@ -207,6 +216,9 @@ hipError_t launch_ssd_fused_varlen(const int *cu_seqlens, int nseq, int total_to
     a.seg_chunks = a.nchunks + 1;
     a.npairs = nseq * nheads;
     a.tail_from = -1;
+    a.tail_parts = 1;
+    a.tail_state = nullptr;
+    a.tail_decay = nullptr;
     const unsigned items = (unsigned)((long long)nseq * nheads);
     if (dstate == 128)
         ssd_prefill_kernel<128><<<items, kThreads, 0, stream>>>(a);

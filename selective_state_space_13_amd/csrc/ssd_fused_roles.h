@@ -83,7 +83,7 @@ __device__ __forceinline__ void fused_roles_walk(const FusedArgs &a, unsigned bl
     {
         const float *src = nullptr;
         if (half == 1) {
-            src = a.tail_state + (size_t)(pair - a.tail_from) * N * P;
+            src = a.tail_state + (size_t)(pair - a.tail_from) * a.tail_parts * N * P;
         } else if (seg == 0) {
             if (a.h0) src = a.h0 + bh * N * P;
         } else {
@@ -97,6 +97,34 @@ __device__ __forceinline__ void fused_roles_walk(const FusedArgs &a, unsigned bl
                 const int n = 32 * (NT * nh + i) + 8 * (rr >> 2) + 4 * lg + (rr & 3);
                 st[i][rr] = src ? src[n * P + 32 * pt + l32] : 0.0f;
             }
+        // the second half of a cut pair: chain the first half's parts (at most 4).
+        // All their loads are issued at once (from clamped part indices, the extra
+        // ones unused), so that the chain costs one memory round trip, not three.
+        if (half == 1 && state_wave) {
+            const size_t t0 = (size_t)(pair - a.tail_from) * a.tail_parts;
+            float part[3][NT][16];
+#pragma unroll
+            for (int k = 1; k < 4; ++k) {
+                const float *sk = a.tail_state + (t0 + min(k, a.tail_parts - 1)) * N * P;
+#pragma unroll
+                for (int i = 0; i < NT; ++i)
+#pragma unroll
+                    for (int rr = 0; rr < 16; ++rr) {
+                        const int n = 32 * (NT * nh + i) + 8 * (rr >> 2) + 4 * lg + (rr & 3);
+                        part[k - 1][i][rr] = sk[n * P + 32 * pt + l32];
+                    }
+            }
+#pragma unroll
+            for (int k = 1; k < 4; ++k) {
+                if (k < a.tail_parts) {
+                    const float dk = __expf((float)a.tail_decay[t0 + k]);
+#pragma unroll
+                    for (int i = 0; i < NT; ++i)
+#pragma unroll
+                        for (int rr = 0; rr < 16; ++rr) st[i][rr] = dk * st[i][rr] + part[k - 1][i][rr];
+                }
+            }
+        }
         // vmcnt(0) once here: otherwise the first use of st inside the chunk loop
         // waits for every outstanding memory operation, the previous chunk's y
         // stores included, in every chunk

@@ -48,12 +48,17 @@ struct FusedArgs {
     // starts from hin (the true incoming state) instead of zero
     float *chunk_states;
     // pairs (b, h): items < npairs·nseg are (pair, segment); when tail_from >= 0
-    // the pairs from tail_from on are each cut at chunk tail_mid into two halves,
-    // the second half starting from tail_state[pair - tail_from] ([N][P] float),
-    // which the state-only pass (grid = npairs - tail_from) writes from h0
+    // the pairs from tail_from on are each cut at chunk tail_mid into two halves.
+    // The state-only pass (grid = (npairs - tail_from)·tail_parts) splits each
+    // first half into tail_parts parts of equal chunk counts (the last shorter)
+    // and writes part k's end state, from h0 for k = 0 and from zero otherwise,
+    // to tail_state[(pair - tail_from)·tail_parts + k] ([N][P] float) and its
+    // Σ Δ·A to tail_decay[same]; the second half starts from the parts chained:
+    // H = exp(Σ_k)·H + E_k for k = 1 .. tail_parts - 1, from H = E_0
     int npairs;
-    int tail_from, tail_mid;
+    int tail_from, tail_mid, tail_parts;
     float *tail_state;
+    double *tail_decay;
 };
 
 // The (batch row, head) pair, segment or half of a pair that workgroup blk of
@@ -61,6 +66,7 @@ struct FusedArgs {
 // ints, used by the longest-first ranking of packed batches (full pass only).
 struct WalkItem {
     int b, g, h, seg, pair, half;  // half: 0 / 1 for the two halves of a cut pair, -1 otherwise
+    int part;                      // part of a first half (state-only pass), else 0
     size_t row0;                   // rows row0 .. row0 + seqlen - 1 of the [rows][...] inputs
     int seqlen, c0, c1;
 };
@@ -96,6 +102,7 @@ __device__ __forceinline__ WalkItem map_walk_item(const FusedArgs &a, unsigned b
       }
     }
     int pair = 0, half = -1;  // half: 0 / 1 for the two halves of a cut pair, -1 otherwise
+    int part = 0;
     if (!ranked) {
         // pair q = (b, g) fastest, then the head within the group, so that all heads
         // of one B/C group run on the same XCD (workgroups are dealt to the 8 XCDs
@@ -105,6 +112,7 @@ __device__ __forceinline__ WalkItem map_walk_item(const FusedArgs &a, unsigned b
             const int k = STATE_ONLY ? (int)blk : (int)blk - a.tail_from;
             pair = a.tail_from + k % ntail;
             half = STATE_ONLY ? 0 : k / ntail;
+            if (STATE_ONLY) part = k / ntail;
         } else {
             pair = (int)blk % a.npairs;
             seg = (int)blk / a.npairs;
@@ -129,9 +137,14 @@ __device__ __forceinline__ WalkItem map_walk_item(const FusedArgs &a, unsigned b
     if (half >= 0) {
         c0 = half ? a.tail_mid : 0;
         c1 = half ? nchunks : min(a.tail_mid, nchunks);
+        if (STATE_ONLY) {
+            const int len = (a.tail_mid + a.tail_parts - 1) / a.tail_parts;
+            c0 = min(part * len, c1);
+            c1 = min(c0 + len, c1);
+        }
     }
     WalkItem it;
-    it.b = b; it.g = g; it.h = h; it.seg = seg; it.pair = pair; it.half = half;
+    it.b = b; it.g = g; it.h = h; it.seg = seg; it.pair = pair; it.half = half; it.part = part;
     it.row0 = row0; it.seqlen = seqlen; it.c0 = c0; it.c1 = c1;
     return it;
 }
@@ -183,8 +196,8 @@ __device__ __forceinline__ void state_walk(const FusedArgs &a, unsigned blk, uns
     f32x16 st;
     {
         const float *src = nullptr;
-        if (half == 1) {
-            src = a.tail_state + (size_t)(pair - a.tail_from) * N * P;
+        if (half == 0 && item.part > 0) {
+            src = nullptr;  // a later part of a first half starts from zero
         } else if (seg == 0) {
             if (a.h0) src = a.h0 + bh * N * P;
         } else if (a.chunk_states) {
@@ -316,7 +329,9 @@ __device__ __forceinline__ void state_walk(const FusedArgs &a, unsigned blk, uns
     // ---- end of the walk
     float *dst = nullptr;
     if (half == 0) {
-        dst = a.tail_state + (size_t)(pair - a.tail_from) * N * P;
+        const size_t slot = (size_t)(pair - a.tail_from) * a.tail_parts + item.part;
+        dst = a.tail_state + slot * N * P;
+        if (wave == kScanWave && lane == 0) a.tail_decay[slot] = seg_decay;
     } else if (!a.chunk_states) {
         dst = a.seg_state + (bh * a.nseg + seg) * N * P;
         if (wave == kScanWave && lane == 0) a.seg_decay[bh * a.nseg + seg] = seg_decay;

@@ -76,6 +76,7 @@ hipError_t launch_chunk_output_valu(int dtype, const void *x, const void *B, con
 struct FusedPlan {
     int nchunks = 0, nseg = 1, seg_chunks = 1;
     int tail_from = -1, tail_mid = 0;  // pairs from tail_from on are cut at chunk tail_mid
+    int tail_parts = 1;                // the state pass splits each first half into this many parts
     size_t state_bytes = 0, ws_bytes = 0;
 };
 FusedPlan fused_plan(int batch, int seqlen, int nheads, int dstate);

@@ -144,9 +144,12 @@ def test_workspace_size_and_layout(L):
 def test_bf16_workspace_is_small_or_segment_buffers(L):
     # the fused bf16 path keeps its stages on chip: 256 bytes unless the call is
     # cut into segments (few (batch, head) pairs, long sequence) or the last
-    # round's pairs are cut in halves (their states at the cut)
+    # round's pairs are cut in halves (the end states of the first halves' 4 parts,
+    # 16 chunks in 4 parts for 128 cut pairs, and their float64 log-decays)
     assert L.ssd_chunk_scan_workspace_size(8, 2048, 96, 64, 128, 1, 256, BF16) == 256
-    assert L.ssd_chunk_scan_workspace_size(8, 2048, 80, 64, 128, 1, 256, BF16) == 128 * 128 * 64 * 4
+    assert L.ssd_chunk_scan_workspace_size(8, 2048, 80, 64, 128, 1, 256, BF16) == 128 * 4 * 128 * 64 * 4 + 128 * 4 * 8
+    # a first half of 8 chunks is split into 2 parts of 4
+    assert L.ssd_chunk_scan_workspace_size(8, 1024, 80, 64, 128, 1, 256, BF16) == 128 * 2 * 128 * 64 * 4 + 2048
     assert L.ssd_chunk_scan_workspace_size(0, 2048, 80, 64, 128, 1, 256, BF16) == 256
     big = L.ssd_chunk_scan_workspace_size(1, 65536, 80, 64, 128, 8, 256, BF16)
     assert big > 2 * 80 * 128 * 64 * 4 and big % 256 == 0

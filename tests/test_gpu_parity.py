@@ -138,11 +138,14 @@ def test_prefill_segmented_bf16(case):
     assert_parity(to_f64(fs), fo, TAU_BF16, False, f"segmented final {case}")
 
 
-@pytest.mark.parametrize("case", [(3, 1100, 100, 128, 4, True, True), (5, 1024, 60, 64, 1, False, False)],
-                         ids=["b3L1100H100N128G4", "b5L1024H60N64G1"])
+@pytest.mark.parametrize("case", [(3, 1100, 100, 128, 4, True, True), (5, 1024, 60, 64, 1, False, False),
+                                  (2, 2200, 180, 128, 4, True, True)],
+                         ids=["b3L1100H100N128G4", "b5L1024H60N64G1", "b2L2200H180N128G4"])
 def test_prefill_tail_cut(case):
     """Two full rounds of 256 (batch, head) pairs and a short last round, whose
-    pairs are cut in halves (the second half starting from the state at the cut)."""
+    pairs are cut in halves (the second half starting from the state at the cut).
+    The state pass splits the first halves into parts that it chains: 2 parts of
+    5 and 4 chunks, 2 of 4, and 4 parts of 5, 5, 5 and 2 chunks."""
     b, L, H, N, G, wD, wh = case
     launches, nseg, cut = ssd.chunk_scan_plan(b, L, H, 64, N, G, 256, ssd.SSD_BF16)
     assert launches == 2 and nseg == 1 and cut == b * H - 256
