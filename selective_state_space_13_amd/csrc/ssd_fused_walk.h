@@ -199,7 +199,11 @@ __device__ __forceinline__ void state_walk(const FusedArgs &a, unsigned blk, uns
         if (half == 0 && item.part > 0) {
             src = nullptr;  // a later part of a first half starts from zero
         } else if (seg == 0) {
-            if (a.h0) src = a.h0 + bh * N * P;
+            // the first segment starts from h0 where this walk yields true states
+            // (the backward's chunk states, the cut of a pair); the forward's
+            // segment pass starts it from zero, as every other segment, since
+            // the combine adds h0 itself
+            if (a.h0 && (kStoreStates || a.nseg == 1)) src = a.h0 + bh * N * P;
         } else if (a.chunk_states) {
             src = a.hin + (bh * a.nseg + seg) * N * P;
         }

@@ -286,6 +286,21 @@ def test_prefill_segmented_extreme_decay_no_final_state():
     assert_parity(to_f64(y), yo, TAU_BF16, True, "segmented extreme y")
 
 
+def test_prefill_segmented_initial_state_weak_decay():
+    """Segments and an initial state that survives the whole sequence (A close to
+    zero, so exp(Σ Δ·A) over a segment stays near 1): the state pass, the combine
+    and the full pass must count h0 exactly once.  With the decays of the other
+    cases, h0 has vanished by the end of the first segment."""
+    b, L, H, N, G = 1, 4096, 2, 128, 1
+    d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=14, config_id=108, with_h0=True)
+    d["A"] = gen.Tensor(np.array([-1e-3, -3e-2], np.float32), "f32")
+    assert ssd.chunk_scan_plan(b, L, H, 64, N, G, 256, ssd.SSD_BF16)[1] > 1
+    y, fs = run_scan(d, 256, "bf16", True, True)
+    yo, fo = oracle_scan(d, True, True)
+    assert_parity(to_f64(y), yo, TAU_BF16, True, "segmented weak decay y")
+    assert_parity(to_f64(fs), fo, TAU_BF16, False, "segmented weak decay final")
+
+
 def test_prefill_segmented_deterministic():
     b, L, H, N, G = 1, 4096, 3, 128, 3
     d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=13, config_id=107, with_h0=True)
@@ -308,9 +323,11 @@ BWD_CASES = [
 ]
 
 
-def run_bwd(case, softplus=True, seed=0):
+def run_bwd(case, softplus=True, seed=0, A=None):
     b, L, H, N, G, wD, wh, wf = case
     d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=seed + L + H, config_id=130, with_h0=wh)
+    if A is not None:
+        d["A"] = gen.Tensor(np.asarray(A, np.float32), "f32")
     gr = gen.ssd_grad_inputs(b, L, H, 64, N, "bf16", seed=seed + L + H, config_id=130, with_dfinal=wf)
     if not softplus:  # raw dt as Δ: keep it positive and in range
         d["dt"] = gen.Tensor(gen.f32_to_bf16_bits(np.abs(d["dt"].f32()) * 0.05 + 0.01), "bf16")
@@ -337,6 +354,16 @@ def check_bwd(out, ref, what):
 def test_backward(case):
     out, ref = run_bwd(case)
     check_bwd(out, ref, f"bwd {case}")
+
+
+def test_backward_segmented_initial_state_weak_decay():
+    """The backward of a call the forward cuts into segments, with an initial
+    state that survives the whole sequence (A close to zero): the states the
+    backward rebuilds must count h0 once."""
+    case = (1, 1024, 4, 128, 1, True, True, True)
+    assert ssd.chunk_scan_plan(1, 1024, 4, 64, 128, 1, 256, ssd.SSD_BF16)[1] > 1
+    out, ref = run_bwd(case, A=[-1e-3, -3e-3, -1e-2, -3e-2])
+    check_bwd(out, ref, "bwd segmented weak decay")
 
 
 def test_backward_without_softplus():
