@@ -301,6 +301,20 @@ def test_prefill_segmented_initial_state_weak_decay():
     assert_parity(to_f64(fs), fo, TAU_BF16, False, "segmented weak decay final")
 
 
+def test_prefill_tail_cut_initial_state_weak_decay():
+    """The cut of the last round's pairs with an initial state that survives the
+    whole sequence: the first part of each first half starts from h0, the others
+    from zero, and the second half chains them; h0 must be counted once."""
+    b, L, H, N, G = 2, 2200, 180, 128, 4
+    assert ssd.chunk_scan_plan(b, L, H, 64, N, G, 256, ssd.SSD_BF16)[2] > 0
+    d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=15, config_id=109, with_h0=True)
+    d["A"] = gen.Tensor(-np.exp(np.random.default_rng(15).uniform(np.log(1e-3), np.log(3e-2), H)).astype(np.float32), "f32")
+    y, fs = run_scan(d, 256, "bf16", True, True)
+    yo, fo = oracle_scan(d, True, True)
+    assert_parity(to_f64(y), yo, TAU_BF16, True, "tail cut weak decay y")
+    assert_parity(to_f64(fs), fo, TAU_BF16, False, "tail cut weak decay final")
+
+
 def test_prefill_segmented_deterministic():
     b, L, H, N, G = 1, 4096, 3, 128, 3
     d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=13, config_id=107, with_h0=True)
@@ -721,6 +735,26 @@ def test_mamba1_segmented(b, L, dim, N, dtype):
                                    d["C"].f64(), d["D"].f64(), d["z"].f64(), return_final_state=True)
     assert_parity(to_f64(out), oo, tau_of(dtype), dtype == "bf16", f"mamba1 segmented out {dtype}")
     assert_parity(to_f64(fs), fo, tau_of(dtype), False, f"mamba1 segmented final {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mamba1_segmented_weak_decay(dtype):
+    """Time segments with decays near 1 (A from -1e-3 to -1e-2), so that every
+    segment's incoming state carries far into it: the segment states and their
+    combine are checked where the hand-off dominates the output."""
+    b, L, dim, N = 1, 2000, 128, 16
+    code = ssd.SSD_F32 if dtype == "f32" else ssd.SSD_BF16
+    assert ssd.lib().selective_scan_workspace_size(b, L, dim, N, code) > 0
+    d = gen.mamba1_inputs(b, L, dim, N, dtype, seed=3, config_id=123)
+    rng = np.random.default_rng(13)
+    d["A"] = gen.Tensor(-np.exp(rng.uniform(np.log(1e-3), np.log(1e-2), (dim, N))).astype(np.float32), "f32")
+    out, fs = ssd.selective_scan(to_dev(d["u"]), to_dev(d["delta"]), to_dev(d["A"]), to_dev(d["B"]),
+                                 to_dev(d["C"]), to_dev(d["D"]), to_dev(d["z"]), return_final_state=True)
+    torch.cuda.synchronize()
+    oo, fo = oracle.selective_scan(d["u"].f64(), d["delta"].f64(), d["A"].f64(), d["B"].f64(),
+                                   d["C"].f64(), d["D"].f64(), d["z"].f64(), return_final_state=True)
+    assert_parity(to_f64(out), oo, tau_of(dtype), dtype == "bf16", f"mamba1 weak decay out {dtype}")
+    assert_parity(to_f64(fs), fo, tau_of(dtype), False, f"mamba1 weak decay final {dtype}")
 
 
 def test_mamba1_general_A():
