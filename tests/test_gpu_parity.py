@@ -123,6 +123,7 @@ SEGMENTED_CASES = [
     (1, 4096, 2, 128, 1, True, True),
     (2, 3000, 3, 64, 3, False, True),     # ragged last chunk
     (1, 8192, 1, 128, 1, True, False),
+    (1, 16384, 64, 128, 2, True, True),  # 4 segments of 64 chunks, 64 heads
 ]
 
 
@@ -291,9 +292,9 @@ def test_prefill_segmented_initial_state_weak_decay():
     zero, so exp(Σ Δ·A) over a segment stays near 1): the state pass, the combine
     and the full pass must count h0 exactly once.  With the decays of the other
     cases, h0 has vanished by the end of the first segment."""
-    b, L, H, N, G = 1, 4096, 2, 128, 1
+    b, L, H, N, G = 1, 16384, 64, 64, 1  # 4 segments of 64 chunks, 64 heads
     d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=14, config_id=108, with_h0=True)
-    d["A"] = gen.Tensor(np.array([-1e-3, -3e-2], np.float32), "f32")
+    d["A"] = gen.Tensor(-np.exp(np.random.default_rng(14).uniform(np.log(1e-3), np.log(3e-2), H)).astype(np.float32), "f32")
     assert ssd.chunk_scan_plan(b, L, H, 64, N, G, 256, ssd.SSD_BF16)[1] > 1
     y, fs = run_scan(d, 256, "bf16", True, True)
     yo, fo = oracle_scan(d, True, True)
