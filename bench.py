@@ -399,8 +399,9 @@ def main():
                          "known size, against which HBM byte counters are scaled")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU "
-                                   "sharding is not part of this build", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the library has no "
+                                   "multi-GPU path (how the scan would shard is described, not "
+                                   "implemented)", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import torch
