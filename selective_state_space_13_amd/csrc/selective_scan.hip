@@ -105,8 +105,11 @@ struct ScanArgs {
     const float *hin;        // [b][S][dim][N] state entering each segment s >= 1 (MODE 1)
 };
 
+// At most 128 registers (4 waves per SIMD): the dstate-16 output pass would
+// otherwise take 133 and fit 3 waves; the cap costs a small spill and measured
+// 3.5% faster.
 template <typename T, int N, int MODE>
-__global__ __launch_bounds__(256) void selective_scan_kernel(
+__global__ __launch_bounds__(256, 4) void selective_scan_kernel(
     const T *__restrict__ u, const T *__restrict__ delta, const float *__restrict__ A,
     const T *__restrict__ B, const T *__restrict__ C, const float *__restrict__ D,
     const T *__restrict__ z, ScanArgs sa, T *__restrict__ out, float *__restrict__ final_state) {
