@@ -371,14 +371,15 @@ def test_backward(case):
     check_bwd(out, ref, f"bwd {case}")
 
 
-def test_backward_segmented_initial_state_weak_decay():
+@pytest.mark.parametrize("N", [128, 64])
+def test_backward_segmented_initial_state_weak_decay(N):
     """The backward of a call the forward cuts into segments, with an initial
     state that survives the whole sequence (A close to zero): the states the
-    backward rebuilds must count h0 once."""
-    case = (1, 1024, 4, 128, 1, True, True, True)
-    assert ssd.chunk_scan_plan(1, 1024, 4, 64, 128, 1, 256, ssd.SSD_BF16)[1] > 1
+    backward rebuilds must count h0 once (dstate 64 walks with half the waves)."""
+    case = (1, 1024, 4, N, 1, True, True, True)
+    assert ssd.chunk_scan_plan(1, 1024, 4, 64, N, 1, 256, ssd.SSD_BF16)[1] > 1
     out, ref = run_bwd(case, A=[-1e-3, -3e-3, -1e-2, -3e-2])
-    check_bwd(out, ref, "bwd segmented weak decay")
+    check_bwd(out, ref, f"bwd segmented weak decay N{N}")
 
 
 def test_backward_without_softplus():
