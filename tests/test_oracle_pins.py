@@ -598,3 +598,47 @@ def test_pin16_bf16_state_decode_exact_case_and_rounding_bound():
     assert np.max(np.abs(s16[nz] - s64[nz]) / np.abs(s64[nz])) <= 2.0**-8
     assert np.array_equal(oracle.round_bf16(s16), s16)
     assert not np.array_equal(s16, s64)
+
+
+# ---------------------------------------------------------------- golden fixtures
+# tests/golden/*.json: small fixed inputs and the oracle's float64 outputs,
+# written by tests/golden/make_golden.py (which calls only the oracle).  The
+# pages print no worked example; these fixtures pin the oracle against silent
+# change of its arithmetic.
+
+def _golden(name):
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", name)) as f:
+        d = json.load(f)
+    arr = {k: np.asarray(v, np.float64).reshape(d["shapes"][k]) for k, v in d["inputs"].items()}
+    return d, arr
+
+
+def _same(got, want, what):
+    got = np.asarray(got, np.float64).ravel()
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, what
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14, err_msg=what)
+
+
+def test_golden_ssd_scan():
+    d, a = _golden("ssd_scan.json")
+    y, fs = oracle.ssd_scan(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["h0"], return_final_state=True)
+    _same(y, d["outputs"]["y"], "y")
+    _same(fs, d["outputs"]["final_state"], "final state")
+
+
+def test_golden_ssd_decode():
+    d, a = _golden("ssd_decode.json")
+    y, st = oracle.ssd_decode(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["state"])
+    _same(y, d["outputs"]["y"], "y")
+    _same(st, d["outputs"]["state"], "state")
+
+
+def test_golden_selective_scan():
+    d, a = _golden("selective_scan.json")
+    out, fs = oracle.selective_scan(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"],
+                                    return_final_state=True)
+    _same(out, d["outputs"]["out"], "out")
+    _same(fs, d["outputs"]["final_state"], "final state")
