@@ -316,6 +316,19 @@ def test_prefill_tail_cut_initial_state_weak_decay():
     assert_parity(to_f64(fs), fo, TAU_BF16, False, "tail cut weak decay final")
 
 
+@pytest.mark.parametrize("L,H", [(700, 4), (4096, 2)], ids=["L700H4", "L4096H2segmented"])
+def test_prefill_zero_decay(L, H):
+    """A_h = 0 (the degenerate end of A_h <= 0): nothing decays, every state is
+    the running sum of Δ·B xᵀ, and each segment hands on exp(0) = 1."""
+    b, N, G = 1, 128, 1
+    d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=L, config_id=110, with_h0=True)
+    d["A"] = gen.Tensor(np.zeros(H, np.float32), "f32")
+    y, fs = run_scan(d, 256, "bf16", True, True)
+    yo, fo = oracle_scan(d, True, True)
+    assert_parity(to_f64(y), yo, TAU_BF16, True, f"zero decay y L{L}")
+    assert_parity(to_f64(fs), fo, TAU_BF16, False, f"zero decay final L{L}")
+
+
 def test_prefill_segmented_deterministic():
     b, L, H, N, G = 1, 4096, 3, 128, 3
     d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=13, config_id=107, with_h0=True)
