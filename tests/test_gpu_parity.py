@@ -395,6 +395,13 @@ def test_backward_segmented_initial_state_weak_decay(N):
     check_bwd(out, ref, f"bwd segmented weak decay N{N}")
 
 
+def test_backward_zero_decay():
+    """A_h = 0: no decay anywhere, cs = 0 in every chunk; dA is then the plain
+    sum Σ Δ·dℓ of the per-token gradients."""
+    out, ref = run_bwd((2, 300, 4, 128, 2, True, True, True), A=[0.0, 0.0, 0.0, 0.0])
+    check_bwd(out, ref, "bwd zero decay")
+
+
 def test_backward_without_softplus():
     out, ref = run_bwd((2, 150, 4, 128, 1, True, True, True), softplus=False)
     check_bwd(out, ref, "bwd raw dt")
