@@ -193,6 +193,27 @@ def test_prefill_varlen_packed(case):
             assert torch.equal(fs[s], ref)
 
 
+@pytest.mark.parametrize("wh", [False, True], ids=["zero_start", "own_h0"])
+def test_prefill_varlen_weak_decay(wh):
+    """Packed sequences with decays near 1 (A from -1e-3 to -3e-2), so that a
+    state carried over a sequence boundary, or a wrong sequence's initial state,
+    would persist through the whole next sequence instead of decaying away."""
+    lengths, H, N, G = [700, 1, 0, 1300, 64, 900], 4, 128, 2
+    d = gen.ssd_varlen_inputs(lengths, H, 64, N, G, "bf16", seed=5, config_id=111, with_D=True, with_h0=wh)
+    d["A"] = gen.Tensor(-np.exp(np.random.default_rng(5).uniform(np.log(1e-3), np.log(3e-2), H)).astype(np.float32), "f32")
+    x, dt, B, C, A, D = (to_dev(d[k]) for k in ("x", "dt", "B", "C", "A", "D"))
+    h0 = to_dev(d["h0"]) if wh else None
+    cu = torch.from_numpy(d["cu_seqlens"]).cuda()
+    y, fs = ssd.ssd_chunk_scan_varlen(x, dt, A, B, C, D, cu_seqlens=cu, initial_states=h0,
+                                      return_final_states=True)
+    torch.cuda.synchronize()
+    yo, fo = oracle.ssd_scan_varlen(d["x"].f64(), d["dt"].f64(), d["A"].f64(), d["B"].f64(),
+                                    d["C"].f64(), d["cu_seqlens"], d["D"].f64(),
+                                    d["h0"].f64() if wh else None, return_final_state=True)
+    assert_parity(to_f64(y), yo, TAU_BF16, True, f"varlen weak decay y h0={wh}")
+    assert_parity(to_f64(fs), fo, TAU_BF16, False, f"varlen weak decay final h0={wh}")
+
+
 def test_prefill_extreme_decay_and_large_steps():
     """Δ up to ~10 with A = -16: chunk decays underflow float32; results stay finite
     and match the oracle."""
