@@ -609,6 +609,29 @@ def test_decode_small_chain(N, G, wD, dtype):
     assert_parity(to_f64(state), ost, tau_of(dtype), False, "decode state")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_without_softplus(dtype):
+    """dt_softplus = 0: the dt values are Δ itself (positive, stored in the
+    input dtype), for a short chain of steps."""
+    b, H, P, N, G, steps = 3, 4, 64, 64, 2, 4
+    A, D = gen.ssd_params(H, seed=3, config_id=112)
+    rng = np.random.default_rng(33)
+    st0 = (rng.standard_normal((b, H, N, P)) * 0.05).astype(np.float32)
+    state = torch.from_numpy(st0).cuda()
+    ost = st0.astype(np.float64)
+    for k in range(steps):
+        s = gen.decode_inputs(b, H, P, N, G, dtype, step=k, seed=3, config_id=112)
+        raw = np.abs(s["dt"].f32()) * 0.05 + 0.01  # Δ in [0.01, ~0.2]
+        s["dt"] = gen._store(raw.astype(np.float32), dtype)
+        y = ssd.ssd_decode_step(to_dev(s["x"]), to_dev(s["dt"]), to_dev(A), to_dev(s["B"]), to_dev(s["C"]),
+                                to_dev(D), state, dt_softplus=False)
+        torch.cuda.synchronize()
+        yo, ost = oracle.ssd_decode(s["x"].f64(), s["dt"].f64(), A.f64(), s["B"].f64(), s["C"].f64(),
+                                    D.f64(), ost, dt_softplus=False)
+        assert_parity(to_f64(y), yo, tau_of(dtype), dtype == "bf16", f"decode raw dt y step {k}")
+    assert_parity(to_f64(state), ost, tau_of(dtype), False, "decode raw dt state")
+
+
 def test_config4_decode_chain_full(config2):
     """64 single-token steps at batch 256 from the state a 2.7B-layer-shaped
     prefill leaves (the oracle's own prefill of the 8-row prefill workload,
