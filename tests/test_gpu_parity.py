@@ -823,6 +823,25 @@ def test_mamba1_segmented_weak_decay(dtype):
     assert_parity(to_f64(fs), fo, tau_of(dtype), False, f"mamba1 weak decay final {dtype}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mamba1_without_softplus(dtype):
+    """delta_softplus = 0: the delta values are Δ itself (positive), on a
+    segmented call (state pass, combine, output pass)."""
+    b, L, dim, N = 1, 2000, 128, 16
+    d = gen.mamba1_inputs(b, L, dim, N, dtype, seed=4, config_id=124)
+    raw = np.abs(d["delta"].f32()) * 0.05 + 0.01
+    d["delta"] = gen._store(raw.astype(np.float32), dtype)
+    out, fs = ssd.selective_scan(to_dev(d["u"]), to_dev(d["delta"]), to_dev(d["A"]), to_dev(d["B"]),
+                                 to_dev(d["C"]), to_dev(d["D"]), to_dev(d["z"]), delta_softplus=False,
+                                 return_final_state=True)
+    torch.cuda.synchronize()
+    oo, fo = oracle.selective_scan(d["u"].f64(), d["delta"].f64(), d["A"].f64(), d["B"].f64(),
+                                   d["C"].f64(), d["D"].f64(), d["z"].f64(), delta_softplus=False,
+                                   return_final_state=True)
+    assert_parity(to_f64(out), oo, tau_of(dtype), dtype == "bf16", f"mamba1 raw delta out {dtype}")
+    assert_parity(to_f64(fs), fo, tau_of(dtype), False, f"mamba1 raw delta final {dtype}")
+
+
 def test_mamba1_general_A():
     """A not of the -(n+1) form: per-channel, per-state random decay rates."""
     b, L, dim, N = 2, 200, 128, 16
