@@ -15,7 +15,8 @@ links or calls it, and the two share no code.
 Parity status: every function is pinned by the CPU tests in
 ``tests/test_oracle_pins.py`` (closed forms, the dual form, the block
 decomposition, state hand-off, linearity, reductions between the scan
-variants); none is "parity unpinned".
+variants; for the gated RMSNorm, closed forms that fix its per-channel weight
+and its silu gate); none is "parity unpinned".
 """
 from __future__ import annotations
 

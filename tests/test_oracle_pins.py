@@ -451,6 +451,43 @@ def test_rmsnorm_scale_invariance_groups_and_gate():
     assert np.all(oracle.gated_rmsnorm(y, np.zeros_like(y), w, 4, 1e-5) == 0.0)
 
 
+def test_rmsnorm_constant_group_gives_sign_times_weight():
+    """A group whose values are all one constant c has mean square c², so with
+    no gate and eps = 0 each output is c/|c| times its channel's weight, exactly
+    (page 1 §4.1: the norm divides each group by its own root mean square, then
+    scales per channel).  Random weights pin the per-channel scale and its
+    channel index."""
+    rng = np.random.default_rng(25)
+    rows, ch, ng = 6, 24, 3
+    cg = ch // ng
+    w = rng.normal(size=ch)
+    consts = rng.uniform(0.5, 4.0, size=(rows, ng)) * rng.choice([-1.0, 1.0], size=(rows, ng))
+    y = np.repeat(consts, cg, axis=1)
+    out = oracle.gated_rmsnorm(y, None, w, ngroups=ng, eps=0.0)
+    np.testing.assert_allclose(out, np.sign(y) * w[None, :], rtol=1e-15, atol=0)
+
+
+def test_rmsnorm_silu_gate_closed_form():
+    """y = 1 with z alternating +ln 3 and -ln 3: silu(±ln 3) = ±ln 3 · σ(±ln 3)
+    gives g = (3/4) ln 3 and -(1/4) ln 3.  A group of such pairs has mean square
+    (9/16 + 1/16)/2 · ln²3 = (5/16) ln²3, so with eps = 0 the outputs are
+    3/√5 · weight and -1/√5 · weight.  A gate applied as z itself, or as
+    σ(z), gives other values; so does a dropped weight."""
+    rng = np.random.default_rng(26)
+    rows, ch, ng = 3, 16, 2
+    w = rng.normal(size=ch)
+    z = np.tile(np.array([math.log(3.0), -math.log(3.0)]), (rows, ch // 2))
+    out = oracle.gated_rmsnorm(np.ones((rows, ch)), z, w, ngroups=ng, eps=0.0)
+    expect = np.tile(np.array([3.0, -1.0]) / math.sqrt(5.0), (rows, ch // 2)) * w[None, :]
+    np.testing.assert_allclose(out, expect, rtol=1e-14, atol=0)
+    # with eps the group scale becomes 1/sqrt((5/16) ln²3 + eps)
+    eps = 0.25
+    out_e = oracle.gated_rmsnorm(np.ones((rows, ch)), z, w, ngroups=ng, eps=eps)
+    g = np.tile(np.array([0.75, -0.25]) * math.log(3.0), (rows, ch // 2))
+    np.testing.assert_allclose(out_e, g / math.sqrt(5.0 / 16.0 * math.log(3.0) ** 2 + eps) * w,
+                               rtol=1e-14, atol=0)
+
+
 # ------------------------------------------------------------------ backward
 # The gradient of the scan (the chunked backward of page "5.3 텐서 병렬화(Tensor
 # Parallelism) 지원과 대규모 클러스터 학습", §3.2 decomposition differentiated) is
