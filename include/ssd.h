@@ -30,14 +30,24 @@
  *    outputs are rounded to the input dtype, states stay float32.
  *  - The caller owns every buffer, including the workspace.  The library never
  *    allocates device memory, never synchronises, and keeps no pointer after
- *    return.  Work is enqueued on `stream` (a hipStream_t; NULL = null stream).
+ *    return, with one exception: ssd_set_launch_events (a benchmarking hook)
+ *    keeps the caller's event array, per thread, until it is cleared.  Work is
+ *    enqueued on `stream` (a hipStream_t passed as void *, so that this header
+ *    needs no HIP include; NULL = null stream).
+ *  - `dtype` arguments take an ssd_dtype value passed as int, for the same
+ *    reason of a plain-C ABI; any other value returns SSD_ERR_UNSUPPORTED.
  *  - Outputs must not overlap inputs or each other (SSD_ERR_ALIAS).
  *  - All validation happens on the host before anything is enqueued: on a
  *    non-zero return nothing ran.  SSD_ERR_HIP means a launch failed part-way
  *    (outputs undefined).  Device faults surface at the caller's next sync.
  *  - Return value: 0 (SSD_OK) or a negative ssd_status; ssd_last_error()
  *    gives a thread-local detail string for the last non-OK return.
- *  - Reentrant and thread-safe; the only mutable global is that string.
+ *  - Reentrant and thread-safe.  The mutable state is per thread: the last
+ *    error string, and the event array of ssd_set_launch_events while set.
+ *  - Decay sign.  The method's regime is A < 0 (decay; A = 0 holds the state).
+ *    A > 0 (growth) is computed by the same formulas and matches the float64
+ *    recurrence as long as every true intermediate stays in float32 range;
+ *    where it does not, the outputs are inf or NaN, as the arithmetic gives.
  */
 #ifndef LIBSSD_SSD_H
 #define LIBSSD_SSD_H
@@ -84,7 +94,7 @@ const char *ssd_last_error(void);
  *
  *   x      [batch][seqlen][nheads][headdim]      dtype
  *   dt     [batch][seqlen][nheads]               dtype  (raw if dt_softplus)
- *   A      [nheads]                              float  (A_h, normally < 0)
+ *   A      [nheads]                              float  (A_h; < 0 decays, see "Decay sign")
  *   B, C   [batch][seqlen][ngroups][dstate]      dtype
  *   D      [nheads]                              float  or NULL (= 0)
  *   initial_state [batch][nheads][dstate][headdim] float or NULL (= 0)

@@ -287,7 +287,7 @@ __device__ __forceinline__ void fused_roles_walk(const FusedArgs &a, unsigned bl
             const double cs_i = T.cs[32 * I + l32];
             const double cs_r = T.cs[32 * J + 31];
             float m[16];
-            const bool exact = J == I && (float)(T.cs[32 * J] - cs_r) > kMaxBlockDecay;
+            const bool exact = J == I && fabsf((float)(T.cs[32 * J] - cs_r)) > kMaxBlockDecay;
             if (!exact) {
                 const float u = __expf((float)(cs_i - cs_r));
 #pragma unroll
