@@ -118,6 +118,34 @@ int ssd_chunk_scan_fwd(int batch, int seqlen, int nheads, int headdim, int dstat
                        void *y, float *final_state,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * ssd_chunk_scan_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as ssd_chunk_scan_fwd, without the
+ * workspace: the call uses the library's own scratch array instead, a
+ * file-scope device array of ssd_noalloc_scratch_bytes() bytes (128 MiB) that
+ * every GPU the library runs on holds from its first use there until the
+ * process ends.  Nothing is allocated by the call.
+ *
+ *  - A call whose workspace (ssd_chunk_scan_workspace_size) would exceed that
+ *    size returns SSD_ERR_WORKSPACE before anything runs.  That covers every
+ *    bf16 call up to the 64K-token, 80-head shape (80 MiB); float32 calls need
+ *    their stages, about batch·seqlen·nheads·dstate·headdim·4/chunk bytes.
+ *  - Every call on one GPU shares that GPU's array, which keeps the last call's
+ *    contents.  Calls that overlap in time on one GPU (other streams, other
+ *    host threads) race on it: the caller serialises them.
+ *  - The scratch address of a device is looked up on the first call made with
+ *    that device current (SSD_ERR_HIP if the lookup fails).
+ * ------------------------------------------------------------------------ */
+int ssd_chunk_scan_fwd_noalloc(int batch, int seqlen, int nheads, int headdim, int dstate,
+                               int ngroups, int chunk, int dtype, int dt_softplus,
+                               const void *x, const void *dt, const float *A, const void *B,
+                               const void *C, const float *D, const float *initial_state,
+                               void *y, float *final_state, void *stream);
+
+/* Size in bytes of the scratch array ssd_chunk_scan_fwd_noalloc uses. */
+size_t ssd_noalloc_scratch_bytes(void);
+
 /* Byte offsets of the intermediate stages that the SSD_F32 path leaves in the
  * workspace, for inspection by tests (contents valid after the call):
  *   delta  [batch][nheads][nchunks][chunk] float   Δ per token (0 past the end)

@@ -64,6 +64,9 @@ def lib() -> ctypes.CDLL:
     L.ssd_chunk_scan_plan.restype = i
     L.ssd_chunk_scan_fwd.argtypes = [i] * 9 + [vp] * 10 + [sz, vp]
     L.ssd_chunk_scan_fwd.restype = i
+    L.ssd_chunk_scan_fwd_noalloc.argtypes = [i] * 9 + [vp] * 10
+    L.ssd_chunk_scan_fwd_noalloc.restype = i
+    L.ssd_noalloc_scratch_bytes.restype = sz
     L.ssd_chunk_scan_bwd_workspace_size.argtypes = [i] * 7
     L.ssd_chunk_scan_bwd_workspace_size.restype = sz
     L.ssd_chunk_scan_bwd.argtypes = [i] * 8 + [vp] * 17 + [sz, vp]
@@ -203,6 +206,39 @@ def ssd_chunk_scan(x, dt, A, B, C, D=None, *, chunk, initial_state=None,
         _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(initial_state),
         _ptr(y), _ptr(fs), _ptr(workspace), workspace.numel(), _stream(dev)))
     return (y, fs) if return_final_state else y
+
+
+def ssd_chunk_scan_fwd_noalloc(x, dt, A, B, C, D=None, *, chunk, initial_state=None,
+                               out, final_state=None, dt_softplus=True):
+    """ssd_chunk_scan through the entry point that allocates nothing: the caller
+    passes the output y (`out`) and, optionally, `final_state`; the library uses
+    its own per-device scratch array in place of a workspace.  Returns
+    y or (y, final_state)."""
+    torch = _torch()
+    x = _req(x, "x")
+    dev = x.device
+    code = _dtype_code(x)
+    b, L, H, P = x.shape
+    _req(dt, "dt", x.dtype, dev)
+    _req(B, "B", x.dtype, dev)
+    _req(C, "C", x.dtype, dev)
+    _req(A, "A", torch.float32, dev)
+    _req(D, "D", torch.float32, dev)
+    _req(initial_state, "initial_state", torch.float32, dev)
+    _req(out, "out", x.dtype, dev)
+    _req(final_state, "final_state", torch.float32, dev)
+    G, N = B.shape[2], B.shape[3]
+    if tuple(dt.shape) != (b, L, H) or tuple(B.shape) != (b, L, G, N) or C.shape != B.shape:
+        raise ValueError("shape mismatch among x, dt, B, C")
+    if out.shape != x.shape:
+        raise ValueError("out must have the shape of x")
+    if final_state is not None and tuple(final_state.shape) != (b, H, N, P):
+        raise ValueError("final_state must be [batch, nheads, dstate, headdim]")
+    check(lib().ssd_chunk_scan_fwd_noalloc(
+        b, L, H, P, N, G, chunk, code, int(bool(dt_softplus)),
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(initial_state),
+        _ptr(out), _ptr(final_state), _stream(dev)))
+    return (out, final_state) if final_state is not None else out
 
 
 def ssd_chunk_scan_bwd(x, dt, A, B, C, dy, D=None, *, initial_state=None, dfinal_state=None,

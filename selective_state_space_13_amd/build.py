@@ -28,6 +28,7 @@ SOURCES = [
     "decode.hip",
     "selective_scan.hip",
     "misc.hip",
+    "noalloc.hip",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -199,6 +199,109 @@ int decode_step(int batch, int nheads, int headdim, int dstate, int ngroups, int
     return e == hipSuccess ? SSD_OK : hip_fail(e, "decode launch");
 }
 
+// ssd_chunk_scan_fwd, with the caller's workspace or (use_scratch) the
+// library's own scratch buffer on the current device.
+int chunk_scan_fwd(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
+                   int chunk, int dtype, int dt_softplus, const void *x, const void *dt,
+                   const float *A, const void *B, const void *C, const float *D,
+                   const float *initial_state, void *y, float *final_state, void *workspace,
+                   size_t workspace_bytes, void *stream_, bool use_scratch) {
+    ScanLayout lay;
+    int st = scan_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, lay);
+    if (st) return st;
+    if (use_scratch && lay.total > ssd::kScratchBytes)
+        return fail(SSD_ERR_WORKSPACE,
+                    "this call needs %zu bytes of scratch; the no-allocation entry point has %zu",
+                    lay.total, (size_t)ssd::kScratchBytes);
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    const int es = elem_size(dtype);
+    uint64_t n_x, n_dt, n_bc, n_state;
+    prod(n_x, {batch, seqlen, nheads, headdim});
+    prod(n_dt, {batch, seqlen, nheads});
+    prod(n_bc, {batch, seqlen, ngroups, dstate});
+    prod(n_state, {batch, nheads, dstate, headdim});
+
+    if (batch == 0) return SSD_OK;
+    if (seqlen == 0) {
+        // empty sequence: the final state is the initial one
+        if (!final_state) return SSD_OK;
+        if (!aligned(final_state, 16) || (initial_state && !aligned(initial_state, 16)))
+            return fail(SSD_ERR_ALIGN, "state pointers must be 16-byte aligned");
+        st = check_alias({span("final_state", final_state, n_state * 4)},
+                         {span("initial_state", initial_state, n_state * 4)});
+        if (st) return st;
+        hipError_t e = ssd::launch_copy_state(initial_state, final_state, n_state, stream);
+        return e == hipSuccess ? SSD_OK : hip_fail(e, "state copy");
+    }
+    if (!x || !dt || !A || !B || !C || !y)
+        return fail(SSD_ERR_NULL, "x, dt, A, B, C and y are required");
+    const void *ptrs[] = {x, dt, A, B, C, D, initial_state, y, final_state};
+    for (const void *p : ptrs)
+        if (p && !aligned(p, 16)) return fail(SSD_ERR_ALIGN, "tensor pointer %p is not 16-byte aligned", p);
+    if (use_scratch) {
+        hipError_t se = ssd::scratch_for_current_device(&workspace);
+        if (se != hipSuccess) return hip_fail(se, "scratch address lookup");
+        workspace_bytes = ssd::kScratchBytes;
+    }
+    if (!workspace || workspace_bytes < lay.total)
+        return fail(SSD_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", lay.total,
+                    workspace_bytes, workspace ? "" : " (NULL)");
+    if (!aligned(workspace, 256)) return fail(SSD_ERR_ALIGN, "workspace must be 256-byte aligned");
+    st = check_alias(
+        {span("y", y, n_x * es), span("final_state", final_state, n_state * 4),
+         span("workspace", workspace, lay.total)},
+        {span("x", x, n_x * es), span("dt", dt, n_dt * es), span("A", A, (uint64_t)nheads * 4),
+         span("B", B, n_bc * es), span("C", C, n_bc * es), span("D", D, D ? (uint64_t)nheads * 4 : 0),
+         span("initial_state", initial_state, initial_state ? n_state * 4 : 0)});
+    if (st) return st;
+
+    char *ws = static_cast<char *>(workspace);
+    LaunchMarks marks(stream);
+    hipError_t e;
+    if (prefill_fused(dtype)) {
+        static const char *what[3] = {"state pass launch", "segment combine launch",
+                                      "fused prefill launch"};
+        const bool cut = lay.plan.nseg > 1 || lay.plan.tail_from >= 0;
+        for (int phase = cut ? 0 : 2; phase < 3; ++phase) {
+            if (phase == 1 && lay.plan.nseg <= 1) continue;  // a tail cut needs no combine
+            marks.before();
+            e = ssd::launch_ssd_fused(phase, lay.plan, x, dt, A, B, C, D, initial_state, dt_softplus,
+                                      batch, seqlen, nheads, headdim, dstate, ngroups, y,
+                                      final_state, ws, stream);
+            marks.after();
+            if (e != hipSuccess) return hip_fail(e, what[phase]);
+        }
+        return SSD_OK;
+    }
+    float *delta = reinterpret_cast<float *>(ws + lay.off_delta);
+    double *cs = reinterpret_cast<double *>(ws + lay.off_cs);
+    const int K = lay.nchunks;
+    marks.before();
+    e = ssd::launch_dt_cumsum(dtype, dt, A, dt_softplus, batch, seqlen, nheads, chunk, K, delta, cs,
+                              stream);
+    marks.after();
+    if (e != hipSuccess) return hip_fail(e, "dt cumsum launch");
+    {
+        float *S = reinterpret_cast<float *>(ws + lay.off_hprev);
+        marks.before();
+        e = ssd::launch_chunk_state_valu(dtype, x, B, delta, cs, batch, seqlen, nheads, headdim,
+                                         dstate, ngroups, chunk, K, S, stream);
+        marks.after();
+        if (e != hipSuccess) return hip_fail(e, "chunk state launch");
+        marks.before();
+        e = ssd::launch_state_pass_valu(cs, initial_state, batch, nheads, headdim, dstate, chunk,
+                                        K, S, final_state, stream);
+        marks.after();
+        if (e != hipSuccess) return hip_fail(e, "state pass launch");
+        marks.before();
+        e = ssd::launch_chunk_output_valu(dtype, x, B, C, D, delta, cs, S, batch, seqlen, nheads,
+                                          headdim, dstate, ngroups, chunk, K, y, stream);
+        marks.after();
+        if (e != hipSuccess) return hip_fail(e, "chunk output launch");
+    }
+    return SSD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -273,92 +376,22 @@ int ssd_chunk_scan_fwd(int batch, int seqlen, int nheads, int headdim, int dstat
                        const float *A, const void *B, const void *C, const float *D,
                        const float *initial_state, void *y, float *final_state, void *workspace,
                        size_t workspace_bytes, void *stream_) {
-    ScanLayout lay;
-    int st = scan_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, lay);
-    if (st) return st;
-    hipStream_t stream = static_cast<hipStream_t>(stream_);
-    const int es = elem_size(dtype);
-    uint64_t n_x, n_dt, n_bc, n_state;
-    prod(n_x, {batch, seqlen, nheads, headdim});
-    prod(n_dt, {batch, seqlen, nheads});
-    prod(n_bc, {batch, seqlen, ngroups, dstate});
-    prod(n_state, {batch, nheads, dstate, headdim});
-
-    if (batch == 0) return SSD_OK;
-    if (seqlen == 0) {
-        // empty sequence: the final state is the initial one
-        if (!final_state) return SSD_OK;
-        if (!aligned(final_state, 16) || (initial_state && !aligned(initial_state, 16)))
-            return fail(SSD_ERR_ALIGN, "state pointers must be 16-byte aligned");
-        st = check_alias({span("final_state", final_state, n_state * 4)},
-                         {span("initial_state", initial_state, n_state * 4)});
-        if (st) return st;
-        hipError_t e = ssd::launch_copy_state(initial_state, final_state, n_state, stream);
-        return e == hipSuccess ? SSD_OK : hip_fail(e, "state copy");
-    }
-    if (!x || !dt || !A || !B || !C || !y)
-        return fail(SSD_ERR_NULL, "x, dt, A, B, C and y are required");
-    const void *ptrs[] = {x, dt, A, B, C, D, initial_state, y, final_state};
-    for (const void *p : ptrs)
-        if (p && !aligned(p, 16)) return fail(SSD_ERR_ALIGN, "tensor pointer %p is not 16-byte aligned", p);
-    if (!workspace || workspace_bytes < lay.total)
-        return fail(SSD_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", lay.total,
-                    workspace_bytes, workspace ? "" : " (NULL)");
-    if (!aligned(workspace, 256)) return fail(SSD_ERR_ALIGN, "workspace must be 256-byte aligned");
-    st = check_alias(
-        {span("y", y, n_x * es), span("final_state", final_state, n_state * 4),
-         span("workspace", workspace, lay.total)},
-        {span("x", x, n_x * es), span("dt", dt, n_dt * es), span("A", A, (uint64_t)nheads * 4),
-         span("B", B, n_bc * es), span("C", C, n_bc * es), span("D", D, D ? (uint64_t)nheads * 4 : 0),
-         span("initial_state", initial_state, initial_state ? n_state * 4 : 0)});
-    if (st) return st;
-
-    char *ws = static_cast<char *>(workspace);
-    LaunchMarks marks(stream);
-    hipError_t e;
-    if (prefill_fused(dtype)) {
-        static const char *what[3] = {"state pass launch", "segment combine launch",
-                                      "fused prefill launch"};
-        const bool cut = lay.plan.nseg > 1 || lay.plan.tail_from >= 0;
-        for (int phase = cut ? 0 : 2; phase < 3; ++phase) {
-            if (phase == 1 && lay.plan.nseg <= 1) continue;  // a tail cut needs no combine
-            marks.before();
-            e = ssd::launch_ssd_fused(phase, lay.plan, x, dt, A, B, C, D, initial_state, dt_softplus,
-                                      batch, seqlen, nheads, headdim, dstate, ngroups, y,
-                                      final_state, ws, stream);
-            marks.after();
-            if (e != hipSuccess) return hip_fail(e, what[phase]);
-        }
-        return SSD_OK;
-    }
-    float *delta = reinterpret_cast<float *>(ws + lay.off_delta);
-    double *cs = reinterpret_cast<double *>(ws + lay.off_cs);
-    const int K = lay.nchunks;
-    marks.before();
-    e = ssd::launch_dt_cumsum(dtype, dt, A, dt_softplus, batch, seqlen, nheads, chunk, K, delta, cs,
-                              stream);
-    marks.after();
-    if (e != hipSuccess) return hip_fail(e, "dt cumsum launch");
-    {
-        float *S = reinterpret_cast<float *>(ws + lay.off_hprev);
-        marks.before();
-        e = ssd::launch_chunk_state_valu(dtype, x, B, delta, cs, batch, seqlen, nheads, headdim,
-                                         dstate, ngroups, chunk, K, S, stream);
-        marks.after();
-        if (e != hipSuccess) return hip_fail(e, "chunk state launch");
-        marks.before();
-        e = ssd::launch_state_pass_valu(cs, initial_state, batch, nheads, headdim, dstate, chunk,
-                                        K, S, final_state, stream);
-        marks.after();
-        if (e != hipSuccess) return hip_fail(e, "state pass launch");
-        marks.before();
-        e = ssd::launch_chunk_output_valu(dtype, x, B, C, D, delta, cs, S, batch, seqlen, nheads,
-                                          headdim, dstate, ngroups, chunk, K, y, stream);
-        marks.after();
-        if (e != hipSuccess) return hip_fail(e, "chunk output launch");
-    }
-    return SSD_OK;
+    return chunk_scan_fwd(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype,
+                          dt_softplus, x, dt, A, B, C, D, initial_state, y, final_state, workspace,
+                          workspace_bytes, stream_, false);
 }
+
+int ssd_chunk_scan_fwd_noalloc(int batch, int seqlen, int nheads, int headdim, int dstate,
+                               int ngroups, int chunk, int dtype, int dt_softplus, const void *x,
+                               const void *dt, const float *A, const void *B, const void *C,
+                               const float *D, const float *initial_state, void *y,
+                               float *final_state, void *stream_) {
+    return chunk_scan_fwd(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype,
+                          dt_softplus, x, dt, A, B, C, D, initial_state, y, final_state, nullptr, 0,
+                          stream_, true);
+}
+
+size_t ssd_noalloc_scratch_bytes(void) { return ssd::kScratchBytes; }
 
 size_t ssd_chunk_scan_bwd_workspace_size(int batch, int seqlen, int nheads, int headdim, int dstate,
                                          int ngroups, int dtype) {

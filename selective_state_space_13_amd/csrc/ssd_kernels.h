@@ -134,6 +134,12 @@ hipError_t launch_selective_scan(int phase, const ScanPlan &pl, int dtype, const
                                  int seqlen, int dim, int dstate, void *out, float *final_state,
                                  void *workspace, hipStream_t stream);
 
+// The library's device scratch buffer (noalloc.hip), used in place of a
+// caller's workspace by the entry point that allocates nothing.  Its device
+// address on the current device, looked up once per device.
+constexpr size_t kScratchBytes = 128ull << 20;
+hipError_t scratch_for_current_device(void **ptr);
+
 // copy or zero the state for an empty sequence
 hipError_t launch_copy_state(const float *src, float *dst, size_t n, hipStream_t stream);
 

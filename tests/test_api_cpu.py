@@ -397,3 +397,19 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(ValueError):
         ssd.ssd_chunk_scan(x, torch.zeros(1, 4, 8), torch.zeros(8), torch.zeros(1, 4, 1, 64),
                            torch.zeros(1, 4, 1, 64), chunk=64)
+
+
+def test_noalloc_validates_before_any_device_call(L):
+    """ssd_chunk_scan_fwd_noalloc refuses a call whose workspace would exceed its
+    scratch array, and shape errors, before it looks up any device."""
+    assert L.ssd_noalloc_scratch_bytes() == 128 << 20
+    b, Lq, H, N, G, Q = 8, 2048, 80, 128, 1, 64
+    assert L.ssd_chunk_scan_workspace_size(b, Lq, H, 64, N, G, Q, F32) > L.ssd_noalloc_scratch_bytes()
+    st = L.ssd_chunk_scan_fwd_noalloc(b, Lq, H, 64, N, G, Q, F32, 1, fake(1), fake(2), fake(3), fake(4),
+                                      fake(5), None, None, fake(7), None, None)
+    assert st == WS and b"scratch" in L.ssd_last_error()
+    st = L.ssd_chunk_scan_fwd_noalloc(1, 10, 8, 32, 128, 1, 64, BF16, 1, fake(1), fake(2), fake(3),
+                                      fake(4), fake(5), None, None, fake(7), None, None)
+    assert st == UNSUP
+    # the 64K-token, 80-head bf16 call fits
+    assert L.ssd_chunk_scan_workspace_size(1, 65536, 80, 64, 128, 8, 256, BF16) <= L.ssd_noalloc_scratch_bytes()

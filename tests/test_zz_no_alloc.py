@@ -1,0 +1,72 @@
+"""The prefill entry point that allocates nothing (ssd_chunk_scan_fwd_noalloc):
+same results as ssd_chunk_scan_fwd with a caller's workspace, on two calls in a
+row (the second smaller, so it runs over what the first left in the library's
+scratch array), for a segmented bf16 call, a call whose last round is cut, and
+the float32 path."""
+import numpy as np
+import pytest
+
+import oracle
+from workloads import gen
+
+from parity import TAU_BF16, TAU_F32, assert_parity, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+ssd = pytest.importorskip("selective_state_space_13_amd")
+
+
+def _both(d, chunk, with_h0):
+    x, dt, B, C, A, D = (to_dev(d[k]) for k in ("x", "dt", "B", "C", "A", "D"))
+    h0 = to_dev(d["h0"]) if with_h0 else None
+    y_ref, f_ref = ssd.ssd_chunk_scan(x, dt, A, B, C, D, chunk=chunk, initial_state=h0,
+                                      return_final_state=True)
+    y = torch.empty_like(x)
+    f = torch.empty_like(f_ref)
+    ssd.ssd_chunk_scan_fwd_noalloc(x, dt, A, B, C, D, chunk=chunk, initial_state=h0, out=y,
+                                   final_state=f)
+    torch.cuda.synchronize()
+    return y, f, y_ref, f_ref
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_noalloc_matches_workspace_entry_point(dtype):
+    if dtype == "bf16":
+        # 1: segmented (workspace holds segment states), 2: smaller, last round cut
+        cases = [(1, 16384, 64, 128, 2, 256), (3, 1100, 100, 128, 4, 256)]
+    else:
+        # float32 stages live in the workspace; the second call is smaller
+        cases = [(2, 2048, 16, 128, 2, 128), (1, 300, 8, 64, 1, 64)]
+    for i, (b, L, H, N, G, Q) in enumerate(cases):
+        need = ssd.chunk_scan_workspace_size(b, L, H, 64, N, G, Q,
+                                             ssd.SSD_BF16 if dtype == "bf16" else ssd.SSD_F32)
+        assert 256 < need <= ssd.lib().ssd_noalloc_scratch_bytes()
+        print(f"[noalloc] {dtype} call {i}: b{b} L{L} H{H} N{N} G{G} Q{Q}, scratch use {need} bytes",
+              flush=True)
+        d = gen.ssd_inputs(b, L, H, 64, N, G, dtype, seed=40 + i, config_id=115, with_h0=True)
+        y, f, y_ref, f_ref = _both(d, Q, True)
+        # the same kernels on the same inputs: identical bits
+        assert torch.equal(y, y_ref), f"{dtype} call {i}: y differs from the workspace entry point"
+        assert torch.equal(f, f_ref), f"{dtype} call {i}: final state differs"
+        if i == 1:
+            yo, fo = oracle.ssd_scan(d["x"].f64(), d["dt"].f64(), d["A"].f64(), d["B"].f64(),
+                                     d["C"].f64(), d["D"].f64(), d["h0"].f64(), return_final_state=True)
+            tau = TAU_BF16 if dtype == "bf16" else TAU_F32
+            assert_parity(to_f64(y), yo, tau, dtype == "bf16", f"noalloc {dtype} y")
+            assert_parity(to_f64(f), fo, tau, False, f"noalloc {dtype} final")
+
+
+def test_noalloc_rejects_calls_beyond_the_scratch_size():
+    """A float32 call whose stages exceed the scratch array is refused before
+    anything runs, and the error says why."""
+    b, L, H, N, G, Q = 8, 2048, 80, 128, 1, 64
+    assert ssd.chunk_scan_workspace_size(b, L, H, 64, N, G, Q, ssd.SSD_F32) > ssd.lib().ssd_noalloc_scratch_bytes()
+    x = torch.zeros((b, L, H, 64), dtype=torch.float32, device="cuda")
+    dt = torch.zeros((b, L, H), dtype=torch.float32, device="cuda")
+    Bm = torch.zeros((b, L, G, N), dtype=torch.float32, device="cuda")
+    A = torch.zeros(H, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    with pytest.raises(ssd.SSDError) as e:
+        ssd.ssd_chunk_scan_fwd_noalloc(x, dt, A, Bm, Bm.clone(), None, chunk=Q, out=y)
+    assert e.value.status == -4 and "scratch" in e.value.msg
