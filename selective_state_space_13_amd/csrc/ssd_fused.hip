@@ -39,7 +39,7 @@
 // x, B, C are exact bf16 and enter unsplit.  cs is summed in float64 so that
 // exp of a difference of nearby cs values keeps float32 accuracy.  A_h <= 0
 // is assumed (cs non-increasing within a chunk).
-#include "ssd_fused_roles.h"
+#include "ssd_fused_pair.h"
 
 namespace ssd {
 namespace {
@@ -52,10 +52,11 @@ __global__ __launch_bounds__(kThreads, 4) void ssd_state_kernel(FusedArgs a) {
     state_walk<N, false>(a, blockIdx.x, gridDim.x, sm);
 }
 
-// The full pass: states and outputs.
+// The full pass: states and outputs.  Two workgroups of 8 waves per CU: 4
+// waves per SIMD (at most 128 VGPRs), at most 80 KB of LDS each.
 template <int N>
-__global__ __launch_bounds__(kThreads, 1) void ssd_prefill_kernel(FusedArgs a) {
-    fused_roles_walk<N>(a, blockIdx.x, gridDim.x);
+__global__ __launch_bounds__(kThreads, 4) void ssd_prefill_kernel(FusedArgs a) {
+    fused_pair_walk<N>(a, blockIdx.x, gridDim.x);
 }
 
 // State entering each segment s >= 1: H_s = exp(decay_{s-1})·H_{s-1} + E_{s-1},
@@ -79,17 +80,23 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(const float *__res
 
 }  // namespace
 
+// workgroups of the full pass the chip runs at once: two per CU
+constexpr long long kSlots = 512;
+
 FusedPlan fused_plan(int batch, int seqlen, int nheads, int dstate) {
     FusedPlan pl;
     pl.nchunks = (seqlen + kC - 1) / kC;
     const long long bh = (long long)batch * nheads;
-    // cost ~ rounds of the chip (256 CUs, one workgroup each) x chunks per
+    // cost ~ rounds of the chip (256 CUs, two workgroups each) x chunks per
     // segment; splitting adds a state-only pass (~0.4 of a full one)
     int best = 1;
     double best_cost = 0.0;
-    for (int s = 1; s <= 64; ++s) {
+    // Only calls that leave slots empty are cut into segments (at most 16);
+    // fuller ones cut their last round's pairs instead (below).
+    const int max_seg = bh < kSlots ? 16 : 1;
+    for (int s = 1; s <= max_seg; ++s) {
         if (s > 1 && pl.nchunks / s < 8) break;
-        const double rounds = (double)((bh * s + 255) / 256);
+        const double rounds = (double)((bh * s + kSlots - 1) / kSlots);
         const double cost = rounds * ((pl.nchunks + s - 1) / s) * (s > 1 ? 1.4 : 1.0);
         if (s == 1 || cost < best_cost) {
             best = s;
@@ -104,13 +111,13 @@ FusedPlan fused_plan(int batch, int seqlen, int nheads, int dstate) {
         pl.state_bytes = (st + 255) / 256 * 256;
         pl.ws_bytes = 2 * pl.state_bytes + ((size_t)bh * pl.nseg * sizeof(double) + 255) / 256 * 256;
     } else {
-        // Whole pairs in rounds of 256 workgroups: when the last round is at most
-        // half full, its pairs are cut in two halves, so that it takes about half
-        // the time.  The second halves start from the state at the cut, which a
-        // state-only pass over the first halves computes beforehand.
-        const long long rounds = (bh + 255) / 256;
-        const long long rem = bh - 256 * (rounds - 1);
-        if (rounds >= 2 && rem <= 128 && pl.nchunks >= 16) {
+        // Whole pairs in rounds of kSlots workgroups: when the last round is at
+        // most half full, its pairs are cut in two halves, so that it takes about
+        // half the time.  The second halves start from the state at the cut, which
+        // a state-only pass over the first halves computes beforehand.
+        const long long rounds = (bh + kSlots - 1) / kSlots;
+        const long long rem = bh - kSlots * (rounds - 1);
+        if (rounds >= 2 && rem <= kSlots / 2 && pl.nchunks >= 16) {
             pl.tail_from = (int)(bh - rem);
             pl.tail_mid = pl.nchunks / 2;
             // the state pass over the first halves is as long as its parts: up to

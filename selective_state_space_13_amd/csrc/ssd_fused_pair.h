@@ -1,0 +1,374 @@
+// The full pass of the fused prefill, sized so that two workgroups share a
+// compute unit (at most 80 KB of LDS and 128 VGPRs per lane each).
+//
+// Waves 0-3 hold the state.  State wave s owns headdim columns p = 16s..16s+15
+// and every row n, as N/16 accumulator tiles of the 16x16x32 bf16 MFMA.  The
+// rows of tile i are a permutation of n chosen so that the accumulator of two
+// tiles is directly the k-contiguous A operand of the product with C:
+//     tile i, lane group q (lane >> 4), register r  <->  n = 32(i >> 1) + 8q + 4(i & 1) + r,
+//     column p = 16s + (lane & 15).
+// Each chunk a state wave
+//   - forms its 16 x 64 slice of yᵀ = Hᵀ·Cᵀ (the state entering the chunk, split
+//     head/tail, times C read as 16-byte rows), scaled per token by exp(cs_t):
+//     the output is transposed, so a lane holds 4 consecutive p of one token and
+//     stores them as one 8-byte word, with no exchange between waves;
+//   - decays its tiles and adds Bᵀ(w·x);
+//   - adds the intra-chunk products of its columns, xᵀ·Mᵀ, where M is the masked
+//     (C Bᵀ) with D on its diagonal, so the D skip needs no separate step.
+// Waves 4-7 stage.  Waves 4-6 each form one causal 32 x 32 block of (C Bᵀ)ᵀ,
+// mask it with the decay (factorised per block, exact when a diagonal block's
+// own log-change exceeds kMaxBlockDecay), split it head/tail and store it in
+// the k order the state waves' B operand reads; wave 7 scans the next chunk's
+// Δ·A.  After the barrier they stage the next chunk (x, w·x, B, C) from
+// registers and issue the loads of the chunk after it.  Raw x is
+// double-buffered, since the state waves read the current chunk's x while the
+// next one is staged.
+#pragma once
+#include "ssd_fused_walk.h"
+
+namespace ssd {
+namespace {
+
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int N>
+struct PairSmem {
+    uint16_t xs[2][kC * P];   // raw x [t][p], swz<64>, by chunk parity
+    uint16_t xw[2][kC * P];   // w·x head and tail [t][p], swz<64>
+    uint16_t bs[kC * N];      // B [t][n], swz<N>
+    uint16_t cr[kC * N];      // C [t][n], swz<N>
+    // masked blocks (T, S) = (0,0), (1,0), (1,1) of M = mask ⊙ (C Bᵀ) (+ D on the
+    // diagonal): [block][head, tail][row t][16-byte chunk q ^ ((t >> 1) & 3)];
+    // chunk q holds M[t][s] for s = 4q..4q+3 and 16+4q..16+4q+3 of block S
+    uint4 mt[3][2][32][4];
+    TokSmem tok[2];
+};
+
+// row n of the state for tile i, lane group q, register r
+__device__ __forceinline__ int pair_n(int i, int q, int r) { return 32 * (i >> 1) + 8 * q + 4 * (i & 1) + r; }
+
+template <int N>
+__device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk, unsigned nblk) {
+    constexpr int NT = N / 16;      // state tiles of a state wave
+    constexpr int KS = N / 32;      // k-steps over n of C·H
+    constexpr int KG = N / 16;      // k-steps over n of a (C Bᵀ)ᵀ block
+    constexpr int BPR = N / 8;      // 16-byte vectors per B/C row
+    constexpr int GV = N / 32;      // B (and C) vectors per staging lane
+    constexpr int BSTEP = 256 / BPR;
+    constexpr int kScanRole = 3;    // staging wave 7
+    __shared__ __attribute__((aligned(16))) PairSmem<N> sm;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, lg = lane >> 5;
+    const int c16 = lane & 15, q = lane >> 4;
+    const int jr = (lane >> 2) & 3, jc = 4 * (lane & 3);  // source row / column of a transposed read
+    const bool state_wave = wave < 4;
+    const int role = wave & 3;      // state wave index (its 16 columns), or staging role
+
+    const WalkItem item = map_walk_item<false>(a, blk, nblk, reinterpret_cast<int *>(&sm.mt[0][0][0][0]));
+    const int b = item.b, g = item.g, h = item.h, seg = item.seg, pair = item.pair, half = item.half;
+    const size_t row0 = item.row0;
+    const int seqlen = item.seqlen, c0 = item.c0, c1 = item.c1;
+    const float Ah = a.A[h];
+    const float Dh = a.D ? a.D[h] : 0.0f;
+    const size_t bh = (size_t)b * a.nheads + h;
+    const size_t xstride = (size_t)a.nheads * P, bstride = (size_t)a.ngroups * N;
+    const int last = seqlen - 1;
+    const int pc = 16 * role + c16;  // state waves: this lane's column p
+
+    // ---- staging waves: lane gl stages x rows xrow, xrow + 32 and B/C rows brow + BSTEP·k
+    const int gl = tid & 255;
+    const int xrow = gl >> 3, xcol = (gl & 7) * 8;
+    const int brow = gl / BPR, bcol = (gl % BPR) * 8;
+    uint4 rx[2], rb[GV], rc[GV];
+    uint32_t rdt = 0;  // raw bf16 Δ of a token (lane), converted where the scan uses it
+    auto load_dt = [&](int c) {  // every staging wave: no branch, hence no wait for it here
+        const int t0 = c * kC;
+        rdt = a.dt[(row0 + t0 + min(lane, last - t0)) * a.nheads + h];
+    };
+    auto prefetch = [&](int c) {
+        const int t0 = c * kC, lim = last - t0;  // rows past the end are clamped to the last one
+        const uint16_t *xc = a.x + ((row0 + t0) * a.nheads + h) * P + xcol;
+        rx[0] = ld16(xc + (size_t)min(xrow, lim) * xstride);
+        rx[1] = ld16(xc + (size_t)min(xrow + 32, lim) * xstride);
+        const uint16_t *bc = a.B + (row0 + t0) * bstride + (size_t)g * N + bcol;
+        const uint16_t *cc = a.C + (row0 + t0) * bstride + (size_t)g * N + bcol;
+#pragma unroll
+        for (int k = 0; k < GV; ++k) {
+            const size_t rw = (size_t)min(brow + BSTEP * k, lim) * bstride;
+            rb[k] = ld16(bc + rw);
+            rc[k] = ld16(cc + rw);
+        }
+    };
+    auto stage = [&](int c) {  // chunk c from registers into LDS; needs its per-token values
+        const TokSmem &T = sm.tok[c & 1];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const int row = xrow + 32 * k2, ox = swz<64>(row, xcol);
+            const float w = T.w[row];
+            const uint32_t in[4] = {rx[k2].x, rx[k2].y, rx[k2].z, rx[k2].w};
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float f0 = bf16lo(in[e]) * w, f1 = bf16hi(in[e]) * w;
+                hi[e] = pack_bf16x2(f0, f1);
+                lo[e] = pack_bf16x2(f0 - bf16lo(hi[e]), f1 - bf16hi(hi[e]));
+            }
+            *reinterpret_cast<uint4 *>(&sm.xs[c & 1][ox]) = rx[k2];
+            *reinterpret_cast<uint4 *>(&sm.xw[0][ox]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            *reinterpret_cast<uint4 *>(&sm.xw[1][ox]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        }
+#pragma unroll
+        for (int k = 0; k < GV; ++k) {
+            *reinterpret_cast<uint4 *>(&sm.bs[swz<N>(brow + BSTEP * k, bcol)]) = rb[k];
+            *reinterpret_cast<uint4 *>(&sm.cr[swz<N>(brow + BSTEP * k, bcol)]) = rc[k];
+        }
+    };
+    // Δ, the float64 inclusive cumsum of Δ·A over the chunk (lane = token) and
+    // the values derived from it
+    auto scan_chunk = [&](int c, uint32_t bits, TokSmem &T) {
+        const float raw = __uint_as_float(bits << 16);
+        const bool ok = c * kC + lane < seqlen;
+        const float delta = ok ? (a.dt_softplus ? softplus_f32(raw) : raw) : 0.0f;
+        const double cs = wave_inclusive_scan((double)(delta * Ah));
+        const double cs_end = read_lane(cs, 63);
+        const double cs_r = lane < 32 ? read_lane(cs, 31) : cs_end;
+        T.cs[lane] = cs;
+        T.d[lane] = delta;
+        T.e[lane] = __expf((float)cs);
+        T.v[lane] = __expf((float)(cs_r - cs)) * delta;
+        T.w[lane] = __expf((float)(cs_end - cs)) * delta;
+    };
+
+    // The two roles run separate loops (their loop-carried registers never
+    // overlap: the state tiles, or the prefetched inputs), with the same two
+    // barriers per chunk.
+    if (state_wave) {
+        // ---- state waves: the state entering the walk
+        f32x4 st[NT];
+        {
+            const float *src = nullptr;
+            if (half == 1) {
+                src = nullptr;  // the parts' chain below
+            } else if (seg == 0) {
+                if (a.h0) src = a.h0 + bh * N * P;
+            } else {
+                src = a.hin + (bh * a.nseg + seg) * N * P;
+            }
+#pragma unroll
+            for (int i = 0; i < NT; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) st[i][r] = src ? src[pair_n(i, q, r) * P + pc] : 0.0f;
+            // the second half of a cut pair: the first half's parts chained,
+            // H = E_0, then H = d_k·H + E_k for k = 1 .. parts - 1, is the sum
+            // Σ_k (Π_{j > k} d_j)·E_k; each tile adds its terms with all their loads
+            // issued together (from clamped part indices, the extra weights zero)
+            if (half == 1) {
+                const size_t t0 = (size_t)(pair - a.tail_from) * a.tail_parts;
+                float coef[4];
+                coef[3] = 1.0f;
+#pragma unroll
+                for (int k = 3; k >= 1; --k) {
+                    const float dk = k < a.tail_parts ? __expf((float)a.tail_decay[t0 + k]) : 1.0f;
+                    coef[k - 1] = coef[k] * dk;
+                }
+                // coef[k] = Π_{j = k+1}^{parts-1} d_j for k < parts; parts past the last get 0
+#pragma unroll
+                for (int k = 0; k < 4; ++k) coef[k] = k < a.tail_parts ? coef[k] : 0.0f;
+#pragma unroll 2
+                for (int i = 0; i < NT; ++i) {
+                    float e[4][4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const float *sk = a.tail_state + (t0 + min(k, a.tail_parts - 1)) * N * P;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) e[k][r] = sk[pair_n(i, q, r) * P + pc];
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        st[i][r] = coef[0] * e[0][r] + coef[1] * e[1][r] + coef[2] * e[2][r] + coef[3] * e[3][r];
+                }
+            }
+            // vmcnt(0) once here: otherwise the first use of st inside the chunk loop
+            // waits for every outstanding memory operation, the y stores included
+            __builtin_amdgcn_s_waitcnt(0x0f70);
+        }
+        __syncthreads();  // the staging waves' first scan and staging
+        __syncthreads();
+        for (int c = c0; c < c1; ++c) {
+            const int buf = c & 1;
+            const TokSmem &T = sm.tok[buf];
+            f32x4 y[4] = {};
+            // ============ A: yᵀ = Hᵀ·Cᵀ scaled by exp(cs_t); H = exp(cs_end)·H + Bᵀ(w·x)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                float hv[8];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    hv[r] = st[2 * ks][r];
+                    hv[4 + r] = st[2 * ks + 1][r];
+                }
+                bf16x8 hh, ht;
+                split8(hv, hh, ht);
+#pragma unroll
+                for (int tau = 0; tau < 4; ++tau) {
+                    const bf16x8 cop = as8(ld16(sm.cr + swz<N>(16 * tau + c16, 32 * ks + 8 * q)));
+                    y[tau] = mfma16(hh, cop, y[tau]);
+                    y[tau] = mfma16(ht, cop, y[tau]);
+                }
+            }
+#pragma unroll
+            for (int tau = 0; tau < 4; ++tau) {
+                const float et = T.e[16 * tau + c16];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) y[tau][r] *= et;
+            }
+            const float dec = T.e[kC - 1];
+#pragma unroll
+            for (int i = 0; i < NT; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) st[i][r] *= dec;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                const int ra = 32 * kt + 8 * q + jr, rb4 = ra + 4;
+                const bf16x8 whi = cat8(tr4(sm.xw[0] + swz<64>(ra, 16 * role + jc)),
+                                        tr4(sm.xw[0] + swz<64>(rb4, 16 * role + jc)));
+                const bf16x8 wlo = cat8(tr4(sm.xw[1] + swz<64>(ra, 16 * role + jc)),
+                                        tr4(sm.xw[1] + swz<64>(rb4, 16 * role + jc)));
+#pragma unroll
+                for (int i = 0; i < NT; ++i) {
+                    const int col = 32 * (i >> 1) + 2 * jc + 4 * (i & 1);
+                    const bf16x8 aop = cat8(tr4(sm.bs + swz<N>(ra, col)), tr4(sm.bs + swz<N>(rb4, col)));
+                    st[i] = mfma16(aop, whi, st[i]);
+                    st[i] = mfma16(aop, wlo, st[i]);
+                }
+            }
+            __syncthreads();
+            // ============ B: + xᵀ·Mᵀ (intra-chunk products and the D skip), store y
+            // xᵀ operands: k-slots j 0-3 <-> s = 32ks + 4q + j, j 4-7 <-> s = 32ks + 16 + 4q + j - 4
+            bf16x8 xop[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                xop[ks] = cat8(tr4(sm.xs[buf] + swz<64>(32 * ks + 4 * q + jr, 16 * role + jc)),
+                               tr4(sm.xs[buf] + swz<64>(32 * ks + 16 + 4 * q + jr, 16 * role + jc)));
+#pragma unroll
+            for (int tau = 0; tau < 4; ++tau) {
+                const int trow = 16 * (tau & 1) + c16;
+                const int ch = q ^ ((trow >> 1) & 3);
+#pragma unroll
+                for (int ks = 0; ks <= (tau >> 1); ++ks) {
+                    const int mb = (tau >> 1) == 0 ? 0 : 1 + ks;
+                    y[tau] = mfma16(xop[ks], as8(sm.mt[mb][0][trow][ch]), y[tau]);
+                    y[tau] = mfma16(xop[ks], as8(sm.mt[mb][1][trow][ch]), y[tau]);
+                }
+            }
+            // lane holds p = 16·role + 4q + r of token t = 16τ + c16: one 8-byte store each
+            const int t0 = c * kC;
+#pragma unroll
+            for (int tau = 0; tau < 4; ++tau) {
+                const int t = t0 + 16 * tau + c16;
+                if (t < seqlen) {
+                    const uint2 v = make_uint2(pack_bf16x2(y[tau][0], y[tau][1]),
+                                               pack_bf16x2(y[tau][2], y[tau][3]));
+                    *reinterpret_cast<uint2 *>(a.y + (row0 + t) * xstride + (size_t)h * P + 16 * role + 4 * q) = v;
+                }
+            }
+            __syncthreads();
+        }
+        // ---- end of the walk
+        if (a.final_state && half != 0 && seg == a.nseg - 1) {
+            float *dst = a.final_state + bh * N * P;
+#pragma unroll
+            for (int i = 0; i < NT; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[pair_n(i, q, r) * P + pc] = st[i][r];
+        }
+    } else {
+        if (c0 < c1) {  // an empty sequence loads nothing and returns its initial state
+            load_dt(c0);
+            prefetch(c0);
+            if (role == kScanRole) scan_chunk(c0, rdt, sm.tok[c0 & 1]);
+        }
+        __syncthreads();
+        if (c0 < c1) {
+            stage(c0);
+            load_dt(min(c0 + 1, c1 - 1));
+            prefetch(min(c0 + 1, c1 - 1));
+        }
+        __syncthreads();
+        for (int c = c0; c < c1; ++c) {
+            const int buf = c & 1;
+            const TokSmem &T = sm.tok[buf];
+            // ============ A: masked blocks | the next chunk's scan
+            if (role < 3) {
+                // block (T, S) = (0,0), (1,0), (1,1): Gᵀ[s][t] with s = 32S + row, t = 32T + l32
+                const int Tb = role > 0, Sb = role == 2;
+                f32x16 gt = {};
+#pragma unroll
+                for (int kg = 0; kg < KG; ++kg)
+                    gt = mfma(as8(ld16(sm.bs + swz<N>(32 * Sb + l32, 16 * kg + 8 * lg))),
+                              as8(ld16(sm.cr + swz<N>(32 * Tb + l32, 16 * kg + 8 * lg))), gt);
+                const double cs_t = T.cs[32 * Tb + l32];
+                const double cs_r = T.cs[32 * Sb + 31];
+                float m[16];
+                const bool exact = Tb == Sb && fabsf((float)(T.cs[32 * Sb] - cs_r)) > kMaxBlockDecay;
+                if (!exact) {
+                    const float u = __expf((float)(cs_t - cs_r));
+#pragma unroll
+                    for (int qq = 0; qq < 4; ++qq) {
+                        const float4 v4 = *reinterpret_cast<const float4 *>(T.v + 32 * Sb + 8 * qq + 4 * lg);
+                        m[4 * qq + 0] = gt[4 * qq + 0] * (v4.x * u);
+                        m[4 * qq + 1] = gt[4 * qq + 1] * (v4.y * u);
+                        m[4 * qq + 2] = gt[4 * qq + 2] * (v4.z * u);
+                        m[4 * qq + 3] = gt[4 * qq + 3] * (v4.w * u);
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int s = 32 * Sb + 8 * (r >> 2) + 4 * lg + (r & 3);
+                        m[r] = gt[r] * __expf((float)(cs_t - T.cs[s])) * T.d[s];
+                    }
+                }
+                if (Tb == Sb) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int sr = 8 * (r >> 2) + 4 * lg + (r & 3);
+                        m[r] = sr > l32 ? 0.0f : (sr == l32 ? m[r] + Dh : m[r]);
+                    }
+                }
+                // chunk lg: rows s of slabs lg and lg + 4 (registers 0-3, 8-11);
+                // chunk 2 + lg: slabs 2 + lg and 6 + lg (registers 4-7, 12-15)
+                const float v0[8] = {m[0], m[1], m[2], m[3], m[8], m[9], m[10], m[11]};
+                const float v1[8] = {m[4], m[5], m[6], m[7], m[12], m[13], m[14], m[15]};
+                bf16x8 h0v, t0v, h1v, t1v;
+                split8(v0, h0v, t0v);
+                split8(v1, h1v, t1v);
+                const int sw = (l32 >> 1) & 3;
+                sm.mt[role][0][l32][lg ^ sw] = __builtin_bit_cast(uint4, h0v);
+                sm.mt[role][1][l32][lg ^ sw] = __builtin_bit_cast(uint4, t0v);
+                sm.mt[role][0][l32][(2 + lg) ^ sw] = __builtin_bit_cast(uint4, h1v);
+                sm.mt[role][1][l32][(2 + lg) ^ sw] = __builtin_bit_cast(uint4, t1v);
+            } else if (c + 1 < c1) {
+                scan_chunk(c + 1, rdt, sm.tok[buf ^ 1]);  // its buffer was last read before the previous barrier
+            }
+            __syncthreads();
+            // ============ B: stage the next chunk, issue the loads of the one after
+            if (c + 1 < c1) {
+                __builtin_amdgcn_s_setprio(2);
+                stage(c + 1);
+                load_dt(min(c + 2, c1 - 1));
+                prefetch(min(c + 2, c1 - 1));
+                __builtin_amdgcn_s_setprio(0);
+            }
+            __syncthreads();
+        }
+    }
+
+}
+
+}  // namespace
+}  // namespace ssd

@@ -146,7 +146,7 @@ def test_bf16_workspace_is_small_or_segment_buffers(L):
     # cut into segments (few (batch, head) pairs, long sequence) or the last
     # round's pairs are cut in halves (the end states of the first halves' 4 parts,
     # 16 chunks in 4 parts for 128 cut pairs, and their float64 log-decays)
-    assert L.ssd_chunk_scan_workspace_size(8, 2048, 96, 64, 128, 1, 256, BF16) == 256
+    assert L.ssd_chunk_scan_workspace_size(8, 2048, 128, 64, 128, 1, 256, BF16) == 256
     assert L.ssd_chunk_scan_workspace_size(8, 2048, 80, 64, 128, 1, 256, BF16) == 128 * 4 * 128 * 64 * 4 + 128 * 4 * 8
     # a first half of 8 chunks is split into 2 parts of 4
     assert L.ssd_chunk_scan_workspace_size(8, 1024, 80, 64, 128, 1, 256, BF16) == 128 * 2 * 128 * 64 * 4 + 2048
@@ -273,12 +273,13 @@ def _plan(L, *args):
 
 
 def test_chunk_scan_plan(L):
-    # 640 pairs: two full rounds of 256, the last 128 pairs cut in halves
+    # 640 pairs on 512 slots (two workgroups per CU): one full round, the last
+    # 128 pairs cut in halves
     assert _plan(L, 8, 2048, 80, 64, 128, 1, 256, BF16) == (OK, (2, 1, 128))
-    # 80 pairs of 64K tokens: 16 segments
-    assert _plan(L, 1, 65536, 80, 64, 128, 8, 256, BF16) == (OK, (3, 16, 0))
-    # three full rounds: nothing to cut
-    assert _plan(L, 8, 2048, 96, 64, 128, 1, 256, BF16) == (OK, (1, 1, 0))
+    # 80 pairs of 64K tokens: 6 segments fill one round
+    assert _plan(L, 1, 65536, 80, 64, 128, 8, 256, BF16) == (OK, (3, 6, 0))
+    # two full rounds: nothing to cut
+    assert _plan(L, 8, 2048, 128, 64, 128, 1, 256, BF16) == (OK, (1, 1, 0))
     # float32: four stages
     assert _plan(L, 1, 512, 8, 64, 64, 1, 64, F32) == (OK, (4, 1, 0))
     assert _plan(L, 1, 512, 8, 64, 96, 1, 64, BF16)[0] == UNSUP

@@ -139,17 +139,18 @@ def test_prefill_segmented_bf16(case):
     assert_parity(to_f64(fs), fo, TAU_BF16, False, f"segmented final {case}")
 
 
-@pytest.mark.parametrize("case", [(3, 1100, 100, 128, 4, True, True), (5, 1024, 60, 64, 1, False, False),
-                                  (2, 2200, 180, 128, 4, True, True)],
-                         ids=["b3L1100H100N128G4", "b5L1024H60N64G1", "b2L2200H180N128G4"])
+@pytest.mark.parametrize("case", [(3, 1100, 200, 128, 4, True, True), (10, 1024, 60, 64, 1, False, False),
+                                  (3, 2200, 180, 128, 4, True, True)],
+                         ids=["b3L1100H200N128G4", "b10L1024H60N64G1", "b3L2200H180N128G4"])
 def test_prefill_tail_cut(case):
-    """Two full rounds of 256 (batch, head) pairs and a short last round, whose
-    pairs are cut in halves (the second half starting from the state at the cut).
-    The state pass splits the first halves into parts that it chains: 2 parts of
-    5 and 4 chunks, 2 of 4, and 4 parts of 5, 5, 5 and 2 chunks."""
+    """A full round of 512 (batch, head) pairs (two workgroups per CU) and a
+    short last round, whose pairs are cut in halves (the second half starting
+    from the state at the cut).  The state pass splits the first halves into
+    parts that it chains: 2 parts of 5 and 4 chunks, 2 of 4, and 4 parts of 5,
+    5, 5 and 2 chunks."""
     b, L, H, N, G, wD, wh = case
     launches, nseg, cut = ssd.chunk_scan_plan(b, L, H, 64, N, G, 256, ssd.SSD_BF16)
-    assert launches == 2 and nseg == 1 and cut == b * H - 256
+    assert launches == 2 and nseg == 1 and cut == b * H - 512
     d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=L + H, config_id=104, with_h0=wh)
     y, fs = run_scan(d, 256, "bf16", wD, wh)
     yo, fo = oracle_scan(d, wD, wh)
@@ -327,7 +328,7 @@ def test_prefill_tail_cut_initial_state_weak_decay():
     """The cut of the last round's pairs with an initial state that survives the
     whole sequence: the first part of each first half starts from h0, the others
     from zero, and the second half chains them; h0 must be counted once."""
-    b, L, H, N, G = 2, 2200, 180, 128, 4
+    b, L, H, N, G = 3, 2200, 180, 128, 4
     assert ssd.chunk_scan_plan(b, L, H, 64, N, G, 256, ssd.SSD_BF16)[2] > 0
     d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=15, config_id=109, with_h0=True)
     d["A"] = gen.Tensor(-np.exp(np.random.default_rng(15).uniform(np.log(1e-3), np.log(3e-2), H)).astype(np.float32), "f32")
@@ -363,7 +364,7 @@ def test_prefill_small_growth(kind):
     combine multiplies by exp(+Σ Δ·A)) and the cut of the last round."""
     dtype = "f32" if kind == "f32" else "bf16"
     shape = {"f32": (2, 700, 8, 128, 2), "bf16": (2, 700, 8, 128, 2),
-             "bf16_segmented": (1, 8192, 4, 128, 1), "bf16_tail_cut": (3, 1100, 100, 128, 4)}[kind]
+             "bf16_segmented": (1, 8192, 4, 128, 1), "bf16_tail_cut": (3, 1100, 200, 128, 4)}[kind]
     b, L, H, N, G = shape
     d = gen.ssd_inputs(b, L, H, 64, N, G, dtype, seed=L + 1, config_id=111, with_h0=True)
     d["A"] = _growth_A(H, L)
