@@ -105,8 +105,9 @@ const char *ssd_last_error(void);
  *                 SSD_F32: the stages below)
  *
  * Supported: headdim == 64; dstate in {64, 128}; chunk in {64, 128, 256};
- * ngroups >= 1 dividing nheads; batch, seqlen >= 0 (an empty call writes
- * final_state = initial_state or 0).  Element counts must stay below 2^62.
+ * ngroups >= 1 dividing nheads; nheads*headdim and ngroups*dstate at most 2^25;
+ * batch, seqlen >= 0 (an empty call writes final_state = initial_state or 0).
+ * Element counts must stay below 2^62.
  * ------------------------------------------------------------------------ */
 size_t ssd_chunk_scan_workspace_size(int batch, int seqlen, int nheads, int headdim, int dstate,
                                      int ngroups, int chunk, int dtype);

@@ -128,6 +128,9 @@ int check_scan_sizes(int batch, int seqlen, int nheads, int headdim, int dstate,
         return fail(SSD_ERR_UNSUPPORTED, "dstate %d: only 64 and 128 are supported", dstate);
     if (chunk != 64 && chunk != 128 && chunk != 256)
         return fail(SSD_ERR_UNSUPPORTED, "chunk %d: only 64, 128 and 256 are supported", chunk);
+    // the kernels address a 64-token chunk of a tensor with 32-bit offsets
+    if ((long long)nheads * headdim > (1ll << 25) || (long long)ngroups * dstate > (1ll << 25))
+        return fail(SSD_ERR_UNSUPPORTED, "nheads*headdim and ngroups*dstate must be at most 2^25");
     uint64_t n;
     if (!prod(n, {batch, seqlen, nheads, headdim}) || !prod(n, {batch, seqlen, ngroups, dstate}))
         return fail(SSD_ERR_SHAPE, "tensor sizes overflow");

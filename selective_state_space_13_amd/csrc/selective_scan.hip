@@ -33,18 +33,7 @@
 namespace ssd {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kT = 8;  // time steps per tile
-
-// log(1 + e^r) to a few ulps: log1p via log(u)·e/(u - 1) with u = 1 + e
-// (exact where u rounds to 1), e = e^-|r|.
-__device__ __forceinline__ float softplus_fast(float r) {
-    const float e = __builtin_amdgcn_exp2f(-fabsf(r) * kLog2e);
-    const float u = 1.0f + e;
-    const float lp = u == 1.0f ? e : __builtin_amdgcn_logf(u) * kLn2 * e * __builtin_amdgcn_rcpf(u - 1.0f);
-    return fmaxf(r, 0.0f) + lp;
-}
 
 template <typename T>
 __device__ __forceinline__ float ldf(const T *p) { return to_f32(*p); }

@@ -42,7 +42,7 @@ struct PairSmem {
     uint16_t bs[kC * N];      // B [t][n], swz<N>
     uint16_t cr[kC * N];      // C [t][n], swz<N>
     // masked blocks (T, S) = (0,0), (1,0), (1,1) of M = mask ⊙ (C Bᵀ) (+ D on the
-    // diagonal): [block][head, tail][row t][16-byte chunk q ^ ((t >> 1) & 3)];
+    // diagonal): [block][head, tail][row t][16-byte chunk q ^ mt_swz(t)];
     // chunk q holds M[t][s] for s = 4q..4q+3 and 16+4q..16+4q+3 of block S
     uint4 mt[3][2][32][4];
     TokSmem tok[2];
@@ -50,6 +50,9 @@ struct PairSmem {
 
 // row n of the state for tile i, lane group q, register r
 __device__ __forceinline__ int pair_n(int i, int q, int r) { return 32 * (i >> 1) + 8 * q + 4 * (i & 1) + r; }
+
+// 16-byte chunk of row t of a masked block: q XOR this
+__device__ __forceinline__ int mt_swz(int t) { return (t >> 1) & 3; }
 
 template <int N>
 __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk, unsigned nblk) {
@@ -70,9 +73,13 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
     const int role = wave & 3;      // state wave index (its 16 columns), or staging role
 
     const WalkItem item = map_walk_item<false>(a, blk, nblk, reinterpret_cast<int *>(&sm.mt[0][0][0][0]));
-    const int b = item.b, g = item.g, h = item.h, seg = item.seg, pair = item.pair, half = item.half;
-    const size_t row0 = item.row0;
-    const int seqlen = item.seqlen, c0 = item.c0, c1 = item.c1;
+    // the work item is the same for every lane; saying so keeps it (and every
+    // address base derived from it) in scalar registers
+    const auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+    const int b = uni(item.b), g = uni(item.g), h = uni(item.h), seg = uni(item.seg), pair = uni(item.pair),
+              half = uni(item.half);
+    const size_t row0 = ((size_t)(uint32_t)uni((int)(item.row0 >> 32)) << 32) | (uint32_t)uni((int)item.row0);
+    const int seqlen = uni(item.seqlen), c0 = uni(item.c0), c1 = uni(item.c1);
     const float Ah = a.A[h];
     const float Dh = a.D ? a.D[h] : 0.0f;
     const size_t bh = (size_t)b * a.nheads + h;
@@ -81,27 +88,32 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
     const int pc = 16 * role + c16;  // state waves: this lane's column p
 
     // ---- staging waves: lane gl stages x rows xrow, xrow + 32 and B/C rows brow + BSTEP·k
+    // the staging lanes: x and w·x rows xrow and xrow + 32, B and C rows brow + BSTEP·k
     const int gl = tid & 255;
     const int xrow = gl >> 3, xcol = (gl & 7) * 8;
     const int brow = gl / BPR, bcol = (gl % BPR) * 8;
     uint4 rx[2], rb[GV], rc[GV];
     uint32_t rdt = 0;  // raw bf16 Δ of a token (lane), converted where the scan uses it
+    // Chunk bases are wave-uniform (scalar registers); the per-lane offsets within
+    // a chunk fit in 32 bits (64 rows of at most 2^25 elements, checked by the host).
+    const uint32_t xs32 = (uint32_t)xstride, bs32 = (uint32_t)bstride, hs32 = (uint32_t)a.nheads;
     auto load_dt = [&](int c) {  // every staging wave: no branch, hence no wait for it here
         const int t0 = c * kC;
-        rdt = a.dt[(row0 + t0 + min(lane, last - t0)) * a.nheads + h];
+        const uint16_t *db = a.dt + (row0 + t0) * a.nheads + h;
+        rdt = db[(uint32_t)min(lane, last - t0) * hs32];
     };
     auto prefetch = [&](int c) {
         const int t0 = c * kC, lim = last - t0;  // rows past the end are clamped to the last one
-        const uint16_t *xc = a.x + ((row0 + t0) * a.nheads + h) * P + xcol;
-        rx[0] = ld16(xc + (size_t)min(xrow, lim) * xstride);
-        rx[1] = ld16(xc + (size_t)min(xrow + 32, lim) * xstride);
-        const uint16_t *bc = a.B + (row0 + t0) * bstride + (size_t)g * N + bcol;
-        const uint16_t *cc = a.C + (row0 + t0) * bstride + (size_t)g * N + bcol;
+        const uint16_t *xb = a.x + ((row0 + t0) * a.nheads + h) * P;
+        rx[0] = ld16(xb + ((uint32_t)min(xrow, lim) * xs32 + xcol));
+        rx[1] = ld16(xb + ((uint32_t)min(xrow + 32, lim) * xs32 + xcol));
+        const uint16_t *bb = a.B + (row0 + t0) * bstride + (size_t)g * N;
+        const uint16_t *cb = a.C + (row0 + t0) * bstride + (size_t)g * N;
 #pragma unroll
         for (int k = 0; k < GV; ++k) {
-            const size_t rw = (size_t)min(brow + BSTEP * k, lim) * bstride;
-            rb[k] = ld16(bc + rw);
-            rc[k] = ld16(cc + rw);
+            const uint32_t o = (uint32_t)min(brow + BSTEP * k, lim) * bs32 + bcol;
+            rb[k] = ld16(bb + o);
+            rc[k] = ld16(cb + o);
         }
     };
     auto stage = [&](int c) {  // chunk c from registers into LDS; needs its per-token values
@@ -133,7 +145,7 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
     auto scan_chunk = [&](int c, uint32_t bits, TokSmem &T) {
         const float raw = __uint_as_float(bits << 16);
         const bool ok = c * kC + lane < seqlen;
-        const float delta = ok ? (a.dt_softplus ? softplus_f32(raw) : raw) : 0.0f;
+        const float delta = ok ? (a.dt_softplus ? softplus_fast(raw) : raw) : 0.0f;
         const double cs = wave_inclusive_scan((double)(delta * Ah));
         const double cs_end = read_lane(cs, 63);
         const double cs_r = lane < 32 ? read_lane(cs, 31) : cs_end;
@@ -258,7 +270,7 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
 #pragma unroll
             for (int tau = 0; tau < 4; ++tau) {
                 const int trow = 16 * (tau & 1) + c16;
-                const int ch = q ^ ((trow >> 1) & 3);
+                const int ch = q ^ mt_swz(trow);
 #pragma unroll
                 for (int ks = 0; ks <= (tau >> 1); ++ks) {
                     const int mb = (tau >> 1) == 0 ? 0 : 1 + ks;
@@ -266,15 +278,21 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
                     y[tau] = mfma16(xop[ks], as8(sm.mt[mb][1][trow][ch]), y[tau]);
                 }
             }
-            // lane holds p = 16·role + 4q + r of token t = 16τ + c16: one 8-byte store each
+            // lane holds p = 16·role + 4q + r of token t = 16τ + c16: one 8-byte store each.
+            // The lane's offset is formed here from an opaque copy of the lane index:
+            // hoisted out of the loop, the four offsets would be kept in registers
+            // the loop does not have.
             const int t0 = c * kC;
+            uint16_t *yb = a.y + ((row0 + t0) * a.nheads + h) * P;
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const uint32_t yo = (uint32_t)(ln & 15) * (uint32_t)xstride + 16 * role + 4 * (ln >> 4);
 #pragma unroll
             for (int tau = 0; tau < 4; ++tau) {
-                const int t = t0 + 16 * tau + c16;
-                if (t < seqlen) {
+                if (t0 + 16 * tau + c16 < seqlen) {
                     const uint2 v = make_uint2(pack_bf16x2(y[tau][0], y[tau][1]),
                                                pack_bf16x2(y[tau][2], y[tau][3]));
-                    *reinterpret_cast<uint2 *>(a.y + (row0 + t) * xstride + (size_t)h * P + 16 * role + 4 * q) = v;
+                    *reinterpret_cast<uint2 *>(yb + (yo + (uint32_t)(16 * tau) * (uint32_t)xstride)) = v;
                 }
             }
             __syncthreads();
@@ -347,7 +365,7 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
                 bf16x8 h0v, t0v, h1v, t1v;
                 split8(v0, h0v, t0v);
                 split8(v1, h1v, t1v);
-                const int sw = (l32 >> 1) & 3;
+                const int sw = mt_swz(l32);
                 sm.mt[role][0][l32][lg ^ sw] = __builtin_bit_cast(uint4, h0v);
                 sm.mt[role][1][l32][lg ^ sw] = __builtin_bit_cast(uint4, t0v);
                 sm.mt[role][0][l32][(2 + lg) ^ sw] = __builtin_bit_cast(uint4, h1v);

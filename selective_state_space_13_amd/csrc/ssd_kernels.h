@@ -41,6 +41,21 @@ __device__ __forceinline__ float softplus_f32(float r) {
     return fmaxf(r, 0.0f) + log1pf(__expf(-fabsf(r)));
 }
 
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// The same to a few ulps on the hardware exp2/log2/rcp: log1p(e) computed as
+// log(u)·e/(u - 1) with u = 1 + e (exact where u rounds to 1), the log1p
+// formula from Goldberg, "What every computer scientist should know about
+// floating-point arithmetic" (1991).  For the bf16 paths, whose tolerance is
+// far above these few ulps.
+__device__ __forceinline__ float softplus_fast(float r) {
+    const float e = __builtin_amdgcn_exp2f(-fabsf(r) * kLog2e);
+    const float u = 1.0f + e;
+    const float lp = u == 1.0f ? e : __builtin_amdgcn_logf(u) * kLn2 * e * __builtin_amdgcn_rcpf(u - 1.0f);
+    return fmaxf(r, 0.0f) + lp;
+}
+
 constexpr int kWave = 64;
 
 // ---------------------------------------------------------------- launchers
