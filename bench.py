@@ -6,19 +6,25 @@ state passing, intra-chunk and state-to-output products in one launch) over the
 Mamba-2-2.7B-like layer shape: batch 8, seqlen 2048, 80 heads of
 headdim 64, dstate 128, one B/C group, chunk 256, bf16 inputs with float32
 accumulation and state.  Inputs are seeded synthetic tensors resident in HBM
-before the timed region.  W untimed warm-up steps, then K steps timed back to
-back between two device synchronisations; per-kernel durations come from HIP
-events recorded around each kernel launch on the call's stream.
+before the timed region.
+
+Timing: W untimed warm-up calls, then K calls.  Before each timed call a 1 GiB
+buffer is read, outside the timed region, so that the 256 MB last-level
+cache (MALL) holds none of the call's inputs.  Each call is bracketed by HIP
+events on its stream, and every kernel launch inside it by the library's own
+launch events; ms_per_step and the per-kernel times are medians over the K
+calls (the mean of K back-to-back calls without the flush is reported beside
+them).  GPU clocks are read with rocm-smi before and after the timed region.
 
 The same run also times, as separate legs of the JSON line: the single-token
-decode step at batch 256 (state cache of a 2.7B-layer prefill), the 64K-token
-long-context prefill with eight groups, the Mamba-1 selective scan (batch 8,
-seqlen 4096, 5120 channels, dstate 16), and a packed variable-length prefill
-(8 sequences of mixed lengths, 16384 tokens), the causal conv1d (width 4 over
-5376 channels) and the gated RMSNorm (5120 channels) of the same layer, the
-chunked backward at the prefill shape; and the
-CPU float64 oracle on the prefill workload (the `cpu_baseline`, timed on this
-host's cores).
+decode step at batch 256 (state cache of a 2.7B-layer prefill; each of the 64
+steps timed, median per step, and the 64-step chain back to back), the
+64K-token long-context prefill with eight groups, the Mamba-1 selective scan
+(batch 8, seqlen 4096, 5120 channels, dstate 16), a packed variable-length
+prefill (8 sequences of mixed lengths, 16384 tokens), the causal conv1d (width
+4 over 5376 channels) and the gated RMSNorm (5120 channels) of the same layer,
+the chunked backward at the prefill shape; and the CPU float64 oracle on the
+prefill workload (the `cpu_baseline`, timed on this host's cores).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs ...]
        [--no-cpu-baseline]
@@ -40,6 +46,7 @@ if ROOT not in sys.path:
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
 MFMA_BF16_PEAK = 2.5e15    # dense bf16 flop/s
 VALU_F32_PEAK = 78.6e12    # non-packed fp32 FMA flop/s (256 CU x 64 lanes x 2 x 2.4 GHz)
+VALU_LANE_OPS = 39.3e12    # non-packed vector lane-ops/s (256 CU x 4 SIMD x 16 lanes x 2.4 GHz)
 METRIC = "SSD prefill tokens/s and decode tokens/s at 2.7B-layer shape; % MFMA/HBM roofline"
 
 # kernels of one bf16 prefill call: the fused kernel alone, or, when the call is
@@ -49,6 +56,12 @@ FUSED_KERNELS = ["ssd_fused"]
 SEGMENTED_KERNELS = ["segment_states", "segment_combine", "ssd_fused"]
 # when only the last round of (batch, head) pairs is cut in halves: the state at the cut first
 CUT_KERNELS = ["cut_states", "ssd_fused"]
+# the sources of each kernel family: counter records in profiles/ apply while they match
+_C = "selective_state_space_13_amd/csrc/"
+FUSED_SOURCES = [_C + f for f in ("ssd_fused.hip", "ssd_fused_pair.h", "ssd_fused_walk.h", "mfma_tile.h",
+                                  "ssd_kernels.h")]
+DECODE_SOURCES = [_C + f for f in ("decode.hip", "ssd_kernels.h")]
+BWD_SOURCES = [_C + f for f in ("ssd_bwd.hip", "ssd_fused_walk.h", "mfma_tile.h", "ssd_kernels.h")]
 
 
 def log(*a):
@@ -87,32 +100,86 @@ class LaunchTimer:
     def disarm(lib):
         lib.ssd_set_launch_events(None, 0)
 
-    def per_kernel_ms(self):
+    def per_kernel_ms(self, reduce=None):
         out = []
         for k in range(self.nk):
             ts = [self.ev[2 * self.nk * c + 2 * k].elapsed_time(self.ev[2 * self.nk * c + 2 * k + 1])
                   for c in range(self.nc)]
-            out.append(sum(ts) / len(ts))
+            out.append(reduce(ts) if reduce else sum(ts) / len(ts))
         return out
 
 
-def time_calls(fn, nkernels, steps, warmup):
-    """Warm-up, then `steps` back-to-back calls; returns (wall ms per call, per-kernel ms)."""
+def median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+_FLUSH = []
+
+
+def flush_mall():
+    """Read a 1 GiB device buffer (a sum into one value): afterwards the 256 MB
+    last-level cache holds none of the benchmark's inputs, and no dirty lines that
+    the next kernel would have to write back.  Enqueued on the current stream,
+    outside any timed region."""
+    import torch
+    if not _FLUSH:
+        _FLUSH.append(torch.ones(1 << 28, dtype=torch.int32, device="cuda"))
+        _FLUSH.append(torch.empty((), dtype=torch.int64, device="cuda"))
+    torch.sum(_FLUSH[0], dtype=torch.int64, out=_FLUSH[1])
+
+
+def time_calls(fn, nkernels, steps, warmup, flush=True):
+    """Warm-up, then `steps` calls, each bracketed by events (and its kernels by
+    the library's launch events), with the MALL flushed before each when `flush`.
+    Returns (median ms per call, median ms per kernel, mean ms per call back to
+    back without the flush)."""
     import torch
     import selective_state_space_13_amd as ssd
     lib = ssd.lib()
     for _ in range(warmup):
         fn()
     timer = LaunchTimer(nkernels, steps)
+    calls = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(steps):
+        if flush:
+            flush_mall()
         timer.arm(lib, i)
+        calls[i][0].record()
         fn()
+        calls[i][1].record()
     LaunchTimer.disarm(lib)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    return (t1 - t0) * 1e3 / steps, timer.per_kernel_ms()
+    per_call = [a.elapsed_time(b) for a, b in calls]
+    per_kernel = timer.per_kernel_ms(median)
+    # the same calls back to back (MALL warm), wall clock
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    b2b = (time.perf_counter() - t0) * 1e3 / steps
+    return median(per_call), per_kernel, b2b
+
+
+def gpu_clocks():
+    """Current GPU clocks from rocm-smi (None when it is unavailable)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=30)
+        d = json.loads(r.stdout)
+    except Exception:  # noqa: BLE001 - any failure just means no clock record
+        return None
+    out = {}
+    for card, v in d.items():
+        if isinstance(v, dict):
+            out[card] = {k: v[k] for k in v if "clock" in k.lower() or "sclk" in k.lower()
+                         or "mclk" in k.lower() or "fclk" in k.lower()}
+    return out or None
 
 
 def source_digest(paths):
@@ -138,6 +205,19 @@ def measured_traffic(kernel, workload, digest):
     return e.get("bytes_per_launch")
 
 
+def counter_rates(kernel_ms, workload, sources):
+    """For each timed kernel with a counter record taken on its current sources:
+    the measured HBM bytes per launch and those bytes over the kernel's time."""
+    dg = source_digest(sources)
+    out = {}
+    for k, ms in kernel_ms.items():
+        b = measured_traffic(k, workload, dg)
+        if b:
+            out[k] = {"bytes": b, "achieved_gbps": round(b / (ms * 1e-3) / 1e9, 1),
+                      "frac": round(b / (ms * 1e-3) / HBM_PEAK, 4)}
+    return out or None
+
+
 def prefill_work(c, cut_pairs=0):
     """Algorithmic bytes and flops of a prefill call (inputs read once, outputs
     written once; causal flops of the block decomposition at the workload's
@@ -151,8 +231,12 @@ def prefill_work(c, cut_pairs=0):
     final = b * H * N * P * 4 if c.get("final_state") else 0
     units_h = b * K * H
     units_g = b * K * G
+    # the same causal count at the 64-token blocking the bf16 kernel uses
+    K64 = (L + 63) // 64
+    flops_q64 = b * K64 * H * (4 * 64 * N * P + 64 * 65 * P) + b * K64 * G * 64 * 65 * N
     total = dict(bytes=2 * x_bytes + 2 * bc_bytes + dt_bytes + final,
-                 flops=units_h * (4 * Q * N * P + Q * (Q + 1) * P) + units_g * Q * (Q + 1) * N)
+                 flops=units_h * (4 * Q * N * P + Q * (Q + 1) * P) + units_g * Q * (Q + 1) * N,
+                 flops_q64=flops_q64)
     # the fused kernel does all of it; the segment passes re-read x, B and dt
     # a cut of the last round's pairs re-reads the first halves of those pairs
     cut = cut_pairs / (b * H) * 0.5
@@ -188,10 +272,25 @@ def bench_prefill(cfg, steps, warmup, seed=0):
                            return_final_state=fs is not None, final_state=fs)
 
     log(f"[bench] prefill {cfg['name']}: timing {steps} steps after {warmup} warm-up")
-    ms, per = time_calls(step, len(names), steps, warmup)
+    ms, per, b2b = time_calls(step, len(names), steps, warmup)
     tokens = cfg["batch"] * cfg["seqlen"]
-    return dict(ms=ms, per_kernel_ms=dict(zip(names, per)), tokens=tokens,
+    return dict(ms=ms, b2b_ms=b2b, per_kernel_ms=dict(zip(names, per)), tokens=tokens,
                 work=prefill_work(cfg, cut_pairs), final_state=fs, y=y)
+
+
+def measured_mfma_flops(kernel, workload, digest):
+    """Issued MFMA flops per launch (rocprofv3 SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512)
+    from the committed counter summary, if taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = rec.get(f"{kernel}@{workload}")
+    if not e or e.get("source_digest") != digest:
+        return None
+    return e.get("mfma_flops_per_launch")
 
 
 def roofline_entry(kernel, ms, work, workload, digest):
@@ -203,10 +302,14 @@ def roofline_entry(kernel, ms, work, workload, digest):
     else:
         bound, achieved, peak, unit = "mfma", work["flops"] / t / 1e12, MFMA_BF16_PEAK / 1e12, "TFLOP/s"
     traffic = measured_traffic(kernel, workload, digest)
+    issued = measured_mfma_flops(kernel, workload, digest)
     return {"kernel": kernel, "bound": bound, "achieved": round(achieved, 3), "peak": peak,
             "unit": unit, "frac": round(achieved / peak, 4),
-            "traffic": traffic, "hbm_frac": round(byte_frac, 4), "mfma_frac": round(flop_frac, 4),
-            "avg_launch_ms": round(ms, 5)}
+            "traffic": traffic, "hbm_frac": round(byte_frac, 4),
+            "mfma_frac": round(flop_frac, 4),
+            "mfma_frac_q64": round(work["flops_q64"] / t / MFMA_BF16_PEAK, 4) if "flops_q64" in work else None,
+            "mfma_frac_issued": round(issued / t / MFMA_BF16_PEAK, 4) if issued else None,
+            "median_launch_ms": round(ms, 5)}
 
 
 def bench_decode(steps, warmup, prefill_state, bf16_state=False):
@@ -235,11 +338,11 @@ def bench_decode(steps, warmup, prefill_state, bf16_state=False):
         it[0] += 1
         step_fn(x, dt, A, B, C, D, state, out=y)
 
-    ms, per = time_calls(one, 1, c["steps"], warmup)
+    ms, per, b2b = time_calls(one, 1, c["steps"], warmup)
     state_bytes = c["batch"] * c["nheads"] * c["dstate"] * c["headdim"] * (2 if bf16_state else 4)
     io = c["batch"] * (c["nheads"] * c["headdim"] * 2 * 2 + c["nheads"] * 2 + 2 * c["ngroups"] * c["dstate"] * 2)
-    return dict(ms=ms, kernel_ms=per[0], tokens=c["batch"], bytes=2 * state_bytes + io,
-                flops=c["batch"] * c["nheads"] * c["dstate"] * c["headdim"] * 5)
+    return dict(ms=ms, b2b_ms=b2b, kernel_ms=per[0], tokens=c["batch"], bytes=2 * state_bytes + io,
+                flops=c["batch"] * c["nheads"] * c["dstate"] * c["headdim"] * 5, steps=c["steps"])
 
 
 def bench_mamba1(steps, warmup):
@@ -259,7 +362,7 @@ def bench_mamba1(steps, warmup):
     def one():
         ssd.selective_scan(u, dl, A, B, C, D, z, out=out)
 
-    ms, per = time_calls(one, len(names), steps, warmup)
+    ms, per, _ = time_calls(one, len(names), steps, warmup)
     n_el = c["batch"] * c["seqlen"] * c["dim"]
     return dict(ms=ms, kernel_ms=sum(per), per_kernel_ms=dict(zip(names, per)),
                 tokens=c["batch"] * c["seqlen"],
@@ -283,7 +386,7 @@ def bench_varlen(steps, warmup):
     def one():
         ssd.ssd_chunk_scan_varlen(x, dt, A, B, C, D, cu_seqlens=cu, out=y)
 
-    ms, per = time_calls(one, 1, steps, warmup)
+    ms, per, _ = time_calls(one, 1, steps, warmup)
     T = sum(c["lengths"])
     nbytes = 2 * T * c["nheads"] * c["headdim"] * 2 + 2 * T * c["ngroups"] * c["dstate"] * 2 \
         + T * c["nheads"] * 2
@@ -319,7 +422,7 @@ def bench_backward(cfg, steps, warmup, seed=0):
         ssd.ssd_chunk_scan_bwd(x, dt, A, B, C, dy, D, workspace=ws)
 
     log(f"[bench] backward: timing {steps} steps after {warmup} warm-up")
-    ms, per = time_calls(step, len(names), steps, warmup)
+    ms, per, _ = time_calls(step, len(names), steps, warmup)
     alg = 3 * b * L * H * P * 2 + 2 * b * L * H * 2 + 4 * b * L * G * N * 2
     states = 2 * b * H * nchunks * N * P * 4
     return dict(ms=ms, per_kernel_ms=dict(zip(names, per)), tokens=b * L, alg_bytes=alg,
@@ -343,7 +446,7 @@ def bench_convnorm(steps, warmup):
     def conv():
         ssd.causal_conv1d(x, w, bias, initial_state=s0, return_final_state=True, out=y, final_state=fs)
 
-    ms_c, per_c = time_calls(conv, 1, steps, warmup)
+    ms_c, per_c, _ = time_calls(conv, 1, steps, warmup)
     n = c["batch"] * c["seqlen"] * c["channels"]
     conv_bytes = 2 * n * 2 + 2 * s0.numel() * 4 + w.numel() * 4 + bias.numel() * 4
     del x, y
@@ -357,7 +460,7 @@ def bench_convnorm(steps, warmup):
     def norm():
         ssd.gated_rmsnorm(yy, z, wn, ngroups=r["ngroups"], out=out)
 
-    ms_n, per_n = time_calls(norm, 1, steps, warmup)
+    ms_n, per_n, _ = time_calls(norm, 1, steps, warmup)
     norm_bytes = 3 * r["rows"] * r["channels"] * 2 + wn.numel() * 4
     return dict(conv_ms=per_c[0], conv_bytes=conv_bytes, norm_ms=per_n[0], norm_bytes=norm_bytes,
                 conv_tokens=c["batch"] * c["seqlen"], norm_rows=r["rows"])
@@ -439,12 +542,10 @@ def main():
     cfg = configs.MAMBA2_LAYER_PREFILL
     workload = f"{cfg['name']}:b{cfg['batch']}L{cfg['seqlen']}H{cfg['nheads']}P{cfg['headdim']}" \
                f"N{cfg['dstate']}G{cfg['ngroups']}Q{cfg['chunk']}"
-    digest = source_digest(["selective_state_space_13_amd/csrc/ssd_fused.hip",
-                            "selective_state_space_13_amd/csrc/ssd_fused_roles.h",
-                            "selective_state_space_13_amd/csrc/ssd_fused_walk.h",
-                            "selective_state_space_13_amd/csrc/mfma_tile.h",
-                            "selective_state_space_13_amd/csrc/ssd_kernels.h"])
+    digest = source_digest(FUSED_SOURCES)
+    clocks_before = gpu_clocks()
     pf = bench_prefill(cfg, args.steps, args.warmup)
+    clocks_after = gpu_clocks()
     per = pf["per_kernel_ms"]
     dom = max(per, key=lambda k: per[k])
     roof = roofline_entry(dom, per[dom], pf["work"][dom], workload, digest)
@@ -458,6 +559,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(pf["ms"], 5),
+        "ms_per_step_back_to_back": round(pf["b2b_ms"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -471,6 +573,11 @@ def main():
                           "mfma_frac": round(total_work["flops"] / t_step / MFMA_BF16_PEAK, 4),
                           "alg_bytes": total_work["bytes"], "alg_flops": total_work["flops"]},
         "per_kernel_ms": {k: round(v, 5) for k, v in per.items()},
+        "per_kernel_measured_hbm": counter_rates(per, workload, FUSED_SOURCES),
+        "timing": "median over the timed calls of HIP events around each call (and each kernel), "
+                  "with a 1 GiB buffer read before every call so the 256 MB MALL holds no input; "
+                  "ms_per_step_back_to_back: mean of the same calls back to back without the flush",
+        "gpu_clocks": {"before": clocks_before, "after": clocks_after},
         "hbm_copy_reference": {"value": round(copy_tbs, 3), "unit": "TB/s",
                                "what": "torch device copy of a 1 GiB buffer, read + write bytes, 5 copies; "
                                        "context for the HBM fractions, which are against the 8 TB/s peak"},
@@ -493,6 +600,10 @@ def main():
                                       + ("bf16" if lp else "float32") + " state cache",
                           "tokens_per_s": round(dec["tokens"] / (dec["ms"] * 1e-3), 1),
                           "ms_per_step": round(dec["ms"], 5), "kernel_ms": round(dec["kernel_ms"], 5),
+                          "chain_ms_back_to_back": round(dec["b2b_ms"] * dec["steps"], 5),
+                          "measured_hbm": counter_rates(
+                              {"decode_step_" + ("bf16" if lp else "f32") + "_state": dec["kernel_ms"]},
+                              "decode_state_cache:b256H80P64N128G1", DECODE_SOURCES),
                           "roofline": {"bound": "hbm", "achieved": round(dec["bytes"] / t / 1e9, 2),
                                        "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                                        "frac": round(dec["bytes"] / t / HBM_PEAK, 4)}}
@@ -504,16 +615,28 @@ def main():
         extra["long_prefill"] = {"workload": "long_context_prefill:b1L65536H80P64N128G8Q256",
                                  "tokens_per_s": round(lp["tokens"] / t, 1), "ms": round(lp["ms"], 5),
                                  "per_kernel_ms": {k: round(v, 5) for k, v in lp["per_kernel_ms"].items()},
+                                 "per_kernel_measured_hbm": counter_rates(
+                                     lp["per_kernel_ms"], "long_context_prefill:b1L65536H80P64N128G8Q256",
+                                     FUSED_SOURCES),
                                  "hbm_frac": round(w["bytes"] / t / HBM_PEAK, 4),
                                  "mfma_frac": round(w["flops"] / t / MFMA_BF16_PEAK, 4)}
         del lp
     if "mamba1" in legs:
         m1 = bench_mamba1(max(3, args.steps // 4), 1)
         t = m1["kernel_ms"] * 1e-3
+        # the state update's minimal ALU work per (token, channel, state): Δ·A, B·(Δu),
+        # the update FMA and the output FMA on the vector ALU, and one exponential on
+        # the transcendental unit, at the chip's unit counts: 256 CUs x 4 SIMDs x 16
+        # lanes x 2.4 GHz = 39.3e12 lane-ops/s, exponentials at a quarter of that
+        alu_roof_s = m1["exps"] * (4 / VALU_LANE_OPS + 1 / (VALU_LANE_OPS / 4))
         extra["mamba1"] = {"workload": "mamba1_selective_scan:b8L4096D5120N16",
                            "tokens_per_s": round(m1["tokens"] / (m1["ms"] * 1e-3), 1),
                            "ms": round(m1["ms"], 5),
                            "per_kernel_ms": {k: round(v, 5) for k, v in m1["per_kernel_ms"].items()},
+                           "roofline": {"bound": "alu", "roof_ms": round(alu_roof_s * 1e3, 5),
+                                        "frac": round(alu_roof_s / t, 4),
+                                        "what": "4 VALU lane-ops + 1 exp per (token, channel, state) at "
+                                                "39.3e12 lane-ops/s and 9.8e12 exp/s"},
                            "hbm_frac": round(m1["bytes"] / t / HBM_PEAK, 4),
                            "exp_per_s": round(m1["exps"] / t, 1)}
     if "varlen" in legs:
@@ -530,6 +653,7 @@ def main():
             "workload": workload + " (dL/dy random; dx, ddt, dA, dB, dC, dD)",
             "tokens_per_s": round(bw["tokens"] / t, 1), "ms": round(bw["ms"], 5),
             "per_kernel_ms": {k: round(v, 5) for k, v in bw["per_kernel_ms"].items()},
+            "per_kernel_measured_hbm": counter_rates(bw["per_kernel_ms"], workload, BWD_SOURCES),
             "alg_bytes": bw["alg_bytes"], "state_bytes_written_and_read": bw["state_bytes"],
             "hbm_frac_algorithmic": round(bw["alg_bytes"] / t / HBM_PEAK, 4),
             "hbm_frac_with_states": round((bw["alg_bytes"] + 2 * bw["state_bytes"]) / t / HBM_PEAK, 4)}

@@ -18,13 +18,14 @@
 // small next to the state products.
 //
 // Work split inside a workgroup (8 waves, 512 lanes), by role
-// (ssd_fused_roles.h): waves 0-3 hold the state in MFMA accumulators, each one
-// half of n for one 32-wide tile of headdim, and multiply C by it straight
-// from those registers; they also decay and update it and produce the 64 x 64
-// outputs as four 32 x 32 quarters.  Waves 4-7 form the three causal blocks of
-// (C Bᵀ)ᵀ with the decay mask, scan the next chunk's Δ·A, and stage the next
-// chunk into LDS while the state waves finish the outputs.  Two barriers per
-// chunk.
+// (ssd_fused_pair.h), sized so that two workgroups share a CU: waves 0-3 hold
+// the state in 16x16x32 MFMA accumulators, each all of n for 16 columns of
+// headdim, multiply it by C straight from those registers (the output formed
+// transposed, one 8-byte store per lane), decay and update it, and add the
+// intra-chunk products.  Waves 4-7 form the three causal blocks of (C Bᵀ)ᵀ
+// with the decay mask (and D on the diagonal), scan the next chunk's Δ·A, and
+// stage the next chunk into LDS while the state waves finish the outputs.  Two
+// barriers per chunk.
 //
 // Long sequences with few (batch, head) pairs are cut into S segments that
 // run in parallel.  A state-only pass (ssd_state_kernel, ssd_fused_walk.h)
@@ -37,8 +38,9 @@
 // values, the state) is split into a bf16 head and tail (value - head, exact
 // in float32) and enters as two products, ~2^-17 relative error; the caller's
 // x, B, C are exact bf16 and enter unsplit.  cs is summed in float64 so that
-// exp of a difference of nearby cs values keeps float32 accuracy.  A_h <= 0
-// is assumed (cs non-increasing within a chunk).
+// exp of a difference of nearby cs values keeps float32 accuracy.  The decay
+// mask of a 32-token diagonal block is factorised, or taken exactly when the
+// block's own log-change exceeds kMaxBlockDecay in either direction.
 #include "ssd_fused_pair.h"
 
 namespace ssd {

@@ -2,7 +2,7 @@
 // segment or half of a pair per workgroup, walking 64-token chunks with the
 // N x 64 state in MFMA accumulators): the per-chunk token values, the launch
 // arguments, the mapping of workgroups to work items, and the state-only walk.
-// The full pass (state and outputs) is in ssd_fused_roles.h; ssd_fused.hip
+// The full pass (state and outputs) is in ssd_fused_pair.h; ssd_fused.hip
 // describes the method.  The backward runs the state-only walk, storing the
 // state entering every chunk, in the same launch as its adjoint walk.
 #pragma once
