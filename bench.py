@@ -127,7 +127,7 @@ def flush_mall():
     if not _FLUSH:
         _FLUSH.append(torch.ones(1 << 28, dtype=torch.int32, device="cuda"))
         _FLUSH.append(torch.empty((), dtype=torch.int64, device="cuda"))
-    torch.sum(_FLUSH[0], dtype=torch.int64, out=_FLUSH[1])
+    torch.sum(_FLUSH[0], dim=0, dtype=torch.int64, out=_FLUSH[1])
 
 
 def time_calls(fn, nkernels, steps, warmup, flush=True):
@@ -345,13 +345,19 @@ def bench_decode(steps, warmup, prefill_state, bf16_state=False):
                 flops=c["batch"] * c["nheads"] * c["dstate"] * c["headdim"] * 5, steps=c["steps"])
 
 
-def bench_mamba1(steps, warmup):
+def bench_mamba1(steps, warmup, general_A=False):
+    """The Mamba-1 workload, with its A = -[1..N] per channel, or (general_A) with an
+    A of per-(channel, state) random rates, which takes one exponential per state."""
+    import numpy as np
     import torch
     import selective_state_space_13_amd as ssd
     from workloads import configs, gen
     c = configs.MAMBA1_SELECTIVE_SCAN
     log("[bench] mamba1: generating inputs")
     d = gen.mamba1_inputs(c["batch"], c["seqlen"], c["dim"], c["dstate"], c["dtype"], config_id=c["id"])
+    if general_A:
+        rng = np.random.default_rng([0, c["id"], 99])
+        d["A"] = gen.Tensor(-np.exp(rng.uniform(0.0, np.log(16.0), (c["dim"], c["dstate"]))).astype(np.float32), "f32")
     u, dl, A, B, C, D, z = (to_dev(d[k]) for k in ("u", "delta", "A", "B", "C", "D", "z"))
     del d
     out = torch.empty_like(u)
@@ -621,24 +627,32 @@ def main():
                                  "hbm_frac": round(w["bytes"] / t / HBM_PEAK, 4),
                                  "mfma_frac": round(w["flops"] / t / MFMA_BF16_PEAK, 4)}
         del lp
-    if "mamba1" in legs:
-        m1 = bench_mamba1(max(3, args.steps // 4), 1)
+    for key in ("mamba1", "mamba1_general_A"):
+        if "mamba1" not in legs:
+            break
+        m1 = bench_mamba1(max(3, args.steps // 4), 1, general_A=key.endswith("general_A"))
         t = m1["kernel_ms"] * 1e-3
-        # the state update's minimal ALU work per (token, channel, state): Δ·A, B·(Δu),
-        # the update FMA and the output FMA on the vector ALU, and one exponential on
-        # the transcendental unit, at the chip's unit counts: 256 CUs x 4 SIMDs x 16
-        # lanes x 2.4 GHz = 39.3e12 lane-ops/s, exponentials at a quarter of that
-        alu_roof_s = m1["exps"] * (4 / VALU_LANE_OPS + 1 / (VALU_LANE_OPS / 4))
-        extra["mamba1"] = {"workload": "mamba1_selective_scan:b8L4096D5120N16",
+        # the state update's minimal ALU work per (token, channel, state): Δ·A (or, with
+        # A = -[1..N], one product of the power tree), B·(Δu), the update FMA and the
+        # output FMA on the vector ALU, and one exponential per state (or per (token,
+        # channel)) on the transcendental unit, at the chip's unit counts: 256 CUs x 4
+        # SIMDs x 16 lanes x 2.4 GHz = 39.3e12 lane-ops/s, exponentials at a quarter
+        gen_A = key.endswith("general_A")
+        n_exp = m1["exps"] if gen_A else m1["exps"] // 16
+        alu_roof_s = m1["exps"] * 4 / VALU_LANE_OPS + n_exp / (VALU_LANE_OPS / 4)
+        extra[key] = {"workload": "mamba1_selective_scan:b8L4096D5120N16"
+                                  + (", A random per (channel, state) in [-16, -1]" if key.endswith("general_A")
+                                     else ", A = -[1..16] per channel (one exponential per step, then powers)"),
                            "tokens_per_s": round(m1["tokens"] / (m1["ms"] * 1e-3), 1),
                            "ms": round(m1["ms"], 5),
                            "per_kernel_ms": {k: round(v, 5) for k, v in m1["per_kernel_ms"].items()},
                            "roofline": {"bound": "alu", "roof_ms": round(alu_roof_s * 1e3, 5),
                                         "frac": round(alu_roof_s / t, 4),
-                                        "what": "4 VALU lane-ops + 1 exp per (token, channel, state) at "
-                                                "39.3e12 lane-ops/s and 9.8e12 exp/s"},
+                                        "what": "4 VALU lane-ops per (token, channel, state) and 1 exp per "
+                                                + ("(token, channel, state)" if gen_A else "(token, channel)")
+                                                + " at 39.3e12 lane-ops/s and 9.8e12 exp/s"},
                            "hbm_frac": round(m1["bytes"] / t / HBM_PEAK, 4),
-                           "exp_per_s": round(m1["exps"] / t, 1)}
+                           "exp_per_s": round(n_exp / t, 1)}
     if "varlen" in legs:
         vl = bench_varlen(args.steps, args.warmup)
         t = vl["kernel_ms"] * 1e-3

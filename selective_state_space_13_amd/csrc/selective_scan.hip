@@ -28,6 +28,15 @@
 // and one v_exp_f32 per state element and step; v_exp_f32 issues at about a
 // quarter of the FMA rate, so the 16 exponentials per step and lane bound the
 // kernel.
+// Structured A: where every channel of a wave has A[d][n] = (n+1)·A[d][0]
+// exactly in float32 (the real diagonal initialisation of Mamba-1, the
+// benchmark's A = -[1..N]), exp(Δ·A[d][n]) = exp(Δ·A[d][0])^(n+1): one
+// exponential per step and lane and N-1 multiplications, in a tree of depth
+// log2 N.  The powers carry a few ulps more rounding than N exponentials, so
+// only bf16 inputs (tolerance 2e-2) take this path; the test runs per wave and
+// needs no host synchronisation.
+#include <type_traits>
+
 #include "ssd_kernels.h"
 
 namespace ssd {
@@ -38,13 +47,42 @@ constexpr int kT = 8;  // time steps per tile
 template <typename T>
 __device__ __forceinline__ float ldf(const T *p) { return to_f32(*p); }
 
+// The decay factors of one step in order n = 0..N-1, each handed to f(n, a):
+// exp2(dl·A2[n]) each, or (POW) with A[d][n] = (n+1)·A[d][0], the powers
+// e^(n+1) of e = exp2(dl·A2[0]) by products of depth log2 N (e^(k+j+1) = e^k·e^(j+1),
+// k = 1, 2, 4, 8), the last eight formed one at a time from e^8 so that only
+// eight powers are live at once.
+template <int N, bool POW, typename F>
+__device__ __forceinline__ void for_each_decay(float dl, const float *A2, F &&f) {
+    if constexpr (POW) {
+        float p[8];
+        p[0] = __builtin_amdgcn_exp2f(dl * A2[0]);
+        p[1] = p[0] * p[0];
+        p[2] = p[1] * p[0];
+        p[3] = p[1] * p[1];
+        if constexpr (N > 4) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p[4 + j] = p[3] * p[j];
+        }
+#pragma unroll
+        for (int n = 0; n < (N < 8 ? N : 8); ++n) f(n, p[n]);
+        if constexpr (N > 8) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) f(8 + j, p[7] * p[j]);
+        }
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) f(n, __builtin_amdgcn_exp2f(dl * A2[n]));
+    }
+}
+
 // Per-lane u, Δ, z of kT consecutive steps (bf16: raw bits, widened on use).
-template <typename T>
+template <typename T, int KT>
 struct StepTile {
-    float u[kT], r[kT], z[kT];
+    float u[KT], r[KT], z[KT];
     __device__ __forceinline__ void load(const T *up, const T *rp, const T *zp, size_t base, size_t stride, int nvalid) {
 #pragma unroll
-        for (int tt = 0; tt < kT; ++tt) {
+        for (int tt = 0; tt < KT; ++tt) {
             const size_t idx = base + (size_t)(tt < nvalid ? tt : 0) * stride;
             u[tt] = ldf(up + idx);
             r[tt] = ldf(rp + idx);
@@ -55,12 +93,12 @@ struct StepTile {
     __device__ __forceinline__ float gr(int tt) const { return r[tt]; }
     __device__ __forceinline__ float gz(int tt) const { return z[tt]; }
 };
-template <>
-struct StepTile<bf16_t> {
-    uint32_t u[kT], r[kT], z[kT];  // one 16-bit load per register
+template <int KT>
+struct StepTile<bf16_t, KT> {
+    uint32_t u[KT], r[KT], z[KT];  // one 16-bit load per register
     __device__ __forceinline__ void load(const bf16_t *up, const bf16_t *rp, const bf16_t *zp, size_t base, size_t stride, int nvalid) {
 #pragma unroll
-        for (int tt = 0; tt < kT; ++tt) {
+        for (int tt = 0; tt < KT; ++tt) {
             const size_t idx = base + (size_t)(tt < nvalid ? tt : 0) * stride;
             u[tt] = up[idx].bits;
             r[tt] = rp[idx].bits;
@@ -88,7 +126,7 @@ struct StepRows {
 
 struct ScanArgs {
     int delta_softplus, seqlen, dim;
-    int nseg, seg_len;       // segments of seg_len steps (a multiple of kT)
+    int nseg, seg_len;       // segments of seg_len steps (a multiple of kT, and so of 4)
     float *seg_state;        // [b][S][dim][N] local end state of each segment (MODE 0)
     float *seg_dsum;         // [b][S][dim] Σ Δ over each segment (MODE 0)
     const float *hin;        // [b][S][dim][N] state entering each segment s >= 1 (MODE 1)
@@ -103,6 +141,9 @@ __global__ __launch_bounds__(256, 4) void selective_scan_kernel(
     const T *__restrict__ B, const T *__restrict__ C, const float *__restrict__ D,
     const T *__restrict__ z, ScanArgs sa, T *__restrict__ out, float *__restrict__ final_state) {
     constexpr int W = StepRows<T, N>::W;
+    // the output pass keeps the gate and the partial outputs as well: tiles of 4
+    // steps keep it within 128 registers
+    constexpr int KT = MODE == 1 ? 4 : kT;
     const int delta_softplus = sa.delta_softplus, seqlen = sa.seqlen, dim = sa.dim;
 
     const int d = blockIdx.x * blockDim.x + threadIdx.x;
@@ -113,17 +154,23 @@ __global__ __launch_bounds__(256, 4) void selective_scan_kernel(
     const size_t sidx = ((size_t)b * sa.nseg + seg) * dim + dd;  // (b, segment, channel)
 
     float A2[N], s[N];
+    bool structured = sizeof(T) == 2;  // bf16 inputs only
+    const float A0 = A[(size_t)dd * N];
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-        A2[n] = A[(size_t)dd * N + n] * kLog2e;
+        const float An = A[(size_t)dd * N + n];
+        structured = structured && An == (float)(n + 1) * A0;
+        A2[n] = An * kLog2e;
         s[n] = (MODE == 1 && seg > 0) ? sa.hin[sidx * N + n] : 0.0f;
     }
+    // every lane of the wave (inactive lanes repeat the last channel) must agree
+    structured = __all(structured);
     const float Dd = D ? D[dd] : 0.0f;
     const int tbeg = seg * sa.seg_len;
     const int tend = min(seqlen, tbeg + sa.seg_len);
     const int len = tend - tbeg;
     const size_t row0 = (size_t)b * seqlen + tbeg;  // first row of this segment
-    const int ntiles = len > 0 ? (len + kT - 1) / kT : 0;
+    const int ntiles = len > 0 ? (len + KT - 1) / KT : 0;
     const uint32_t *Bw = reinterpret_cast<const uint32_t *>(B) + row0 * W;
     const uint32_t *Cw = reinterpret_cast<const uint32_t *>(C) + row0 * W;
     float dsum = 0.0f;
@@ -139,31 +186,29 @@ __global__ __launch_bounds__(256, 4) void selective_scan_kernel(
     // z is read unconditionally (u stands in when there is no gate): a load under a
     // branch would make the join wait for every load in flight, the prefetch included
     const T *zsrc = z ? z : u;
-    auto load_tile = [&](StepTile<T> &tl, int k) {
-        tl.load(u, delta, zsrc, (row0 + (size_t)k * kT) * dim + dd, (size_t)dim, len - k * kT);
+    auto load_tile = [&](StepTile<T, KT> &tl, int k) {
+        tl.load(u, delta, zsrc, (row0 + (size_t)k * KT) * dim + dd, (size_t)dim, len - k * KT);
     };
-    auto run_tile = [&](const StepTile<T> &tl, int k) {
-        const int nt = min(kT, len - k * kT);
+    auto run_tile = [&](const StepTile<T, KT> &tl, int k, auto pw) {
+        constexpr bool kPow = decltype(pw)::value;
+        const int nt = min(KT, len - k * KT);
 #pragma unroll
-        for (int tt = 0; tt < kT; ++tt) {
+        for (int tt = 0; tt < KT; ++tt) {
             if (tt < nt) {
-                const int t = k * kT + tt;
+                const int t = k * KT + tt;
                 StepRows<T, N> nxt;
                 load_rows(nxt, min(t + 1, len - 1));
                 const float dl = delta_softplus ? softplus_fast(tl.gr(tt)) : tl.gr(tt);
                 const float du = dl * tl.gu(tt);
                 if (MODE == 0) {
                     dsum += dl;
-#pragma unroll
-                    for (int n = 0; n < N; ++n) s[n] = __builtin_amdgcn_exp2f(dl * A2[n]) * s[n] + du * cur.gb(n);
+                    for_each_decay<N, kPow>(dl, A2, [&](int n, float a) { s[n] = a * s[n] + du * cur.gb(n); });
                 } else {
                     float yp[4] = {Dd * tl.gu(tt), 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                    for (int n = 0; n < N; ++n) {
-                        const float dA = __builtin_amdgcn_exp2f(dl * A2[n]);
-                        s[n] = dA * s[n] + du * cur.gb(n);
+                    for_each_decay<N, kPow>(dl, A2, [&](int n, float a) {
+                        s[n] = a * s[n] + du * cur.gb(n);
                         yp[n & 3] += cur.gc(n) * s[n];
-                    }
+                    });
                     float yv = (yp[0] + yp[1]) + (yp[2] + yp[3]);
                     if (z) {
                         const float zz = tl.gz(tt);
@@ -176,18 +221,29 @@ __global__ __launch_bounds__(256, 4) void selective_scan_kernel(
         }
     };
 
-    StepTile<T> ta, tb;
+    StepTile<T, KT> ta, tb;
     if (ntiles > 0) {
         load_rows(cur, 0);
         load_tile(ta, 0);
     }
     // two register sets: tile k+1 loads while tile k runs
-    for (int k = 0; k < ntiles; k += 2) {
-        if (k + 1 < ntiles) load_tile(tb, k + 1);
-        run_tile(ta, k);
-        if (k + 1 < ntiles) {
-            if (k + 2 < ntiles) load_tile(ta, k + 2);
-            run_tile(tb, k + 1);
+    if (sizeof(T) == 2 && structured) {
+        for (int k = 0; k < ntiles; k += 2) {
+            if (k + 1 < ntiles) load_tile(tb, k + 1);
+            run_tile(ta, k, std::true_type{});
+            if (k + 1 < ntiles) {
+                if (k + 2 < ntiles) load_tile(ta, k + 2);
+                run_tile(tb, k + 1, std::true_type{});
+            }
+        }
+    } else {
+        for (int k = 0; k < ntiles; k += 2) {
+            if (k + 1 < ntiles) load_tile(tb, k + 1);
+            run_tile(ta, k, std::false_type{});
+            if (k + 1 < ntiles) {
+                if (k + 2 < ntiles) load_tile(ta, k + 2);
+                run_tile(tb, k + 1, std::false_type{});
+            }
         }
     }
     if (!active) return;

@@ -986,6 +986,30 @@ def test_mamba1_general_A():
     assert_parity(to_f64(out), oo, TAU_BF16, True, "mamba1 general A")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mamba1_structured_A_waves(dtype):
+    """Waves whose channels all have A[d][n] = (n+1)·A[d][0] (here with a
+    different A[d][0] per channel) take one exponential per step and its powers;
+    a wave holding one channel whose A is off that form by one float32 unit takes
+    the exponential per state; float32 inputs always do.  Both against the oracle,
+    over time segments."""
+    b, L, dim, N = 2, 1500, 192, 16
+    d = gen.mamba1_inputs(b, L, dim, N, dtype, seed=3, config_id=124)
+    rng = np.random.default_rng(13)
+    a0 = -np.exp(rng.uniform(-1.0, 1.0, dim)).astype(np.float32)
+    A = (np.arange(1, N + 1, dtype=np.float32)[None, :] * a0[:, None]).astype(np.float32)
+    A[70, 5] = np.nextafter(A[70, 5], np.float32(0.0))   # channel 70 (second wave) off the form
+    d["A"] = gen.Tensor(np.ascontiguousarray(A), "f32")
+    assert ssd.lib().selective_scan_workspace_size(b, L, dim, N, ssd.SSD_BF16 if dtype == "bf16" else ssd.SSD_F32) > 0
+    out, fs = ssd.selective_scan(to_dev(d["u"]), to_dev(d["delta"]), to_dev(d["A"]), to_dev(d["B"]),
+                                 to_dev(d["C"]), to_dev(d["D"]), to_dev(d["z"]), return_final_state=True)
+    torch.cuda.synchronize()
+    oo, fo = oracle.selective_scan(d["u"].f64(), d["delta"].f64(), d["A"].f64(), d["B"].f64(),
+                                   d["C"].f64(), d["D"].f64(), d["z"].f64(), return_final_state=True)
+    assert_parity(to_f64(out), oo, tau_of(dtype), dtype == "bf16", f"mamba1 structured-A waves out {dtype}")
+    assert_parity(to_f64(fs), fo, tau_of(dtype), False, f"mamba1 structured-A waves final {dtype}")
+
+
 def test_config5_mamba1_full():
     c = configs.MAMBA1_SELECTIVE_SCAN
     say("C5: generating inputs")
