@@ -60,6 +60,14 @@ extern "C" {
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 
+/* OR'ed into the dtype of ssd_chunk_scan_fwd (and its size, plan and layout
+ * queries, and ssd_chunk_scan_fwd_noalloc), ssd_decode_step and
+ * ssd_decode_step_bf16_state: y is written as float32 whatever the inputs'
+ * dtype (arithmetic unchanged; only the final rounding of y to bf16 is
+ * skipped).  With SSD_F32 inputs it changes nothing.  Other entry points
+ * return SSD_ERR_UNSUPPORTED for it. */
+#define SSD_OUT_F32 0x100
+
 typedef enum {
     SSD_OK = 0,
     SSD_ERR_NULL = -1,        /* a required pointer is NULL                      */
@@ -98,7 +106,7 @@ const char *ssd_last_error(void);
  *   B, C   [batch][seqlen][ngroups][dstate]      dtype
  *   D      [nheads]                              float  or NULL (= 0)
  *   initial_state [batch][nheads][dstate][headdim] float or NULL (= 0)
- *   y      [batch][seqlen][nheads][headdim]      dtype, written
+ *   y      [batch][seqlen][nheads][headdim]      dtype (float with SSD_OUT_F32), written
  *   final_state   [batch][nheads][dstate][headdim] float or NULL, written
  *   workspace     >= ssd_chunk_scan_workspace_size(...) bytes, 256-byte aligned
  *                 (SSD_BF16: 256 bytes, unused, unless the call is segmented;
@@ -281,7 +289,7 @@ int ssd_gated_rmsnorm_fwd(int rows, int channels, int ngroups, int dtype, float 
  *   A, D   [nheads] float (D may be NULL)
  *   B, C   [batch][ngroups][dstate]   dtype
  *   state  [batch][nheads][dstate][headdim] float, read and overwritten in place
- *   y      [batch][nheads][headdim]   dtype, written
+ *   y      [batch][nheads][headdim]   dtype (float with SSD_OUT_F32), written
  *
  * Supported: headdim == 64; dstate a multiple of 32 in [32, 256].
  * ------------------------------------------------------------------------ */

@@ -25,6 +25,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libssd.so")
 
 SSD_F32, SSD_BF16 = 0, 1
+SSD_OUT_F32 = 0x100  # flag: float32 y from the prefill and decode entry points
 STATUS = {0: "SSD_OK", -1: "SSD_ERR_NULL", -2: "SSD_ERR_SHAPE", -3: "SSD_ERR_UNSUPPORTED",
           -4: "SSD_ERR_WORKSPACE", -5: "SSD_ERR_ALIGN", -6: "SSD_ERR_ALIAS", -7: "SSD_ERR_HIP"}
 
@@ -116,6 +117,20 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
 
 
+def _y_dtype(x, out, out_dtype):
+    """dtype of y: that of `out` if given, else `out_dtype`, else that of x.
+    float32 y with bfloat16 inputs is the SSD_OUT_F32 flag."""
+    torch = _torch()
+    want = out.dtype if out is not None else (out_dtype if out_dtype is not None else x.dtype)
+    if want != x.dtype and want != torch.float32:
+        raise TypeError(f"y may be {x.dtype} or float32, not {want}")
+    return want
+
+
+def _with_out_flag(code, x, ydt):
+    return code | SSD_OUT_F32 if ydt != x.dtype else code
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -167,12 +182,12 @@ def chunk_scan_plan(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtyp
 
 def ssd_chunk_scan(x, dt, A, B, C, D=None, *, chunk, initial_state=None,
                    return_final_state=False, dt_softplus=True, workspace=None,
-                   out=None, final_state=None):
+                   out=None, final_state=None, out_dtype=None):
     """Chunked SSD prefill.  x [b,L,H,P], dt [b,L,H], A [H] fp32, B, C [b,L,G,N],
     D [H] fp32 or None, initial_state [b,H,N,P] fp32 or None.
-    Returns y (same dtype as x) or (y, final_state fp32 [b,H,N,P]).
-    `workspace` (uint8 tensor), `out` and `final_state` may be passed to reuse
-    buffers."""
+    Returns y (dtype of x, or float32 when out_dtype or out says so) or
+    (y, final_state fp32 [b,H,N,P]).  `workspace` (uint8 tensor), `out` and
+    `final_state` may be passed to reuse buffers."""
     torch = _torch()
     x = _req(x, "x")
     dev = x.device
@@ -191,8 +206,12 @@ def ssd_chunk_scan(x, dt, A, B, C, D=None, *, chunk, initial_state=None,
         raise ValueError("A and D must have shape [nheads]")
     if initial_state is not None and tuple(initial_state.shape) != (b, H, N, P):
         raise ValueError("initial_state must be [batch, nheads, dstate, headdim]")
-    y = out if out is not None else torch.empty_like(x)
-    _req(y, "out", x.dtype, dev)
+    ydt = _y_dtype(x, out, out_dtype)
+    y = out if out is not None else torch.empty(x.shape, dtype=ydt, device=dev)
+    _req(y, "out", ydt, dev)
+    if y.shape != x.shape:
+        raise ValueError("out must have the shape of x")
+    code = _with_out_flag(code, x, ydt)
     fs = None
     if return_final_state:
         fs = final_state if final_state is not None else torch.empty(
@@ -225,7 +244,9 @@ def ssd_chunk_scan_fwd_noalloc(x, dt, A, B, C, D=None, *, chunk, initial_state=N
     _req(A, "A", torch.float32, dev)
     _req(D, "D", torch.float32, dev)
     _req(initial_state, "initial_state", torch.float32, dev)
-    _req(out, "out", x.dtype, dev)
+    ydt = _y_dtype(x, out, None)
+    _req(out, "out", ydt, dev)
+    code = _with_out_flag(code, x, ydt)
     _req(final_state, "final_state", torch.float32, dev)
     G, N = B.shape[2], B.shape[3]
     if tuple(dt.shape) != (b, L, H) or tuple(B.shape) != (b, L, G, N) or C.shape != B.shape:
@@ -382,7 +403,7 @@ def gated_rmsnorm(y, z, weight, *, ngroups=1, eps=1e-5, out=None):
     return o
 
 
-def _decode(fn, state_dtype, x, dt, A, B, C, D, state, dt_softplus, out):
+def _decode(fn, state_dtype, x, dt, A, B, C, D, state, dt_softplus, out, out_dtype):
     torch = _torch()
     x = _req(x, "x")
     dev = x.device
@@ -399,24 +420,31 @@ def _decode(fn, state_dtype, x, dt, A, B, C, D, state, dt_softplus, out):
         raise ValueError("shape mismatch among x, dt, B, C")
     if tuple(state.shape) != (b, H, N, P):
         raise ValueError("state must be [batch, nheads, dstate, headdim]")
-    y = out if out is not None else torch.empty_like(x)
-    _req(y, "out", x.dtype, dev)
+    ydt = _y_dtype(x, out, out_dtype)
+    y = out if out is not None else torch.empty(x.shape, dtype=ydt, device=dev)
+    _req(y, "out", ydt, dev)
+    if y.shape != x.shape:
+        raise ValueError("out must have the shape of x")
+    code = _with_out_flag(code, x, ydt)
     check(fn(b, H, P, N, G, code, int(bool(dt_softplus)), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
              _ptr(C), _ptr(D), _ptr(state), _ptr(y), _stream(dev)))
     return y
 
 
-def ssd_decode_step(x, dt, A, B, C, D, state, *, dt_softplus=True, out=None):
+def ssd_decode_step(x, dt, A, B, C, D, state, *, dt_softplus=True, out=None, out_dtype=None):
     """One decode step.  x [b,H,P], dt [b,H], A [H], B, C [b,G,N], D [H] or None,
-    state [b,H,N,P] fp32 (updated in place).  Returns y [b,H,P]."""
-    return _decode(lib().ssd_decode_step, _torch().float32, x, dt, A, B, C, D, state, dt_softplus, out)
+    state [b,H,N,P] fp32 (updated in place).  Returns y [b,H,P] (dtype of x,
+    or float32 when out_dtype or out says so)."""
+    return _decode(lib().ssd_decode_step, _torch().float32, x, dt, A, B, C, D, state, dt_softplus,
+                   out, out_dtype)
 
 
-def ssd_decode_step_bf16_state(x, dt, A, B, C, D, state, *, dt_softplus=True, out=None):
+def ssd_decode_step_bf16_state(x, dt, A, B, C, D, state, *, dt_softplus=True, out=None,
+                               out_dtype=None):
     """One decode step against a bf16 state cache: as ssd_decode_step, with
     state [b,H,N,P] bfloat16 (updated in place, rounded to nearest even)."""
     return _decode(lib().ssd_decode_step_bf16_state, _torch().bfloat16, x, dt, A, B, C, D, state,
-                   dt_softplus, out)
+                   dt_softplus, out, out_dtype)
 
 
 def selective_scan(u, delta, A, B, C, D=None, z=None, *, delta_softplus=True,

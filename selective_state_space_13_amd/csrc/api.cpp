@@ -103,6 +103,14 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 int elem_size(int dtype) { return dtype == SSD_BF16 ? 2 : 4; }
 
+// dtype of the prefill and decode entry points: an ssd_dtype, optionally with
+// SSD_OUT_F32 (float32 y whatever the inputs' dtype)
+int strip_out_flag(int &dtype) {
+    const int yf = (dtype & SSD_OUT_F32) ? 1 : 0;
+    dtype &= ~SSD_OUT_F32;
+    return yf;
+}
+
 // bf16 prefill runs as the fused matrix-core kernel; float32 inputs take the
 // vector-ALU path, whose stages (Δ, cs, hand-off states) live in the workspace.
 bool prefill_fused(int dtype) { return dtype == SSD_BF16; }
@@ -165,6 +173,7 @@ int scan_layout(int batch, int seqlen, int nheads, int headdim, int dstate, int 
 int decode_step(int batch, int nheads, int headdim, int dstate, int ngroups, int dtype,
                 int dt_softplus, const void *x, const void *dt, const float *A, const void *B,
                 const void *C, const float *D, void *state, int state_bf16, void *y, void *stream_) {
+    const int y_f32 = strip_out_flag(dtype);
     if (dtype != SSD_F32 && dtype != SSD_BF16)
         return fail(SSD_ERR_UNSUPPORTED, "dtype %d is not SSD_F32 or SSD_BF16", dtype);
     if (batch < 0) return fail(SSD_ERR_SHAPE, "batch (%d) must be >= 0", batch);
@@ -188,15 +197,15 @@ int decode_step(int batch, int nheads, int headdim, int dstate, int ngroups, int
         if (p && !aligned(p, 16)) return fail(SSD_ERR_ALIGN, "tensor pointer %p is not 16-byte aligned", p);
     const int es = elem_size(dtype);
     int st = check_alias(
-        {span("state", state, n_state * (state_bf16 ? 2 : 4)), span("y", y, n_x * es)},
+        {span("state", state, n_state * (state_bf16 ? 2 : 4)), span("y", y, n_x * (y_f32 ? 4 : es))},
         {span("x", x, n_x * es), span("dt", dt, (uint64_t)batch * nheads * es),
          span("A", A, (uint64_t)nheads * 4), span("B", B, n_bc * es), span("C", C, n_bc * es),
          span("D", D, D ? (uint64_t)nheads * 4 : 0)});
     if (st) return st;
     LaunchMarks marks(static_cast<hipStream_t>(stream_));
     marks.before();
-    hipError_t e = ssd::launch_decode_step(dtype, state_bf16, x, dt, A, B, C, D, dt_softplus, batch,
-                                           nheads, headdim, dstate, ngroups, state, y,
+    hipError_t e = ssd::launch_decode_step(dtype, state_bf16, y_f32, x, dt, A, B, C, D, dt_softplus,
+                                           batch, nheads, headdim, dstate, ngroups, state, y,
                                            static_cast<hipStream_t>(stream_));
     marks.after();
     return e == hipSuccess ? SSD_OK : hip_fail(e, "decode launch");
@@ -209,6 +218,7 @@ int chunk_scan_fwd(int batch, int seqlen, int nheads, int headdim, int dstate, i
                    const float *A, const void *B, const void *C, const float *D,
                    const float *initial_state, void *y, float *final_state, void *workspace,
                    size_t workspace_bytes, void *stream_, bool use_scratch) {
+    const int y_f32 = strip_out_flag(dtype);
     ScanLayout lay;
     int st = scan_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, lay);
     if (st) return st;
@@ -251,7 +261,7 @@ int chunk_scan_fwd(int batch, int seqlen, int nheads, int headdim, int dstate, i
                     workspace_bytes, workspace ? "" : " (NULL)");
     if (!aligned(workspace, 256)) return fail(SSD_ERR_ALIGN, "workspace must be 256-byte aligned");
     st = check_alias(
-        {span("y", y, n_x * es), span("final_state", final_state, n_state * 4),
+        {span("y", y, n_x * (y_f32 ? 4 : es)), span("final_state", final_state, n_state * 4),
          span("workspace", workspace, lay.total)},
         {span("x", x, n_x * es), span("dt", dt, n_dt * es), span("A", A, (uint64_t)nheads * 4),
          span("B", B, n_bc * es), span("C", C, n_bc * es), span("D", D, D ? (uint64_t)nheads * 4 : 0),
@@ -270,7 +280,7 @@ int chunk_scan_fwd(int batch, int seqlen, int nheads, int headdim, int dstate, i
             marks.before();
             e = ssd::launch_ssd_fused(phase, lay.plan, x, dt, A, B, C, D, initial_state, dt_softplus,
                                       batch, seqlen, nheads, headdim, dstate, ngroups, y,
-                                      final_state, ws, stream);
+                                      final_state, ws, stream, y_f32);
             marks.after();
             if (e != hipSuccess) return hip_fail(e, what[phase]);
         }
@@ -336,6 +346,7 @@ int ssd_set_launch_events(void *const *events, int count) {
 
 size_t ssd_chunk_scan_workspace_size(int batch, int seqlen, int nheads, int headdim, int dstate,
                                      int ngroups, int chunk, int dtype) {
+    strip_out_flag(dtype);
     ScanLayout lay;
     if (scan_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, lay)) return 0;
     return lay.total;
@@ -343,6 +354,7 @@ size_t ssd_chunk_scan_workspace_size(int batch, int seqlen, int nheads, int head
 
 int ssd_chunk_scan_plan(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
                         int chunk, int dtype, int *launches, int *segments, int *cut_pairs) {
+    strip_out_flag(dtype);
     ScanLayout lay;
     int st = scan_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, lay);
     if (st) return st;
@@ -362,6 +374,7 @@ int ssd_chunk_scan_plan(int batch, int seqlen, int nheads, int headdim, int dsta
 int ssd_chunk_scan_workspace_layout(int batch, int seqlen, int nheads, int headdim, int dstate,
                                     int ngroups, int chunk, int dtype, size_t *off_delta,
                                     size_t *off_cs, size_t *off_hprev) {
+    strip_out_flag(dtype);
     ScanLayout lay;
     int st = scan_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, lay);
     if (st) return st;

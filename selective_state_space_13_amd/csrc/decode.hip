@@ -108,11 +108,11 @@ struct StateIO<bf16_t> {
     }
 };
 
-template <typename T, typename S, int N>
+template <typename T, typename S, typename O, int N>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const T *__restrict__ x, const T *__restrict__ dt, const float *__restrict__ A,
     const T *__restrict__ B, const T *__restrict__ C, const float *__restrict__ D, int dt_softplus,
-    int nbh, int nheads, int ngroups, S *__restrict__ state, T *__restrict__ y) {
+    int nbh, int nheads, int ngroups, S *__restrict__ state, O *__restrict__ y) {
     typedef StateIO<S> IO;
     constexpr int RPL = N / 4;  // rows per lane
     constexpr int NG = RPL / kGroup;
@@ -178,28 +178,28 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         yacc.y += Dh * xv.y;
         yacc.z += Dh * xv.z;
         yacc.w += Dh * xv.w;
-        store4<T>(y + (size_t)bh * P + 4 * q, yacc);
+        store4<O>(y + (size_t)bh * P + 4 * q, yacc);
     }
 }
 
-template <typename T, typename S, int N>
+template <typename T, typename S, typename O, int N>
 void launch_n(unsigned blocks, hipStream_t stream, const void *x, const void *dt, const float *A,
               const void *B, const void *C, const float *D, int dt_softplus, int nbh, int nheads,
               int ngroups, void *state, void *y) {
-    decode_step_kernel<T, S, N><<<dim3(blocks), dim3(256), 0, stream>>>(
+    decode_step_kernel<T, S, O, N><<<dim3(blocks), dim3(256), 0, stream>>>(
         static_cast<const T *>(x), static_cast<const T *>(dt), A, static_cast<const T *>(B),
         static_cast<const T *>(C), D, dt_softplus, nbh, nheads, ngroups, static_cast<S *>(state),
-        static_cast<T *>(y));
+        static_cast<O *>(y));
 }
 
-template <typename T, typename S>
+template <typename T, typename S, typename O>
 hipError_t launch_t(int dstate, unsigned blocks, hipStream_t stream, const void *x, const void *dt,
                     const float *A, const void *B, const void *C, const float *D, int dt_softplus,
                     int nbh, int nheads, int ngroups, void *state, void *y) {
     switch (dstate) {
 #define SSD_DEC(NN)                                                                                  \
     case NN:                                                                                         \
-        launch_n<T, S, NN>(blocks, stream, x, dt, A, B, C, D, dt_softplus, nbh, nheads, ngroups, state, y); \
+        launch_n<T, S, O, NN>(blocks, stream, x, dt, A, B, C, D, dt_softplus, nbh, nheads, ngroups, state, y); \
         break;
         SSD_DEC(32)
         SSD_DEC(64)
@@ -216,22 +216,30 @@ hipError_t launch_t(int dstate, unsigned blocks, hipStream_t stream, const void 
     return hipGetLastError();
 }
 
+template <typename T, typename S>
+hipError_t launch_ts(int y_f32, int dstate, unsigned blocks, hipStream_t stream, const void *x,
+                     const void *dt, const float *A, const void *B, const void *C, const float *D,
+                     int dt_softplus, int nbh, int nheads, int ngroups, void *state, void *y) {
+    return y_f32 ? launch_t<T, S, float>(dstate, blocks, stream, x, dt, A, B, C, D, dt_softplus, nbh, nheads, ngroups, state, y)
+                 : launch_t<T, S, T>(dstate, blocks, stream, x, dt, A, B, C, D, dt_softplus, nbh, nheads, ngroups, state, y);
+}
+
 }  // namespace
 
-hipError_t launch_decode_step(int dtype, int state_bf16, const void *x, const void *dt, const float *A,
-                              const void *B, const void *C, const float *D, int dt_softplus,
-                              int batch, int nheads, int headdim, int dstate, int ngroups,
-                              void *state, void *y, hipStream_t stream) {
+hipError_t launch_decode_step(int dtype, int state_bf16, int y_f32, const void *x, const void *dt,
+                              const float *A, const void *B, const void *C, const float *D,
+                              int dt_softplus, int batch, int nheads, int headdim, int dstate,
+                              int ngroups, void *state, void *y, hipStream_t stream) {
     if (headdim != P || dstate % 32) return hipErrorInvalidValue;
     const long long nbh = (long long)batch * nheads;
     if (nbh == 0) return hipSuccess;
     const unsigned blocks = (unsigned)((nbh + 3) / 4);
     const int n = (int)nbh;
     if (dtype == 0)
-        return state_bf16 ? launch_t<float, bf16_t>(dstate, blocks, stream, x, dt, A, B, C, D, dt_softplus, n, nheads, ngroups, state, y)
-                          : launch_t<float, float>(dstate, blocks, stream, x, dt, A, B, C, D, dt_softplus, n, nheads, ngroups, state, y);
-    return state_bf16 ? launch_t<bf16_t, bf16_t>(dstate, blocks, stream, x, dt, A, B, C, D, dt_softplus, n, nheads, ngroups, state, y)
-                      : launch_t<bf16_t, float>(dstate, blocks, stream, x, dt, A, B, C, D, dt_softplus, n, nheads, ngroups, state, y);
+        return state_bf16 ? launch_ts<float, bf16_t>(1, dstate, blocks, stream, x, dt, A, B, C, D, dt_softplus, n, nheads, ngroups, state, y)
+                          : launch_ts<float, float>(1, dstate, blocks, stream, x, dt, A, B, C, D, dt_softplus, n, nheads, ngroups, state, y);
+    return state_bf16 ? launch_ts<bf16_t, bf16_t>(y_f32, dstate, blocks, stream, x, dt, A, B, C, D, dt_softplus, n, nheads, ngroups, state, y)
+                      : launch_ts<bf16_t, float>(y_f32, dstate, blocks, stream, x, dt, A, B, C, D, dt_softplus, n, nheads, ngroups, state, y);
 }
 
 }  // namespace ssd

@@ -56,9 +56,9 @@ __global__ __launch_bounds__(kThreads, 4) void ssd_state_kernel(FusedArgs a) {
 
 // The full pass: states and outputs.  Two workgroups of 8 waves per CU: 4
 // waves per SIMD (at most 128 VGPRs), at most 80 KB of LDS each.
-template <int N>
+template <int N, bool YF32>
 __global__ __launch_bounds__(kThreads, 4) void ssd_prefill_kernel(FusedArgs a) {
-    fused_pair_walk<N>(a, blockIdx.x, gridDim.x);
+    fused_pair_walk<N, YF32>(a, blockIdx.x, gridDim.x);
 }
 
 // State entering each segment s >= 1: H_s = exp(decay_{s-1})·H_{s-1} + E_{s-1},
@@ -138,10 +138,11 @@ hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const
                             const float *A, const void *B, const void *C, const float *D,
                             const float *h0, int dt_softplus, int batch, int seqlen, int nheads,
                             int headdim, int dstate, int ngroups, void *y, float *final_state,
-                            void *workspace, hipStream_t stream) {
+                            void *workspace, hipStream_t stream, int y_f32) {
     if (headdim != P || (dstate != 64 && dstate != 128)) return hipErrorInvalidValue;
     if ((long long)batch * nheads == 0 || seqlen == 0) return hipSuccess;
     FusedArgs a{};
+    a.yf = y_f32 ? static_cast<float *>(y) : nullptr;
     a.x = static_cast<const uint16_t *>(x);
     a.dt = static_cast<const uint16_t *>(dt);
     a.B = static_cast<const uint16_t *>(B);
@@ -188,11 +189,16 @@ hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const
         const long long total = (long long)batch * nheads * dstate * P;
         segment_combine_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(
             a.h0, a.seg_state, a.seg_decay, const_cast<float *>(a.hin), a.nseg, dstate * P, total);
+    } else if (y_f32) {
+        if (dstate == 128)
+            ssd_prefill_kernel<128, true><<<items, kThreads, 0, stream>>>(a);
+        else
+            ssd_prefill_kernel<64, true><<<items, kThreads, 0, stream>>>(a);
     } else {
         if (dstate == 128)
-            ssd_prefill_kernel<128><<<items, kThreads, 0, stream>>>(a);
+            ssd_prefill_kernel<128, false><<<items, kThreads, 0, stream>>>(a);
         else
-            ssd_prefill_kernel<64><<<items, kThreads, 0, stream>>>(a);
+            ssd_prefill_kernel<64, false><<<items, kThreads, 0, stream>>>(a);
     }
     return hipGetLastError();
 }
@@ -230,9 +236,9 @@ hipError_t launch_ssd_fused_varlen(const int *cu_seqlens, int nseq, int total_to
     a.tail_decay = nullptr;
     const unsigned items = (unsigned)((long long)nseq * nheads);
     if (dstate == 128)
-        ssd_prefill_kernel<128><<<items, kThreads, 0, stream>>>(a);
+        ssd_prefill_kernel<128, false><<<items, kThreads, 0, stream>>>(a);
     else
-        ssd_prefill_kernel<64><<<items, kThreads, 0, stream>>>(a);
+        ssd_prefill_kernel<64, false><<<items, kThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -54,7 +54,7 @@ __device__ __forceinline__ int pair_n(int i, int q, int r) { return 32 * (i >> 1
 // 16-byte chunk of row t of a masked block: q XOR this
 __device__ __forceinline__ int mt_swz(int t) { return (t >> 1) & 3; }
 
-template <int N>
+template <int N, bool YF32>
 __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk, unsigned nblk) {
     constexpr int NT = N / 16;      // state tiles of a state wave
     constexpr int KS = N / 32;      // k-steps over n of C·H
@@ -283,16 +283,21 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
             // hoisted out of the loop, the four offsets would be kept in registers
             // the loop does not have.
             const int t0 = c * kC;
-            uint16_t *yb = a.y + ((row0 + t0) * a.nheads + h) * P;
+            const size_t ybase = ((row0 + t0) * a.nheads + h) * P;
             int ln = lane;
             asm volatile("" : "+v"(ln));
             const uint32_t yo = (uint32_t)(ln & 15) * (uint32_t)xstride + 16 * role + 4 * (ln >> 4);
 #pragma unroll
             for (int tau = 0; tau < 4; ++tau) {
                 if (t0 + 16 * tau + c16 < seqlen) {
-                    const uint2 v = make_uint2(pack_bf16x2(y[tau][0], y[tau][1]),
-                                               pack_bf16x2(y[tau][2], y[tau][3]));
-                    *reinterpret_cast<uint2 *>(yb + (yo + (uint32_t)(16 * tau) * (uint32_t)xstride)) = v;
+                    const uint32_t o = yo + (uint32_t)(16 * tau) * (uint32_t)xstride;
+                    if constexpr (YF32) {
+                        *reinterpret_cast<float4 *>(a.yf + ybase + o) =
+                            make_float4(y[tau][0], y[tau][1], y[tau][2], y[tau][3]);
+                    } else {
+                        *reinterpret_cast<uint2 *>(a.y + ybase + o) =
+                            make_uint2(pack_bf16x2(y[tau][0], y[tau][1]), pack_bf16x2(y[tau][2], y[tau][3]));
+                    }
                 }
             }
             __syncthreads();

@@ -31,7 +31,8 @@ struct FusedArgs {
     const float *A, *D;
     const float *h0;      // [b][H][N][P] state entering the sequence, or null (zeros)
     const float *hin;     // [b][H][S][N][P] state entering each segment s >= 1 (full pass, S > 1)
-    uint16_t *y;
+    uint16_t *y;          // bf16 outputs, or
+    float *yf;            // float32 outputs (full pass with float32 y)
     float *final_state;   // [b][H][N][P] or null (full pass, last segment writes it)
     float *seg_state;     // [b][H][S][N][P] local end state of each segment (state-only pass)
     double *seg_decay;    // [b][H][S] Σ Δ·A over each segment (state-only pass)

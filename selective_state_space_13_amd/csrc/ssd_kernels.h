@@ -99,7 +99,7 @@ hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const
                             const float *A, const void *B, const void *C, const float *D,
                             const float *h0, int dt_softplus, int batch, int seqlen, int nheads,
                             int headdim, int dstate, int ngroups, void *y, float *final_state,
-                            void *workspace, hipStream_t stream);
+                            void *workspace, hipStream_t stream, int y_f32 = 0);
 // Chunked backward (bf16).  Workspace: the forward plan's, then the chunk
 // states, the chunk adjoints and the per-(b, h, chunk) dA, dD partials.
 struct BwdPlan {
@@ -128,11 +128,12 @@ hipError_t launch_ssd_fused_varlen(const int *cu_seqlens, int nseq, int total_to
                                    hipStream_t stream);
 
 
-// decode step, in-place state: float, or bf16 when state_bf16
-hipError_t launch_decode_step(int dtype, int state_bf16, const void *x, const void *dt, const float *A,
-                              const void *B, const void *C, const float *D, int dt_softplus,
-                              int batch, int nheads, int headdim, int dstate, int ngroups,
-                              void *state, void *y, hipStream_t stream);
+// decode step, in-place state: float, or bf16 when state_bf16; y in the input
+// dtype, or float when y_f32
+hipError_t launch_decode_step(int dtype, int state_bf16, int y_f32, const void *x, const void *dt,
+                              const float *A, const void *B, const void *C, const float *D,
+                              int dt_softplus, int batch, int nheads, int headdim, int dstate,
+                              int ngroups, void *state, void *y, hipStream_t stream);
 
 // Mamba-1 selective scan.  The sequence is cut into nseg time segments: phase 0
 // gives each segment's local end state and Σ Δ, phase 1 chains them into

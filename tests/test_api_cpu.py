@@ -414,3 +414,44 @@ def test_noalloc_validates_before_any_device_call(L):
     assert st == UNSUP
     # the 64K-token, 80-head bf16 call fits
     assert L.ssd_chunk_scan_workspace_size(1, 65536, 80, 64, 128, 8, 256, BF16) <= L.ssd_noalloc_scratch_bytes()
+
+
+OUT_F32 = 0x100
+
+
+def test_out_f32_flag_value_matches_binding():
+    assert ssd.SSD_OUT_F32 == OUT_F32
+    assert re.search(r"#define\s+SSD_OUT_F32\s+0x100\b", open(HEADER).read())
+
+
+def test_out_f32_flag_prefill_and_decode(L):
+    # the flag leaves sizes and plans alone
+    for dt in (F32, BF16):
+        assert (L.ssd_chunk_scan_workspace_size(2, 300, 8, 64, 128, 2, 256, dt | OUT_F32)
+                == L.ssd_chunk_scan_workspace_size(2, 300, 8, 64, 128, 2, 256, dt))
+    assert _plan(L, 3, 1100, 200, 64, 128, 4, 256, BF16 | OUT_F32) == _plan(L, 3, 1100, 200, 64, 128,
+                                                                          4, 256, BF16)
+    # y right before the final state: disjoint at 2 bytes a value, overlapping at 4
+    n_x = 2 * 300 * 8 * 64
+    y = fake(8, -2 * n_x)
+    assert scan_call(L, ptrs={"y": y}) != ALIAS
+    assert scan_call(L, dtype=BF16 | OUT_F32, ptrs={"y": y}) == ALIAS
+    assert scan_call(L, dtype=F32 | OUT_F32, ptrs={"y": y}) == ALIAS
+    assert scan_call(L, dtype=BF16 | OUT_F32, b=0) == OK
+    assert scan_call(L, dtype=2 | OUT_F32) == UNSUP
+    # decode: y right before the state
+    n_y = 4 * 8 * 64
+    y = fake(7, -2 * n_y)
+    assert decode_call(L, ptrs={"y": y}) != ALIAS
+    assert decode_call(L, dtype=BF16 | OUT_F32, ptrs={"y": y}) == ALIAS
+    assert decode_call(L, dtype=BF16 | OUT_F32, ptrs={"y": y}, bf16_state=True) == ALIAS
+    assert decode_call(L, dtype=BF16 | OUT_F32, ptrs={"y": fake(8, 8)}) == ALIGN
+
+
+def test_out_f32_flag_rejected_elsewhere(L):
+    assert bwd_call(L, dtype=BF16 | OUT_F32) == UNSUP
+    assert varlen_call(L, dtype=BF16 | OUT_F32) == UNSUP
+    assert m1_call(L, dtype=BF16 | OUT_F32) == UNSUP
+    assert L.selective_scan_workspace_size(8, 4096, 5120, 16, BF16 | OUT_F32) == 0
+    assert conv_call(L, dtype=BF16 | OUT_F32) == UNSUP
+    assert norm_call(L, dtype=BF16 | OUT_F32) == UNSUP

@@ -25,14 +25,14 @@ def say(*a):
     print(*a, flush=True)
 
 
-def run_scan(d, chunk, dtype, with_D=True, with_h0=False, final=True):
+def run_scan(d, chunk, dtype, with_D=True, with_h0=False, final=True, out_dtype=None):
     dev = "cuda"
     x, dt, B, C = (to_dev(d[k], dev) for k in ("x", "dt", "B", "C"))
     A = to_dev(d["A"], dev)
     D = to_dev(d["D"], dev) if with_D and d["D"] is not None else None
     h0 = to_dev(d["h0"], dev) if with_h0 else None
     out = ssd.ssd_chunk_scan(x, dt, A, B, C, D, chunk=chunk, initial_state=h0,
-                             return_final_state=final)
+                             return_final_state=final, out_dtype=out_dtype)
     torch.cuda.synchronize()
     return out
 
@@ -156,6 +156,22 @@ def test_prefill_tail_cut(case):
     yo, fo = oracle_scan(d, wD, wh)
     assert_parity(to_f64(y), yo, TAU_BF16, True, f"tail cut y {case}")
     assert_parity(to_f64(fs), fo, TAU_BF16, False, f"tail cut final {case}")
+
+
+@pytest.mark.parametrize("case", [(2, 700, 6, 128, 2, True, True), (1, 16384, 8, 64, 1, False, True),
+                                  (3, 1100, 200, 128, 4, True, False)],
+                         ids=["b2L700ragged", "b1L16384segmented", "b3L1100H200tailcut"])
+def test_prefill_float32_y(case):
+    """float32 y from bf16 inputs through each kind of plan (one launch with a
+    ragged last chunk, segments, a cut last round), held to the bare bar; the
+    bf16 y of the same call is its round to nearest even."""
+    b, L, H, N, G, wD, wh = case
+    d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=L + H, config_id=113, with_h0=wh)
+    y32, fs32 = run_scan(d, 256, "bf16", wD, wh, out_dtype=torch.float32)
+    y, fs = run_scan(d, 256, "bf16", wD, wh)
+    yo, fo = oracle_scan(d, wD, wh)
+    assert_parity(to_f64(y32), yo, TAU_BF16, False, f"float32 y {case}")
+    assert torch.equal(y, y32.to(torch.bfloat16)) and torch.equal(fs, fs32)
 
 
 VARLEN_GPU_CASES = [
@@ -621,14 +637,22 @@ def config2():
 
 
 def test_config2_prefill_full(config2):
+    """bf16 y (the bar plus its own rounding step) and float32 y from the same
+    bf16 inputs (the bare bar, no allowance), both against one oracle run."""
     c, d = config2
     for wD in (True, False):
         say(f"C2: GPU run D={wD}")
         y, fs = run_scan(d, c["chunk"], "bf16", wD)
+        y32, fs32 = run_scan(d, c["chunk"], "bf16", wD, out_dtype=torch.float32)
+        assert y32.dtype == torch.float32
         say("C2: oracle")
         yo, fo = oracle_scan(d, wD)
         assert_parity(to_f64(y), yo, TAU_BF16, True, f"C2 y D={wD}")
+        assert_parity(to_f64(y32), yo, TAU_BF16, False, f"C2 float32 y D={wD}")
         assert_parity(to_f64(fs), fo, TAU_BF16, False, f"C2 final D={wD}")
+        # the output dtype changes only the last rounding of y
+        assert torch.equal(fs, fs32)
+        assert torch.equal(y, y32.to(torch.bfloat16))
 
 
 def test_config2_backward_full(config2):
@@ -658,11 +682,15 @@ def test_config3_long_context_full():
                        c["ngroups"], c["dtype"], config_id=c["id"])
     say("C3: GPU run")
     y, fs = run_scan(d, c["chunk"], "bf16", True)
+    y32, _ = run_scan(d, c["chunk"], "bf16", True, out_dtype=torch.float32)
+    assert torch.equal(y, y32.to(torch.bfloat16))
     y = to_f64(y)
+    y32 = to_f64(y32)
     fs = to_f64(fs)
     say("C3: oracle")
     yo, fo = oracle_scan(d, True)
     assert_parity(y, yo, TAU_BF16, True, "C3 y")
+    assert_parity(y32, yo, TAU_BF16, False, "C3 float32 y")
     assert_parity(fs, fo, TAU_BF16, False, "C3 final state vs sequential recurrence")
 
 
@@ -687,6 +715,31 @@ def test_decode_small_chain(N, G, wD, dtype):
                                     s["C"].f64(), D.f64() if wD else None, ost)
         assert_parity(to_f64(y), yo, tau_of(dtype), dtype == "bf16", f"decode y step {k}")
     assert_parity(to_f64(state), ost, tau_of(dtype), False, "decode state")
+
+
+@pytest.mark.parametrize("bf16_state", [False, True])
+def test_decode_float32_y(bf16_state):
+    """float32 y from bf16 inputs, both state caches: the bare bar, the same state
+    as the bf16-y call, and bf16 y its round to nearest even."""
+    b, H, P, N, G = 4, 8, 64, 128, 2
+    A, D = gen.ssd_params(H, seed=5, config_id=114)
+    rng = np.random.default_rng(5)
+    st0 = (rng.standard_normal((b, H, N, P)) * 0.05).astype(np.float32)
+    if bf16_state:
+        st0 = bf16_state_tensor(st0).float().cpu().numpy()
+    fn = ssd.ssd_decode_step_bf16_state if bf16_state else ssd.ssd_decode_step
+    sdt = torch.bfloat16 if bf16_state else torch.float32
+    s = gen.decode_inputs(b, H, P, N, G, "bf16", step=0, seed=5, config_id=114)
+    args = (to_dev(s["x"]), to_dev(s["dt"]), to_dev(A), to_dev(s["B"]), to_dev(s["C"]), to_dev(D))
+    st_a = torch.from_numpy(st0).to(sdt).cuda()
+    st_b = st_a.clone()
+    y = fn(*args, st_a)
+    y32 = fn(*args, st_b, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    yo, _ = oracle.ssd_decode(s["x"].f64(), s["dt"].f64(), A.f64(), s["B"].f64(), s["C"].f64(),
+                              D.f64(), st0.astype(np.float64))
+    assert_parity(to_f64(y32), yo, TAU_BF16, False, f"decode float32 y bf16_state={bf16_state}")
+    assert torch.equal(y, y32.to(torch.bfloat16)) and torch.equal(st_a, st_b)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -723,22 +776,28 @@ def test_config4_decode_chain_full(config2):
     reps = c["batch"] // c2["batch"]
     st0 = np.tile(f8, (reps, 1, 1, 1)).astype(np.float32)
     state = torch.from_numpy(st0).cuda()
+    state32 = state.clone()  # the chain run with float32 y
     ost = st0.astype(np.float64)
     A, D = gen.ssd_params(c["nheads"], config_id=c2["id"])
     Ad, Dd = to_dev(A), to_dev(D)
-    worst = 0.0
+    worst = worst32 = 0.0
     for k in range(c["steps"]):
         s = gen.decode_inputs(c["batch"], c["nheads"], c["headdim"], c["dstate"], c["ngroups"],
                               c["dtype"], step=k, config_id=c["id"])
-        y = ssd.ssd_decode_step(to_dev(s["x"]), to_dev(s["dt"]), Ad, to_dev(s["B"]),
-                                to_dev(s["C"]), Dd, state)
+        args = (to_dev(s["x"]), to_dev(s["dt"]), Ad, to_dev(s["B"]), to_dev(s["C"]), Dd)
+        y = ssd.ssd_decode_step(*args, state)
+        y32 = ssd.ssd_decode_step(*args, state32, out_dtype=torch.float32)
         torch.cuda.synchronize()
+        assert y32.dtype == torch.float32 and torch.equal(y, y32.to(torch.bfloat16))
         yo, ost = oracle.ssd_decode(s["x"].f64(), s["dt"].f64(), A.f64(), s["B"].f64(),
                                     s["C"].f64(), D.f64(), ost)
         r = assert_parity(to_f64(y), yo, TAU_BF16, True, f"C4 y step {k}")
         worst = max(worst, r["excess_over_rms"])
+        r = assert_parity(to_f64(y32), yo, TAU_BF16, False, f"C4 float32 y step {k}")
+        worst32 = max(worst32, r["excess_over_rms"])
+    assert torch.equal(state, state32)
     assert_parity(to_f64(state), ost, TAU_BF16, False, "C4 state after 64 steps")
-    say(f"C4 worst step excess/RMS {worst:.3e}")
+    say(f"C4 worst step excess/RMS {worst:.3e} (bf16 y), {worst32:.3e} (float32 y, bare rule)")
 
 
 # ------------------------------------------------- decode against a bf16 state cache
