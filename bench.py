@@ -19,7 +19,8 @@ them).  GPU clocks are read with rocm-smi before and after the timed region.
 The same run also times, as separate legs of the JSON line: the single-token
 decode step at batch 256 (state cache of a 2.7B-layer prefill; each of the 64
 steps timed, median per step, and the 64-step chain back to back), the
-64K-token long-context prefill with eight groups, the Mamba-1 selective scan
+64K-token long-context prefill with eight groups, the 2.7B-layer prefill with
+float8 e4m3fn x, B and C (bf16 dt and y), the Mamba-1 selective scan
 (batch 8, seqlen 4096, 5120 channels, dstate 16), a packed variable-length
 prefill (8 sequences of mixed lengths, 16384 tokens), the causal conv1d (width
 4 over 5376 channels) and the gated RMSNorm (5120 channels) of the same layer,
@@ -75,6 +76,8 @@ def to_dev(t):
         return None
     if t.dtype == "f32":
         return torch.from_numpy(np.ascontiguousarray(t.data)).cuda()
+    if t.dtype == "fp8":
+        return torch.from_numpy(np.ascontiguousarray(t.data)).cuda().view(torch.float8_e4m3fn)
     return torch.from_numpy(np.ascontiguousarray(t.data).view(np.int16)).view(torch.bfloat16).cuda()
 
 
@@ -225,16 +228,19 @@ def prefill_work(c, cut_pairs=0):
     b, L, H, P, N, G, Q = (c[k] for k in ("batch", "seqlen", "nheads", "headdim", "dstate",
                                           "ngroups", "chunk"))
     K = (L + Q - 1) // Q
-    x_bytes = b * L * H * P * 2          # x, and likewise y
-    bc_bytes = b * L * G * N * 2         # B, and likewise C
-    dt_bytes = b * L * H * 2
+    es = {"fp8": 1, "bf16": 2, "f32": 4}[c["dtype"]]   # x, B, C
+    ea = 2 if c["dtype"] == "fp8" else es              # dt, y (bf16 beside float8 inputs)
+    x_bytes = b * L * H * P * es         # x
+    y_bytes = b * L * H * P * ea         # y
+    bc_bytes = b * L * G * N * es        # B, and likewise C
+    dt_bytes = b * L * H * ea
     final = b * H * N * P * 4 if c.get("final_state") else 0
     units_h = b * K * H
     units_g = b * K * G
     # the same causal count at the 64-token blocking the bf16 kernel uses
     K64 = (L + 63) // 64
     flops_q64 = b * K64 * H * (4 * 64 * N * P + 64 * 65 * P) + b * K64 * G * 64 * 65 * N
-    total = dict(bytes=2 * x_bytes + 2 * bc_bytes + dt_bytes + final,
+    total = dict(bytes=x_bytes + y_bytes + 2 * bc_bytes + dt_bytes + final,
                  flops=units_h * (4 * Q * N * P + Q * (Q + 1) * P) + units_g * Q * (Q + 1) * N,
                  flops_q64=flops_q64)
     # the fused kernel does all of it; the segment passes re-read x, B and dt
@@ -256,11 +262,11 @@ def bench_prefill(cfg, steps, warmup, seed=0):
                        cfg["ngroups"], cfg["dtype"], seed=seed, config_id=cfg["id"])
     x, dt, B, C, A, D = (to_dev(d[k]) for k in ("x", "dt", "B", "C", "A", "D"))
     del d
-    code = ssd.SSD_BF16 if cfg["dtype"] == "bf16" else ssd.SSD_F32
+    code = {"bf16": ssd.SSD_BF16, "f32": ssd.SSD_F32, "fp8": ssd.SSD_FP8}[cfg["dtype"]]
     ws = torch.empty(ssd.chunk_scan_workspace_size(cfg["batch"], cfg["seqlen"], cfg["nheads"],
                                                    cfg["headdim"], cfg["dstate"], cfg["ngroups"],
                                                    cfg["chunk"], code), dtype=torch.uint8, device="cuda")
-    y = torch.empty_like(x)
+    y = torch.empty(x.shape, dtype=dt.dtype, device="cuda")  # bf16 beside float8 inputs
     fs = torch.empty(cfg["batch"], cfg["nheads"], cfg["dstate"], cfg["headdim"], device="cuda") \
         if cfg.get("final_state") else None
     launches, _, cut_pairs = ssd.chunk_scan_plan(cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["headdim"],
@@ -500,7 +506,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="decode,long,mamba1,varlen,convnorm,backward",
+    ap.add_argument("--legs", default="decode,long,fp8,mamba1,varlen,convnorm,backward",
                     help="extra legs to time besides the prefill step (comma list or 'none')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -653,6 +659,23 @@ def main():
                                                 + " at 39.3e12 lane-ops/s and 9.8e12 exp/s"},
                            "hbm_frac": round(m1["bytes"] / t / HBM_PEAK, 4),
                            "exp_per_s": round(n_exp / t, 1)}
+    if "fp8" in legs:
+        # the 2.7B-layer prefill with float8 e4m3fn x, B, C (bf16 dt and y)
+        c8 = dict(cfg, dtype="fp8", name=cfg["name"] + "_fp8")
+        f8 = bench_prefill(c8, args.steps, args.warmup)
+        per8 = f8["per_kernel_ms"]
+        w8 = f8["work"]["ssd_fused"]
+        t8 = per8["ssd_fused"] * 1e-3
+        extra["fp8_prefill"] = {
+            "workload": workload + ", x B C float8 e4m3fn, dt and y bf16",
+            "tokens_per_s": round(f8["tokens"] / (f8["ms"] * 1e-3), 1), "ms": round(f8["ms"], 5),
+            "per_kernel_ms": {k: round(v, 5) for k, v in per8.items()},
+            "alg_bytes": w8["bytes"],
+            "roofline": {"kernel": "ssd_fused", "bound": "hbm",
+                         "achieved": round(w8["bytes"] / t8 / 1e9, 3), "peak": HBM_PEAK / 1e9,
+                         "unit": "GB/s", "frac": round(w8["bytes"] / t8 / HBM_PEAK, 4),
+                         "mfma_frac_q64": round(w8["flops_q64"] / t8 / MFMA_BF16_PEAK, 4)}}
+        del f8
     if "varlen" in legs:
         vl = bench_varlen(args.steps, args.warmup)
         t = vl["kernel_ms"] * 1e-3

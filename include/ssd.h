@@ -24,10 +24,12 @@
  * Conventions for every entry point
  *  - All tensor pointers are device pointers on the current HIP device,
  *    contiguous row-major in the layout given, 16-byte aligned.
- *  - "dtype" tensors hold float (SSD_F32) or bfloat16 (SSD_BF16) elements;
+ *  - "dtype" tensors hold float (SSD_F32) or bfloat16 (SSD_BF16) elements
+ *    (the prefill also takes float8 x, B, C: SSD_FP8 below);
  *    A, D and every state are always float32.  Arithmetic is float32
  *    (bf16 inputs feed bf16 matrix-core products with float32 accumulation);
- *    outputs are rounded to the input dtype, states stay float32.
+ *    outputs are rounded to the input dtype (bf16 for SSD_FP8), states stay
+ *    float32.
  *  - The caller owns every buffer, including the workspace.  The library never
  *    allocates device memory, never synchronises, and keeps no pointer after
  *    return, with one exception: ssd_set_launch_events (a benchmarking hook)
@@ -58,7 +60,15 @@
 extern "C" {
 #endif
 
-typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+/* SSD_FP8 ([TP] §5.1: the SSD's low-precision matrix products; [INF]'s related
+ * work on 8-bit SSM inputs): x, B and C are float8 e4m3fn, the OCP format
+ * (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, no infinities,
+ * S.1111.111 = NaN; largest finite 448, smallest subnormal 2^-9), taken as
+ * they are (no scale); dt and y are bfloat16.  Every e4m3fn value is a
+ * bfloat16 value, so the result is that of the same values given as SSD_BF16
+ * (computed identically; only the loads differ).  ssd_chunk_scan_fwd, its
+ * no-alloc variant and its size and plan queries only. */
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1, SSD_FP8 = 2 } ssd_dtype;
 
 /* OR'ed into the dtype of ssd_chunk_scan_fwd (and its size, plan and layout
  * queries, and ssd_chunk_scan_fwd_noalloc), ssd_decode_step and
@@ -95,21 +105,23 @@ const char *ssd_last_error(void);
  * the scan above over t = 0..seqlen-1 starting from initial_state (or 0), by
  * the block decomposition.  The chunk length changes rounding only, not the
  * result: SSD_F32 uses chunks of `chunk` tokens (the last may be shorter);
- * SSD_BF16 runs one fused kernel with 64-token chunks whatever `chunk` says,
+ * SSD_BF16 and SSD_FP8 run one fused kernel with 64-token chunks whatever `chunk` says,
  * keeps every intermediate on chip, and for calls with few (batch, head)
  * pairs and long sequences cuts the sequence into segments scanned in
  * parallel (their end states are chained through the workspace).
  *
  *   x      [batch][seqlen][nheads][headdim]      dtype
- *   dt     [batch][seqlen][nheads]               dtype  (raw if dt_softplus)
+ *   dt     [batch][seqlen][nheads]               dtype, bf16 for SSD_FP8  (raw if dt_softplus)
  *   A      [nheads]                              float  (A_h; < 0 decays, see "Decay sign")
  *   B, C   [batch][seqlen][ngroups][dstate]      dtype
  *   D      [nheads]                              float  or NULL (= 0)
  *   initial_state [batch][nheads][dstate][headdim] float or NULL (= 0)
- *   y      [batch][seqlen][nheads][headdim]      dtype (float with SSD_OUT_F32), written
+ *   y      [batch][seqlen][nheads][headdim]      dtype, bf16 for SSD_FP8
+ *                                                (float with SSD_OUT_F32), written
  *   final_state   [batch][nheads][dstate][headdim] float or NULL, written
  *   workspace     >= ssd_chunk_scan_workspace_size(...) bytes, 256-byte aligned
- *                 (SSD_BF16: 256 bytes, unused, unless the call is segmented;
+ *                 (SSD_BF16, SSD_FP8: 256 bytes, unused, unless the call is
+ *                 segmented or its last round of pairs is cut;
  *                 SSD_F32: the stages below)
  *
  * Supported: headdim == 64; dstate in {64, 128}; chunk in {64, 128, 256};

@@ -11,6 +11,9 @@ links or calls it, and the two share no code.
 * ``round_bf16``, ``ssd_decode_bf16_state``: the decode step against a bf16
   state cache -- the float64 step of ``ssd_decode`` on the stored values, the
   new state then rounded to the nearest bf16 (ties to even).
+* ``fp8_e4m3_values``, ``round_fp8_e4m3``: the float8 e4m3fn format of 8-bit
+  inputs (values of the bytes; rounding to it), so that the scans above run on
+  exactly the values a float8 input holds.
 
 Parity status: every function is pinned by the CPU tests in
 ``tests/test_oracle_pins.py`` (closed forms, the dual form, the block
@@ -183,6 +186,40 @@ def round_bf16(v):
     v = np.asarray(v, dtype=np.float64)
     m, e = np.frexp(v)                      # v = m·2^e, 0.5 <= |m| < 1
     return np.ldexp(np.round(m * 256.0) / 256.0, e)   # np.round: half to even
+
+
+# float8 e4m3fn (the OCP 8-bit format with 4 exponent bits): 1 sign bit, a
+# 4-bit exponent with bias 7, 3 mantissa bits; exponent field 0 holds the
+# subnormals m·2^-9; no infinities; S.1111.111 is NaN, so the largest finite
+# magnitude is 1.75·2^8 = 448.  Low-precision inputs to the SSD's matrix
+# products are the subject of page "5.3 텐서 병렬화(Tensor Parallelism) 지원과
+# 대규모 클러스터 학습", §5.1 (FP8 on the H100's tensor cores).
+
+def fp8_e4m3_values(codes):
+    """The value of each float8 e4m3fn byte (uint8 codes), as float64."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((e == 15) & (c & 7 == 7), np.nan, mag)
+    return sign * mag
+
+
+def round_fp8_e4m3(v):
+    """Each value rounded to the nearest float8 e4m3fn value, ties to even;
+    returned as float64.  Magnitudes that round beyond 448 (from 464 up: the
+    tie at 464 goes to 448), infinities and NaN give NaN, the format having no
+    infinity.  Below 2^-6 the spacing is the subnormal quantum 2^-9."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    with np.errstate(invalid="ignore"):
+        sub = np.round(a / 2.0 ** -9) * 2.0 ** -9          # np.round: half to even
+        m, e = np.frexp(a)                                 # a = m·2^e, 0.5 <= m < 1
+        nrm = np.ldexp(np.round(m * 16.0) / 16.0, e)       # 4 significant bits
+        q = np.where(a < 2.0 ** -6, sub, nrm)
+        q = np.where(np.isfinite(v) & (q <= 448.0), q, np.nan)
+    return np.copysign(q, v)
 
 
 def ssd_decode_bf16_state(x, dt, A, B, C, D, state, dt_softplus=True):

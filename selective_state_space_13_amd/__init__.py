@@ -24,7 +24,7 @@ import os
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libssd.so")
 
-SSD_F32, SSD_BF16 = 0, 1
+SSD_F32, SSD_BF16, SSD_FP8 = 0, 1, 2
 SSD_OUT_F32 = 0x100  # flag: float32 y from the prefill and decode entry points
 STATUS = {0: "SSD_OK", -1: "SSD_ERR_NULL", -2: "SSD_ERR_SHAPE", -3: "SSD_ERR_UNSUPPORTED",
           -4: "SSD_ERR_WORKSPACE", -5: "SSD_ERR_ALIGN", -6: "SSD_ERR_ALIAS", -7: "SSD_ERR_HIP"}
@@ -114,21 +114,31 @@ def _dtype_code(t) -> int:
         return SSD_F32
     if t.dtype == torch.bfloat16:
         return SSD_BF16
+    if t.dtype == torch.float8_e4m3fn:
+        return SSD_FP8  # the prefill's x, B, C only; other entry points refuse it
     raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
 
 
-def _y_dtype(x, out, out_dtype):
-    """dtype of y: that of `out` if given, else `out_dtype`, else that of x.
-    float32 y with bfloat16 inputs is the SSD_OUT_F32 flag."""
+def _aux_dtype(x):
+    """dtype of dt and (by default) y for inputs x: bfloat16 for float8 x, B, C."""
     torch = _torch()
-    want = out.dtype if out is not None else (out_dtype if out_dtype is not None else x.dtype)
-    if want != x.dtype and want != torch.float32:
-        raise TypeError(f"y may be {x.dtype} or float32, not {want}")
+    return torch.bfloat16 if x.dtype == torch.float8_e4m3fn else x.dtype
+
+
+def _y_dtype(x, out, out_dtype):
+    """dtype of y: that of `out` if given, else `out_dtype`, else the inputs'
+    (bfloat16 for float8 inputs).  float32 y with bfloat16 or float8 inputs is
+    the SSD_OUT_F32 flag."""
+    torch = _torch()
+    base = _aux_dtype(x)
+    want = out.dtype if out is not None else (out_dtype if out_dtype is not None else base)
+    if want != base and want != torch.float32:
+        raise TypeError(f"y may be {base} or float32, not {want}")
     return want
 
 
 def _with_out_flag(code, x, ydt):
-    return code | SSD_OUT_F32 if ydt != x.dtype else code
+    return code | SSD_OUT_F32 if ydt != _aux_dtype(x) else code
 
 
 def _ptr(t):
@@ -187,13 +197,14 @@ def ssd_chunk_scan(x, dt, A, B, C, D=None, *, chunk, initial_state=None,
     D [H] fp32 or None, initial_state [b,H,N,P] fp32 or None.
     Returns y (dtype of x, or float32 when out_dtype or out says so) or
     (y, final_state fp32 [b,H,N,P]).  `workspace` (uint8 tensor), `out` and
-    `final_state` may be passed to reuse buffers."""
+    `final_state` may be passed to reuse buffers.  float8_e4m3fn x, B, C take
+    bfloat16 dt and give bfloat16 (or float32) y."""
     torch = _torch()
     x = _req(x, "x")
     dev = x.device
     code = _dtype_code(x)
     b, L, H, P = x.shape
-    _req(dt, "dt", x.dtype, dev)
+    _req(dt, "dt", _aux_dtype(x), dev)
     _req(B, "B", x.dtype, dev)
     _req(C, "C", x.dtype, dev)
     _req(A, "A", torch.float32, dev)
@@ -238,7 +249,7 @@ def ssd_chunk_scan_fwd_noalloc(x, dt, A, B, C, D=None, *, chunk, initial_state=N
     dev = x.device
     code = _dtype_code(x)
     b, L, H, P = x.shape
-    _req(dt, "dt", x.dtype, dev)
+    _req(dt, "dt", _aux_dtype(x), dev)
     _req(B, "B", x.dtype, dev)
     _req(C, "C", x.dtype, dev)
     _req(A, "A", torch.float32, dev)

@@ -103,6 +103,11 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 int elem_size(int dtype) { return dtype == SSD_BF16 ? 2 : 4; }
 
+// bytes of an element of x, B and C (SSD_FP8: one byte), and of dt and y
+// (bf16 for SSD_FP8 inputs) in the prefill
+int in_size(int dtype) { return dtype == SSD_FP8 ? 1 : elem_size(dtype); }
+int aux_size(int dtype) { return dtype == SSD_FP8 ? 2 : elem_size(dtype); }
+
 // dtype of the prefill and decode entry points: an ssd_dtype, optionally with
 // SSD_OUT_F32 (float32 y whatever the inputs' dtype)
 int strip_out_flag(int &dtype) {
@@ -111,9 +116,10 @@ int strip_out_flag(int &dtype) {
     return yf;
 }
 
-// bf16 prefill runs as the fused matrix-core kernel; float32 inputs take the
-// vector-ALU path, whose stages (Δ, cs, hand-off states) live in the workspace.
-bool prefill_fused(int dtype) { return dtype == SSD_BF16; }
+// bf16 and float8 prefill runs as the fused matrix-core kernel; float32 inputs
+// take the vector-ALU path, whose stages (Δ, cs, hand-off states) live in the
+// workspace.
+bool prefill_fused(int dtype) { return dtype == SSD_BF16 || dtype == SSD_FP8; }
 
 struct ScanLayout {
     int nchunks = 0;
@@ -123,8 +129,8 @@ struct ScanLayout {
 
 int check_scan_sizes(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
                      int chunk, int dtype) {
-    if (dtype != SSD_F32 && dtype != SSD_BF16)
-        return fail(SSD_ERR_UNSUPPORTED, "dtype %d is not SSD_F32 or SSD_BF16", dtype);
+    if (dtype != SSD_F32 && dtype != SSD_BF16 && dtype != SSD_FP8)
+        return fail(SSD_ERR_UNSUPPORTED, "dtype %d is not SSD_F32, SSD_BF16 or SSD_FP8", dtype);
     if (batch < 0 || seqlen < 0)
         return fail(SSD_ERR_SHAPE, "batch (%d) and seqlen (%d) must be >= 0", batch, seqlen);
     if (nheads < 1 || headdim < 1 || dstate < 1 || ngroups < 1 || chunk < 1)
@@ -227,7 +233,7 @@ int chunk_scan_fwd(int batch, int seqlen, int nheads, int headdim, int dstate, i
                     "this call needs %zu bytes of scratch; the no-allocation entry point has %zu",
                     lay.total, (size_t)ssd::kScratchBytes);
     hipStream_t stream = static_cast<hipStream_t>(stream_);
-    const int es = elem_size(dtype);
+    const int es = in_size(dtype), as = aux_size(dtype);  // x, B, C | dt, y
     uint64_t n_x, n_dt, n_bc, n_state;
     prod(n_x, {batch, seqlen, nheads, headdim});
     prod(n_dt, {batch, seqlen, nheads});
@@ -261,9 +267,9 @@ int chunk_scan_fwd(int batch, int seqlen, int nheads, int headdim, int dstate, i
                     workspace_bytes, workspace ? "" : " (NULL)");
     if (!aligned(workspace, 256)) return fail(SSD_ERR_ALIGN, "workspace must be 256-byte aligned");
     st = check_alias(
-        {span("y", y, n_x * (y_f32 ? 4 : es)), span("final_state", final_state, n_state * 4),
+        {span("y", y, n_x * (y_f32 ? 4 : as)), span("final_state", final_state, n_state * 4),
          span("workspace", workspace, lay.total)},
-        {span("x", x, n_x * es), span("dt", dt, n_dt * es), span("A", A, (uint64_t)nheads * 4),
+        {span("x", x, n_x * es), span("dt", dt, n_dt * as), span("A", A, (uint64_t)nheads * 4),
          span("B", B, n_bc * es), span("C", C, n_bc * es), span("D", D, D ? (uint64_t)nheads * 4 : 0),
          span("initial_state", initial_state, initial_state ? n_state * 4 : 0)});
     if (st) return st;
@@ -280,7 +286,7 @@ int chunk_scan_fwd(int batch, int seqlen, int nheads, int headdim, int dstate, i
             marks.before();
             e = ssd::launch_ssd_fused(phase, lay.plan, x, dt, A, B, C, D, initial_state, dt_softplus,
                                       batch, seqlen, nheads, headdim, dstate, ngroups, y,
-                                      final_state, ws, stream, y_f32);
+                                      final_state, ws, stream, y_f32, dtype == SSD_FP8);
             marks.after();
             if (e != hipSuccess) return hip_fail(e, what[phase]);
         }

@@ -1,4 +1,5 @@
-// Fused chunked SSD prefill for bf16 inputs on the gfx950 matrix cores.
+// Fused chunked SSD prefill for bf16 (or float8 e4m3fn) inputs on the gfx950
+// matrix cores.
 //
 // One kernel carries the whole block decomposition of page "5.3 텐서
 // 병렬화(Tensor Parallelism) 지원과 대규모 클러스터 학습", §3.2, for one
@@ -47,18 +48,36 @@ namespace ssd {
 namespace {
 
 // The state-only pass (segment end states, states at the cut of a pair).
-template <int N>
+// F8: x, B and C stored as float8 e4m3fn (decoded to bf16 at the staging).
+template <int N, bool F8>
 // two workgroups of 8 waves per CU: 4 waves per SIMD (at most 128 VGPRs)
 __global__ __launch_bounds__(kThreads, 4) void ssd_state_kernel(FusedArgs a) {
     __shared__ __attribute__((aligned(16))) StateSmem<N> sm;
-    state_walk<N, false>(a, blockIdx.x, gridDim.x, sm);
+    state_walk<N, false, F8>(a, blockIdx.x, gridDim.x, sm);
 }
 
 // The full pass: states and outputs.  Two workgroups of 8 waves per CU: 4
-// waves per SIMD (at most 128 VGPRs), at most 80 KB of LDS each.
-template <int N, bool YF32>
+// waves per SIMD (at most 128 VGPRs), at most 80 KB of LDS each.  YF32:
+// float32 y; F8: float8 e4m3fn x, B and C.
+template <int N, bool YF32, bool F8>
 __global__ __launch_bounds__(kThreads, 4) void ssd_prefill_kernel(FusedArgs a) {
-    fused_pair_walk<N, YF32>(a, blockIdx.x, gridDim.x);
+    fused_pair_walk<N, YF32, F8>(a, blockIdx.x, gridDim.x);
+}
+
+template <bool YF32, bool F8>
+void launch_prefill(int dstate, unsigned items, hipStream_t stream, const FusedArgs &a) {
+    if (dstate == 128)
+        ssd_prefill_kernel<128, YF32, F8><<<items, kThreads, 0, stream>>>(a);
+    else
+        ssd_prefill_kernel<64, YF32, F8><<<items, kThreads, 0, stream>>>(a);
+}
+
+template <bool F8>
+void launch_state(int dstate, unsigned items, hipStream_t stream, const FusedArgs &a) {
+    if (dstate == 128)
+        ssd_state_kernel<128, F8><<<items, kThreads, 0, stream>>>(a);
+    else
+        ssd_state_kernel<64, F8><<<items, kThreads, 0, stream>>>(a);
 }
 
 // State entering each segment s >= 1: H_s = exp(decay_{s-1})·H_{s-1} + E_{s-1},
@@ -138,15 +157,15 @@ hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const
                             const float *A, const void *B, const void *C, const float *D,
                             const float *h0, int dt_softplus, int batch, int seqlen, int nheads,
                             int headdim, int dstate, int ngroups, void *y, float *final_state,
-                            void *workspace, hipStream_t stream, int y_f32) {
+                            void *workspace, hipStream_t stream, int y_f32, int in_f8) {
     if (headdim != P || (dstate != 64 && dstate != 128)) return hipErrorInvalidValue;
     if ((long long)batch * nheads == 0 || seqlen == 0) return hipSuccess;
     FusedArgs a{};
     a.yf = y_f32 ? static_cast<float *>(y) : nullptr;
-    a.x = static_cast<const uint16_t *>(x);
+    a.x = x;
     a.dt = static_cast<const uint16_t *>(dt);
-    a.B = static_cast<const uint16_t *>(B);
-    a.C = static_cast<const uint16_t *>(C);
+    a.B = B;
+    a.C = C;
     a.A = A;
     a.D = D;
     a.h0 = h0;
@@ -181,24 +200,24 @@ hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const
         return hipErrorInvalidValue;
     }
     if (phase == 0) {
-        if (dstate == 128)
-            ssd_state_kernel<128><<<items, kThreads, 0, stream>>>(a);
+        if (in_f8)
+            launch_state<true>(dstate, items, stream, a);
         else
-            ssd_state_kernel<64><<<items, kThreads, 0, stream>>>(a);
+            launch_state<false>(dstate, items, stream, a);
     } else if (phase == 1) {
         const long long total = (long long)batch * nheads * dstate * P;
         segment_combine_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(
             a.h0, a.seg_state, a.seg_decay, const_cast<float *>(a.hin), a.nseg, dstate * P, total);
-    } else if (y_f32) {
-        if (dstate == 128)
-            ssd_prefill_kernel<128, true><<<items, kThreads, 0, stream>>>(a);
+    } else if (in_f8) {
+        if (y_f32)
+            launch_prefill<true, true>(dstate, items, stream, a);
         else
-            ssd_prefill_kernel<64, true><<<items, kThreads, 0, stream>>>(a);
+            launch_prefill<false, true>(dstate, items, stream, a);
     } else {
-        if (dstate == 128)
-            ssd_prefill_kernel<128, false><<<items, kThreads, 0, stream>>>(a);
+        if (y_f32)
+            launch_prefill<true, false>(dstate, items, stream, a);
         else
-            ssd_prefill_kernel<64, false><<<items, kThreads, 0, stream>>>(a);
+            launch_prefill<false, false>(dstate, items, stream, a);
     }
     return hipGetLastError();
 }
@@ -211,10 +230,10 @@ hipError_t launch_ssd_fused_varlen(const int *cu_seqlens, int nseq, int total_to
     if (headdim != P || (dstate != 64 && dstate != 128)) return hipErrorInvalidValue;
     if ((long long)nseq * nheads == 0) return hipSuccess;
     FusedArgs a{};
-    a.x = static_cast<const uint16_t *>(x);
+    a.x = x;
     a.dt = static_cast<const uint16_t *>(dt);
-    a.B = static_cast<const uint16_t *>(B);
-    a.C = static_cast<const uint16_t *>(C);
+    a.B = B;
+    a.C = C;
     a.A = A;
     a.D = D;
     a.h0 = h0;
@@ -235,10 +254,7 @@ hipError_t launch_ssd_fused_varlen(const int *cu_seqlens, int nseq, int total_to
     a.tail_state = nullptr;
     a.tail_decay = nullptr;
     const unsigned items = (unsigned)((long long)nseq * nheads);
-    if (dstate == 128)
-        ssd_prefill_kernel<128, false><<<items, kThreads, 0, stream>>>(a);
-    else
-        ssd_prefill_kernel<64, false><<<items, kThreads, 0, stream>>>(a);
+    launch_prefill<false, false>(dstate, items, stream, a);
     return hipGetLastError();
 }
 

@@ -54,8 +54,9 @@ __device__ __forceinline__ int pair_n(int i, int q, int r) { return 32 * (i >> 1
 // 16-byte chunk of row t of a masked block: q XOR this
 __device__ __forceinline__ int mt_swz(int t) { return (t >> 1) & 3; }
 
-template <int N, bool YF32>
+template <int N, bool YF32, bool F8>
 __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk, unsigned nblk) {
+    typedef typename InStore<F8>::elem E;
     constexpr int NT = N / 16;      // state tiles of a state wave
     constexpr int KS = N / 32;      // k-steps over n of C·H
     constexpr int KG = N / 16;      // k-steps over n of a (C Bᵀ)ᵀ block
@@ -92,7 +93,7 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
     const int gl = tid & 255;
     const int xrow = gl >> 3, xcol = (gl & 7) * 8;
     const int brow = gl / BPR, bcol = (gl % BPR) * 8;
-    uint4 rx[2], rb[GV], rc[GV];
+    typename InStore<F8>::vec8 rx[2], rb[GV], rc[GV];  // as stored; decoded at the staging
     uint32_t rdt = 0;  // raw bf16 Δ of a token (lane), converted where the scan uses it
     // Chunk bases are wave-uniform (scalar registers); the per-lane offsets within
     // a chunk fit in 32 bits (64 rows of at most 2^25 elements, checked by the host).
@@ -104,16 +105,16 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
     };
     auto prefetch = [&](int c) {
         const int t0 = c * kC, lim = last - t0;  // rows past the end are clamped to the last one
-        const uint16_t *xb = a.x + ((row0 + t0) * a.nheads + h) * P;
-        rx[0] = ld16(xb + ((uint32_t)min(xrow, lim) * xs32 + xcol));
-        rx[1] = ld16(xb + ((uint32_t)min(xrow + 32, lim) * xs32 + xcol));
-        const uint16_t *bb = a.B + (row0 + t0) * bstride + (size_t)g * N;
-        const uint16_t *cb = a.C + (row0 + t0) * bstride + (size_t)g * N;
+        const E *xb = static_cast<const E *>(a.x) + ((row0 + t0) * a.nheads + h) * P;
+        rx[0] = ld_in8<F8>(xb + ((uint32_t)min(xrow, lim) * xs32 + xcol));
+        rx[1] = ld_in8<F8>(xb + ((uint32_t)min(xrow + 32, lim) * xs32 + xcol));
+        const E *bb = static_cast<const E *>(a.B) + (row0 + t0) * bstride + (size_t)g * N;
+        const E *cb = static_cast<const E *>(a.C) + (row0 + t0) * bstride + (size_t)g * N;
 #pragma unroll
         for (int k = 0; k < GV; ++k) {
             const uint32_t o = (uint32_t)min(brow + BSTEP * k, lim) * bs32 + bcol;
-            rb[k] = ld16(bb + o);
-            rc[k] = ld16(cb + o);
+            rb[k] = ld_in8<F8>(bb + o);
+            rc[k] = ld_in8<F8>(cb + o);
         }
     };
     auto stage = [&](int c) {  // chunk c from registers into LDS; needs its per-token values
@@ -122,7 +123,8 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
         for (int k2 = 0; k2 < 2; ++k2) {
             const int row = xrow + 32 * k2, ox = swz<64>(row, xcol);
             const float w = T.w[row];
-            const uint32_t in[4] = {rx[k2].x, rx[k2].y, rx[k2].z, rx[k2].w};
+            const uint4 xv = in_bf16x8(rx[k2]);
+            const uint32_t in[4] = {xv.x, xv.y, xv.z, xv.w};
             uint32_t hi[4], lo[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -130,14 +132,14 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
                 hi[e] = pack_bf16x2(f0, f1);
                 lo[e] = pack_bf16x2(f0 - bf16lo(hi[e]), f1 - bf16hi(hi[e]));
             }
-            *reinterpret_cast<uint4 *>(&sm.xs[c & 1][ox]) = rx[k2];
+            *reinterpret_cast<uint4 *>(&sm.xs[c & 1][ox]) = xv;
             *reinterpret_cast<uint4 *>(&sm.xw[0][ox]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
             *reinterpret_cast<uint4 *>(&sm.xw[1][ox]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
         }
 #pragma unroll
         for (int k = 0; k < GV; ++k) {
-            *reinterpret_cast<uint4 *>(&sm.bs[swz<N>(brow + BSTEP * k, bcol)]) = rb[k];
-            *reinterpret_cast<uint4 *>(&sm.cr[swz<N>(brow + BSTEP * k, bcol)]) = rc[k];
+            *reinterpret_cast<uint4 *>(&sm.bs[swz<N>(brow + BSTEP * k, bcol)]) = in_bf16x8(rb[k]);
+            *reinterpret_cast<uint4 *>(&sm.cr[swz<N>(brow + BSTEP * k, bcol)]) = in_bf16x8(rc[k]);
         }
     };
     // Δ, the float64 inclusive cumsum of Δ·A over the chunk (lane = token) and

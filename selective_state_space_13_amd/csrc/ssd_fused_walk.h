@@ -17,6 +17,30 @@ constexpr int kThreads = 512;    // 8 waves
 constexpr float kMaxBlockDecay = 60.0f;  // above this, a diagonal block uses the exact mask
 constexpr int kMaxRankedSeq = 256;       // packed batches up to this many sequences run longest first
 
+// Storage of x, B and C: bf16, or float8 e4m3fn (F8; the OCP format: sign, 4
+// exponent bits with bias 7, 3 mantissa bits, no infinities).  Every e4m3fn
+// value is a bf16 value, so the walks decode the bytes to bf16 when they stage
+// them (the hardware conversion is exact) and compute exactly as for bf16
+// inputs; only the loads differ, 8 elements being 8 bytes instead of 16.
+template <bool F8> struct InStore { typedef uint16_t elem; typedef uint4 vec8; };
+template <> struct InStore<true> { typedef uint8_t elem; typedef uint2 vec8; };
+
+template <bool F8>
+__device__ __forceinline__ typename InStore<F8>::vec8 ld_in8(const typename InStore<F8>::elem *p) {
+    return *reinterpret_cast<const typename InStore<F8>::vec8 *>(p);
+}
+
+// 8 loaded elements as 8 bf16 (element 0 in the low half of .x)
+__device__ __forceinline__ uint4 in_bf16x8(uint4 v) { return v; }
+template <bool kHi>  // bytes 2-3 of w (else 0-1) as two bf16
+__device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi));
+}
+__device__ __forceinline__ uint4 in_bf16x8(uint2 v) {
+    return make_uint4(fp8x2_bf16<false>(v.x), fp8x2_bf16<true>(v.x), fp8x2_bf16<false>(v.y),
+                      fp8x2_bf16<true>(v.y));
+}
+
 // Per-token values of one chunk (index = token), written by one wave.
 struct TokSmem {
     double cs[kC];  // within-chunk inclusive cumsum of Δ·A_h (cs[63] closes the chunk)
@@ -27,7 +51,8 @@ struct TokSmem {
 };
 
 struct FusedArgs {
-    const uint16_t *x, *dt, *B, *C;
+    const void *x, *B, *C;  // bf16, or float8 e4m3fn (F8 walks)
+    const uint16_t *dt;
     const float *A, *D;
     const float *h0;      // [b][H][N][P] state entering the sequence, or null (zeros)
     const float *hin;     // [b][H][S][N][P] state entering each segment s >= 1 (full pass, S > 1)
@@ -174,8 +199,9 @@ struct StateSmem {
 // It writes the end state of a segment (and its total log-decay) or of the
 // first half of a cut pair, or, for the backward, the state entering every
 // chunk (kStoreStates; a.chunk_states must then be set).
-template <int N, bool kStoreStates>
+template <int N, bool kStoreStates, bool F8 = false>
 __device__ __forceinline__ void state_walk(const FusedArgs &a, unsigned blk, unsigned nblk, StateSmem<N> &sm) {
+    typedef typename InStore<F8>::elem E;
     constexpr int BV = N / 64;        // 16-byte vectors of B per lane
     constexpr int BPR = N / 8;        // 16-byte vectors per B row
     constexpr int kScanWave = N == 128 ? 0 : 4;
@@ -234,16 +260,18 @@ __device__ __forceinline__ void state_walk(const FusedArgs &a, unsigned blk, uns
     // x, B and Δ of one chunk, loaded two chunks ahead of their use into one of
     // two register sets that the loop alternates (a load one chunk ahead
     // arrived after the short update phase, and every chunk waited for it)
-    struct Loads { uint4 x, b[BV]; uint16_t dt; };  // dt: raw bf16 bits, widened at the scan
+    // dt: raw bf16 bits, widened at the scan; x and B as stored, decoded at the staging
+    struct Loads { typename InStore<F8>::vec8 x, b[BV]; uint16_t dt; };
     auto prefetch = [&](Loads &L, int c) {
         const int t0 = c * kC, lim = last - t0;  // rows past the end are clamped to the last one
         // dt first: the scan wave uses it before the rest has arrived, and loads
         // complete in issue order
         L.dt = a.dt[(row0 + t0 + min(lane, lim)) * a.nheads + h];
-        L.x = ld16(a.x + ((row0 + t0) * a.nheads + h) * P + xcol + (size_t)min(xrow, lim) * xstride);
-        const uint16_t *bc = a.B + (row0 + t0) * bstride + (size_t)g * N + bcol;
+        L.x = ld_in8<F8>(static_cast<const E *>(a.x) + ((row0 + t0) * a.nheads + h) * P + xcol +
+                         (size_t)min(xrow, lim) * xstride);
+        const E *bc = static_cast<const E *>(a.B) + (row0 + t0) * bstride + (size_t)g * N + bcol;
 #pragma unroll
-        for (int k = 0; k < BV; ++k) L.b[k] = ld16(bc + (size_t)min(brow + (kThreads / BPR) * k, lim) * bstride);
+        for (int k = 0; k < BV; ++k) L.b[k] = ld_in8<F8>(bc + (size_t)min(brow + (kThreads / BPR) * k, lim) * bstride);
     };
     // Δ and the float64 inclusive cumsum of Δ·A over the chunk (lane = token),
     // the token weights and the chunk's decay; returns Σ Δ·A over the chunk
@@ -279,7 +307,8 @@ __device__ __forceinline__ void state_walk(const FusedArgs &a, unsigned blk, uns
         // ================= staging of chunk c
         {
             const float w = T.w[xrow];
-            const uint32_t in[4] = {cur.x.x, cur.x.y, cur.x.z, cur.x.w};
+            const uint4 xv = in_bf16x8(cur.x);
+            const uint32_t in[4] = {xv.x, xv.y, xv.z, xv.w};
             uint32_t hi[4], lo[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -291,7 +320,7 @@ __device__ __forceinline__ void state_walk(const FusedArgs &a, unsigned blk, uns
             *reinterpret_cast<uint4 *>(&xl[ox]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
         }
 #pragma unroll
-        for (int k = 0; k < BV; ++k) *reinterpret_cast<uint4 *>(&bs[ob + k * (kThreads / BPR) * N]) = cur.b[k];
+        for (int k = 0; k < BV; ++k) *reinterpret_cast<uint4 *>(&bs[ob + k * (kThreads / BPR) * N]) = in_bf16x8(cur.b[k]);
         // the state entering the chunk (stored for the backward), then its decay over the chunk
         if (owns_state) {
             const float dec = T.dec;

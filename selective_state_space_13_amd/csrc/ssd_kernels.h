@@ -99,7 +99,7 @@ hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const
                             const float *A, const void *B, const void *C, const float *D,
                             const float *h0, int dt_softplus, int batch, int seqlen, int nheads,
                             int headdim, int dstate, int ngroups, void *y, float *final_state,
-                            void *workspace, hipStream_t stream, int y_f32 = 0);
+                            void *workspace, hipStream_t stream, int y_f32 = 0, int in_f8 = 0);
 // Chunked backward (bf16).  Workspace: the forward plan's, then the chunk
 // states, the chunk adjoints and the per-(b, h, chunk) dA, dD partials.
 struct BwdPlan {

@@ -22,12 +22,15 @@ TAU_BF16 = 2e-2
 
 
 def to_dev(t, device="cuda"):
-    """gen.Tensor -> torch tensor on `device` (bf16 bits reinterpreted, no rounding)."""
+    """gen.Tensor -> torch tensor on `device` (bf16 and float8 bits reinterpreted,
+    no rounding)."""
     import torch
     if t is None:
         return None
     if t.dtype == "f32":
         return torch.from_numpy(np.ascontiguousarray(t.data)).to(device)
+    if t.dtype == "fp8":
+        return torch.from_numpy(np.ascontiguousarray(t.data)).to(device).view(torch.float8_e4m3fn)
     return torch.from_numpy(np.ascontiguousarray(t.data).view(np.int16)).view(torch.bfloat16).to(device)
 
 

@@ -20,6 +20,20 @@ OK, NULL, SHAPE, UNSUP, WS, ALIGN, ALIAS, HIP = 0, -1, -2, -3, -4, -5, -6, -7
 F32, BF16 = 0, 1
 
 
+def _devices():
+    try:
+        import torch
+        return torch.cuda.device_count()  # counts without initialising a device
+    except Exception:
+        return 0
+
+
+# Calls that pass validation go on to launch kernels on the fake addresses
+# below: harmless without a device (the launch fails, SSD_ERR_HIP), a memory
+# fault with one.  This module is for machines without a GPU.
+pytestmark = pytest.mark.skipif(_devices() > 0, reason="fake device pointers; host-only checks")
+
+
 @pytest.fixture(scope="module")
 def L():
     return ssd.lib()
@@ -438,7 +452,7 @@ def test_out_f32_flag_prefill_and_decode(L):
     assert scan_call(L, dtype=BF16 | OUT_F32, ptrs={"y": y}) == ALIAS
     assert scan_call(L, dtype=F32 | OUT_F32, ptrs={"y": y}) == ALIAS
     assert scan_call(L, dtype=BF16 | OUT_F32, b=0) == OK
-    assert scan_call(L, dtype=2 | OUT_F32) == UNSUP
+    assert scan_call(L, dtype=3 | OUT_F32) == UNSUP
     # decode: y right before the state
     n_y = 4 * 8 * 64
     y = fake(7, -2 * n_y)
@@ -455,3 +469,45 @@ def test_out_f32_flag_rejected_elsewhere(L):
     assert L.selective_scan_workspace_size(8, 4096, 5120, 16, BF16 | OUT_F32) == 0
     assert conv_call(L, dtype=BF16 | OUT_F32) == UNSUP
     assert norm_call(L, dtype=BF16 | OUT_F32) == UNSUP
+
+
+FP8 = 2
+
+
+def test_fp8_dtype_prefill_only(L):
+    assert ssd.SSD_FP8 == FP8
+    assert re.search(r"SSD_FP8\s*=\s*2\b", open(HEADER).read())
+    # the bf16 kernel's plan and workspace
+    assert (L.ssd_chunk_scan_workspace_size(8, 2048, 80, 64, 128, 1, 256, FP8)
+            == L.ssd_chunk_scan_workspace_size(8, 2048, 80, 64, 128, 1, 256, BF16))
+    assert _plan(L, 1, 65536, 80, 64, 128, 8, 256, FP8) == _plan(L, 1, 65536, 80, 64, 128, 8, 256, BF16)
+    assert scan_call(L, dtype=FP8) != UNSUP
+    assert scan_call(L, dtype=FP8 | OUT_F32, b=0) == OK
+    # other entry points refuse float8
+    assert decode_call(L, dtype=FP8) == UNSUP
+    assert decode_call(L, dtype=FP8, bf16_state=True) == UNSUP
+    assert bwd_call(L, dtype=FP8) == UNSUP
+    assert L.ssd_chunk_scan_bwd_workspace_size(2, 300, 8, 64, 128, 2, FP8) == 0
+    assert varlen_call(L, dtype=FP8) == UNSUP
+    assert m1_call(L, dtype=FP8) == UNSUP
+    assert conv_call(L, dtype=FP8) == UNSUP
+    assert norm_call(L, dtype=FP8) == UNSUP
+
+
+def test_fp8_spans_are_one_byte_for_x_b_c(L):
+    # x, B, C one byte a value; dt and y two (bf16), or four for float32 y
+    b, Lq, H, G, N = 2, 300, 8, 2, 128
+    n_x, n_bc = b * Lq * H * 64, b * Lq * G * N
+    # y right after an x of n_x bytes: disjoint for float8 x, overlapping for bf16 x
+    assert scan_call(L, dtype=FP8, ptrs={"y": fake(1, n_x)}) != ALIAS
+    assert scan_call(L, dtype=BF16, ptrs={"y": fake(1, n_x)}) == ALIAS
+    # y right before the final state: 2 bytes a value disjoint, 4 overlapping
+    assert scan_call(L, dtype=FP8, ptrs={"y": fake(8, -2 * n_x)}) != ALIAS
+    assert scan_call(L, dtype=FP8 | OUT_F32, ptrs={"y": fake(8, -2 * n_x)}) == ALIAS
+    # final state right after B: disjoint at one byte a value
+    assert scan_call(L, dtype=FP8, ptrs={"fs": fake(4, n_bc)}) != ALIAS
+    assert scan_call(L, dtype=BF16, ptrs={"fs": fake(4, n_bc)}) == ALIAS
+    # dt stays two bytes a value
+    n_dt = b * Lq * H
+    assert scan_call(L, dtype=FP8, ptrs={"fs": fake(2, n_dt)}) == ALIAS
+    assert scan_call(L, dtype=FP8, ptrs={"fs": fake(2, 2 * n_dt)}) != ALIAS

@@ -37,8 +37,14 @@ def run_scan(d, chunk, dtype, with_D=True, with_h0=False, final=True, out_dtype=
     return out
 
 
+def ovals(t):
+    """The values the oracle takes for a generated tensor: float8 bytes through
+    the oracle's own e4m3fn decoding, the rest widened exactly."""
+    return oracle.fp8_e4m3_values(t.data) if t.dtype == "fp8" else t.f64()
+
+
 def oracle_scan(d, with_D=True, with_h0=False):
-    return oracle.ssd_scan(d["x"].f64(), d["dt"].f64(), d["A"].f64(), d["B"].f64(), d["C"].f64(),
+    return oracle.ssd_scan(ovals(d["x"]), d["dt"].f64(), d["A"].f64(), ovals(d["B"]), ovals(d["C"]),
                            d["D"].f64() if with_D and d["D"] is not None else None,
                            d["h0"].f64() if with_h0 else None, return_final_state=True)
 
@@ -172,6 +178,79 @@ def test_prefill_float32_y(case):
     yo, fo = oracle_scan(d, wD, wh)
     assert_parity(to_f64(y32), yo, TAU_BF16, False, f"float32 y {case}")
     assert torch.equal(y, y32.to(torch.bfloat16)) and torch.equal(fs, fs32)
+
+
+# ---------------------------------------------------------- float8 e4m3fn inputs
+
+def as_bf16_inputs(d):
+    """The same values with x, B and C stored as bf16 (every e4m3fn value is one)."""
+    e = dict(d)
+    for k in ("x", "B", "C"):
+        e[k] = gen.Tensor(gen.f32_to_bf16_bits(d[k].f32()), "bf16")
+        assert np.array_equal(e[k].f64(), ovals(d[k]))
+    return e
+
+
+@pytest.mark.parametrize("case", [(2, 700, 6, 128, 2, True, True), (1, 16384, 8, 64, 1, False, True),
+                                  (3, 1100, 200, 128, 4, True, False), (1, 1, 4, 64, 1, True, True),
+                                  (4, 130, 16, 64, 4, False, False)],
+                         ids=["b2L700ragged", "b1L16384segmented", "b3L1100H200tailcut", "b1L1",
+                              "b4L130N64G4"])
+def test_prefill_fp8(case):
+    """float8 e4m3fn x, B, C (bf16 dt) through each kind of plan: the bf16 bar
+    against the oracle on the bytes' values, and bit for bit the result of the
+    same values given as bf16 (the kernel decodes the bytes exactly, then
+    computes as for bf16)."""
+    b, L, H, N, G, wD, wh = case
+    d = gen.ssd_inputs(b, L, H, 64, N, G, "fp8", seed=L + H, config_id=115, with_h0=wh)
+    y, fs = run_scan(d, 256, "fp8", wD, wh)
+    assert y.dtype == torch.bfloat16
+    yo, fo = oracle_scan(d, wD, wh)
+    assert_parity(to_f64(y), yo, TAU_BF16, True, f"fp8 y {case}")
+    assert_parity(to_f64(fs), fo, TAU_BF16, False, f"fp8 final {case}")
+    y16, fs16 = run_scan(as_bf16_inputs(d), 256, "bf16", wD, wh)
+    assert torch.equal(y, y16) and torch.equal(fs, fs16)
+
+
+def test_prefill_fp8_every_code():
+    """x holding every finite e4m3fn byte (±448, the subnormals, both zeros),
+    B and C every finite byte of magnitude at most 1: decoded exactly (equal to
+    the bf16 call on the same values) and to the bar against the oracle."""
+    b, L, H, N, G = 2, 300, 4, 64, 2
+    d = gen.ssd_inputs(b, L, H, 64, N, G, "fp8", seed=3, config_id=116, with_h0=True)
+    codes = np.arange(256, dtype=np.uint8)
+    vals = oracle.fp8_e4m3_values(codes)
+    fin = codes[np.isfinite(vals)]
+    small = codes[np.isfinite(vals) & (np.abs(vals) <= 1.0)]
+    rng = np.random.default_rng(116)
+    d["x"] = gen.Tensor(rng.permutation(np.resize(fin, d["x"].data.size)).reshape(d["x"].shape), "fp8")
+    for k in ("B", "C"):
+        d[k] = gen.Tensor(rng.choice(small, d[k].shape).astype(np.uint8), "fp8")
+    assert set(np.unique(d["x"].data)) == set(fin.tolist())
+    y, fs = run_scan(d, 256, "fp8", True, True)
+    yo, fo = oracle_scan(d, True, True)
+    assert_parity(to_f64(y), yo, TAU_BF16, True, "fp8 every code y")
+    assert_parity(to_f64(fs), fo, TAU_BF16, False, "fp8 every code final")
+    y16, fs16 = run_scan(as_bf16_inputs(d), 256, "bf16", True, True)
+    assert torch.equal(y, y16) and torch.equal(fs, fs16)
+
+
+def test_config2_prefill_fp8_full():
+    """The 2.7B-layer prefill with float8 e4m3fn x, B, C: bf16 y to the bar (with
+    its rounding step), float32 y to the bare bar, and the final state."""
+    c = configs.MAMBA2_LAYER_PREFILL
+    say("C2 fp8: generating inputs")
+    d = gen.ssd_inputs(c["batch"], c["seqlen"], c["nheads"], c["headdim"], c["dstate"],
+                       c["ngroups"], "fp8", config_id=c["id"])
+    say("C2 fp8: GPU run")
+    y, fs = run_scan(d, c["chunk"], "fp8", True)
+    y32, _ = run_scan(d, c["chunk"], "fp8", True, out_dtype=torch.float32)
+    assert torch.equal(y, y32.to(torch.bfloat16))
+    say("C2 fp8: oracle")
+    yo, fo = oracle_scan(d, True)
+    assert_parity(to_f64(y), yo, TAU_BF16, True, "C2 fp8 y")
+    assert_parity(to_f64(y32), yo, TAU_BF16, False, "C2 fp8 float32 y")
+    assert_parity(to_f64(fs), fo, TAU_BF16, False, "C2 fp8 final")
 
 
 VARLEN_GPU_CASES = [

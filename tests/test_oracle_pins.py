@@ -637,6 +637,52 @@ def test_pin16_bf16_state_decode_exact_case_and_rounding_bound():
     assert not np.array_equal(s16, s64)
 
 
+# ---- float8 e4m3fn inputs (low-precision matrix-product inputs of page 1 §5.1)
+
+def test_pin17_fp8_e4m3_values_match_torch_on_every_code():
+    """The value of every one of the 256 e4m3fn bytes against torch's
+    float8_e4m3fn decoding, NaN codes included; and the format's landmarks
+    written out: 448 the largest, 2^-6 the smallest normal, 2^-9 the smallest
+    subnormal, no infinity."""
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.fp8_e4m3_values(codes)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(got, want, equal_nan=True)
+    assert np.flatnonzero(np.isnan(got)).tolist() == [0x7F, 0xFF]
+    fin = got[np.isfinite(got)]
+    assert fin.max() == 448.0 and fin.min() == -448.0
+    assert got[0x01] == 2.0**-9 and got[0x08] == 2.0**-6 and got[0x07] == 7 * 2.0**-9
+    assert got[0x38] == 1.0 and got[0xB8] == -1.0 and got[0x3C] == 1.5
+    assert np.copysign(1.0, got[0x80]) == -1.0 and got[0x80] == 0.0
+
+
+def test_pin17_round_fp8_e4m3_matches_torch_round_to_nearest_even():
+    """round_fp8_e4m3 against torch's float32 -> float8_e4m3fn conversion on
+    float32 values over the format's range and beyond: exact ties (normal and
+    subnormal), the overflow boundary (464 rounds to 448, above it NaN),
+    infinities, signed zeros; idempotent on its results; within 2^-4 relative
+    (4 significant bits) on the normal range."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(17)
+    v = (rng.standard_normal(60000) * np.exp2(rng.integers(-14, 10, 60000))).astype(np.float32)
+    grid = oracle.fp8_e4m3_values(np.arange(256, dtype=np.uint8))
+    grid = np.sort(grid[np.isfinite(grid) & (grid >= 0)])
+    mids = ((grid[1:] + grid[:-1]) / 2).astype(np.float32)          # every tie
+    edges = np.array([448.0, 456.0, 463.99997, 464.0, 464.00003, 480.0, 1e6, np.inf, -np.inf,
+                      0.0, -0.0, 2.0**-10, 3 * 2.0**-11, 2.0**-6 - 2.0**-11], np.float32)
+    v = np.concatenate([v, mids, -mids, edges])
+    want = torch.from_numpy(v).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.round_fp8_e4m3(v.astype(np.float64))
+    assert np.array_equal(got, want, equal_nan=True)
+    ok = np.isfinite(got)
+    assert np.array_equal(oracle.round_fp8_e4m3(got[ok]), got[ok])  # idempotent
+    nrm = ok & (np.abs(v) >= 2.0**-6)
+    assert np.max(np.abs(got[nrm] - v[nrm]) / np.abs(v[nrm])) <= 2.0**-4
+    sub = ok & (np.abs(v) < 2.0**-6)
+    assert np.max(np.abs(got[sub] - v[sub])) <= 2.0**-10
+
+
 # ---------------------------------------------------------------- golden fixtures
 # tests/golden/*.json: small fixed inputs and the oracle's float64 outputs,
 # written by tests/golden/make_golden.py (which calls only the oracle).  The

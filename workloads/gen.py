@@ -6,8 +6,10 @@ or resized.  Low-precision inputs are rounded to bf16 once (round to nearest
 even) and the stored bits are the ground truth: the oracle widens exactly those
 values to float64 and the GPU reads exactly those bits.
 
-A generated tensor is a ``Tensor``: ``data`` holds float32 values for "f32" and
-uint16 bf16 bit patterns for "bf16".
+A generated tensor is a ``Tensor``: ``data`` holds float32 values for "f32",
+uint16 bf16 bit patterns for "bf16" and uint8 float8 e4m3fn bytes for "fp8"
+(rounded by torch's float32 -> float8_e4m3fn conversion, nearest even).  For
+"fp8" calls only x, B and C are float8; dt stays bf16.
 """
 from __future__ import annotations
 
@@ -23,7 +25,7 @@ _X, _DT, _A, _B, _C, _D, _H0, _Z, _DY, _DHF = range(10)
 @dataclass
 class Tensor:
     data: np.ndarray
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "fp8"
 
     @property
     def shape(self):
@@ -32,6 +34,9 @@ class Tensor:
     def f32(self) -> np.ndarray:
         if self.dtype == "f32":
             return self.data
+        if self.dtype == "fp8":
+            import torch
+            return torch.from_numpy(np.ascontiguousarray(self.data)).view(torch.float8_e4m3fn).float().numpy()
         return bf16_bits_to_f32(self.data)
 
     def f64(self) -> np.ndarray:
@@ -54,7 +59,16 @@ def _store(values_f32: np.ndarray, dtype: str) -> Tensor:
         return Tensor(np.ascontiguousarray(values_f32, dtype=np.float32), "f32")
     if dtype == "bf16":
         return Tensor(f32_to_bf16_bits(values_f32), "bf16")
+    if dtype == "fp8":
+        import torch
+        v = torch.from_numpy(np.ascontiguousarray(values_f32, dtype=np.float32))
+        return Tensor(v.to(torch.float8_e4m3fn).view(torch.uint8).numpy(), "fp8")
     raise ValueError(dtype)
+
+
+def _aux(dtype: str) -> str:
+    """Storage of dt (and of y) for inputs of `dtype`: bf16 beside float8 x, B, C."""
+    return "bf16" if dtype == "fp8" else dtype
 
 
 def _rng(seed, config_id, tensor_id, step=None):
@@ -98,7 +112,7 @@ def ssd_inputs(batch, seqlen, nheads, headdim, dstate, ngroups, dtype,
     A, D = ssd_params(nheads, seed, config_id)
     out = dict(
         x=_store(_normal(_rng(seed, config_id, _X), (batch, seqlen, nheads, headdim)), dtype),
-        dt=_store(_dt_raw(_rng(seed, config_id, _DT), (batch, seqlen, nheads)), dtype),
+        dt=_store(_dt_raw(_rng(seed, config_id, _DT), (batch, seqlen, nheads)), _aux(dtype)),
         A=A,
         B=_store(_normal(_rng(seed, config_id, _B), (batch, seqlen, ngroups, dstate),
                          1.0 / math.sqrt(dstate)), dtype),
