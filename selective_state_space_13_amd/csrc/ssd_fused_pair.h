@@ -12,17 +12,20 @@
 //     head/tail, times C read as 16-byte rows), scaled per token by exp(cs_t):
 //     the output is transposed, so a lane holds 4 consecutive p of one token and
 //     stores them as one 8-byte word, with no exchange between waves;
-//   - decays its tiles and adds Bᵀ(w·x);
+//   - decays its tiles and adds Bᵀ(w·x), forming w·x for its own 16 columns in
+//     registers from the raw x tile (a transposed read gives each lane the 8
+//     tokens of its k-slots) and splitting it head/tail there;
 //   - adds the intra-chunk products of its columns, xᵀ·Mᵀ, where M is the masked
 //     (C Bᵀ) with D on its diagonal, so the D skip needs no separate step.
-// Waves 4-7 stage.  Waves 4-6 each form one causal 32 x 32 block of (C Bᵀ)ᵀ,
-// mask it with the decay (factorised per block, exact when a diagonal block's
-// own log-change exceeds kMaxBlockDecay), split it head/tail and store it in
-// the k order the state waves' B operand reads; wave 7 scans the next chunk's
-// Δ·A.  After the barrier they stage the next chunk (x, w·x, B, C) from
-// registers and issue the loads of the chunk after it.  Raw x is
-// double-buffered, since the state waves read the current chunk's x while the
-// next one is staged.
+// Waves 4-7 stage.  In the first phase waves 4-6 each form one causal 32 x 32
+// block of (C Bᵀ)ᵀ, mask it with the decay (factorised per block, exact when a
+// diagonal block's own log-change exceeds kMaxBlockDecay), split it head/tail
+// and store it in the k order the state waves' B operand reads, while wave 7
+// scans the next chunk's Δ·A; then all four stage the next chunk's x and B
+// (both double-buffered by chunk parity) and issue the loads of the chunk
+// after it.  In the second phase they stage the next chunk's C (its one buffer
+// is read only in the first phase) and issue that chunk's C loads, so every
+// load has a full chunk to arrive.
 #pragma once
 #include "ssd_fused_walk.h"
 
@@ -38,8 +41,7 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 template <int N>
 struct PairSmem {
     uint16_t xs[2][kC * P];   // raw x [t][p], swz<64>, by chunk parity
-    uint16_t xw[2][kC * P];   // w·x head and tail [t][p], swz<64>
-    uint16_t bs[kC * N];      // B [t][n], swz<N>
+    uint16_t bs[2][kC * N];   // B [t][n], swz<N>, by chunk parity
     uint16_t cr[kC * N];      // C [t][n], swz<N>
     // masked blocks (T, S) = (0,0), (1,0), (1,1) of M = mask ⊙ (C Bᵀ) (+ D on the
     // diagonal): [block][head, tail][row t][16-byte chunk q ^ mt_swz(t)];
@@ -103,44 +105,34 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
         const uint16_t *db = a.dt + (row0 + t0) * a.nheads + h;
         rdt = db[(uint32_t)min(lane, last - t0) * hs32];
     };
-    auto prefetch = [&](int c) {
-        const int t0 = c * kC, lim = last - t0;  // rows past the end are clamped to the last one
+    // rows past the end of the sequence are clamped to the last one
+    auto load_xb = [&](int c) {  // x and B of chunk c
+        const int t0 = c * kC, lim = last - t0;
         const E *xb = static_cast<const E *>(a.x) + ((row0 + t0) * a.nheads + h) * P;
         rx[0] = ld_in8<F8>(xb + ((uint32_t)min(xrow, lim) * xs32 + xcol));
         rx[1] = ld_in8<F8>(xb + ((uint32_t)min(xrow + 32, lim) * xs32 + xcol));
         const E *bb = static_cast<const E *>(a.B) + (row0 + t0) * bstride + (size_t)g * N;
+#pragma unroll
+        for (int k = 0; k < GV; ++k) rb[k] = ld_in8<F8>(bb + ((uint32_t)min(brow + BSTEP * k, lim) * bs32 + bcol));
+    };
+    auto load_c = [&](int c) {  // C of chunk c
+        const int t0 = c * kC, lim = last - t0;
         const E *cb = static_cast<const E *>(a.C) + (row0 + t0) * bstride + (size_t)g * N;
 #pragma unroll
-        for (int k = 0; k < GV; ++k) {
-            const uint32_t o = (uint32_t)min(brow + BSTEP * k, lim) * bs32 + bcol;
-            rb[k] = ld_in8<F8>(bb + o);
-            rc[k] = ld_in8<F8>(cb + o);
-        }
+        for (int k = 0; k < GV; ++k) rc[k] = ld_in8<F8>(cb + ((uint32_t)min(brow + BSTEP * k, lim) * bs32 + bcol));
     };
-    auto stage = [&](int c) {  // chunk c from registers into LDS; needs its per-token values
-        const TokSmem &T = sm.tok[c & 1];
+    auto stage_xb = [&](int c) {  // x and B of chunk c from registers into LDS
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            const int row = xrow + 32 * k2, ox = swz<64>(row, xcol);
-            const float w = T.w[row];
-            const uint4 xv = in_bf16x8(rx[k2]);
-            const uint32_t in[4] = {xv.x, xv.y, xv.z, xv.w};
-            uint32_t hi[4], lo[4];
+        for (int k2 = 0; k2 < 2; ++k2)
+            *reinterpret_cast<uint4 *>(&sm.xs[c & 1][swz<64>(xrow + 32 * k2, xcol)]) = in_bf16x8(rx[k2]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float f0 = bf16lo(in[e]) * w, f1 = bf16hi(in[e]) * w;
-                hi[e] = pack_bf16x2(f0, f1);
-                lo[e] = pack_bf16x2(f0 - bf16lo(hi[e]), f1 - bf16hi(hi[e]));
-            }
-            *reinterpret_cast<uint4 *>(&sm.xs[c & 1][ox]) = xv;
-            *reinterpret_cast<uint4 *>(&sm.xw[0][ox]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-            *reinterpret_cast<uint4 *>(&sm.xw[1][ox]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-        }
+        for (int k = 0; k < GV; ++k)
+            *reinterpret_cast<uint4 *>(&sm.bs[c & 1][swz<N>(brow + BSTEP * k, bcol)]) = in_bf16x8(rb[k]);
+    };
+    auto stage_c = [&](int c) {  // C of chunk c
 #pragma unroll
-        for (int k = 0; k < GV; ++k) {
-            *reinterpret_cast<uint4 *>(&sm.bs[swz<N>(brow + BSTEP * k, bcol)]) = in_bf16x8(rb[k]);
+        for (int k = 0; k < GV; ++k)
             *reinterpret_cast<uint4 *>(&sm.cr[swz<N>(brow + BSTEP * k, bcol)]) = in_bf16x8(rc[k]);
-        }
     };
     // Δ, the float64 inclusive cumsum of Δ·A over the chunk (lane = token) and
     // the values derived from it
@@ -246,17 +238,26 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
             for (int i = 0; i < NT; ++i)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) st[i][r] *= dec;
+            // the update's B operand w·x, formed here for this wave's columns: the
+            // transposed read of raw x gives the lane x[t][p] for t = 32kt + 8q + j,
+            // j = 0..7 (its k-slots), p = 16·role + c16; each is scaled by its
+            // token's weight and split head/tail
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
                 const int ra = 32 * kt + 8 * q + jr, rb4 = ra + 4;
-                const bf16x8 whi = cat8(tr4(sm.xw[0] + swz<64>(ra, 16 * role + jc)),
-                                        tr4(sm.xw[0] + swz<64>(rb4, 16 * role + jc)));
-                const bf16x8 wlo = cat8(tr4(sm.xw[1] + swz<64>(ra, 16 * role + jc)),
-                                        tr4(sm.xw[1] + swz<64>(rb4, 16 * role + jc)));
+                const uint4 xv = __builtin_bit_cast(uint4, cat8(tr4(sm.xs[buf] + swz<64>(ra, 16 * role + jc)),
+                                                                tr4(sm.xs[buf] + swz<64>(rb4, 16 * role + jc))));
+                const float4 w0 = *reinterpret_cast<const float4 *>(T.w + 32 * kt + 8 * q);
+                const float4 w1 = *reinterpret_cast<const float4 *>(T.w + 32 * kt + 8 * q + 4);
+                const float wv[8] = {bf16lo(xv.x) * w0.x, bf16hi(xv.x) * w0.y, bf16lo(xv.y) * w0.z,
+                                     bf16hi(xv.y) * w0.w, bf16lo(xv.z) * w1.x, bf16hi(xv.z) * w1.y,
+                                     bf16lo(xv.w) * w1.z, bf16hi(xv.w) * w1.w};
+                bf16x8 whi, wlo;
+                split8(wv, whi, wlo);
 #pragma unroll
                 for (int i = 0; i < NT; ++i) {
                     const int col = 32 * (i >> 1) + 2 * jc + 4 * (i & 1);
-                    const bf16x8 aop = cat8(tr4(sm.bs + swz<N>(ra, col)), tr4(sm.bs + swz<N>(rb4, col)));
+                    const bf16x8 aop = cat8(tr4(sm.bs[buf] + swz<N>(ra, col)), tr4(sm.bs[buf] + swz<N>(rb4, col)));
                     st[i] = mfma16(aop, whi, st[i]);
                     st[i] = mfma16(aop, wlo, st[i]);
                 }
@@ -315,14 +316,17 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
     } else {
         if (c0 < c1) {  // an empty sequence loads nothing and returns its initial state
             load_dt(c0);
-            prefetch(c0);
+            load_xb(c0);
+            load_c(c0);
             if (role == kScanRole) scan_chunk(c0, rdt, sm.tok[c0 & 1]);
         }
         __syncthreads();
         if (c0 < c1) {
-            stage(c0);
+            stage_xb(c0);
+            stage_c(c0);
             load_dt(min(c0 + 1, c1 - 1));
-            prefetch(min(c0 + 1, c1 - 1));
+            load_xb(min(c0 + 1, c1 - 1));
+            load_c(min(c0 + 1, c1 - 1));
         }
         __syncthreads();
         for (int c = c0; c < c1; ++c) {
@@ -335,7 +339,7 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
                 f32x16 gt = {};
 #pragma unroll
                 for (int kg = 0; kg < KG; ++kg)
-                    gt = mfma(as8(ld16(sm.bs + swz<N>(32 * Sb + l32, 16 * kg + 8 * lg))),
+                    gt = mfma(as8(ld16(sm.bs[buf] + swz<N>(32 * Sb + l32, 16 * kg + 8 * lg))),
                               as8(ld16(sm.cr + swz<N>(32 * Tb + l32, 16 * kg + 8 * lg))), gt);
                 const double cs_t = T.cs[32 * Tb + l32];
                 const double cs_r = T.cs[32 * Sb + 31];
@@ -380,15 +384,20 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
             } else if (c + 1 < c1) {
                 scan_chunk(c + 1, rdt, sm.tok[buf ^ 1]);  // its buffer was last read before the previous barrier
             }
+            // x and B of the next chunk into the other buffers (last read in the
+            // previous chunk, before its barriers), then the loads of the chunk
+            // after it into the registers just freed.  The staging and the loads
+            // are unconditional (after the last chunk they stage a clamped copy
+            // into buffers nobody reads): under a branch, the compiler's count
+            // of outstanding loads takes the path without them, and the stores
+            // of the next phase would wait for the loads issued here as well.
+            stage_xb(c + 1);
+            load_dt(min(c + 2, c1 - 1));
+            load_xb(min(c + 2, c1 - 1));
             __syncthreads();
-            // ============ B: stage the next chunk, issue the loads of the one after
-            if (c + 1 < c1) {
-                __builtin_amdgcn_s_setprio(2);
-                stage(c + 1);
-                load_dt(min(c + 2, c1 - 1));
-                prefetch(min(c + 2, c1 - 1));
-                __builtin_amdgcn_s_setprio(0);
-            }
+            // ============ B: C of the next chunk (its one buffer was read in phase A)
+            stage_c(c + 1);
+            load_c(min(c + 2, c1 - 1));
             __syncthreads();
         }
     }
