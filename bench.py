@@ -134,29 +134,37 @@ def flush_mall():
 
 
 def time_calls(fn, nkernels, steps, warmup, flush=True):
-    """Warm-up, then `steps` calls, each bracketed by events (and its kernels by
-    the library's launch events), with the MALL flushed before each when `flush`.
-    Returns (median ms per call, median ms per kernel, mean ms per call back to
-    back without the flush)."""
+    """Warm-up, then `steps` calls, each bracketed by events, with the MALL
+    flushed before each when `flush`; then `steps` more calls, flushed the same
+    way, with the library's launch events around each kernel for the per-kernel
+    times (kept apart so that the step time carries no event records between
+    kernels).  Returns (median ms per call, median ms per kernel, mean ms per
+    call back to back without the flush)."""
     import torch
     import selective_state_space_13_amd as ssd
     lib = ssd.lib()
     for _ in range(warmup):
         fn()
-    timer = LaunchTimer(nkernels, steps)
     calls = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
         if flush:
             flush_mall()
-        timer.arm(lib, i)
         calls[i][0].record()
         fn()
         calls[i][1].record()
-    LaunchTimer.disarm(lib)
     torch.cuda.synchronize()
     per_call = [a.elapsed_time(b) for a, b in calls]
+    timer = LaunchTimer(nkernels, steps)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        if flush:
+            flush_mall()
+        timer.arm(lib, i)
+        fn()
+    LaunchTimer.disarm(lib)
+    torch.cuda.synchronize()
     per_kernel = timer.per_kernel_ms(median)
     # the same calls back to back (MALL warm), wall clock
     torch.cuda.synchronize()
@@ -586,9 +594,10 @@ def main():
                           "alg_bytes": total_work["bytes"], "alg_flops": total_work["flops"]},
         "per_kernel_ms": {k: round(v, 5) for k, v in per.items()},
         "per_kernel_measured_hbm": counter_rates(per, workload, FUSED_SOURCES),
-        "timing": "median over the timed calls of HIP events around each call (and each kernel), "
-                  "with a 1 GiB buffer read before every call so the 256 MB MALL holds no input; "
-                  "ms_per_step_back_to_back: mean of the same calls back to back without the flush",
+        "timing": "median over the timed calls of HIP events around each call, with a 1 GiB buffer "
+                  "read before every call so the 256 MB MALL holds no input; per-kernel times from as "
+                  "many calls again with events around each kernel; ms_per_step_back_to_back: mean of "
+                  "the same calls back to back without the flush",
         "gpu_clocks": {"before": clocks_before, "after": clocks_after},
         "hbm_copy_reference": {"value": round(copy_tbs, 3), "unit": "TB/s",
                                "what": "torch device copy of a 1 GiB buffer, read + write bytes, 5 copies; "

@@ -366,11 +366,11 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
         R0.dt = __uint_as_float((uint32_t)a.dt[(row0 + min(lane, lim)) * a.nheads + h] << 16);
     };
     // per-token values of head hh (its Δ in R0.dt) into buffer tb (one wave)
-    auto scan_head = [&](int hh, int tb) {
+    auto scan_head = [&](float Ahh, int tb) {
         const bool ok = lane <= lim;
         const float raw = R0.dt;
         const float delta = ok ? (a.dt_softplus ? softplus_f32(raw) : raw) : 0.0f;
-        const double cs = wave_inclusive_scan((double)(delta * a.A[hh]));
+        const double cs = wave_inclusive_scan((double)(delta * Ahh));
         const double cs_end = read_lane(cs, 63);
         sm.cst[tb][lane] = cs;
         sm.d[tb][lane] = delta;
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
         sm.sg[tb][lane] = a.dt_softplus ? 1.0f / (1.0f + __expf(-raw)) : 1.0f;
     };
     prefetch(g * R);
-    if (wave == 6) scan_head(g * R, 0);
+    if (wave == 6) scan_head(a.A[g * R], 0);
 
     for (int r = 0; r < R; ++r) {
         // lane-derived offsets are recomputed per head (an opaque copy of the
@@ -390,6 +390,12 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
         const int srow = tdv >> 3, scol = (tdv & 7) * 8;   // x / dy staging: token, 8 columns of p
         const int h = g * R + r;
         const int rb = r & 1;  // this head's per-token buffer
+        // this head's A and D and the next head's A, read before this head's
+        // loads are issued: read later, under a branch or not, a load waits for
+        // every load in flight, the next head's prefetch included
+        const float Ah = a.A[h], Anext = a.A[g * R + min(r + 1, R - 1)];
+        const float Dv = (a.D ? a.D : a.A)[h];  // unconditional (A stands in without D)
+        const float Dh = a.D ? Dv : 0.0f;
         const size_t bh = (size_t)b * a.nheads + h;
         const size_t bhc = bh * a.nchunks + c;
         // ================= staging of head h (from the registers loaded a head ahead)
@@ -422,7 +428,19 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
             }
         }
         __syncthreads();
-        prefetch(g * R + min(r + 1, R - 1));  // next head (the last one again at the end)
+        // the chunk state this head's dC2 needs, loaded now so that the first
+        // products hide its latency (the next head's inputs follow once it is used)
+        // (half of it; the other half before the x·G_out products, within the
+        // registers the kernel has)
+        float4 hreg[P / 16][2];
+        const bool owns_bc_h = wave < 2 * NT;
+        const float *hinp = a.hst + bhc * N * P + (size_t)(32 * (wave % NT) + l32) * P + 8 * lg;
+        auto load_h = [&](int ks) {
+            hreg[ks][0] = owns_bc_h ? *reinterpret_cast<const float4 *>(hinp + 16 * ks) : make_float4(0, 0, 0, 0);
+            hreg[ks][1] = owns_bc_h ? *reinterpret_cast<const float4 *>(hinp + 16 * ks + 4) : make_float4(0, 0, 0, 0);
+        };
+        load_h(0);
+        load_h(1);
 
         // ================= products that need no decayed blocks
         f32x16 inter = {};
@@ -490,7 +508,8 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
             // dB2[s][n] = Σ_p x[s][p] G_out[n][p]; dC2[u][n] = Σ_p dy[u][p] h_in[n][p]
             f32x16 t2 = {}, t3 = {};
             float ghp = 0.0f;
-            const float *hin = a.hst + bhc * N * P + (size_t)(32 * nt + l32) * P + 8 * lg;
+            load_h(2);
+            load_h(3);
 #pragma unroll
             for (int ks = 0; ks < P / 16; ++ks) {
                 const bf16x8 xa = rop<PQ>(sm.xs, 32 * bt, 16 * ks, ln);
@@ -499,8 +518,8 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
             }
 #pragma unroll
             for (int ks = 0; ks < P / 16; ++ks) {
-                const float4 h0v = *reinterpret_cast<const float4 *>(hin + 16 * ks);
-                const float4 h1v = *reinterpret_cast<const float4 *>(hin + 16 * ks + 4);
+                const float4 h0v = hreg[ks][0];
+                const float4 h1v = hreg[ks][1];
                 const float hv[8] = {h0v.x, h0v.y, h0v.z, h0v.w, h1v.x, h1v.y, h1v.z, h1v.w};
                 bf16x8 hhi, hlo;
                 split8(hv, hhi, hlo);
@@ -532,6 +551,7 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
             const float csa = row_sums(cc, ln, cr);
             if ((ln & 1) == 0) sm.dcsa[nt][32 * bt + cr] = csa;
         }
+        prefetch(g * R + min(r + 1, R - 1));  // next head (the last one again at the end)
         __syncthreads();
 
         // ================= products with the decayed blocks
@@ -545,7 +565,6 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
                 intra = mfma(rop<PQ>(sm.mb[0], 32 * dst_, 16 * ks, ln), bop, intra);
                 intra = mfma(rop<PQ>(sm.mb[1], 32 * dst_, 16 * ks, ln), bop, intra);
             }
-            const float Dh = a.D ? a.D[h] : 0.0f;
             f32x16 dd, qq;
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
@@ -585,7 +604,7 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
         }
         // the next head's per-token values, on a wave that is otherwise idle here
         // (its Δ arrived with the prefetch after the first barrier)
-        if (wave == 6 && r + 1 < R) scan_head(h + 1, rb ^ 1);
+        if (wave == 6 && r + 1 < R) scan_head(Anext, rb ^ 1);
         __syncthreads();
 
         // ================= dx rows; per-token decay gradients (wave 7)
@@ -611,7 +630,7 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
             const double rev = wave_inclusive_scan(shfl_d(dcs, 63 - t));
             const double dl = shfl_d(rev, 63 - t);
             const float dlf = (float)dl;
-            const float ddelta = a.A[h] * dlf + ddirect;
+            const float ddelta = Ah * dlf + ddirect;
             const bool ok = t <= lim;
             if (ok) a.ddt[(row0 + t) * a.nheads + h] = f32_to_bf16_bits(ddelta * sm.sg[rb][t]);
             const float dA = wave_sum(ok ? sm.d[rb][t] * dlf : 0.0f);
