@@ -177,8 +177,12 @@ def time_calls(fn, nkernels, steps, warmup, flush=True):
 
 
 def gpu_clocks():
-    """Current GPU clocks from rocm-smi (None when it is unavailable)."""
+    """Current GPU clocks from rocm-smi (None when it is unavailable, or under a
+    profiler, whose preloaded library would initialise the GPU in the child
+    before rocm-smi's interpreter starts)."""
     import subprocess
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
+        return None
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
                            timeout=30)
