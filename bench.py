@@ -198,10 +198,18 @@ def gpu_clocks():
 
 
 def source_digest(paths):
+    """Digest of the code of the kernel's source files: comments and trailing blanks
+    are left out, so that a comment edit does not retire counters taken on the
+    same code."""
+    import re
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        text = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+        h.update(text.encode("utf-8"))
     return h.hexdigest()[:16]
 
 

@@ -22,10 +22,11 @@
 // (ssd_fused_pair.h), sized so that two workgroups share a CU: waves 0-3 hold
 // the state in 16x16x32 MFMA accumulators, each all of n for 16 columns of
 // headdim, multiply it by C straight from those registers (the output formed
-// transposed, one 8-byte store per lane), decay and update it, and add the
-// intra-chunk products.  Waves 4-7 form the three causal blocks of (C Bᵀ)ᵀ
-// with the decay mask (and D on the diagonal), scan the next chunk's Δ·A, and
-// stage the next chunk into LDS while the state waves finish the outputs.  Two
+// transposed, one 8-byte store per lane), decay and update it (forming w·x
+// for their own columns in registers), and add the intra-chunk products.
+// Waves 4-7 form the three causal blocks of (C Bᵀ)ᵀ with the decay mask (and
+// D on the diagonal) and scan the next chunk's Δ·A, then stage the next
+// chunk's x and B; C follows while the state waves finish the outputs.  Two
 // barriers per chunk.
 //
 // Long sequences with few (batch, head) pairs are cut into S segments that
@@ -38,7 +39,8 @@
 // Precision: every bf16 operand the kernel computes (w·x, the masked C·Bᵀ
 // values, the state) is split into a bf16 head and tail (value - head, exact
 // in float32) and enters as two products, ~2^-17 relative error; the caller's
-// x, B, C are exact bf16 and enter unsplit.  cs is summed in float64 so that
+// x, B, C are exact bf16 (or float8 e4m3fn, decoded to bf16 exactly) and
+// enter unsplit.  cs is summed in float64 so that
 // exp of a difference of nearby cs values keeps float32 accuracy.  The decay
 // mask of a 32-token diagonal block is factorised, or taken exactly when the
 // block's own log-change exceeds kMaxBlockDecay in either direction.
