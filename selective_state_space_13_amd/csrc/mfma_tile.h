@@ -37,7 +37,7 @@ __device__ __forceinline__ void split8(const float *v, bf16x8 &head, bf16x8 &tai
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         hw[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
-        tw[e] = pack_bf16x2(v[2 * e] - bf16lo(hw[e]), v[2 * e + 1] - bf16hi(hw[e]));
+        tw[e] = split_tail(hw[e], v[2 * e], v[2 * e + 1]);
     }
     head = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
     tail = __builtin_bit_cast(bf16x8, make_uint4(tw[0], tw[1], tw[2], tw[3]));

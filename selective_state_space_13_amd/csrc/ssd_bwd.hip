@@ -145,7 +145,7 @@ __device__ __forceinline__ void adjoint_walk(const BwdArgs &a, unsigned blk, uns
             for (int q = 0; q < 4; ++q) {
                 const float f0 = bf16lo(in[q]) * e, f1 = bf16hi(in[q]) * e;
                 hi[q] = pack_bf16x2(f0, f1);
-                lo[q] = pack_bf16x2(f0 - bf16lo(hi[q]), f1 - bf16hi(hi[q]));
+                lo[q] = split_tail(hi[q], f0, f1);
             }
             *reinterpret_cast<uint4 *>(&eyh[oy]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
             *reinterpret_cast<uint4 *>(&eyl[oy]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
@@ -487,12 +487,12 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
                 const uint32_t kh01 = pack_bf16x2(k4[0], k4[1]), kh23 = pack_bf16x2(k4[2], k4[3]);
                 *reinterpret_cast<uint2 *>(&sm.mb[0][off]) = make_uint2(mh01, mh23);
                 *reinterpret_cast<uint2 *>(&sm.mb[1][off]) =
-                    make_uint2(pack_bf16x2(m4[0] - bf16lo(mh01), m4[1] - bf16hi(mh01)),
-                               pack_bf16x2(m4[2] - bf16lo(mh23), m4[3] - bf16hi(mh23)));
+                    make_uint2(split_tail(mh01, m4[0], m4[1]),
+                               split_tail(mh23, m4[2], m4[3]));
                 *reinterpret_cast<uint2 *>(&sm.kd[0][off]) = make_uint2(kh01, kh23);
                 *reinterpret_cast<uint2 *>(&sm.kd[1][off]) =
-                    make_uint2(pack_bf16x2(k4[0] - bf16lo(kh01), k4[1] - bf16hi(kh01)),
-                               pack_bf16x2(k4[2] - bf16lo(kh23), k4[3] - bf16hi(kh23)));
+                    make_uint2(split_tail(kh01, k4[0], k4[1]),
+                               split_tail(kh23, k4[2], k4[3]));
             }
             // Z sums: over s (lanes) per row u, and over u (registers, both lane halves) per s
             int zr;

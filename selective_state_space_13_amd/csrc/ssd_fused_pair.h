@@ -68,7 +68,8 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
     constexpr int kScanRole = 3;    // staging wave 7
     __shared__ __attribute__((aligned(16))) PairSmem<N> sm;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: role values stay scalar
     const int l32 = lane & 31, lg = lane >> 5;
     const int c16 = lane & 15, q = lane >> 4;
     const int jr = (lane >> 2) & 3, jc = 4 * (lane & 3);  // source row / column of a transposed read
@@ -209,6 +210,7 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
             const int buf = c & 1;
             const TokSmem &T = sm.tok[buf];
             f32x4 y[4] = {};
+            const float dec = T.e[kC - 1];
             // ============ A: yᵀ = Hᵀ·Cᵀ scaled by exp(cs_t); H = exp(cs_end)·H + Bᵀ(w·x)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
@@ -218,8 +220,20 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
                     hv[r] = st[2 * ks][r];
                     hv[4 + r] = st[2 * ks + 1][r];
                 }
-                bf16x8 hh, ht;
-                split8(hv, hh, ht);
+                // split head/tail, each pair of entries decayed between its head and
+                // its tails: the in-place tail products are then the last use of the
+                // entering values (no copies), and only two extra values are live
+                uint32_t hw[4], tw[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    hw[e] = pack_bf16x2(hv[2 * e], hv[2 * e + 1]);
+                    f32x4 &sd = st[2 * ks + (e >> 1)];
+                    sd[2 * (e & 1)] *= dec;
+                    sd[2 * (e & 1) + 1] *= dec;
+                    tw[e] = split_tail(hw[e], hv[2 * e], hv[2 * e + 1]);
+                }
+                const bf16x8 hh = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+                const bf16x8 ht = __builtin_bit_cast(bf16x8, make_uint4(tw[0], tw[1], tw[2], tw[3]));
 #pragma unroll
                 for (int tau = 0; tau < 4; ++tau) {
                     const bf16x8 cop = as8(ld16(sm.cr + swz<N>(16 * tau + c16, 32 * ks + 8 * q)));
@@ -233,11 +247,6 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
 #pragma unroll
                 for (int r = 0; r < 4; ++r) y[tau][r] *= et;
             }
-            const float dec = T.e[kC - 1];
-#pragma unroll
-            for (int i = 0; i < NT; ++i)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) st[i][r] *= dec;
             // the update's B operand w·x, formed here for this wave's columns: the
             // transposed read of raw x gives the lane x[t][p] for t = 32kt + 8q + j,
             // j = 0..7 (its k-slots), p = 16·role + c16; each is scaled by its
@@ -270,15 +279,18 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
             for (int ks = 0; ks < 2; ++ks)
                 xop[ks] = cat8(tr4(sm.xs[buf] + swz<64>(32 * ks + 4 * q + jr, 16 * role + jc)),
                                tr4(sm.xs[buf] + swz<64>(32 * ks + 16 + 4 * q + jr, 16 * role + jc)));
+            // the lane reads row t = 16(τ & 1) + c16 of each block, whose chunk swizzle
+            // is that of c16 (it depends on bits 1-2 of t only): one base address,
+            // every read at a constant offset from it
+            const uint4 *mtl = &sm.mt[0][0][c16][q ^ mt_swz(c16)];
 #pragma unroll
             for (int tau = 0; tau < 4; ++tau) {
-                const int trow = 16 * (tau & 1) + c16;
-                const int ch = q ^ mt_swz(trow);
 #pragma unroll
                 for (int ks = 0; ks <= (tau >> 1); ++ks) {
                     const int mb = (tau >> 1) == 0 ? 0 : 1 + ks;
-                    y[tau] = mfma16(xop[ks], as8(sm.mt[mb][0][trow][ch]), y[tau]);
-                    y[tau] = mfma16(xop[ks], as8(sm.mt[mb][1][trow][ch]), y[tau]);
+#pragma unroll
+                    for (int pl = 0; pl < 2; ++pl)
+                        y[tau] = mfma16(xop[ks], as8(mtl[((2 * mb + pl) * 32 + 16 * (tau & 1)) * 4]), y[tau]);
                 }
             }
             // lane holds p = 16·role + 4q + r of token t = 16τ + c16: one 8-byte store each.
@@ -308,10 +320,15 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
         // ---- end of the walk
         if (a.final_state && half != 0 && seg == a.nseg - 1) {
             float *dst = a.final_state + bh * N * P;
+            // offsets from an opaque copy of the lane index, formed here: kept
+            // from before the loop, they would be spilled around it
+            int ln = lane;
+            asm volatile("" : "+v"(ln));
+            const int qf = ln >> 4, pf = 16 * role + (ln & 15);
 #pragma unroll
             for (int i = 0; i < NT; ++i)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) dst[pair_n(i, q, r) * P + pc] = st[i][r];
+                for (int r = 0; r < 4; ++r) dst[pair_n(i, qf, r) * P + pf] = st[i][r];
         }
     } else {
         if (c0 < c1) {  // an empty sequence loads nothing and returns its initial state

@@ -314,7 +314,7 @@ __device__ __forceinline__ void state_walk(const FusedArgs &a, unsigned blk, uns
             for (int e = 0; e < 4; ++e) {
                 const float f0 = bf16lo(in[e]) * w, f1 = bf16hi(in[e]) * w;
                 hi[e] = pack_bf16x2(f0, f1);
-                lo[e] = pack_bf16x2(f0 - bf16lo(hi[e]), f1 - bf16hi(hi[e]));
+                lo[e] = split_tail(hi[e], f0, f1);
             }
             *reinterpret_cast<uint4 *>(&xh[ox]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
             *reinterpret_cast<uint4 *>(&xl[ox]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);

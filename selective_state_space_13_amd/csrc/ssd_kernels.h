@@ -33,6 +33,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// The tails of a head/tail split: head = pack_bf16x2(lo, hi), and the packed
+// pair bf16(lo - head.lo), bf16(hi - head.hi).  Each difference is one
+// v_dot2c_f32_bf16, lo + (-1)·head.lo + 0·head.hi (and the same for hi): both
+// products are exact and the difference of a float and its nearest bf16 is
+// exactly representable, so it equals lo - bf16lo(head) bit for bit, without
+// first widening the head half to float32.  The dot2c form accumulates in
+// place: where lo or hi is used again after this, the compiler copies it first.
+// The (-1, 0) and (0, -1) operands come from scalar registers: written as
+// constants, the compiler encodes (-1, 0) as the inline constant -1.0, which
+// the instruction does not read as that pair (the result is then wrong).
+__device__ __forceinline__ uint32_t split_tail(uint32_t head, float lo, float hi) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf2_t;
+    uint32_t mlo = 0x0000bf80u, mhi = 0xbf800000u;
+    asm volatile("" : "+s"(mlo), "+s"(mhi));
+    const bf2_t h = __builtin_bit_cast(bf2_t, head);
+    const float tl = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf2_t, mlo), lo, false);
+    const float th = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf2_t, mhi), hi, false);
+    return pack_bf16x2(tl, th);
+}
+
 __device__ __forceinline__ void store_out(float *p, float v) { *p = v; }
 __device__ __forceinline__ void store_out(bf16_t *p, float v) { p->bits = f32_to_bf16_bits(v); }
 
