@@ -32,12 +32,12 @@ __device__ __forceinline__ bf16x8 as8(uint4 v) { return __builtin_bit_cast(bf16x
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 
 // v = head + tail, head = bf16(v), tail = bf16(v - head)
-__device__ __forceinline__ void split8(const float *v, bf16x8 &head, bf16x8 &tail) {
+__device__ __forceinline__ void split8(const float *v, bf16x8 &head, bf16x8 &tail, TailK k = tail_consts()) {
     uint32_t hw[4], tw[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         hw[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
-        tw[e] = split_tail(hw[e], v[2 * e], v[2 * e + 1]);
+        tw[e] = split_tail(hw[e], v[2 * e], v[2 * e + 1], k);
     }
     head = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
     tail = __builtin_bit_cast(bf16x8, make_uint4(tw[0], tw[1], tw[2], tw[3]));

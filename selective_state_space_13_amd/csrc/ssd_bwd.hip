@@ -82,7 +82,6 @@ __device__ __forceinline__ void adjoint_walk(const BwdArgs &a, unsigned blk, uns
     const size_t bh = (size_t)b * a.nheads + h;
     const size_t row0 = (size_t)b * a.seqlen;
     const float Ah = a.A[h];
-    const int last = a.seqlen - 1;
 
     const bool owns = wave < (N / 32) * 2;
     const int snt = wave >> 1, spt = wave & 1;
@@ -105,19 +104,27 @@ __device__ __forceinline__ void adjoint_walk(const BwdArgs &a, unsigned blk, uns
 
     // dy, C and Δ of one chunk, loaded two chunks ahead of their use into one of
     // two register sets that the loop alternates
+    // through buffer resources from the chunk's first row to the end of the
+    // sequence: rows past the end read 0 (their e and Δ are 0 as well)
     struct Loads { uint4 y, c[BV]; uint16_t dt; };  // dt: raw bf16 bits, widened at the scan
+    const uint32_t yrb = (uint32_t)xstride * 2, brb = (uint32_t)bstride * 2, drb = (uint32_t)a.nheads * 2;
+    const uint32_t yoff = (uint32_t)yrow * yrb + (uint32_t)ycol * 2, doff = (uint32_t)lane * drb;
+    // vector k of C: one lane offset, a resource from row (kThreads / BPR)·k on
+    const uint32_t boff = (uint32_t)brow * brb + (uint32_t)bcol * 2;
     auto prefetch = [&](Loads &L, int c) {
-        const int t0 = c * kC, lim = last - t0;
-        L.dt = a.dt[(row0 + t0 + min(lane, lim)) * a.nheads + h];
-        L.y = ld16(a.dy + ((row0 + t0) * a.nheads + h) * P + ycol + (size_t)min(yrow, lim) * xstride);
-        const uint16_t *cc = a.C + (row0 + t0) * bstride + (size_t)g * N + bcol;
+        const int t0 = c * kC, rows = a.seqlen - t0;
+        L.dt = __builtin_amdgcn_raw_buffer_load_b16(buf_rsrc(a.dt + (row0 + t0) * a.nheads + h, rows, drb), doff, 0, 0);
+        L.y = buf_in8<false>(buf_rsrc(a.dy + ((row0 + t0) * a.nheads + h) * P, rows, yrb), yoff);
 #pragma unroll
-        for (int k = 0; k < BV; ++k) L.c[k] = ld16(cc + (size_t)min(brow + (kThreads / BPR) * k, lim) * bstride);
+        for (int k = 0; k < BV; ++k) {
+            const int r0 = (kThreads / BPR) * k;
+            L.c[k] = buf_in8<false>(buf_rsrc(a.C + (row0 + t0 + r0) * bstride + (size_t)g * N, rows - r0, brb), boff);
+        }
     };
     auto scan = [&](int c, int pb, uint16_t bits) {
         const float rdt = __uint_as_float((uint32_t)bits << 16);
         const bool ok = c * kC + lane < a.seqlen;
-        const float delta = ok ? (a.dt_softplus ? softplus_f32(rdt) : rdt) : 0.0f;
+        const float delta = ok ? (a.dt_softplus ? softplus_fast(rdt) : rdt) : 0.0f;
         const double cs = wave_inclusive_scan((double)(delta * Ah));
         sm.cst[pb][lane] = cs;
         sm.e[pb][lane] = ok ? __expf((float)cs) : 0.0f;
@@ -369,14 +376,14 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
     auto scan_head = [&](float Ahh, int tb) {
         const bool ok = lane <= lim;
         const float raw = R0.dt;
-        const float delta = ok ? (a.dt_softplus ? softplus_f32(raw) : raw) : 0.0f;
+        const float delta = ok ? (a.dt_softplus ? softplus_fast(raw) : raw) : 0.0f;
         const double cs = wave_inclusive_scan((double)(delta * Ahh));
         const double cs_end = read_lane(cs, 63);
         sm.cst[tb][lane] = cs;
         sm.d[tb][lane] = delta;
         sm.ee[tb][lane] = ok ? __expf((float)(cs_end - cs)) : 0.0f;
         sm.eu[tb][lane] = ok ? __expf((float)cs) : 0.0f;
-        sm.sg[tb][lane] = a.dt_softplus ? 1.0f / (1.0f + __expf(-raw)) : 1.0f;
+        sm.sg[tb][lane] = a.dt_softplus ? __builtin_amdgcn_rcpf(1.0f + __expf(-raw)) : 1.0f;
     };
     prefetch(g * R);
     if (wave == 6) scan_head(a.A[g * R], 0);

@@ -56,6 +56,28 @@ __device__ __forceinline__ int pair_n(int i, int q, int r) { return 32 * (i >> 1
 // 16-byte chunk of row t of a masked block: q XOR this
 __device__ __forceinline__ int mt_swz(int t) { return (t >> 1) & 3; }
 
+// The lanes of a diagonal 32 x 32 block whose register r lies above the
+// diagonal (s > t: zeroed) or on it (s = t: + D), as wave masks: lane L holds
+// t = L & 31 and, in register r, s = 8(r >> 2) + 4(L >> 5) + (r & 3).  They are
+// constants, so each costs one v_cndmask with a scalar-register mask and no
+// per-lane compare (hoisted, the 32 masks took 64 scalar registers, spilled).
+constexpr uint64_t diag_lanes(int r, bool above) {
+    uint64_t m = 0;
+    for (int L = 0; L < 64; ++L) {
+        const int t = L & 31, s = 8 * (r >> 2) + 4 * (L >> 5) + (r & 3);
+        if (above ? s > t : s == t) m |= 1ull << L;
+    }
+    return m;
+}
+__device__ __forceinline__ float causal_diag(int r, float m, float D) {
+    const uint64_t on = diag_lanes(r, false), above = diag_lanes(r, true);
+    const float md = m + D;
+    float o;
+    asm("v_cndmask_b32 %0, %1, %2, %3" : "=v"(o) : "v"(m), "v"(md), "s"(on));  // on ? m + D : m
+    asm("v_cndmask_b32 %0, %1, 0, %2" : "=v"(o) : "v"(o), "s"(above));        // above ? 0 : o
+    return o;
+}
+
 template <int N, bool YF32, bool F8>
 __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk, unsigned nblk) {
     typedef typename InStore<F8>::elem E;
@@ -88,7 +110,7 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
     const float Dh = a.D ? a.D[h] : 0.0f;
     const size_t bh = (size_t)b * a.nheads + h;
     const size_t xstride = (size_t)a.nheads * P, bstride = (size_t)a.ngroups * N;
-    const int last = seqlen - 1;
+    const TailK tk = tail_consts();  // the split's tail operands, once
     const int pc = 16 * role + c16;  // state waves: this lane's column p
 
     // ---- staging waves: lane gl stages x rows xrow, xrow + 32 and B/C rows brow + BSTEP·k
@@ -98,29 +120,41 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
     const int brow = gl / BPR, bcol = (gl % BPR) * 8;
     typename InStore<F8>::vec8 rx[2], rb[GV], rc[GV];  // as stored; decoded at the staging
     uint32_t rdt = 0;  // raw bf16 Δ of a token (lane), converted where the scan uses it
-    // Chunk bases are wave-uniform (scalar registers); the per-lane offsets within
-    // a chunk fit in 32 bits (64 rows of at most 2^25 elements, checked by the host).
-    const uint32_t xs32 = (uint32_t)xstride, bs32 = (uint32_t)bstride, hs32 = (uint32_t)a.nheads;
+    // Each chunk's loads go through buffer resources from the chunk's first row to
+    // the end of the sequence (scalar registers), so rows past the end read 0 (Δ
+    // there is taken as 0, so they add nothing).  The per-lane byte offsets are
+    // the same for every chunk; they fit in 32 bits (64 rows of at most 2^25
+    // elements, checked by the host).
+    const uint32_t es = sizeof(E);
+    const uint32_t xrb = (uint32_t)xstride * es, brb = (uint32_t)bstride * es;  // bytes per token row
+    const uint32_t xo0 = (uint32_t)xrow * xrb + (uint32_t)xcol * es, xo1 = xo0 + 32 * xrb;
+    uint32_t bo[GV];
+#pragma unroll
+    for (int k = 0; k < GV; ++k) bo[k] = (uint32_t)(brow + BSTEP * k) * brb + (uint32_t)bcol * es;
+    const uint32_t dto = (uint32_t)lane * (uint32_t)a.nheads * 2;
+    auto rows_from = [&](int c) { return seqlen - c * kC; };
     auto load_dt = [&](int c) {  // every staging wave: no branch, hence no wait for it here
         const int t0 = c * kC;
         const uint16_t *db = a.dt + (row0 + t0) * a.nheads + h;
-        rdt = db[(uint32_t)min(lane, last - t0) * hs32];
+        rdt = __builtin_amdgcn_raw_buffer_load_b16(buf_rsrc(db, rows_from(c), (uint32_t)a.nheads * 2), dto, 0, 0);
     };
-    // rows past the end of the sequence are clamped to the last one
     auto load_xb = [&](int c) {  // x and B of chunk c
-        const int t0 = c * kC, lim = last - t0;
+        const int t0 = c * kC;
         const E *xb = static_cast<const E *>(a.x) + ((row0 + t0) * a.nheads + h) * P;
-        rx[0] = ld_in8<F8>(xb + ((uint32_t)min(xrow, lim) * xs32 + xcol));
-        rx[1] = ld_in8<F8>(xb + ((uint32_t)min(xrow + 32, lim) * xs32 + xcol));
+        const auto rxs = buf_rsrc(xb, rows_from(c), xrb);
+        rx[0] = buf_in8<F8>(rxs, xo0);
+        rx[1] = buf_in8<F8>(rxs, xo1);
         const E *bb = static_cast<const E *>(a.B) + (row0 + t0) * bstride + (size_t)g * N;
+        const auto rbs = buf_rsrc(bb, rows_from(c), brb);
 #pragma unroll
-        for (int k = 0; k < GV; ++k) rb[k] = ld_in8<F8>(bb + ((uint32_t)min(brow + BSTEP * k, lim) * bs32 + bcol));
+        for (int k = 0; k < GV; ++k) rb[k] = buf_in8<F8>(rbs, bo[k]);
     };
     auto load_c = [&](int c) {  // C of chunk c
-        const int t0 = c * kC, lim = last - t0;
+        const int t0 = c * kC;
         const E *cb = static_cast<const E *>(a.C) + (row0 + t0) * bstride + (size_t)g * N;
+        const auto rcs = buf_rsrc(cb, rows_from(c), brb);
 #pragma unroll
-        for (int k = 0; k < GV; ++k) rc[k] = ld_in8<F8>(cb + ((uint32_t)min(brow + BSTEP * k, lim) * bs32 + bcol));
+        for (int k = 0; k < GV; ++k) rc[k] = buf_in8<F8>(rcs, bo[k]);
     };
     auto stage_xb = [&](int c) {  // x and B of chunk c from registers into LDS
 #pragma unroll
@@ -204,6 +238,11 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
             // waits for every outstanding memory operation, the y stores included
             __builtin_amdgcn_s_waitcnt(0x0f70);
         }
+        // the y stores: bytes per token row, and the lane's byte offset within a
+        // 16-token group of rows (p = 16·role + 4q .. +3 of token c16)
+        constexpr uint32_t kYSize = YF32 ? 4 : 2;
+        const uint32_t yrb = (uint32_t)xstride * kYSize;
+        const uint32_t yoff = (uint32_t)c16 * yrb + (uint32_t)(16 * role + 4 * q) * kYSize;
         __syncthreads();  // the staging waves' first scan and staging
         __syncthreads();
         for (int c = c0; c < c1; ++c) {
@@ -230,7 +269,7 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
                     f32x4 &sd = st[2 * ks + (e >> 1)];
                     sd[2 * (e & 1)] *= dec;
                     sd[2 * (e & 1) + 1] *= dec;
-                    tw[e] = split_tail(hw[e], hv[2 * e], hv[2 * e + 1]);
+                    tw[e] = split_tail(hw[e], hv[2 * e], hv[2 * e + 1], tk);
                 }
                 const bf16x8 hh = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
                 const bf16x8 ht = __builtin_bit_cast(bf16x8, make_uint4(tw[0], tw[1], tw[2], tw[3]));
@@ -262,7 +301,7 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
                                      bf16hi(xv.y) * w0.w, bf16lo(xv.z) * w1.x, bf16hi(xv.z) * w1.y,
                                      bf16lo(xv.w) * w1.z, bf16hi(xv.w) * w1.w};
                 bf16x8 whi, wlo;
-                split8(wv, whi, wlo);
+                split8(wv, whi, wlo, tk);
 #pragma unroll
                 for (int i = 0; i < NT; ++i) {
                     const int col = 32 * (i >> 1) + 2 * jc + 4 * (i & 1);
@@ -293,26 +332,24 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
                         y[tau] = mfma16(xop[ks], as8(mtl[((2 * mb + pl) * 32 + 16 * (tau & 1)) * 4]), y[tau]);
                 }
             }
-            // lane holds p = 16·role + 4q + r of token t = 16τ + c16: one 8-byte store each.
-            // The lane's offset is formed here from an opaque copy of the lane index:
-            // hoisted out of the loop, the four offsets would be kept in registers
-            // the loop does not have.
+            // lane holds p = 16·role + 4q + r of token t = 16τ + c16: one 8-byte store
+            // each, through a buffer resource from row 16τ of the chunk to the end of
+            // the sequence (stores past it are dropped), at the lane's fixed offset
             const int t0 = c * kC;
-            const size_t ybase = ((row0 + t0) * a.nheads + h) * P;
-            int ln = lane;
-            asm volatile("" : "+v"(ln));
-            const uint32_t yo = (uint32_t)(ln & 15) * (uint32_t)xstride + 16 * role + 4 * (ln >> 4);
+            const char *yb = reinterpret_cast<const char *>(YF32 ? static_cast<void *>(a.yf) : static_cast<void *>(a.y)) +
+                             ((row0 + t0) * a.nheads + h) * P * kYSize;
 #pragma unroll
             for (int tau = 0; tau < 4; ++tau) {
-                if (t0 + 16 * tau + c16 < seqlen) {
-                    const uint32_t o = yo + (uint32_t)(16 * tau) * (uint32_t)xstride;
-                    if constexpr (YF32) {
-                        *reinterpret_cast<float4 *>(a.yf + ybase + o) =
-                            make_float4(y[tau][0], y[tau][1], y[tau][2], y[tau][3]);
-                    } else {
-                        *reinterpret_cast<uint2 *>(a.y + ybase + o) =
-                            make_uint2(pack_bf16x2(y[tau][0], y[tau][1]), pack_bf16x2(y[tau][2], y[tau][3]));
-                    }
+                const auto yr = buf_rsrc(yb + (size_t)(16 * tau) * yrb, seqlen - t0 - 16 * tau, yrb);
+                if constexpr (YF32) {
+                    typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+                    const u32x4 v = {__float_as_uint(y[tau][0]), __float_as_uint(y[tau][1]),
+                                     __float_as_uint(y[tau][2]), __float_as_uint(y[tau][3])};
+                    __builtin_amdgcn_raw_buffer_store_b128(v, yr, yoff, 0, 0);
+                } else {
+                    typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+                    const u32x2 v = {pack_bf16x2(y[tau][0], y[tau][1]), pack_bf16x2(y[tau][2], y[tau][3])};
+                    __builtin_amdgcn_raw_buffer_store_b64(v, yr, yoff, 0, 0);
                 }
             }
             __syncthreads();
@@ -381,18 +418,15 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
                 }
                 if (Tb == Sb) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int sr = 8 * (r >> 2) + 4 * lg + (r & 3);
-                        m[r] = sr > l32 ? 0.0f : (sr == l32 ? m[r] + Dh : m[r]);
-                    }
+                    for (int r = 0; r < 16; ++r) m[r] = causal_diag(r, m[r], Dh);
                 }
                 // chunk lg: rows s of slabs lg and lg + 4 (registers 0-3, 8-11);
                 // chunk 2 + lg: slabs 2 + lg and 6 + lg (registers 4-7, 12-15)
                 const float v0[8] = {m[0], m[1], m[2], m[3], m[8], m[9], m[10], m[11]};
                 const float v1[8] = {m[4], m[5], m[6], m[7], m[12], m[13], m[14], m[15]};
                 bf16x8 h0v, t0v, h1v, t1v;
-                split8(v0, h0v, t0v);
-                split8(v1, h1v, t1v);
+                split8(v0, h0v, t0v, tk);
+                split8(v1, h1v, t1v, tk);
                 const int sw = mt_swz(l32);
                 sm.mt[role][0][l32][lg ^ sw] = __builtin_bit_cast(uint4, h0v);
                 sm.mt[role][1][l32][lg ^ sw] = __builtin_bit_cast(uint4, t0v);

@@ -41,6 +41,30 @@ __device__ __forceinline__ uint4 in_bf16x8(uint2 v) {
                       fp8x2_bf16<true>(v.y));
 }
 
+// A raw buffer resource over rows rows of rowbytes bytes from base (the size
+// clipped to 2^32 - 1; no rows gives an empty range).  Loads past its end read 0
+// and stores past it are dropped, so the ragged end of a sequence needs no
+// per-lane clamp or compare.  Base and size are wave-uniform (the resource
+// lives in scalar registers); lane offsets are 32-bit byte offsets from base.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, int rows, uint32_t rowbytes) {
+    // rows·rowbytes in 64 bits, clipped with 32-bit compares (scalar ALU has no
+    // ordered 64-bit compare)
+    const uint64_t p = (uint64_t)(uint32_t)max(rows, 0) * rowbytes;
+    const uint32_t n = (uint32_t)(p >> 32) ? 0xffffffffu : (uint32_t)p;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n, 0x00020000);
+}
+// 8 stored elements at byte offset off of a buffer (zeros past its end)
+template <bool F8>
+__device__ __forceinline__ typename InStore<F8>::vec8 buf_in8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (F8) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        return make_uint2(v[0], v[1]);
+    } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        return make_uint4(v[0], v[1], v[2], v[3]);
+    }
+}
+
 // Per-token values of one chunk (index = token), written by one wave.
 struct TokSmem {
     double cs[kC];  // within-chunk inclusive cumsum of Δ·A_h (cs[63] closes the chunk)
@@ -255,30 +279,39 @@ __device__ __forceinline__ void state_walk(const FusedArgs &a, unsigned blk, uns
     const int o_xa = swz<64>(8 * lg + rrow, 32 * spt + rcol), o_xb = swz<64>(8 * lg + 4 + rrow, 32 * spt + rcol);
 
     const size_t xstride = (size_t)a.nheads * P, bstride = (size_t)a.ngroups * N;
-    const int last = seqlen - 1;
 
     // x, B and Δ of one chunk, loaded two chunks ahead of their use into one of
     // two register sets that the loop alternates (a load one chunk ahead
     // arrived after the short update phase, and every chunk waited for it)
-    // dt: raw bf16 bits, widened at the scan; x and B as stored, decoded at the staging
+    // dt: raw bf16 bits, widened at the scan; x and B as stored, decoded at the staging.
+    // The loads go through buffer resources from the chunk's first row to the
+    // end of the sequence, so rows past the end read 0 (their Δ is taken as 0);
+    // the per-lane byte offsets are the same for every chunk.
     struct Loads { typename InStore<F8>::vec8 x, b[BV]; uint16_t dt; };
+    const uint32_t es = sizeof(E);
+    const uint32_t xrb = (uint32_t)xstride * es, brb = (uint32_t)bstride * es, drb = (uint32_t)a.nheads * 2;
+    const uint32_t xoff = (uint32_t)xrow * xrb + (uint32_t)xcol * es, doff = (uint32_t)lane * drb;
+    // vector k of B: one lane offset, a resource from row (kThreads / BPR)·k on
+    const uint32_t boff = (uint32_t)brow * brb + (uint32_t)bcol * es;
     auto prefetch = [&](Loads &L, int c) {
-        const int t0 = c * kC, lim = last - t0;  // rows past the end are clamped to the last one
+        const int t0 = c * kC, rows = seqlen - t0;
         // dt first: the scan wave uses it before the rest has arrived, and loads
         // complete in issue order
-        L.dt = a.dt[(row0 + t0 + min(lane, lim)) * a.nheads + h];
-        L.x = ld_in8<F8>(static_cast<const E *>(a.x) + ((row0 + t0) * a.nheads + h) * P + xcol +
-                         (size_t)min(xrow, lim) * xstride);
-        const E *bc = static_cast<const E *>(a.B) + (row0 + t0) * bstride + (size_t)g * N + bcol;
+        L.dt = __builtin_amdgcn_raw_buffer_load_b16(buf_rsrc(a.dt + (row0 + t0) * a.nheads + h, rows, drb), doff, 0, 0);
+        L.x = buf_in8<F8>(buf_rsrc(static_cast<const E *>(a.x) + ((row0 + t0) * a.nheads + h) * P, rows, xrb), xoff);
 #pragma unroll
-        for (int k = 0; k < BV; ++k) L.b[k] = ld_in8<F8>(bc + (size_t)min(brow + (kThreads / BPR) * k, lim) * bstride);
+        for (int k = 0; k < BV; ++k) {
+            const int r0 = (kThreads / BPR) * k;
+            L.b[k] = buf_in8<F8>(
+                buf_rsrc(static_cast<const E *>(a.B) + (row0 + t0 + r0) * bstride + (size_t)g * N, rows - r0, brb), boff);
+        }
     };
     // Δ and the float64 inclusive cumsum of Δ·A over the chunk (lane = token),
     // the token weights and the chunk's decay; returns Σ Δ·A over the chunk
     auto scan_chunk = [&](int c, uint16_t bits, StateTok &T) -> double {
         const float raw = __uint_as_float((uint32_t)bits << 16);
         const bool ok = c * kC + lane < seqlen;
-        const float delta = ok ? (a.dt_softplus ? softplus_f32(raw) : raw) : 0.0f;
+        const float delta = ok ? (a.dt_softplus ? softplus_fast(raw) : raw) : 0.0f;
         const double cs = wave_inclusive_scan((double)(delta * Ah));
         const double cs_end = read_lane(cs, 63);
         T.w[lane] = __expf((float)(cs_end - cs)) * delta;

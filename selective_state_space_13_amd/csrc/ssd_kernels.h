@@ -42,14 +42,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // place: where lo or hi is used again after this, the compiler copies it first.
 // The (-1, 0) and (0, -1) operands come from scalar registers: written as
 // constants, the compiler encodes (-1, 0) as the inline constant -1.0, which
-// the instruction does not read as that pair (the result is then wrong).
-__device__ __forceinline__ uint32_t split_tail(uint32_t head, float lo, float hi) {
+// the instruction does not read as that pair (the result is then wrong).  A
+// kernel that splits in a loop makes them once (tail_consts) and passes them.
+struct TailK {
+    uint32_t lo, hi;
+};
+__device__ __forceinline__ TailK tail_consts() {
+    TailK k{0x0000bf80u, 0xbf800000u};
+    asm volatile("" : "+s"(k.lo), "+s"(k.hi));
+    return k;
+}
+__device__ __forceinline__ uint32_t split_tail(uint32_t head, float lo, float hi, TailK k = tail_consts()) {
     typedef __attribute__((ext_vector_type(2))) __bf16 bf2_t;
-    uint32_t mlo = 0x0000bf80u, mhi = 0xbf800000u;
-    asm volatile("" : "+s"(mlo), "+s"(mhi));
     const bf2_t h = __builtin_bit_cast(bf2_t, head);
-    const float tl = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf2_t, mlo), lo, false);
-    const float th = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf2_t, mhi), hi, false);
+    const float tl = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf2_t, k.lo), lo, false);
+    const float th = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf2_t, k.hi), hi, false);
     return pack_bf16x2(tl, th);
 }
 
