@@ -56,6 +56,21 @@ __device__ __forceinline__ int swz(int row, int col) {
     return row * W + ((((col >> 3) ^ m)) << 3) + (col & 7);
 }
 
+// Tiles of the fused prefill with swizzles of their own, found by a search over
+// the bank model above (every read and write pattern the kernel makes on the
+// tile is conflict-free):
+//   C [t][n], W = 128: chunk XOR (row & 15); W = 64: chunk XOR ((row >> 1) & 7);
+//   x [t][p] (64 wide): chunk XOR (2·bit 1 of row + 4·(bit 2 XOR bit 3)).
+template <int W>
+__device__ __forceinline__ int swz_c(int row, int col) {
+    const int m = W == 128 ? (row & 15) : ((row >> 1) & 7);
+    return row * W + (((col >> 3) ^ m) << 3) + (col & 7);
+}
+__device__ __forceinline__ int swz_x(int row, int col) {
+    const int m = (row & 2) | ((((row >> 2) ^ (row >> 3)) & 1) << 2);
+    return row * 64 + (((col >> 3) ^ m) << 3) + (col & 7);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave in float64, on DPP lane
 // moves (no LDS round trips): shifts by 1, 2, 4, 8 within each row of 16
 // lanes, then row 0's total into row 1 and row 2's into row 3, then lane 31's

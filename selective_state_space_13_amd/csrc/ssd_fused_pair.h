@@ -40,9 +40,9 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 
 template <int N>
 struct PairSmem {
-    uint16_t xs[2][kC * P];   // raw x [t][p], swz<64>, by chunk parity
+    uint16_t xs[2][kC * P];   // raw x [t][p], swz_x, by chunk parity
     uint16_t bs[2][kC * N];   // B [t][n], swz<N>, by chunk parity
-    uint16_t cr[kC * N];      // C [t][n], swz<N>
+    uint16_t cr[kC * N];      // C [t][n], swz_c<N>
     // masked blocks (T, S) = (0,0), (1,0), (1,1) of M = mask ⊙ (C Bᵀ) (+ D on the
     // diagonal): [block][head, tail][row t][16-byte chunk q ^ mt_swz(t)];
     // chunk q holds M[t][s] for s = 4q..4q+3 and 16+4q..16+4q+3 of block S
@@ -159,7 +159,7 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
     auto stage_xb = [&](int c) {  // x and B of chunk c from registers into LDS
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2)
-            *reinterpret_cast<uint4 *>(&sm.xs[c & 1][swz<64>(xrow + 32 * k2, xcol)]) = in_bf16x8(rx[k2]);
+            *reinterpret_cast<uint4 *>(&sm.xs[c & 1][swz_x(xrow + 32 * k2, xcol)]) = in_bf16x8(rx[k2]);
 #pragma unroll
         for (int k = 0; k < GV; ++k)
             *reinterpret_cast<uint4 *>(&sm.bs[c & 1][swz<N>(brow + BSTEP * k, bcol)]) = in_bf16x8(rb[k]);
@@ -167,7 +167,7 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
     auto stage_c = [&](int c) {  // C of chunk c
 #pragma unroll
         for (int k = 0; k < GV; ++k)
-            *reinterpret_cast<uint4 *>(&sm.cr[swz<N>(brow + BSTEP * k, bcol)]) = in_bf16x8(rc[k]);
+            *reinterpret_cast<uint4 *>(&sm.cr[swz_c<N>(brow + BSTEP * k, bcol)]) = in_bf16x8(rc[k]);
     };
     // Δ, the float64 inclusive cumsum of Δ·A over the chunk (lane = token) and
     // the values derived from it
@@ -275,7 +275,7 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
                 const bf16x8 ht = __builtin_bit_cast(bf16x8, make_uint4(tw[0], tw[1], tw[2], tw[3]));
 #pragma unroll
                 for (int tau = 0; tau < 4; ++tau) {
-                    const bf16x8 cop = as8(ld16(sm.cr + swz<N>(16 * tau + c16, 32 * ks + 8 * q)));
+                    const bf16x8 cop = as8(ld16(sm.cr + swz_c<N>(16 * tau + c16, 32 * ks + 8 * q)));
                     y[tau] = mfma16(hh, cop, y[tau]);
                     y[tau] = mfma16(ht, cop, y[tau]);
                 }
@@ -293,8 +293,8 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
                 const int ra = 32 * kt + 8 * q + jr, rb4 = ra + 4;
-                const uint4 xv = __builtin_bit_cast(uint4, cat8(tr4(sm.xs[buf] + swz<64>(ra, 16 * role + jc)),
-                                                                tr4(sm.xs[buf] + swz<64>(rb4, 16 * role + jc))));
+                const uint4 xv = __builtin_bit_cast(uint4, cat8(tr4(sm.xs[buf] + swz_x(ra, 16 * role + jc)),
+                                                                tr4(sm.xs[buf] + swz_x(rb4, 16 * role + jc))));
                 const float4 w0 = *reinterpret_cast<const float4 *>(T.w + 32 * kt + 8 * q);
                 const float4 w1 = *reinterpret_cast<const float4 *>(T.w + 32 * kt + 8 * q + 4);
                 const float wv[8] = {bf16lo(xv.x) * w0.x, bf16hi(xv.x) * w0.y, bf16lo(xv.y) * w0.z,
@@ -316,8 +316,8 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
             bf16x8 xop[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
-                xop[ks] = cat8(tr4(sm.xs[buf] + swz<64>(32 * ks + 4 * q + jr, 16 * role + jc)),
-                               tr4(sm.xs[buf] + swz<64>(32 * ks + 16 + 4 * q + jr, 16 * role + jc)));
+                xop[ks] = cat8(tr4(sm.xs[buf] + swz_x(32 * ks + 4 * q + jr, 16 * role + jc)),
+                               tr4(sm.xs[buf] + swz_x(32 * ks + 16 + 4 * q + jr, 16 * role + jc)));
             // the lane reads row t = 16(τ & 1) + c16 of each block, whose chunk swizzle
             // is that of c16 (it depends on bits 1-2 of t only): one base address,
             // every read at a constant offset from it
@@ -394,7 +394,7 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
 #pragma unroll
                 for (int kg = 0; kg < KG; ++kg)
                     gt = mfma(as8(ld16(sm.bs[buf] + swz<N>(32 * Sb + l32, 16 * kg + 8 * lg))),
-                              as8(ld16(sm.cr + swz<N>(32 * Tb + l32, 16 * kg + 8 * lg))), gt);
+                              as8(ld16(sm.cr + swz_c<N>(32 * Tb + l32, 16 * kg + 8 * lg))), gt);
                 const double cs_t = T.cs[32 * Tb + l32];
                 const double cs_r = T.cs[32 * Sb + 31];
                 float m[16];
