@@ -150,7 +150,7 @@ int ssd_chunk_scan_fwd(int batch, int seqlen, int nheads, int headdim, int dstat
  *
  *  - A call whose workspace (ssd_chunk_scan_workspace_size) would exceed that
  *    size returns SSD_ERR_WORKSPACE before anything runs.  That covers every
- *    bf16 call up to the 64K-token, 80-head shape (80 MiB); float32 calls need
+ *    bf16 call up to the 64K-token, 80-head shape (30 MiB); float32 calls need
  *    their stages, about batch·seqlen·nheads·dstate·headdim·4/chunk bytes.
  *  - Every call on one GPU shares that GPU's array, which keeps the last call's
  *    contents.  Calls that overlap in time on one GPU (other streams, other
