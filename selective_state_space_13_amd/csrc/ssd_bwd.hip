@@ -83,7 +83,10 @@ __device__ __forceinline__ void adjoint_walk(const BwdArgs &a, unsigned blk, uns
     const size_t row0 = (size_t)b * a.seqlen;
     const float Ah = a.A[h];
 
-    const bool owns = wave < (N / 32) * 2;
+    // every wave owns a tile at dstate 128: no branch (under one, the compiler's count of
+    // outstanding memory operations takes the path without the stores, and the
+    // wait for the next chunk's loads then waits for the stores as well)
+    const bool owns = N == 128 || wave < (N / 32) * 2;
     const int snt = wave >> 1, spt = wave & 1;
     f32x16 st = {};
     if (owns && a.dfinal) {
