@@ -364,6 +364,9 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
         float dt;
     } R0;
     auto prefetch = [&](int h) {
+        // Δ first: the scan of the next head uses it in the second product phase,
+        // and loads complete in issue order, so it waits for nothing else
+        R0.dt = __uint_as_float((uint32_t)a.dt[(row0 + min(lane, lim)) * a.nheads + h] << 16);
         const int srow = tid >> 3, scol = (tid & 7) * 8;
         R0.x = ld16(a.x + (row0 + min(srow, lim)) * xstride + (size_t)h * P + scol);
         R0.y = ld16(a.dy + (row0 + min(srow, lim)) * xstride + (size_t)h * P + scol);
@@ -373,7 +376,6 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
             R0.g[2 * k] = go[(tid + k * kThreads) * 2];
             R0.g[2 * k + 1] = go[(tid + k * kThreads) * 2 + 1];
         }
-        R0.dt = __uint_as_float((uint32_t)a.dt[(row0 + min(lane, lim)) * a.nheads + h] << 16);
     };
     // per-token values of head hh (its Δ in R0.dt) into buffer tb (one wave)
     auto scan_head = [&](float Ahh, int tb) {
@@ -443,7 +445,7 @@ __global__ __launch_bounds__(kThreads, 1) void ssd_bwd_chunk_kernel(BwdArgs a) {
         // (half of it; the other half before the x·G_out products, within the
         // registers the kernel has)
         float4 hreg[P / 16][2];
-        const bool owns_bc_h = wave < 2 * NT;
+        const bool owns_bc_h = N == 128 || wave < 2 * NT;
         const float *hinp = a.hst + bhc * N * P + (size_t)(32 * (wave % NT) + l32) * P + 8 * lg;
         auto load_h = [&](int ks) {
             hreg[ks][0] = owns_bc_h ? *reinterpret_cast<const float4 *>(hinp + 16 * ks) : make_float4(0, 0, 0, 0);
