@@ -12,9 +12,10 @@
 // u, delta, z and out access of the wave is one contiguous 128-byte (bf16)
 // segment.  A batch x channels grid alone gives well under one wave per SIMD,
 // so the sequence is cut into segments scanned in parallel: a state-only pass
-// (MODE 0) gives each segment's end state from a zero start and its Σ Δ, a
-// small combine chains them into each segment's incoming state, and the
-// output pass (MODE 1) runs every segment from that state.  The recurrence is
+// (MODE 0, every segment but the last) gives each segment's end state from a
+// zero start and its Σ Δ, a small combine chains them into each segment's
+// incoming state, and the output pass (MODE 1) runs every segment from that
+// state.  The recurrence is
 // linear in the state, so this is the same computation regrouped.
 // Time is processed in tiles of kT steps: while a tile is computed, the next
 // tile's u/delta/z are already in flight into a second set of registers.
@@ -281,7 +282,9 @@ template <typename T, int N>
 hipError_t launch_n(int phase, const ScanArgs &sa, const void *u, const void *delta, const float *A,
                     const void *B, const void *C, const float *D, const void *z, int batch,
                     void *out, float *final_state, hipStream_t stream) {
-    const dim3 grid((unsigned)((sa.dim + 255) / 256), (unsigned)batch, (unsigned)sa.nseg);
+    // the state pass covers segments 0 .. S-2: the combine chains only their end states
+    const dim3 grid((unsigned)((sa.dim + 255) / 256), (unsigned)batch,
+                    (unsigned)(phase == 0 ? sa.nseg - 1 : sa.nseg));
     const T *up = static_cast<const T *>(u), *dp = static_cast<const T *>(delta);
     const T *Bp = static_cast<const T *>(B), *Cp = static_cast<const T *>(C), *zp = static_cast<const T *>(z);
     if (phase == 0) {

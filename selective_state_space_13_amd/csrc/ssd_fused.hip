@@ -31,7 +31,8 @@
 //
 // Long sequences with few (batch, head) pairs are cut into S segments that
 // run in parallel.  A state-only pass (ssd_state_kernel, ssd_fused_walk.h)
-// gives each segment's end state from a zero start and its total log-decay;
+// gives each segment's end state from a zero start and its total log-decay
+// (all segments but the last, whose end state is the full pass's final state);
 // a small combine kernel chains them into each segment's incoming state; the
 // full pass then starts segment s from that state.  The recurrence is linear
 // in the state, so this is the same computation regrouped.
@@ -191,6 +192,8 @@ hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const
         a.seg_state = reinterpret_cast<float *>(ws);
         a.hin = reinterpret_cast<const float *>(ws + pl.state_bytes);
         a.seg_decay = reinterpret_cast<double *>(ws + 2 * pl.state_bytes);
+        // the combine chains the end states of segments 0 .. S-2 only
+        if (phase == 0) items = (unsigned)((long long)batch * nheads * (pl.nseg - 1));
     } else if (pl.tail_from >= 0) {
         // phase 0: the state at the cut of every tail pair; phase 2: whole pairs and halves
         if (phase == 1) return hipErrorInvalidValue;
