@@ -55,6 +55,8 @@ METRIC = "SSD prefill tokens/s and decode tokens/s at 2.7B-layer shape; % MFMA/H
 # segment-state pass and the segment combine before it
 FUSED_KERNELS = ["ssd_fused"]
 SEGMENTED_KERNELS = ["segment_states", "segment_combine", "ssd_fused"]
+# with a short segment 0 run whole beside the state walks of segments 1 .. S-2
+LEAD_KERNELS = ["lead_segment_and_states", "segment_combine", "ssd_fused"]
 # when only the last round of (batch, head) pairs is cut in halves: the state at the cut first
 CUT_KERNELS = ["cut_states", "ssd_fused"]
 # the sources of each kernel family: counter records in profiles/ apply while they match
@@ -289,9 +291,9 @@ def bench_prefill(cfg, steps, warmup, seed=0):
     y = torch.empty(x.shape, dtype=dt.dtype, device="cuda")  # bf16 beside float8 inputs
     fs = torch.empty(cfg["batch"], cfg["nheads"], cfg["dstate"], cfg["headdim"], device="cuda") \
         if cfg.get("final_state") else None
-    launches, _, cut_pairs = ssd.chunk_scan_plan(cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["headdim"],
+    launches, _, cut_pairs, lead = ssd.chunk_scan_plan(cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["headdim"],
                                          cfg["dstate"], cfg["ngroups"], cfg["chunk"], code)
-    names = {3: SEGMENTED_KERNELS, 2: CUT_KERNELS}.get(launches, FUSED_KERNELS)
+    names = {3: LEAD_KERNELS if lead else SEGMENTED_KERNELS, 2: CUT_KERNELS}.get(launches, FUSED_KERNELS)
 
     def step():
         ssd.ssd_chunk_scan(x, dt, A, B, C, D, chunk=cfg["chunk"], workspace=ws, out=y,
@@ -447,7 +449,7 @@ def bench_backward(cfg, steps, warmup, seed=0):
                      dtype=torch.uint8, device="cuda")
     nchunks = (L + 63) // 64
     # the forward state pass is cut into segments exactly when the forward's is
-    _, nseg, _ = ssd.chunk_scan_plan(b, L, H, P, N, G, cfg["chunk"], ssd.SSD_BF16)
+    _, nseg, _, _ = ssd.chunk_scan_plan(b, L, H, P, N, G, cfg["chunk"], ssd.SSD_BF16)
     names = BWD_SEGMENTED if nseg > 1 else BWD_KERNELS
 
     def step():

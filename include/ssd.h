@@ -150,7 +150,7 @@ int ssd_chunk_scan_fwd(int batch, int seqlen, int nheads, int headdim, int dstat
  *
  *  - A call whose workspace (ssd_chunk_scan_workspace_size) would exceed that
  *    size returns SSD_ERR_WORKSPACE before anything runs.  That covers every
- *    bf16 call up to the 64K-token, 80-head shape (30 MiB); float32 calls need
+ *    bf16 call up to the 64K-token, 80-head shape (35 MiB); float32 calls need
  *    their stages, about batch·seqlen·nheads·dstate·headdim·4/chunk bytes.
  *  - Every call on one GPU shares that GPU's array, which keeps the last call's
  *    contents.  Calls that overlap in time on one GPU (other streams, other
@@ -180,10 +180,14 @@ size_t ssd_noalloc_scratch_bytes(void);
  * a state pass that computes the state at the cut; 3 when every sequence is
  * cut into *segments parallel segments, with a state pass and a combine;
  * float32: 4 stages; 1 for an empty sequence's state copy).  *cut_pairs =
- * pairs cut in halves.  Any pointer may be NULL.  Same validation and return
- * codes as ssd_chunk_scan_workspace_size's shape checks. */
+ * pairs cut in halves.  *lead_chunks = the 64-token chunks of segment 0 when it
+ * is shorter than the rest and runs whole, outputs included, in the state
+ * pass's launch (the full pass then covers segments 1 .. S-1), else 0.  Any
+ * pointer may be NULL.  Same validation and return codes as
+ * ssd_chunk_scan_workspace_size's shape checks. */
 int ssd_chunk_scan_plan(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
-                        int chunk, int dtype, int *launches, int *segments, int *cut_pairs);
+                        int chunk, int dtype, int *launches, int *segments, int *cut_pairs,
+                        int *lead_chunks);
 
 int ssd_chunk_scan_workspace_layout(int batch, int seqlen, int nheads, int headdim, int dstate,
                                     int ngroups, int chunk, int dtype, size_t *off_delta,

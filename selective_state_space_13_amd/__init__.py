@@ -61,7 +61,7 @@ def lib() -> ctypes.CDLL:
     L.ssd_chunk_scan_workspace_size.restype = sz
     L.ssd_chunk_scan_workspace_layout.argtypes = [i] * 8 + [ctypes.POINTER(sz)] * 3
     L.ssd_chunk_scan_workspace_layout.restype = i
-    L.ssd_chunk_scan_plan.argtypes = [i] * 8 + [ctypes.POINTER(i)] * 3
+    L.ssd_chunk_scan_plan.argtypes = [i] * 8 + [ctypes.POINTER(i)] * 4
     L.ssd_chunk_scan_plan.restype = i
     L.ssd_chunk_scan_fwd.argtypes = [i] * 9 + [vp] * 10 + [sz, vp]
     L.ssd_chunk_scan_fwd.restype = i
@@ -183,8 +183,9 @@ def chunk_scan_workspace_layout(batch, seqlen, nheads, headdim, dstate, ngroups,
 # ---------------------------------------------------------------- functions
 
 def chunk_scan_plan(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype):
-    """(launches per call, segments, pairs cut in halves) of ssd_chunk_scan_fwd."""
-    v = [ctypes.c_int(), ctypes.c_int(), ctypes.c_int()]
+    """(launches per call, segments, pairs cut in halves, chunks of a lead
+    segment 0 or 0) of ssd_chunk_scan_fwd."""
+    v = [ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()]
     check(lib().ssd_chunk_scan_plan(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype,
                                     *[ctypes.byref(t) for t in v]))
     return tuple(t.value for t in v)

@@ -359,14 +359,16 @@ size_t ssd_chunk_scan_workspace_size(int batch, int seqlen, int nheads, int head
 }
 
 int ssd_chunk_scan_plan(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
-                        int chunk, int dtype, int *launches, int *segments, int *cut_pairs) {
+                        int chunk, int dtype, int *launches, int *segments, int *cut_pairs,
+                        int *lead_chunks) {
     strip_out_flag(dtype);
     ScanLayout lay;
     int st = scan_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, lay);
     if (st) return st;
-    int nl = 4, ns = 1, nc = 0;  // float32: cumsum, chunk states, state passing, outputs
+    int nl = 4, ns = 1, nc = 0, nlead = 0;  // float32: cumsum, chunk states, state passing, outputs
     if (prefill_fused(dtype)) {
         ns = lay.plan.nseg;
+        nlead = lay.plan.lead;
         nc = lay.plan.tail_from >= 0 ? batch * nheads - lay.plan.tail_from : 0;
         nl = ns > 1 ? 3 : nc > 0 ? 2 : 1;
     }
@@ -374,6 +376,7 @@ int ssd_chunk_scan_plan(int batch, int seqlen, int nheads, int headdim, int dsta
     if (launches) *launches = nl;
     if (segments) *segments = ns;
     if (cut_pairs) *cut_pairs = nc;
+    if (lead_chunks) *lead_chunks = nl == 3 ? nlead : 0;
     return SSD_OK;
 }
 

@@ -708,7 +708,7 @@ __global__ __launch_bounds__(64) void bwd_reduce_kernel(const float *__restrict_
 
 BwdPlan bwd_plan(int batch, int seqlen, int nheads, int dstate) {
     BwdPlan pl;
-    pl.fwd = fused_plan(batch, seqlen, nheads, dstate);
+    pl.fwd = fused_plan(batch, seqlen, nheads, dstate, false);  // uniform segments for the walks
     const size_t bhc = (size_t)batch * nheads * pl.fwd.nchunks;
     const size_t st = bhc * dstate * P * sizeof(float);
     pl.states_bytes = (st + 255) / 256 * 256;

@@ -61,10 +61,21 @@ __global__ __launch_bounds__(kThreads, 4) void ssd_state_kernel(FusedArgs a) {
 
 // The full pass: states and outputs.  Two workgroups of 8 waves per CU: 4
 // waves per SIMD (at most 128 VGPRs), at most 80 KB of LDS each.  YF32:
-// float32 y; F8: float8 e4m3fn x, B and C.
+// float32 y; F8: float8 e4m3fn x, B and C.  With a lead segment, the launch
+// that runs it whole also holds the state-only walks of segments 1 .. S-2
+// (workgroups from state_from on), in the same LDS.
+template <int N>
+union FullSmem {
+    PairSmem<N> pair;
+    StateSmem<N> state;
+};
 template <int N, bool YF32, bool F8>
 __global__ __launch_bounds__(kThreads, 4) void ssd_prefill_kernel(FusedArgs a) {
-    fused_pair_walk<N, YF32, F8>(a, blockIdx.x, gridDim.x);
+    __shared__ __attribute__((aligned(16))) FullSmem<N> sm;
+    if (a.state_from > 0 && (int)blockIdx.x >= a.state_from)
+        state_walk<N, false, F8>(a, blockIdx.x - a.state_from, gridDim.x - a.state_from, sm.state, 1);
+    else
+        fused_pair_walk<N, YF32, F8>(a, blockIdx.x, gridDim.x, sm.pair);
 }
 
 template <bool YF32, bool F8>
@@ -84,18 +95,26 @@ void launch_state(int dstate, unsigned items, hipStream_t stream, const FusedArg
 }
 
 // State entering each segment s >= 1: H_s = exp(decay_{s-1})·H_{s-1} + E_{s-1},
-// H_0 = h0 (or 0).  One thread per state element of one (b, h).
+// H_0 = h0 (or 0).  With a lead segment, E_0 is already the true state at the
+// end of segment 0 (its walk started from h0): H_1 = E_0.  One thread per
+// state element of one (b, h).
 __global__ __launch_bounds__(256) void segment_combine_kernel(const float *__restrict__ h0,
                                                               const float *__restrict__ seg_state,
                                                               const double *__restrict__ seg_decay,
-                                                              float *__restrict__ hin, int nseg,
+                                                              float *__restrict__ hin, int nseg, int lead,
                                                               int NP, long long total) {
     const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= total) return;
     const long long bhi = i / NP;
     const int e = (int)(i % NP);
     float H = h0 ? h0[i] : 0.0f;
-    for (int s = 1; s < nseg; ++s) {
+    int s = 1;
+    if (lead) {
+        H = seg_state[(size_t)bhi * nseg * NP + e];
+        hin[((size_t)bhi * nseg + 1) * NP + e] = H;
+        s = 2;
+    }
+    for (; s < nseg; ++s) {
         const size_t prev = (size_t)bhi * nseg + (s - 1);
         H = __expf((float)seg_decay[prev]) * H + seg_state[prev * NP + e];
         hin[((size_t)bhi * nseg + s) * NP + e] = H;
@@ -107,13 +126,15 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(const float *__res
 // workgroups of the full pass the chip runs at once: two per CU
 constexpr long long kSlots = 512;
 
-FusedPlan fused_plan(int batch, int seqlen, int nheads, int dstate) {
+FusedPlan fused_plan(int batch, int seqlen, int nheads, int dstate, bool allow_lead) {
     FusedPlan pl;
     pl.nchunks = (seqlen + kC - 1) / kC;
     const long long bh = (long long)batch * nheads;
     // cost ~ rounds of the chip (256 CUs, two workgroups each) x chunks per
-    // segment; splitting adds a state-only pass (~0.4 of a full one)
-    int best = 1;
+    // segment; splitting adds a state-only pass (a chunk of it costs ~0.4 of a
+    // full one)
+    constexpr double kState = 0.4;
+    int best = 1, best_lead = 0, best_len = pl.nchunks;
     double best_cost = 0.0;
     // Only calls that leave slots empty are cut into segments (at most 16);
     // fuller ones cut their last round's pairs instead (below).
@@ -121,14 +142,39 @@ FusedPlan fused_plan(int batch, int seqlen, int nheads, int dstate) {
     for (int s = 1; s <= max_seg; ++s) {
         if (s > 1 && pl.nchunks / s < 8) break;
         const double rounds = (double)((bh * s + kSlots - 1) / kSlots);
-        const double cost = rounds * ((pl.nchunks + s - 1) / s) * (s > 1 ? 1.4 : 1.0);
+        const int len = (pl.nchunks + s - 1) / s;
+        const double cost = rounds * len * (s > 1 ? 1.0 + kState : 1.0);
         if (s == 1 || cost < best_cost) {
             best = s;
+            best_lead = 0;
+            best_len = len;
             best_cost = cost;
         }
+        // A lead segment: a short segment 0 runs whole beside the state-only
+        // walks of segments 1 .. s-2, in slots that pass leaves empty, and the
+        // full pass covers segments 1 .. s-1; both launches fit one round.  The
+        // lead is as long as the state walks take: lead ≈ kState·len.
+        if (allow_lead && s >= 3 && bh * (s - 1) <= kSlots) {
+            const int lead = max(1, (int)(kState * pl.nchunks / (s - 1 + kState) + 0.5));
+            const int len_l = (pl.nchunks - lead + s - 2) / (s - 1);
+            const int last = pl.nchunks - lead - (s - 2) * len_l;  // the last segment's chunks
+            const double cost_l = fmax((double)lead, kState * len_l) + len_l;
+            if (len_l >= 8 && last >= 1 && cost_l < best_cost) {
+                best = s;
+                best_lead = lead;
+                best_len = len_l;
+                best_cost = cost_l;
+            }
+        }
     }
-    pl.seg_chunks = pl.nchunks > 0 ? (pl.nchunks + best - 1) / best : 1;
-    pl.nseg = pl.nchunks > 0 ? (pl.nchunks + pl.seg_chunks - 1) / pl.seg_chunks : 1;  // none empty
+    pl.lead = best_lead;
+    if (best_lead > 0) {
+        pl.seg_chunks = best_len;
+        pl.nseg = best;
+    } else {
+        pl.seg_chunks = pl.nchunks > 0 ? (pl.nchunks + best - 1) / best : 1;
+        pl.nseg = pl.nchunks > 0 ? (pl.nchunks + pl.seg_chunks - 1) / pl.seg_chunks : 1;  // none empty
+    }
     pl.ws_bytes = 0;
     if (pl.nseg > 1) {
         const size_t st = (size_t)bh * pl.nseg * dstate * P * sizeof(float);
@@ -181,6 +227,9 @@ hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const
     a.nchunks = pl.nchunks;
     a.nseg = pl.nseg;
     a.seg_chunks = pl.seg_chunks;
+    a.lead = pl.lead;
+    a.seg_base = 0;
+    a.state_from = 0;
     a.npairs = batch * nheads;
     a.tail_from = pl.tail_from;
     a.tail_mid = pl.tail_mid;
@@ -192,8 +241,18 @@ hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const
         a.seg_state = reinterpret_cast<float *>(ws);
         a.hin = reinterpret_cast<const float *>(ws + pl.state_bytes);
         a.seg_decay = reinterpret_cast<double *>(ws + 2 * pl.state_bytes);
-        // the combine chains the end states of segments 0 .. S-2 only
+        // the combine chains the end states of segments 0 .. S-2 only.  With a
+        // lead segment, the first launch runs segment 0 whole (workgroups
+        // 0 .. npairs-1, outputs included) beside the state-only walks of
+        // segments 1 .. S-2, and the full pass covers segments 1 .. S-1.
         if (phase == 0) items = (unsigned)((long long)batch * nheads * (pl.nseg - 1));
+        if (pl.lead > 0) {
+            if (phase == 0) a.state_from = a.npairs;
+            if (phase == 2) {
+                a.seg_base = 1;
+                items = (unsigned)((long long)batch * nheads * (pl.nseg - 1));
+            }
+        }
     } else if (pl.tail_from >= 0) {
         // phase 0: the state at the cut of every tail pair; phase 2: whole pairs and halves
         if (phase == 1) return hipErrorInvalidValue;
@@ -204,7 +263,7 @@ hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const
     } else if (phase != 2) {
         return hipErrorInvalidValue;
     }
-    if (phase == 0) {
+    if (phase == 0 && a.state_from == 0) {
         if (in_f8)
             launch_state<true>(dstate, items, stream, a);
         else
@@ -212,7 +271,8 @@ hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const
     } else if (phase == 1) {
         const long long total = (long long)batch * nheads * dstate * P;
         segment_combine_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(
-            a.h0, a.seg_state, a.seg_decay, const_cast<float *>(a.hin), a.nseg, dstate * P, total);
+            a.h0, a.seg_state, a.seg_decay, const_cast<float *>(a.hin), a.nseg, pl.lead > 0,
+            dstate * P, total);
     } else if (in_f8) {
         if (y_f32)
             launch_prefill<true, true>(dstate, items, stream, a);

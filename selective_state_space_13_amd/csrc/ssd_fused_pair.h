@@ -79,7 +79,7 @@ __device__ __forceinline__ float causal_diag(int r, float m, float D) {
 }
 
 template <int N, bool YF32, bool F8>
-__device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk, unsigned nblk) {
+__device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk, unsigned nblk, PairSmem<N> &sm) {
     typedef typename InStore<F8>::elem E;
     constexpr int NT = N / 16;      // state tiles of a state wave
     constexpr int KS = N / 32;      // k-steps over n of C·H
@@ -88,7 +88,6 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
     constexpr int GV = N / 32;      // B (and C) vectors per staging lane
     constexpr int BSTEP = 256 / BPR;
     constexpr int kScanRole = 3;    // staging wave 7
-    __shared__ __attribute__((aligned(16))) PairSmem<N> sm;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: role values stay scalar
@@ -98,7 +97,7 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
     const bool state_wave = wave < 4;
     const int role = wave & 3;      // state wave index (its 16 columns), or staging role
 
-    const WalkItem item = map_walk_item<false>(a, blk, nblk, reinterpret_cast<int *>(&sm.mt[0][0][0][0]));
+    const WalkItem item = map_walk_item<false>(a, blk, nblk, reinterpret_cast<int *>(&sm.mt[0][0][0][0]), a.seg_base);
     // the work item is the same for every lane; saying so keeps it (and every
     // address base derived from it) in scalar registers
     const auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
@@ -354,9 +353,13 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
             }
             __syncthreads();
         }
-        // ---- end of the walk
-        if (a.final_state && half != 0 && seg == a.nseg - 1) {
-            float *dst = a.final_state + bh * N * P;
+        // ---- end of the walk: the final state, or a lead segment's end state
+        float *dst = nullptr;
+        if (a.final_state && half != 0 && seg == a.nseg - 1)
+            dst = a.final_state + bh * N * P;
+        else if (a.lead > 0 && seg == 0)
+            dst = a.seg_state + bh * a.nseg * N * P;
+        if (dst) {
             // offsets from an opaque copy of the lane index, formed here: kept
             // from before the loop, they would be spilled around it
             int ln = lane;

@@ -93,6 +93,13 @@ struct FusedArgs {
     int nchunks;          // 64-token chunks over the sequence
     int seg_chunks;       // chunks per segment
     int nseg;             // S
+    // lead > 0: segment 0 covers chunks [0, lead) and segment s >= 1 starts at
+    // lead + (s - 1)·seg_chunks; segment 0 then runs whole in the launch of the
+    // state-only walks (its workgroups first), writing its outputs and its end
+    // state (a true state, from h0) to seg_state slot 0
+    int lead;
+    int seg_base;         // segment of the full pass's first items (1 when segment 0 ran with the state pass)
+    int state_from;       // full-pass launch: workgroups from this one on walk segments >= 1 state-only (0: none)
     // state-only pass: when set, the state entering every chunk c is stored at
     // chunk_states[(b·H + h)·nchunks + c] ([N][P] float) and segment s >= 1
     // starts from hin (the true incoming state) instead of zero
@@ -120,8 +127,10 @@ struct WalkItem {
     size_t row0;                   // rows row0 .. row0 + seqlen - 1 of the [rows][...] inputs
     int seqlen, c0, c1;
 };
+// seg_base: the segment of items 0 .. npairs - 1 (uniform segments, no cut)
 template <bool STATE_ONLY>
-__device__ __forceinline__ WalkItem map_walk_item(const FusedArgs &a, unsigned blk, unsigned nblk, int *scratch) {
+__device__ __forceinline__ WalkItem map_walk_item(const FusedArgs &a, unsigned blk, unsigned nblk, int *scratch,
+                                                  int seg_base = 0) {
     const int R = a.nheads / a.ngroups;
     int b = 0, g = 0, h = 0, seg = 0;
     bool ranked = false;
@@ -165,7 +174,7 @@ __device__ __forceinline__ WalkItem map_walk_item(const FusedArgs &a, unsigned b
             if (STATE_ONLY) part = k / ntail;
         } else {
             pair = (int)blk % a.npairs;
-            seg = (int)blk / a.npairs;
+            seg = seg_base + (int)blk / a.npairs;
         }
         const int nbg = a.npairs / R;
         const int bg = pair % nbg, r = pair / nbg;
@@ -184,6 +193,10 @@ __device__ __forceinline__ WalkItem map_walk_item(const FusedArgs &a, unsigned b
         nchunks = (seqlen + kC - 1) / kC;
     }
     int c0 = seg * a.seg_chunks, c1 = min(c0 + a.seg_chunks, nchunks);
+    if (a.lead > 0) {  // a short segment 0, then segments of seg_chunks
+        c0 = seg == 0 ? 0 : a.lead + (seg - 1) * a.seg_chunks;
+        c1 = min(seg == 0 ? a.lead : c0 + a.seg_chunks, nchunks);
+    }
     if (half >= 0) {
         c0 = half ? a.tail_mid : 0;
         c1 = half ? nchunks : min(a.tail_mid, nchunks);
@@ -224,7 +237,8 @@ struct StateSmem {
 // first half of a cut pair, or, for the backward, the state entering every
 // chunk (kStoreStates; a.chunk_states must then be set).
 template <int N, bool kStoreStates, bool F8 = false>
-__device__ __forceinline__ void state_walk(const FusedArgs &a, unsigned blk, unsigned nblk, StateSmem<N> &sm) {
+__device__ __forceinline__ void state_walk(const FusedArgs &a, unsigned blk, unsigned nblk, StateSmem<N> &sm,
+                                           int seg_base = 0) {
     typedef typename InStore<F8>::elem E;
     constexpr int BV = N / 64;        // 16-byte vectors of B per lane
     constexpr int BPR = N / 8;        // 16-byte vectors per B row
@@ -234,7 +248,7 @@ __device__ __forceinline__ void state_walk(const FusedArgs &a, unsigned blk, uns
     const int l32 = lane & 31, lg = lane >> 5;
     const int rrow = tr_row(lane), rcol = tr_col(lane);
 
-    const WalkItem item = map_walk_item<true>(a, blk, nblk, nullptr);
+    const WalkItem item = map_walk_item<true>(a, blk, nblk, nullptr, seg_base);
     const int b = item.b, g = item.g, h = item.h, seg = item.seg, pair = item.pair, half = item.half;
     const size_t row0 = item.row0;
     const int seqlen = item.seqlen, c0 = item.c0, c1 = item.c1;

@@ -117,11 +117,16 @@ hipError_t launch_chunk_output_valu(int dtype, const void *x, const void *B, con
 // only phase 2 runs and no workspace is used.
 struct FusedPlan {
     int nchunks = 0, nseg = 1, seg_chunks = 1;
+    // lead > 0: segment 0 is this many chunks and runs whole (outputs included)
+    // in the state pass's launch; segments s >= 1 start at lead + (s - 1)·seg_chunks
+    int lead = 0;
     int tail_from = -1, tail_mid = 0;  // pairs from tail_from on are cut at chunk tail_mid
     int tail_parts = 1;                // the state pass splits each first half into this many parts
     size_t state_bytes = 0, ws_bytes = 0;
 };
-FusedPlan fused_plan(int batch, int seqlen, int nheads, int dstate);
+// allow_lead: whether the plan may run segment 0 beside the state pass (the
+// forward only; the backward's walks take uniform segments)
+FusedPlan fused_plan(int batch, int seqlen, int nheads, int dstate, bool allow_lead = true);
 hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const void *dt,
                             const float *A, const void *B, const void *C, const float *D,
                             const float *h0, int dt_softplus, int batch, int seqlen, int nheads,

@@ -281,7 +281,7 @@ def bwd_call(L, b=2, Lq=300, H=8, P=64, N=128, G=2, dtype=BF16, ptrs=None, ws_by
 
 
 def _plan(L, *args):
-    v = [ctypes.c_int(), ctypes.c_int(), ctypes.c_int()]
+    v = [ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()]
     st = L.ssd_chunk_scan_plan(*args, *[ctypes.byref(t) for t in v])
     return st, tuple(t.value for t in v)
 
@@ -289,13 +289,17 @@ def _plan(L, *args):
 def test_chunk_scan_plan(L):
     # 640 pairs on 512 slots (two workgroups per CU): one full round, the last
     # 128 pairs cut in halves
-    assert _plan(L, 8, 2048, 80, 64, 128, 1, 256, BF16) == (OK, (2, 1, 128))
-    # 80 pairs of 64K tokens: 6 segments fill one round
-    assert _plan(L, 1, 65536, 80, 64, 128, 8, 256, BF16) == (OK, (3, 6, 0))
+    assert _plan(L, 8, 2048, 80, 64, 128, 1, 256, BF16) == (OK, (2, 1, 128, 0))
+    # 80 pairs of 64K tokens (1024 chunks): a lead segment of 64 chunks runs
+    # beside the state walks of segments 1-5 (480 workgroups), then segments
+    # 1-6 of 160 chunks (480 workgroups)
+    assert _plan(L, 1, 65536, 80, 64, 128, 8, 256, BF16) == (OK, (3, 7, 0, 64))
+    # few pairs: 16 uniform segments of 16 chunks (the cap), no lead
+    assert _plan(L, 1, 16384, 8, 64, 64, 1, 256, BF16) == (OK, (3, 16, 0, 0))
     # two full rounds: nothing to cut
-    assert _plan(L, 8, 2048, 128, 64, 128, 1, 256, BF16) == (OK, (1, 1, 0))
+    assert _plan(L, 8, 2048, 128, 64, 128, 1, 256, BF16) == (OK, (1, 1, 0, 0))
     # float32: four stages
-    assert _plan(L, 1, 512, 8, 64, 64, 1, 64, F32) == (OK, (4, 1, 0))
+    assert _plan(L, 1, 512, 8, 64, 64, 1, 64, F32) == (OK, (4, 1, 0, 0))
     assert _plan(L, 1, 512, 8, 64, 96, 1, 64, BF16)[0] == UNSUP
     # the cut pairs' state lives in the workspace
     assert L.ssd_chunk_scan_workspace_size(8, 2048, 80, 64, 128, 1, 256, BF16) >= 128 * 128 * 64 * 4

@@ -126,10 +126,14 @@ def test_stages_delta_and_cumsum_from_workspace():
 SEGMENTED_CASES = [
     # b, L, H, N, G, with_D, with_h0: few (batch, head) pairs and long sequences,
     # which the bf16 path cuts into segments scanned in parallel
-    (1, 4096, 2, 128, 1, True, True),
+    (1, 4096, 2, 128, 1, True, True),     # 8 segments of 8 chunks
     (2, 3000, 3, 64, 3, False, True),     # ragged last chunk
     (1, 8192, 1, 128, 1, True, False),
-    (1, 16384, 64, 128, 2, True, True),  # 4 segments of 64 chunks, 64 heads
+    # a lead segment 0 of 12 chunks run whole beside the state walks of
+    # segments 1-7, then segments 1-8 (31 chunks, the last 27)
+    (1, 16384, 64, 128, 2, True, True),
+    # a lead of 4 chunks, segments of 10, ragged last chunk, dstate 64, 4 groups
+    (2, 4000, 40, 64, 4, True, True),
 ]
 
 
@@ -138,6 +142,8 @@ def test_prefill_segmented_bf16(case):
     b, L, H, N, G, wD, wh = case
     # more than the 256-byte minimum: the call plans several segments
     assert ssd.chunk_scan_workspace_size(b, L, H, 64, N, G, 256, ssd.SSD_BF16) > 256
+    launches, nseg, _, lead = ssd.chunk_scan_plan(b, L, H, 64, N, G, 256, ssd.SSD_BF16)
+    assert launches == 3 and nseg > 1 and (lead > 0) == (b * H >= 64)
     d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=L + N, config_id=102, with_h0=wh)
     y, fs = run_scan(d, 256, "bf16", wD, wh)
     yo, fo = oracle_scan(d, wD, wh)
@@ -155,7 +161,7 @@ def test_prefill_tail_cut(case):
     parts that it chains: 2 parts of 5 and 4 chunks, 2 of 4, and 4 parts of 5,
     5, 5 and 2 chunks."""
     b, L, H, N, G, wD, wh = case
-    launches, nseg, cut = ssd.chunk_scan_plan(b, L, H, 64, N, G, 256, ssd.SSD_BF16)
+    launches, nseg, cut, _ = ssd.chunk_scan_plan(b, L, H, 64, N, G, 256, ssd.SSD_BF16)
     assert launches == 2 and nseg == 1 and cut == b * H - 512
     d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=L + H, config_id=104, with_h0=wh)
     y, fs = run_scan(d, 256, "bf16", wD, wh)
@@ -193,9 +199,9 @@ def as_bf16_inputs(d):
 
 @pytest.mark.parametrize("case", [(2, 700, 6, 128, 2, True, True), (1, 16384, 8, 64, 1, False, True),
                                   (3, 1100, 200, 128, 4, True, False), (1, 1, 4, 64, 1, True, True),
-                                  (4, 130, 16, 64, 4, False, False)],
+                                  (4, 130, 16, 64, 4, False, False), (2, 3900, 40, 128, 2, True, True)],
                          ids=["b2L700ragged", "b1L16384segmented", "b3L1100H200tailcut", "b1L1",
-                              "b4L130N64G4"])
+                              "b4L130N64G4", "b2L3900H40lead"])
 def test_prefill_fp8(case):
     """float8 e4m3fn x, B, C (bf16 dt) through each kind of plan: the bf16 bar
     against the oracle on the bytes' values, and bit for bit the result of the
@@ -404,15 +410,20 @@ def test_prefill_segmented_extreme_decay_no_final_state():
     assert_parity(to_f64(y), yo, TAU_BF16, True, "segmented extreme y")
 
 
-def test_prefill_segmented_initial_state_weak_decay():
+@pytest.mark.parametrize("H,lead", [(64, True), (8, False)], ids=["H64lead", "H8uniform"])
+def test_prefill_segmented_initial_state_weak_decay(H, lead):
     """Segments and an initial state that survives the whole sequence (A close to
     zero, so exp(Σ Δ·A) over a segment stays near 1): the state pass, the combine
     and the full pass must count h0 exactly once.  With the decays of the other
-    cases, h0 has vanished by the end of the first segment."""
-    b, L, H, N, G = 1, 16384, 64, 64, 1  # 4 segments of 64 chunks, 64 heads
+    cases, h0 has vanished by the end of the first segment.  64 heads: a lead
+    segment of 12 chunks (from h0, its end state seeding the combine), then 8
+    of 31; 8 heads: 16 uniform segments (every state walk from zero, the
+    combine adding h0)."""
+    b, L, N, G = 1, 16384, 64, 1
     d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=14, config_id=108, with_h0=True)
     d["A"] = gen.Tensor(-np.exp(np.random.default_rng(14).uniform(np.log(1e-3), np.log(3e-2), H)).astype(np.float32), "f32")
-    assert ssd.chunk_scan_plan(b, L, H, 64, N, G, 256, ssd.SSD_BF16)[1] > 1
+    plan = ssd.chunk_scan_plan(b, L, H, 64, N, G, 256, ssd.SSD_BF16)
+    assert plan[1] > 1 and (plan[3] > 0) == lead
     y, fs = run_scan(d, 256, "bf16", True, True)
     yo, fo = oracle_scan(d, True, True)
     assert_parity(to_f64(y), yo, TAU_BF16, True, "segmented weak decay y")
