@@ -134,6 +134,9 @@ FusedPlan fused_plan(int batch, int seqlen, int nheads, int dstate, bool allow_l
     // segment; splitting adds a state-only pass (a chunk of it costs ~0.4 of a
     // full one)
     constexpr double kState = 0.4;
+    // beside a lead segment's full walks, a state-walk chunk costs more (2.05
+    // against 4.29 µs for a full chunk, at the 64K-token shape)
+    constexpr double kStateLead = 0.48;
     int best = 1, best_lead = 0, best_len = pl.nchunks;
     double best_cost = 0.0;
     // Only calls that leave slots empty are cut into segments (at most 16);
@@ -153,12 +156,12 @@ FusedPlan fused_plan(int batch, int seqlen, int nheads, int dstate, bool allow_l
         // A lead segment: a short segment 0 runs whole beside the state-only
         // walks of segments 1 .. s-2, in slots that pass leaves empty, and the
         // full pass covers segments 1 .. s-1; both launches fit one round.  The
-        // lead is as long as the state walks take: lead ≈ kState·len.
+        // lead is as long as the state walks take: lead ≈ kStateLead·len.
         if (allow_lead && s >= 3 && bh * (s - 1) <= kSlots) {
-            const int lead = max(1, (int)(kState * pl.nchunks / (s - 1 + kState) + 0.5));
+            const int lead = max(1, (int)(kStateLead * pl.nchunks / (s - 1 + kStateLead) + 0.5));
             const int len_l = (pl.nchunks - lead + s - 2) / (s - 1);
             const int last = pl.nchunks - lead - (s - 2) * len_l;  // the last segment's chunks
-            const double cost_l = fmax((double)lead, kState * len_l) + len_l;
+            const double cost_l = fmax((double)lead, kStateLead * len_l) + len_l;
             if (len_l >= 8 && last >= 1 && cost_l < best_cost) {
                 best = s;
                 best_lead = lead;

@@ -290,10 +290,12 @@ def test_chunk_scan_plan(L):
     # 640 pairs on 512 slots (two workgroups per CU): one full round, the last
     # 128 pairs cut in halves
     assert _plan(L, 8, 2048, 80, 64, 128, 1, 256, BF16) == (OK, (2, 1, 128, 0))
-    # 80 pairs of 64K tokens (1024 chunks): a lead segment of 64 chunks runs
+    # 80 pairs of 64K tokens (1024 chunks): a lead segment of 76 chunks runs
     # beside the state walks of segments 1-5 (480 workgroups), then segments
-    # 1-6 of 160 chunks (480 workgroups)
-    assert _plan(L, 1, 65536, 80, 64, 128, 8, 256, BF16) == (OK, (3, 7, 0, 64))
+    # 1-6 of 158 chunks (the last 158; 480 workgroups)
+    assert _plan(L, 1, 65536, 80, 64, 128, 8, 256, BF16) == (OK, (3, 7, 0, 76))
+    # 64 pairs of 16K tokens: 8 uniform segments of 32 chunks fill the slots
+    assert _plan(L, 1, 16384, 64, 64, 128, 2, 256, BF16) == (OK, (3, 8, 0, 0))
     # few pairs: 16 uniform segments of 16 chunks (the cap), no lead
     assert _plan(L, 1, 16384, 8, 64, 64, 1, 256, BF16) == (OK, (3, 16, 0, 0))
     # two full rounds: nothing to cut

@@ -129,12 +129,14 @@ SEGMENTED_CASES = [
     (1, 4096, 2, 128, 1, True, True),     # 8 segments of 8 chunks
     (2, 3000, 3, 64, 3, False, True),     # ragged last chunk
     (1, 8192, 1, 128, 1, True, False),
-    # a lead segment 0 of 12 chunks run whole beside the state walks of
-    # segments 1-7, then segments 1-8 (31 chunks, the last 27)
-    (1, 16384, 64, 128, 2, True, True),
-    # a lead of 4 chunks, segments of 10, ragged last chunk, dstate 64, 4 groups
+    (1, 16384, 64, 128, 2, True, True),   # 8 segments of 32 chunks, 64 heads
+    # a lead segment 0 of 9 chunks run whole beside the state walks of
+    # segments 1-5, then segments 1-6 of 20 chunks (the last 19)
+    (1, 8192, 80, 128, 2, True, True),
+    # a lead of 5 chunks, segments of 10, ragged last chunk, dstate 64, 4 groups
     (2, 4000, 40, 64, 4, True, True),
 ]
+LEAD_CASES = {(1, 8192, 80), (2, 4000, 40)}
 
 
 @pytest.mark.parametrize("case", SEGMENTED_CASES, ids=lambda c: "b{}L{}H{}N{}G{}".format(*c[:5]))
@@ -143,7 +145,7 @@ def test_prefill_segmented_bf16(case):
     # more than the 256-byte minimum: the call plans several segments
     assert ssd.chunk_scan_workspace_size(b, L, H, 64, N, G, 256, ssd.SSD_BF16) > 256
     launches, nseg, _, lead = ssd.chunk_scan_plan(b, L, H, 64, N, G, 256, ssd.SSD_BF16)
-    assert launches == 3 and nseg > 1 and (lead > 0) == (b * H >= 64)
+    assert launches == 3 and nseg > 1 and (lead > 0) == ((b, L, H) in LEAD_CASES)
     d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=L + N, config_id=102, with_h0=wh)
     y, fs = run_scan(d, 256, "bf16", wD, wh)
     yo, fo = oracle_scan(d, wD, wh)
@@ -410,16 +412,17 @@ def test_prefill_segmented_extreme_decay_no_final_state():
     assert_parity(to_f64(y), yo, TAU_BF16, True, "segmented extreme y")
 
 
-@pytest.mark.parametrize("H,lead", [(64, True), (8, False)], ids=["H64lead", "H8uniform"])
-def test_prefill_segmented_initial_state_weak_decay(H, lead):
+@pytest.mark.parametrize("L,H,lead", [(8192, 80, True), (16384, 64, False), (16384, 8, False)],
+                         ids=["H80lead", "H64uniform", "H8uniform"])
+def test_prefill_segmented_initial_state_weak_decay(L, H, lead):
     """Segments and an initial state that survives the whole sequence (A close to
     zero, so exp(Σ Δ·A) over a segment stays near 1): the state pass, the combine
     and the full pass must count h0 exactly once.  With the decays of the other
-    cases, h0 has vanished by the end of the first segment.  64 heads: a lead
-    segment of 12 chunks (from h0, its end state seeding the combine), then 8
-    of 31; 8 heads: 16 uniform segments (every state walk from zero, the
-    combine adding h0)."""
-    b, L, N, G = 1, 16384, 64, 1
+    cases, h0 has vanished by the end of the first segment.  80 heads: a lead
+    segment of 9 chunks (from h0, its end state seeding the combine), then 6
+    of 20; 64 and 8 heads: 8 and 16 uniform segments (every state walk from
+    zero, the combine adding h0)."""
+    b, N, G = 1, 64, 1
     d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=14, config_id=108, with_h0=True)
     d["A"] = gen.Tensor(-np.exp(np.random.default_rng(14).uniform(np.log(1e-3), np.log(3e-2), H)).astype(np.float32), "f32")
     plan = ssd.chunk_scan_plan(b, L, H, 64, N, G, 256, ssd.SSD_BF16)
