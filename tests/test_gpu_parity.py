@@ -135,8 +135,10 @@ SEGMENTED_CASES = [
     (1, 8192, 80, 128, 2, True, True),
     # a lead of 5 chunks, segments of 10, ragged last chunk, dstate 64, 4 groups
     (2, 4000, 40, 64, 4, True, True),
+    # a lead of 7 chunks, no D and no initial state (segment 0 from zero)
+    (1, 6000, 80, 64, 1, False, False),
 ]
-LEAD_CASES = {(1, 8192, 80), (2, 4000, 40)}
+LEAD_CASES = {(1, 8192, 80), (2, 4000, 40), (1, 6000, 80)}
 
 
 @pytest.mark.parametrize("case", SEGMENTED_CASES, ids=lambda c: "b{}L{}H{}N{}G{}".format(*c[:5]))
