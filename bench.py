@@ -57,8 +57,6 @@ FUSED_KERNELS = ["ssd_fused"]
 SEGMENTED_KERNELS = ["segment_states", "segment_combine", "ssd_fused"]
 # with a short segment 0 run whole beside the state walks of segments 1 .. S-2
 LEAD_KERNELS = ["lead_segment_and_states", "segment_combine", "ssd_fused"]
-# when only the last round of (batch, head) pairs is cut in halves: the state at the cut first
-CUT_KERNELS = ["cut_states", "ssd_fused"]
 # the sources of each kernel family: counter records in profiles/ apply while they match
 _C = "selective_state_space_13_amd/csrc/"
 FUSED_SOURCES = [_C + f for f in ("ssd_fused.hip", "ssd_fused_pair.h", "ssd_fused_walk.h", "mfma_tile.h",
@@ -243,7 +241,7 @@ def counter_rates(kernel_ms, workload, sources):
     return out or None
 
 
-def prefill_work(c, cut_pairs=0):
+def prefill_work(c):
     """Algorithmic bytes and flops of a prefill call (inputs read once, outputs
     written once; causal flops of the block decomposition at the workload's
     chunk size)."""
@@ -265,14 +263,12 @@ def prefill_work(c, cut_pairs=0):
     total = dict(bytes=x_bytes + y_bytes + 2 * bc_bytes + dt_bytes + final,
                  flops=units_h * (4 * Q * N * P + Q * (Q + 1) * P) + units_g * Q * (Q + 1) * N,
                  flops_q64=flops_q64)
-    # the fused kernel does all of it; the segment passes re-read x, B and dt
-    # a cut of the last round's pairs re-reads the first halves of those pairs
-    cut = cut_pairs / (b * H) * 0.5
+    # the fused kernel does all of it (a cut last round included: its halves
+    # hand the state at the cut over within the launch); the segment passes
+    # re-read x, B and dt
     return {"ssd_fused": total, "total": total,
             "segment_states": dict(bytes=x_bytes + bc_bytes + dt_bytes, flops=units_h * 2 * Q * N * P),
-            "segment_combine": dict(bytes=0, flops=0),
-            "cut_states": dict(bytes=int(cut * (x_bytes + dt_bytes) + 0.5 * bc_bytes),
-                               flops=int(cut * units_h * 2 * Q * N * P))}
+            "segment_combine": dict(bytes=0, flops=0)}
 
 
 def bench_prefill(cfg, steps, warmup, seed=0):
@@ -291,9 +287,9 @@ def bench_prefill(cfg, steps, warmup, seed=0):
     y = torch.empty(x.shape, dtype=dt.dtype, device="cuda")  # bf16 beside float8 inputs
     fs = torch.empty(cfg["batch"], cfg["nheads"], cfg["dstate"], cfg["headdim"], device="cuda") \
         if cfg.get("final_state") else None
-    launches, _, cut_pairs, lead = ssd.chunk_scan_plan(cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["headdim"],
+    launches, _, _, lead = ssd.chunk_scan_plan(cfg["batch"], cfg["seqlen"], cfg["nheads"], cfg["headdim"],
                                          cfg["dstate"], cfg["ngroups"], cfg["chunk"], code)
-    names = {3: LEAD_KERNELS if lead else SEGMENTED_KERNELS, 2: CUT_KERNELS}.get(launches, FUSED_KERNELS)
+    names = {3: LEAD_KERNELS if lead else SEGMENTED_KERNELS}.get(launches, FUSED_KERNELS)
 
     def step():
         ssd.ssd_chunk_scan(x, dt, A, B, C, D, chunk=cfg["chunk"], workspace=ws, out=y,
@@ -303,7 +299,7 @@ def bench_prefill(cfg, steps, warmup, seed=0):
     ms, per, b2b = time_calls(step, len(names), steps, warmup)
     tokens = cfg["batch"] * cfg["seqlen"]
     return dict(ms=ms, b2b_ms=b2b, per_kernel_ms=dict(zip(names, per)), tokens=tokens,
-                work=prefill_work(cfg, cut_pairs), final_state=fs, y=y)
+                work=prefill_work(cfg), final_state=fs, y=y)
 
 
 def measured_mfma_flops(kernel, workload, digest):

@@ -45,7 +45,8 @@
  *  - Return value: 0 (SSD_OK) or a negative ssd_status; ssd_last_error()
  *    gives a thread-local detail string for the last non-OK return.
  *  - Reentrant and thread-safe.  The mutable state is per thread: the last
- *    error string, and the event array of ssd_set_launch_events while set.
+ *    error string, and the event array of ssd_set_launch_events while set;
+ *    plus one process-wide test setting (ssd_set_cut_wait_polls).
  *  - Decay sign.  The method's regime is A < 0 (decay; A = 0 holds the state).
  *    A > 0 (growth) is computed by the same formulas and matches the float64
  *    recurrence as long as every true intermediate stays in float32 range;
@@ -121,8 +122,10 @@ const char *ssd_last_error(void);
  *   final_state   [batch][nheads][dstate][headdim] float or NULL, written
  *   workspace     >= ssd_chunk_scan_workspace_size(...) bytes, 256-byte aligned
  *                 (SSD_BF16, SSD_FP8: 256 bytes, unused, unless the call is
- *                 segmented or its last round of pairs is cut;
- *                 SSD_F32: the stages below)
+ *                 segmented (segment states) or its last round of pairs is
+ *                 cut (the states at the cut and one flag per cut pair);
+ *                 SSD_F32: the stages below).  Calls in flight at the same
+ *                 time need workspaces of their own.
  *
  * Supported: headdim == 64; dstate in {64, 128}; chunk in {64, 128, 256};
  * ngroups >= 1 dividing nheads; nheads*headdim and ngroups*dstate at most 2^25;
@@ -175,16 +178,16 @@ size_t ssd_noalloc_scratch_bytes(void);
  * Returns SSD_OK, SSD_ERR_UNSUPPORTED for SSD_BF16 (whose stages stay on chip),
  * or the status ssd_chunk_scan_fwd would return for the sizes. */
 /* How ssd_chunk_scan_fwd will run a call of this shape (host query, no GPU
- * work): *launches = kernel launches per call (bf16: 1 for the fused pass
- * alone; 2 when the last round of (batch, head) pairs is cut in halves, after
- * a state pass that computes the state at the cut; 3 when every sequence is
- * cut into *segments parallel segments, with a state pass and a combine;
- * float32: 4 stages; 1 for an empty sequence's state copy).  *cut_pairs =
- * pairs cut in halves.  *lead_chunks = the 64-token chunks of segment 0 when it
- * is shorter than the rest and runs whole, outputs included, in the state
- * pass's launch (the full pass then covers segments 1 .. S-1), else 0.  Any
- * pointer may be NULL.  Same validation and return codes as
- * ssd_chunk_scan_workspace_size's shape checks. */
+ * work): *launches = kernel launches per call (bf16: 1 for the fused pass,
+ * also when the last round of (batch, head) pairs is cut in halves, the first
+ * halves handing the state at the cut to the second halves within the launch;
+ * 3 when every sequence is cut into *segments parallel segments, with a state
+ * pass and a combine; float32: 4 stages; 1 for an empty sequence's state
+ * copy).  *cut_pairs = pairs cut in halves.  *lead_chunks = the 64-token
+ * chunks of segment 0 when it is shorter than the rest and runs whole,
+ * outputs included, in the state pass's launch (the full pass then covers
+ * segments 1 .. S-1), else 0.  Any pointer may be NULL.  Same validation and
+ * return codes as ssd_chunk_scan_workspace_size's shape checks. */
 int ssd_chunk_scan_plan(int batch, int seqlen, int nheads, int headdim, int dstate, int ngroups,
                         int chunk, int dtype, int *launches, int *segments, int *cut_pairs,
                         int *lead_chunks);
@@ -369,6 +372,19 @@ int selective_scan_fwd(int batch, int seqlen, int dim, int dstate, int dtype, in
  * Returns SSD_OK, or SSD_ERR_SHAPE for a negative count.
  * ------------------------------------------------------------------------ */
 int ssd_set_launch_events(void *const *events, int count);
+
+/* ------------------------------------------------------------------------
+ * Test hook for the cut of a last round (ssd_chunk_scan_plan's cut_pairs).
+ * The second half of a cut pair waits for the state that its first half, run
+ * earlier in the same launch, publishes at the cut; the wait is bounded (by
+ * default 2^18 polls, a fraction of a second), and past the bound it walks
+ * the first half's chunks itself, their outputs dropped, so the result is the
+ * same bit for bit.  This sets the bound for later calls in the process
+ * (polls < 0 restores the default; 0 sends every second half down that walk,
+ * which is how tests check it).  Process-wide, so not for use while other
+ * threads enqueue prefill calls.  Returns the previous bound.
+ * ------------------------------------------------------------------------ */
+int ssd_set_cut_wait_polls(int polls);
 
 #ifdef __cplusplus
 }

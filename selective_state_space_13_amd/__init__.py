@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
     L.ssd_chunk_scan_fwd_noalloc.argtypes = [i] * 9 + [vp] * 10
     L.ssd_chunk_scan_fwd_noalloc.restype = i
     L.ssd_noalloc_scratch_bytes.restype = sz
+    L.ssd_set_cut_wait_polls.argtypes = [i]
+    L.ssd_set_cut_wait_polls.restype = i
     L.ssd_chunk_scan_bwd_workspace_size.argtypes = [i] * 7
     L.ssd_chunk_scan_bwd_workspace_size.restype = sz
     L.ssd_chunk_scan_bwd.argtypes = [i] * 8 + [vp] * 17 + [sz, vp]
@@ -181,6 +183,13 @@ def chunk_scan_workspace_layout(batch, seqlen, nheads, headdim, dstate, ngroups,
 
 
 # ---------------------------------------------------------------- functions
+
+def set_cut_wait_polls(polls):
+    """Bound of the wait of a cut pair's second half for its first half's state
+    (ssd_set_cut_wait_polls; a test hook: 0 forces the fallback walk, < 0
+    restores the default).  Returns the previous bound."""
+    return lib().ssd_set_cut_wait_polls(int(polls))
+
 
 def chunk_scan_plan(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype):
     """(launches per call, segments, pairs cut in halves, chunks of a lead

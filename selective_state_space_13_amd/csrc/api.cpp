@@ -280,9 +280,9 @@ int chunk_scan_fwd(int batch, int seqlen, int nheads, int headdim, int dstate, i
     if (prefill_fused(dtype)) {
         static const char *what[3] = {"state pass launch", "segment combine launch",
                                       "fused prefill launch"};
-        const bool cut = lay.plan.nseg > 1 || lay.plan.tail_from >= 0;
-        for (int phase = cut ? 0 : 2; phase < 3; ++phase) {
-            if (phase == 1 && lay.plan.nseg <= 1) continue;  // a tail cut needs no combine
+        // segments: the state pass (with a lead segment), the combine, the full
+        // pass; otherwise the full pass alone (a cut last round included)
+        for (int phase = lay.plan.nseg > 1 ? 0 : 2; phase < 3; ++phase) {
             marks.before();
             e = ssd::launch_ssd_fused(phase, lay.plan, x, dt, A, B, C, D, initial_state, dt_softplus,
                                       batch, seqlen, nheads, headdim, dstate, ngroups, y,
@@ -370,7 +370,7 @@ int ssd_chunk_scan_plan(int batch, int seqlen, int nheads, int headdim, int dsta
         ns = lay.plan.nseg;
         nlead = lay.plan.lead;
         nc = lay.plan.tail_from >= 0 ? batch * nheads - lay.plan.tail_from : 0;
-        nl = ns > 1 ? 3 : nc > 0 ? 2 : 1;
+        nl = ns > 1 ? 3 : 1;
     }
     if (batch == 0 || seqlen == 0) nl = seqlen == 0 && batch > 0 ? 1 : 0;
     if (launches) *launches = nl;
@@ -417,6 +417,8 @@ int ssd_chunk_scan_fwd_noalloc(int batch, int seqlen, int nheads, int headdim, i
 }
 
 size_t ssd_noalloc_scratch_bytes(void) { return ssd::kScratchBytes; }
+
+int ssd_set_cut_wait_polls(int polls) { return ssd::set_cut_wait_polls(polls); }
 
 size_t ssd_chunk_scan_bwd_workspace_size(int batch, int seqlen, int nheads, int headdim, int dstate,
                                          int ngroups, int dtype) {

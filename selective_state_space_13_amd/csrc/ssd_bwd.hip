@@ -777,7 +777,6 @@ hipError_t launch_ssd_bwd(int phase, const BwdPlan &pl, const void *x, const voi
         f.chunk_states = hst;
         f.npairs = batch * nheads;
         f.tail_from = -1;
-        f.tail_parts = 1;
         if (pl.fwd.nseg > 1) f.hin = reinterpret_cast<const float *>(ws + pl.fwd.state_bytes);
         const unsigned nfwd = (unsigned)((long long)batch * nheads * pl.fwd.nseg);
         const unsigned items = nfwd + (unsigned)((long long)batch * nheads);

@@ -45,12 +45,16 @@
 // exp of a difference of nearby cs values keeps float32 accuracy.  The decay
 // mask of a 32-token diagonal block is factorised, or taken exactly when the
 // block's own log-change exceeds kMaxBlockDecay in either direction.
+#include <atomic>
+#include <chrono>
+#include <random>
+
 #include "ssd_fused_pair.h"
 
 namespace ssd {
 namespace {
 
-// The state-only pass (segment end states, states at the cut of a pair).
+// The state-only pass (segment end states).
 // F8: x, B and C stored as float8 e4m3fn (decoded to bf16 at the staging).
 template <int N, bool F8>
 // two workgroups of 8 waves per CU: 4 waves per SIMD (at most 128 VGPRs)
@@ -126,6 +130,28 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(const float *__res
 // workgroups of the full pass the chip runs at once: two per CU
 constexpr long long kSlots = 512;
 
+// A value for the flags of one call's cut pairs: distinct from call to call and
+// never 0 (a cleared flag), from a per-process random start, so that a flag
+// left over in a reused workspace, or the workspace's initial contents, match
+// it only by a 2^-64 chance.
+static std::atomic<int> g_cut_wait_polls{kTailSpin};
+int set_cut_wait_polls(int polls) { return g_cut_wait_polls.exchange(polls < 0 ? kTailSpin : polls); }
+
+static unsigned long long next_token() {
+    static std::atomic<unsigned long long> count{0};
+    static const unsigned long long base = [] {
+        std::random_device rd;
+        return ((unsigned long long)rd() << 32) ^ rd() ^
+               (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+    }();
+    // splitmix64 of the call counter
+    unsigned long long z = base + (count.fetch_add(1) + 1) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return z ? z : 1;
+}
+
 FusedPlan fused_plan(int batch, int seqlen, int nheads, int dstate, bool allow_lead) {
     FusedPlan pl;
     pl.nchunks = (seqlen + kC - 1) / kC;
@@ -186,20 +212,16 @@ FusedPlan fused_plan(int batch, int seqlen, int nheads, int dstate, bool allow_l
     } else {
         // Whole pairs in rounds of kSlots workgroups: when the last round is at
         // most half full, its pairs are cut in two halves, so that it takes about
-        // half the time.  The second halves start from the state at the cut, which
-        // a state-only pass over the first halves computes beforehand.
+        // half the time.  The first halves run first, in the first round beside
+        // whole pairs, and hand the state at the cut to the second halves, which
+        // come last in the same launch (flags in the workspace, one per pair).
         const long long rounds = (bh + kSlots - 1) / kSlots;
         const long long rem = bh - kSlots * (rounds - 1);
         if (rounds >= 2 && rem <= kSlots / 2 && pl.nchunks >= 16) {
             pl.tail_from = (int)(bh - rem);
             pl.tail_mid = pl.nchunks / 2;
-            // the state pass over the first halves is as long as its parts: up to
-            // 4 parts of at least 4 chunks, within one round of two workgroups per CU
-            int parts = 1;
-            while (parts < 4 && rem * parts * 2 <= 512 && pl.tail_mid / (parts * 2) >= 4) parts *= 2;  // at most 4: the fused pass chains up to 4
-            pl.tail_parts = parts;
-            pl.state_bytes = ((size_t)rem * parts * dstate * P * sizeof(float) + 255) / 256 * 256;
-            pl.ws_bytes = pl.state_bytes + ((size_t)rem * parts * sizeof(double) + 255) / 256 * 256;
+            pl.state_bytes = ((size_t)rem * dstate * P * sizeof(float) + 255) / 256 * 256;
+            pl.ws_bytes = pl.state_bytes + ((size_t)rem * sizeof(unsigned long long) + 255) / 256 * 256;
         }
     }
     return pl;
@@ -236,8 +258,6 @@ hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const
     a.npairs = batch * nheads;
     a.tail_from = pl.tail_from;
     a.tail_mid = pl.tail_mid;
-    a.tail_parts = pl.tail_parts;
-    a.tail_decay = nullptr;
     unsigned items = (unsigned)((long long)batch * nheads * pl.nseg);
     if (pl.nseg > 1) {
         char *ws = static_cast<char *>(workspace);
@@ -257,12 +277,14 @@ hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const
             }
         }
     } else if (pl.tail_from >= 0) {
-        // phase 0: the state at the cut of every tail pair; phase 2: whole pairs and halves
-        if (phase == 1) return hipErrorInvalidValue;
+        // one launch: the first halves, the whole pairs, the second halves
+        if (phase != 2) return hipErrorInvalidValue;
         a.tail_state = static_cast<float *>(workspace);
-        a.tail_decay = reinterpret_cast<double *>(static_cast<char *>(workspace) + pl.state_bytes);
+        a.tail_flag = reinterpret_cast<unsigned long long *>(static_cast<char *>(workspace) + pl.state_bytes);
+        a.token = next_token();
+        a.tail_polls = g_cut_wait_polls.load();
         const unsigned ntail = (unsigned)(a.npairs - pl.tail_from);
-        items = phase == 0 ? ntail * (unsigned)pl.tail_parts : (unsigned)pl.tail_from + 2 * ntail;
+        items = (unsigned)pl.tail_from + 2 * ntail;
     } else if (phase != 2) {
         return hipErrorInvalidValue;
     }
@@ -318,9 +340,8 @@ hipError_t launch_ssd_fused_varlen(const int *cu_seqlens, int nseq, int total_to
     a.seg_chunks = a.nchunks + 1;
     a.npairs = nseq * nheads;
     a.tail_from = -1;
-    a.tail_parts = 1;
     a.tail_state = nullptr;
-    a.tail_decay = nullptr;
+    a.tail_flag = nullptr;
     const unsigned items = (unsigned)((long long)nseq * nheads);
     launch_prefill<false, false>(dstate, items, stream, a);
     return hipGetLastError();

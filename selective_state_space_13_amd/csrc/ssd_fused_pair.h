@@ -104,7 +104,28 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
     const int b = uni(item.b), g = uni(item.g), h = uni(item.h), seg = uni(item.seg), pair = uni(item.pair),
               half = uni(item.half);
     const size_t row0 = ((size_t)(uint32_t)uni((int)(item.row0 >> 32)) << 32) | (uint32_t)uni((int)item.row0);
-    const int seqlen = uni(item.seqlen), c0 = uni(item.c0), c1 = uni(item.c1);
+    const int seqlen = uni(item.seqlen), c1 = uni(item.c1);
+    // The second half of a cut pair waits for the state its first half publishes
+    // at the cut (the first halves are the launch's lowest workgroups, so they are
+    // running or done by now).  The wait is bounded: past the bound this
+    // workgroup walks the first half as well, its outputs there dropped.
+    int redo = 0;
+    if (half == 1) {
+        int *ok_lds = reinterpret_cast<int *>(&sm.mt[2][1][31][3]);  // not yet in use
+        if (tid == 0) {
+            unsigned long long *flag = a.tail_flag + (pair - a.tail_from);
+            int ok = 0;
+            for (int n = 0; n < a.tail_polls && !ok; ++n) {
+                ok = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.token;
+                if (!ok) __builtin_amdgcn_s_sleep(2);
+            }
+            *ok_lds = ok;
+        }
+        __syncthreads();
+        redo = uni(*ok_lds == 0);
+    }
+    const int c0 = redo ? 0 : uni(item.c0);
+    const int y_from = redo ? uni(item.c0) : 0;  // chunks before it store no outputs
     const float Ah = a.A[h];
     const float Dh = a.D ? a.D[h] : 0.0f;
     const size_t bh = (size_t)b * a.nheads + h;
@@ -192,46 +213,28 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
         f32x4 st[NT];
         {
             const float *src = nullptr;
-            if (half == 1) {
-                src = nullptr;  // the parts' chain below
+            if (half == 1 && !redo) {
+                src = a.tail_state + (size_t)(pair - a.tail_from) * N * P;  // the state at the cut
             } else if (seg == 0) {
                 if (a.h0) src = a.h0 + bh * N * P;
             } else {
                 src = a.hin + (bh * a.nseg + seg) * N * P;
             }
+            // the state at the cut comes from another workgroup of this launch,
+            // maybe on another XCD: device-coherent loads (no cache maintenance
+            // that would cost the other workgroups their cached B and C)
+            if (half == 1 && !redo) {
 #pragma unroll
-            for (int i = 0; i < NT; ++i)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) st[i][r] = src ? src[pair_n(i, q, r) * P + pc] : 0.0f;
-            // the second half of a cut pair: the first half's parts chained,
-            // H = E_0, then H = d_k·H + E_k for k = 1 .. parts - 1, is the sum
-            // Σ_k (Π_{j > k} d_j)·E_k; each tile adds its terms with all their loads
-            // issued together (from clamped part indices, the extra weights zero)
-            if (half == 1) {
-                const size_t t0 = (size_t)(pair - a.tail_from) * a.tail_parts;
-                float coef[4];
-                coef[3] = 1.0f;
-#pragma unroll
-                for (int k = 3; k >= 1; --k) {
-                    const float dk = k < a.tail_parts ? __expf((float)a.tail_decay[t0 + k]) : 1.0f;
-                    coef[k - 1] = coef[k] * dk;
-                }
-                // coef[k] = Π_{j = k+1}^{parts-1} d_j for k < parts; parts past the last get 0
-#pragma unroll
-                for (int k = 0; k < 4; ++k) coef[k] = k < a.tail_parts ? coef[k] : 0.0f;
-#pragma unroll 2
-                for (int i = 0; i < NT; ++i) {
-                    float e[4][4];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const float *sk = a.tail_state + (t0 + min(k, a.tail_parts - 1)) * N * P;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) e[k][r] = sk[pair_n(i, q, r) * P + pc];
-                    }
+                for (int i = 0; i < NT; ++i)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        st[i][r] = coef[0] * e[0][r] + coef[1] * e[1][r] + coef[2] * e[2][r] + coef[3] * e[3][r];
-                }
+                        st[i][r] = __hip_atomic_load(const_cast<float *>(src) + pair_n(i, q, r) * P + pc,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+#pragma unroll
+                for (int i = 0; i < NT; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) st[i][r] = src ? src[pair_n(i, q, r) * P + pc] : 0.0f;
             }
             // vmcnt(0) once here: otherwise the first use of st inside the chunk loop
             // waits for every outstanding memory operation, the y stores included
@@ -335,11 +338,13 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
             // each, through a buffer resource from row 16τ of the chunk to the end of
             // the sequence (stores past it are dropped), at the lane's fixed offset
             const int t0 = c * kC;
+            // rows of y this chunk may write (none before y_from): one scalar select
+            const int yrows = __builtin_amdgcn_readfirstlane(c < y_from ? 0 : seqlen - t0);
             const char *yb = reinterpret_cast<const char *>(YF32 ? static_cast<void *>(a.yf) : static_cast<void *>(a.y)) +
                              ((row0 + t0) * a.nheads + h) * P * kYSize;
 #pragma unroll
             for (int tau = 0; tau < 4; ++tau) {
-                const auto yr = buf_rsrc(yb + (size_t)(16 * tau) * yrb, seqlen - t0 - 16 * tau, yrb);
+                const auto yr = buf_rsrc(yb + (size_t)(16 * tau) * yrb, yrows - 16 * tau, yrb);
                 if constexpr (YF32) {
                     typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
                     const u32x4 v = {__float_as_uint(y[tau][0]), __float_as_uint(y[tau][1]),
@@ -359,16 +364,27 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
             dst = a.final_state + bh * N * P;
         else if (a.lead > 0 && seg == 0)
             dst = a.seg_state + bh * a.nseg * N * P;
+        else if (half == 0)
+            dst = a.tail_state + (size_t)(pair - a.tail_from) * N * P;  // the state at the cut
         if (dst) {
             // offsets from an opaque copy of the lane index, formed here: kept
             // from before the loop, they would be spilled around it
             int ln = lane;
             asm volatile("" : "+v"(ln));
             const int qf = ln >> 4, pf = 16 * role + (ln & 15);
+            if (half == 0) {  // read by another workgroup of this launch: device-coherent stores
 #pragma unroll
-            for (int i = 0; i < NT; ++i)
+                for (int i = 0; i < NT; ++i)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) dst[pair_n(i, qf, r) * P + pf] = st[i][r];
+                    for (int r = 0; r < 4; ++r)
+                        __hip_atomic_store(dst + pair_n(i, qf, r) * P + pf, st[i][r], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+#pragma unroll
+                for (int i = 0; i < NT; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dst[pair_n(i, qf, r) * P + pf] = st[i][r];
+            }
         }
     } else {
         if (c0 < c1) {  // an empty sequence loads nothing and returns its initial state
@@ -455,7 +471,24 @@ __device__ __forceinline__ void fused_pair_walk(const FusedArgs &a, unsigned blk
             __syncthreads();
         }
     }
-
+    // The first half of a cut pair publishes the state at the cut; the second
+    // half clears its flag for the next call (its state was read at the start).
+    // The state and the flag go through device-coherent accesses of their own,
+    // so no fence writes back or invalidates a whole cache.
+    // One lane of wave 0 does it, the lane found afresh (mbcnt), so that no
+    // register holds the thread index through the walk.
+    if (half >= 0) {
+        const bool first = wave == 0 && __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) == 0;
+        unsigned long long *flag = a.tail_flag + (pair - a.tail_from);
+        if (half == 0) {
+            // every wave's state stores complete (vmcnt 0) before the flag is set
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (first) __hip_atomic_store(flag, a.token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (first) {
+            __hip_atomic_store(flag, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 }  // namespace

@@ -15,6 +15,10 @@ constexpr int P = 64;            // headdim
 constexpr int kC = 64;           // tokens per internal chunk
 constexpr int kThreads = 512;    // 8 waves
 constexpr float kMaxBlockDecay = 60.0f;  // above this, a diagonal block uses the exact mask
+// polls (each a device-coherent load and a sleep of ~128 cycles: a fraction of
+// a second in all) that the second half of a cut pair waits for its first
+// half's state before walking it itself (the default of FusedArgs::tail_polls)
+constexpr int kTailSpin = 1 << 18;
 constexpr int kMaxRankedSeq = 256;       // packed batches up to this many sequences run longest first
 
 // Storage of x, B and C: bf16, or float8 e4m3fn (F8; the OCP format: sign, 4
@@ -105,17 +109,21 @@ struct FusedArgs {
     // starts from hin (the true incoming state) instead of zero
     float *chunk_states;
     // pairs (b, h): items < npairs·nseg are (pair, segment); when tail_from >= 0
-    // the pairs from tail_from on are each cut at chunk tail_mid into two halves.
-    // The state-only pass (grid = (npairs - tail_from)·tail_parts) splits each
-    // first half into tail_parts parts of equal chunk counts (the last shorter)
-    // and writes part k's end state, from h0 for k = 0 and from zero otherwise,
-    // to tail_state[(pair - tail_from)·tail_parts + k] ([N][P] float) and its
-    // Σ Δ·A to tail_decay[same]; the second half starts from the parts chained:
-    // H = exp(Σ_k)·H + E_k for k = 1 .. tail_parts - 1, from H = E_0
+    // the ntail = npairs - tail_from pairs from tail_from on are each cut at
+    // chunk tail_mid into two halves, and the full pass takes its items in the
+    // order: the ntail first halves, the whole pairs 0 .. tail_from-1, the ntail
+    // second halves.  A first half (from h0) writes its end state to
+    // tail_state[pair - tail_from] ([N][P] float) and then sets tail_flag[same]
+    // to token; the second half waits for that value, starts from that state and
+    // clears the flag.  The first halves are the lowest workgroup indices, each
+    // among its XCD's first ones, so they are running (or done) before any
+    // second half starts.
     int npairs;
-    int tail_from, tail_mid, tail_parts;
+    int tail_from, tail_mid;
     float *tail_state;
-    double *tail_decay;
+    unsigned long long *tail_flag;
+    unsigned long long token;  // this call's value of a set flag (never 0)
+    int tail_polls;            // bound of the second half's wait (kTailSpin unless a test lowers it)
 };
 
 // The (batch row, head) pair, segment or half of a pair that workgroup blk of
@@ -123,7 +131,6 @@ struct FusedArgs {
 // ints, used by the longest-first ranking of packed batches (full pass only).
 struct WalkItem {
     int b, g, h, seg, pair, half;  // half: 0 / 1 for the two halves of a cut pair, -1 otherwise
-    int part;                      // part of a first half (state-only pass), else 0
     size_t row0;                   // rows row0 .. row0 + seqlen - 1 of the [rows][...] inputs
     int seqlen, c0, c1;
 };
@@ -161,17 +168,21 @@ __device__ __forceinline__ WalkItem map_walk_item(const FusedArgs &a, unsigned b
       }
     }
     int pair = 0, half = -1;  // half: 0 / 1 for the two halves of a cut pair, -1 otherwise
-    int part = 0;
     if (!ranked) {
         // pair q = (b, g) fastest, then the head within the group, so that all heads
         // of one B/C group run on the same XCD (workgroups are dealt to the 8 XCDs
         // round robin)
-        if (a.tail_from >= 0 && (STATE_ONLY || (int)blk >= a.tail_from)) {
-            const int ntail = a.npairs - a.tail_from;
-            const int k = STATE_ONLY ? (int)blk : (int)blk - a.tail_from;
-            pair = a.tail_from + k % ntail;
-            half = STATE_ONLY ? 0 : k / ntail;
-            if (STATE_ONLY) part = k / ntail;
+        if (!STATE_ONLY && a.tail_from >= 0) {
+            const int ntail = a.npairs - a.tail_from, k = (int)blk;
+            if (k < ntail) {
+                pair = a.tail_from + k;
+                half = 0;
+            } else if (k < ntail + a.tail_from) {
+                pair = k - ntail;
+            } else {
+                pair = a.tail_from + (k - ntail - a.tail_from);
+                half = 1;
+            }
         } else {
             pair = (int)blk % a.npairs;
             seg = seg_base + (int)blk / a.npairs;
@@ -200,14 +211,9 @@ __device__ __forceinline__ WalkItem map_walk_item(const FusedArgs &a, unsigned b
     if (half >= 0) {
         c0 = half ? a.tail_mid : 0;
         c1 = half ? nchunks : min(a.tail_mid, nchunks);
-        if (STATE_ONLY) {
-            const int len = (a.tail_mid + a.tail_parts - 1) / a.tail_parts;
-            c0 = min(part * len, c1);
-            c1 = min(c0 + len, c1);
-        }
     }
     WalkItem it;
-    it.b = b; it.g = g; it.h = h; it.seg = seg; it.pair = pair; it.half = half; it.part = part;
+    it.b = b; it.g = g; it.h = h; it.seg = seg; it.pair = pair; it.half = half;
     it.row0 = row0; it.seqlen = seqlen; it.c0 = c0; it.c1 = c1;
     return it;
 }
@@ -233,9 +239,9 @@ struct StateSmem {
 // then the tile update.  The staged tiles alternate between two buffers, so
 // the next chunk's staging never overwrites a tile that a slower wave may
 // still be reading, and the chunk needs no second barrier.
-// It writes the end state of a segment (and its total log-decay) or of the
-// first half of a cut pair, or, for the backward, the state entering every
-// chunk (kStoreStates; a.chunk_states must then be set).
+// It writes the end state of a segment (and its total log-decay), or, for the
+// backward, the state entering every chunk (kStoreStates; a.chunk_states must
+// then be set).
 template <int N, bool kStoreStates, bool F8 = false>
 __device__ __forceinline__ void state_walk(const FusedArgs &a, unsigned blk, unsigned nblk, StateSmem<N> &sm,
                                            int seg_base = 0) {
@@ -249,7 +255,7 @@ __device__ __forceinline__ void state_walk(const FusedArgs &a, unsigned blk, uns
     const int rrow = tr_row(lane), rcol = tr_col(lane);
 
     const WalkItem item = map_walk_item<true>(a, blk, nblk, nullptr, seg_base);
-    const int b = item.b, g = item.g, h = item.h, seg = item.seg, pair = item.pair, half = item.half;
+    const int b = item.b, g = item.g, h = item.h, seg = item.seg;
     const size_t row0 = item.row0;
     const int seqlen = item.seqlen, c0 = item.c0, c1 = item.c1;
     const float Ah = a.A[h];
@@ -261,14 +267,11 @@ __device__ __forceinline__ void state_walk(const FusedArgs &a, unsigned blk, uns
     f32x16 st;
     {
         const float *src = nullptr;
-        if (half == 0 && item.part > 0) {
-            src = nullptr;  // a later part of a first half starts from zero
-        } else if (seg == 0) {
+        if (seg == 0) {
             // the first segment starts from h0 where this walk yields true states
-            // (the backward's chunk states, the cut of a pair); the forward's
-            // segment pass starts it from zero, as every other segment, since
-            // the combine adds h0 itself
-            if (a.h0 && (kStoreStates || a.nseg == 1)) src = a.h0 + bh * N * P;
+            // (the backward's chunk states); the forward's segment pass starts it
+            // from zero, as every other segment, since the combine adds h0 itself
+            if (a.h0 && kStoreStates) src = a.h0 + bh * N * P;
         } else if (a.chunk_states) {
             src = a.hin + (bh * a.nseg + seg) * N * P;
         }
@@ -409,11 +412,7 @@ __device__ __forceinline__ void state_walk(const FusedArgs &a, unsigned blk, uns
 
     // ---- end of the walk
     float *dst = nullptr;
-    if (half == 0) {
-        const size_t slot = (size_t)(pair - a.tail_from) * a.tail_parts + item.part;
-        dst = a.tail_state + slot * N * P;
-        if (wave == kScanWave && lane == 0) a.tail_decay[slot] = seg_decay;
-    } else if (!a.chunk_states) {
+    if (!a.chunk_states) {
         dst = a.seg_state + (bh * a.nseg + seg) * N * P;
         if (wave == kScanWave && lane == 0) a.seg_decay[bh * a.nseg + seg] = seg_decay;
     }

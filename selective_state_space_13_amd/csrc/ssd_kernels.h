@@ -120,13 +120,17 @@ struct FusedPlan {
     // lead > 0: segment 0 is this many chunks and runs whole (outputs included)
     // in the state pass's launch; segments s >= 1 start at lead + (s - 1)·seg_chunks
     int lead = 0;
-    int tail_from = -1, tail_mid = 0;  // pairs from tail_from on are cut at chunk tail_mid
-    int tail_parts = 1;                // the state pass splits each first half into this many parts
+    // pairs from tail_from on are cut at chunk tail_mid; the first halves hand the
+    // state at the cut to the second halves in the same launch (workspace: the
+    // states, then one flag per cut pair)
+    int tail_from = -1, tail_mid = 0;
     size_t state_bytes = 0, ws_bytes = 0;
 };
 // allow_lead: whether the plan may run segment 0 beside the state pass (the
 // forward only; the backward's walks take uniform segments)
 FusedPlan fused_plan(int batch, int seqlen, int nheads, int dstate, bool allow_lead = true);
+// the bound of a cut pair's wait for its state (polls; < 0: the default); returns the previous
+int set_cut_wait_polls(int polls);
 hipError_t launch_ssd_fused(int phase, const FusedPlan &pl, const void *x, const void *dt,
                             const float *A, const void *B, const void *C, const float *D,
                             const float *h0, int dt_softplus, int batch, int seqlen, int nheads,

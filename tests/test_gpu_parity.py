@@ -160,13 +160,13 @@ def test_prefill_segmented_bf16(case):
                          ids=["b3L1100H200N128G4", "b10L1024H60N64G1", "b3L2200H180N128G4"])
 def test_prefill_tail_cut(case):
     """A full round of 512 (batch, head) pairs (two workgroups per CU) and a
-    short last round, whose pairs are cut in halves (the second half starting
-    from the state at the cut).  The state pass splits the first halves into
-    parts that it chains: 2 parts of 5 and 4 chunks, 2 of 4, and 4 parts of 5,
-    5, 5 and 2 chunks."""
+    short last round, whose pairs are cut in halves, all in one launch: the
+    first halves run first and publish the state at the cut, which the second
+    halves, last in the grid, start from (first halves of 9, 8 and 17 chunks;
+    3 x 200 = 600 pairs leave 88 cut, 10 x 60 leave 88, 3 x 180 leave 28)."""
     b, L, H, N, G, wD, wh = case
     launches, nseg, cut, _ = ssd.chunk_scan_plan(b, L, H, 64, N, G, 256, ssd.SSD_BF16)
-    assert launches == 2 and nseg == 1 and cut == b * H - 512
+    assert launches == 1 and nseg == 1 and cut == b * H - 512
     d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=L + H, config_id=104, with_h0=wh)
     y, fs = run_scan(d, 256, "bf16", wD, wh)
     yo, fo = oracle_scan(d, wD, wh)
@@ -435,10 +435,71 @@ def test_prefill_segmented_initial_state_weak_decay(L, H, lead):
     assert_parity(to_f64(fs), fo, TAU_BF16, False, "segmented weak decay final")
 
 
+def test_prefill_tail_cut_fallback_walk():
+    """The second half of a cut pair starts from the state its first half
+    publishes within the launch.  With the wait's bound set to 0 polls (the
+    library's test hook), every second half takes the fallback instead: it walks
+    the first half's chunks too, with their outputs dropped.  Both give the
+    same bits."""
+    b, L, H, N, G = 3, 1100, 200, 128, 4
+    d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=21, config_id=104, with_h0=True)
+    y1, f1 = run_scan(d, 256, "bf16", True, True)
+    prev = ssd.set_cut_wait_polls(0)
+    try:
+        y2, f2 = run_scan(d, 256, "bf16", True, True)
+    finally:
+        ssd.set_cut_wait_polls(prev)
+    assert prev > 0
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+def test_prefill_tail_cut_graph_replays():
+    """A call with a cut last round, captured in a graph and replayed: the value
+    of a set flag is fixed in the graph, so each second half must clear its flag
+    for the next replay.  New inputs are copied in before every replay, and an
+    eager call on the same inputs and the same workspace runs before it; every
+    replay matches it bit for bit, and takes well under the fallback wait."""
+    b, L, H, N, G = 3, 1100, 200, 128, 4
+    assert ssd.chunk_scan_plan(b, L, H, 64, N, G, 256, ssd.SSD_BF16)[2] > 0
+    d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=30, config_id=104)
+    x, dt, A, B, C, D = (to_dev(d[k]) for k in ("x", "dt", "A", "B", "C", "D"))
+    ws = torch.empty(ssd.chunk_scan_workspace_size(b, L, H, 64, N, G, 256, ssd.SSD_BF16),
+                     dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    fs = torch.empty(b, H, N, 64, device="cuda")
+
+    def call(out, fin):
+        ssd.ssd_chunk_scan(x, dt, A, B, C, D, chunk=256, workspace=ws, out=out,
+                           return_final_state=True, final_state=fin)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(y, fs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(y, fs)
+    y_ref, f_ref = torch.empty_like(y), torch.empty_like(fs)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for k in range(3):
+        dk = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=31 + k, config_id=104)
+        for t, name in ((x, "x"), (dt, "dt"), (B, "B"), (C, "C")):
+            t.copy_(to_dev(dk[name]))
+        call(y_ref, f_ref)
+        start.record()
+        g.replay()
+        end.record()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref) and torch.equal(fs, f_ref), f"replay {k}"
+        assert start.elapsed_time(end) < 50.0, f"replay {k} took {start.elapsed_time(end):.1f} ms"
+
+
 def test_prefill_tail_cut_initial_state_weak_decay():
     """The cut of the last round's pairs with an initial state that survives the
-    whole sequence: the first part of each first half starts from h0, the others
-    from zero, and the second half chains them; h0 must be counted once."""
+    whole sequence: each first half starts from h0 and hands its end state to
+    the second half; h0 must be counted once."""
     b, L, H, N, G = 3, 2200, 180, 128, 4
     assert ssd.chunk_scan_plan(b, L, H, 64, N, G, 256, ssd.SSD_BF16)[2] > 0
     d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=15, config_id=109, with_h0=True)
