@@ -156,8 +156,10 @@ int ssd_chunk_scan_fwd(int batch, int seqlen, int nheads, int headdim, int dstat
  *    bf16 call up to the 64K-token, 80-head shape (35 MiB); float32 calls need
  *    their stages, about batch·seqlen·nheads·dstate·headdim·4/chunk bytes.
  *  - Every call on one GPU shares that GPU's array, which keeps the last call's
- *    contents.  Calls that overlap in time on one GPU (other streams, other
- *    host threads) race on it: the caller serialises them.
+ *    contents (none of which a later call trusts: the flags of a cut last
+ *    round must carry the new call's token).  Calls that overlap in time on
+ *    one GPU (other streams, other host threads) race on it: the caller
+ *    serialises them.
  *  - The scratch address of a device is looked up on the first call made with
  *    that device current (SSD_ERR_HIP if the lookup fails).
  * ------------------------------------------------------------------------ */

@@ -10,8 +10,10 @@
 //
 // Every call on one GPU shares that GPU's array and finds the previous call's
 // contents in it.  Nothing here needs zeroing: each use writes every scratch
-// value it later reads.  Calls that overlap in time on one GPU (two streams, or
-// two host threads) race on the array.
+// value it later reads, except the flags of a cut last round, which a wait
+// accepts only at the call's own 64-bit token and which the reading workgroup
+// clears.  Calls that overlap in time on one GPU (two streams, or two host
+// threads) race on the array.
 #include <mutex>
 
 #include "ssd_kernels.h"
