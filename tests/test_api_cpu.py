@@ -516,3 +516,14 @@ def test_fp8_spans_are_one_byte_for_x_b_c(L):
     n_dt = b * Lq * H
     assert scan_call(L, dtype=FP8, ptrs={"fs": fake(2, n_dt)}) == ALIAS
     assert scan_call(L, dtype=FP8, ptrs={"fs": fake(2, 2 * n_dt)}) != ALIAS
+
+
+def test_cut_wait_polls_hook(L):
+    # the bound of a cut pair's wait is process-wide host state: set, returned,
+    # and restored by a negative value (no GPU work)
+    default = L.ssd_set_cut_wait_polls(-1)
+    assert default > 0
+    assert L.ssd_set_cut_wait_polls(0) == default
+    assert L.ssd_set_cut_wait_polls(7) == 0
+    assert L.ssd_set_cut_wait_polls(-5) == 7
+    assert L.ssd_set_cut_wait_polls(-1) == default
