@@ -496,6 +496,38 @@ def test_prefill_tail_cut_graph_replays():
         assert start.elapsed_time(end) < 50.0, f"replay {k} took {start.elapsed_time(end):.1f} ms"
 
 
+def test_prefill_tail_cut_two_streams():
+    """Two calls with a cut last round in flight at once, on two streams with
+    workspaces of their own: each call's flags carry its own token, and each
+    launch dispatches its first halves before its second halves, so the
+    results equal those of the same calls run alone, bit for bit."""
+    b, L, H, N, G = 3, 1100, 200, 128, 4
+    ins, ref = [], []
+    for k in range(2):
+        d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=40 + k, config_id=104)
+        x, dt, A, B, C, D = (to_dev(d[n]) for n in ("x", "dt", "A", "B", "C", "D"))
+        ws = torch.empty(ssd.chunk_scan_workspace_size(b, L, H, 64, N, G, 256, ssd.SSD_BF16),
+                         dtype=torch.uint8, device="cuda")
+        ins.append((x, dt, A, B, C, D, ws))
+        y, fs = ssd.ssd_chunk_scan(x, dt, A, B, C, D, chunk=256, workspace=ws, return_final_state=True)
+        torch.cuda.synchronize()
+        ref.append((y, fs))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for k in range(2):
+        streams[k].wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        outs = []
+        for k in range(2):
+            x, dt, A, B, C, D, ws = ins[k]
+            with torch.cuda.stream(streams[k]):
+                outs.append(ssd.ssd_chunk_scan(x, dt, A, B, C, D, chunk=256, workspace=ws,
+                                               return_final_state=True))
+        torch.cuda.synchronize()
+        for k in range(2):
+            assert torch.equal(outs[k][0], ref[k][0]) and torch.equal(outs[k][1], ref[k][1]), (rep, k)
+
+
 def test_prefill_tail_cut_initial_state_weak_decay():
     """The cut of the last round's pairs with an initial state that survives the
     whole sequence: each first half starts from h0 and hands its end state to
