@@ -35,7 +35,11 @@
 // (all segments but the last, whose end state is the full pass's final state);
 // a small combine kernel chains them into each segment's incoming state; the
 // full pass then starts segment s from that state.  The recurrence is linear
-// in the state, so this is the same computation regrouped.
+// in the state, so this is the same computation regrouped.  Calls whose last
+// round of pairs would run less than half full cut those pairs in halves
+// instead, within the one launch: the first halves run first and hand the
+// state at the cut to the second halves, which come last (fused_plan,
+// FusedArgs::tail_flag).
 //
 // Precision: every bf16 operand the kernel computes (w·x, the masked C·Bᵀ
 // values, the state) is split into a bf16 head and tail (value - head, exact
