@@ -304,6 +304,15 @@ def test_chunk_scan_plan(L):
     assert _plan(L, 1, 512, 8, 64, 96, 1, 64, BF16)[0] == UNSUP
     # the cut pairs' state lives in the workspace
     assert L.ssd_chunk_scan_workspace_size(8, 2048, 80, 64, 128, 1, 256, BF16) >= 128 * 128 * 64 * 4
+    # the cut's boundaries: a last round of exactly half the 512 slots is cut,
+    # one pair more is not; a third round's remainder is cut; sequences of
+    # fewer than 16 chunks are not (the workspace then stays at 256 bytes)
+    assert _plan(L, 6, 2048, 128, 64, 128, 1, 256, BF16) == (OK, (1, 1, 256, 0))
+    assert _plan(L, 1, 2048, 769, 64, 128, 1, 256, BF16) == (OK, (1, 1, 0, 0))
+    assert _plan(L, 11, 2048, 100, 64, 128, 1, 256, BF16) == (OK, (1, 1, 76, 0))
+    assert _plan(L, 8, 960, 80, 64, 128, 1, 256, BF16) == (OK, (1, 1, 0, 0))
+    assert L.ssd_chunk_scan_workspace_size(8, 960, 80, 64, 128, 1, 256, BF16) == 256
+    assert L.ssd_chunk_scan_workspace_size(6, 2048, 128, 64, 128, 1, 256, BF16) == 256 * 128 * 64 * 4 + 256 * 8
 
 
 def test_bwd_workspace_size(L):
