@@ -156,17 +156,21 @@ def test_prefill_segmented_bf16(case):
 
 
 @pytest.mark.parametrize("case", [(3, 1100, 200, 128, 4, True, True), (10, 1024, 60, 64, 1, False, False),
-                                  (3, 2200, 180, 128, 4, True, True)],
-                         ids=["b3L1100H200N128G4", "b10L1024H60N64G1", "b3L2200H180N128G4"])
+                                  (3, 2200, 180, 128, 4, True, True), (6, 1100, 128, 64, 2, True, True),
+                                  (11, 1000, 100, 64, 1, False, True)],
+                         ids=["b3L1100H200N128G4", "b10L1024H60N64G1", "b3L2200H180N128G4", "b6L1100H128cut256",
+                              "b11L1000H100threerounds"])
 def test_prefill_tail_cut(case):
-    """A full round of 512 (batch, head) pairs (two workgroups per CU) and a
+    """Full rounds of 512 (batch, head) pairs (two workgroups per CU) and a
     short last round, whose pairs are cut in halves, all in one launch: the
     first halves run first and publish the state at the cut, which the second
-    halves, last in the grid, start from (first halves of 9, 8 and 17 chunks;
-    3 x 200 = 600 pairs leave 88 cut, 10 x 60 leave 88, 3 x 180 leave 28)."""
+    halves, last in the grid, start from (first halves of 9, 8, 17, 9 and 8
+    chunks; 3 x 200 = 600 pairs leave 88 cut, 10 x 60 leave 88, 3 x 180 leave
+    28, 6 x 128 leave 256, the most that is cut, and 11 x 100 = 1100 pairs, two
+    full rounds, leave 76)."""
     b, L, H, N, G, wD, wh = case
     launches, nseg, cut, _ = ssd.chunk_scan_plan(b, L, H, 64, N, G, 256, ssd.SSD_BF16)
-    assert launches == 1 and nseg == 1 and cut == b * H - 512
+    assert launches == 1 and nseg == 1 and cut == (b * H) % 512
     d = gen.ssd_inputs(b, L, H, 64, N, G, "bf16", seed=L + H, config_id=104, with_h0=wh)
     y, fs = run_scan(d, 256, "bf16", wD, wh)
     yo, fo = oracle_scan(d, wD, wh)
