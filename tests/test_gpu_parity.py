@@ -999,8 +999,10 @@ def test_config4_decode_chain_full(config2):
 # values, and in a chain such a one-unit difference persists.  So each step is
 # checked from the kernel's own cached values (every stored value within one bf16
 # unit of the oracle's rounding, y to the bar), and the independent chains are
-# compared with the bound that follows: at most one unit (2^-7 of the largest
-# magnitude) per step, and an RMS-relative difference of at most 1e-3.
+# compared element by element with the bound that follows from that: each
+# element's difference within its own rounding history (one unit of its value
+# per step), within 16 units of 2^-8·(|ref| + RMS), and an RMS-relative
+# difference of at most 1e-3 (check_bf16_chain).
 
 def bf16_units(got, ref):
     """|got - ref| in units of the bf16 spacing at |ref| (ref bf16-representable)."""
